@@ -1,0 +1,174 @@
+"""CPU oracle for the KDA gated delta-rule recurrence (numpy, fp64).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+link anything under ``oracle/``; only the test suite, the smoke check and the
+benchmark's CPU-baseline leg do.  It shares no code with the HIP path.
+
+What is computed (per sequence n and head h; S is d_k x d_v, fp64):
+
+    S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+    o_t = S_t^T q_t
+
+* The closed form and the operator order (I - beta k k^T) D, not
+  D (I - beta k k^T): "GLM-5.3-Flash Architecture Mastery" course index,
+  Course Outcomes (the closed form) and Exit Criteria (five lines expanded to
+  the closed form); Module 11 — Correctness as Architecture Mastery, §2 "The
+  full correctness matrix", KDA row (operator order); Module 12 — Capstone,
+  §1 (ordering errors diverge silently).
+* The five named operations are not printed on the pages (their Module 03 is
+  not among them).  Reading taken: decay, predict, error, write, read — the
+  plainest expansion that multiplies out to the closed form above:
+      S'  = Diag(alpha_t) S_{t-1}          decay
+      p   = S'^T k_t                       predict
+      e   = v_t - p                        error
+      S_t = S' + beta_t k_t e^T            write
+      o_t = S_t^T q_t                      read (post-update state)
+  (S' + beta k (v - S'^T k)^T = (I - beta k k^T) S' + beta k v^T.)
+* alpha_t = exp(log_alpha_t) is per key channel: D acts on the rows of S.
+* No query scale is applied (the pages show none).
+* The affine form S_{t+1} = A_{t+1} S_t + B_{t+1} and its composition
+  (A2 A1, A2 B1 + B2): Module 04 — KDA II, §1 "The recurrence has affine form".
+* Chunked execution agrees with the recurrence on outputs, final state and
+  the state at every chunk boundary: Module 04, §4 "The correctness
+  invariant".  Packed documents never share state: Module 11, §2, row
+  "Padding / packing".
+
+Inputs are taken as given (bf16 inputs arrive widened exactly to fp32) and
+computed on in fp64.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+f64 = np.float64
+
+
+# ------------------------------------------------------- one token ------
+def step(S, q, k, v, beta, log_alpha):
+    """One token of the recurrence, batched over any leading axes.
+
+    S [..., dk, dv]; q, k, log_alpha [..., dk]; v [..., dv]; beta [...].
+    Returns (S_t, o_t)."""
+    S = np.exp(log_alpha)[..., :, None] * S                 # decay
+    p = np.einsum("...kv,...k->...v", S, k)                  # predict
+    e = v - p                                                # error
+    S = S + beta[..., None, None] * k[..., :, None] * e[..., None, :]  # write
+    o = np.einsum("...kv,...k->...v", S, q)                  # read
+    return S, o
+
+
+def recurrent(q, k, v, beta, log_alpha, S0=None, snap_every=0):
+    """Token-by-token recurrence for ONE sequence.
+
+    q, k, log_alpha [T, H, dk]; v [T, H, dv]; beta [T, H]; S0 [H, dk, dv] or None.
+    Returns (o [T, H, dv], S_T [H, dk, dv], snaps) where ``snaps`` lists the
+    state entering tokens 0, c, 2c, ... (c = snap_every) if snap_every > 0."""
+    q, k, v, beta, log_alpha = (np.asarray(a, dtype=f64) for a in (q, k, v, beta, log_alpha))
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    S = np.zeros((H, dk, dv), f64) if S0 is None else np.array(S0, dtype=f64)
+    o = np.zeros((T, H, dv), f64)
+    snaps = []
+    for t in range(T):
+        if snap_every and t % snap_every == 0:
+            snaps.append(S.copy())
+        S, o[t] = step(S, q[t], k[t], v[t], beta[t], log_alpha[t])
+    return o, S, snaps
+
+
+def prefill(q, k, v, beta, log_alpha, cu_seqlens=None, initial_state=None, snap_every=0):
+    """Batched / packed driver.  Layouts as the kernels': q [B,T,H,dk] ...;
+    with ``cu_seqlens`` (B == 1) every document starts from its own state
+    (``initial_state[n]`` or zeros) and shares nothing with its neighbours.
+
+    Returns (o [B,T,H,dv] fp64, final [N,H,dk,dv] fp64, snaps) where snaps is
+    the concatenation over documents of the state entering each chunk."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if cu_seqlens is None:
+        seqs = [(b, 0, T) for b in range(B)]
+    else:
+        seqs = [(0, int(cu_seqlens[n]), int(cu_seqlens[n + 1])) for n in range(len(cu_seqlens) - 1)]
+    o = np.zeros((B, T, H, dv), f64)
+    final = np.zeros((len(seqs), H, dk, dv), f64)
+    snaps = []
+    for n, (b, t0, t1) in enumerate(seqs):
+        S0 = None if initial_state is None else initial_state[n]
+        on, Sn, sn = recurrent(q[b, t0:t1], k[b, t0:t1], v[b, t0:t1], beta[b, t0:t1],
+                               log_alpha[b, t0:t1], S0, snap_every)
+        o[b, t0:t1] = on
+        final[n] = Sn
+        snaps.extend(sn)
+    return o, final, snaps
+
+
+# -------------------------------------------- dense affine form ---------
+def transition(k, beta, log_alpha, v):
+    """Explicit dense affine step for one head and token:
+    A_t = (I - beta k k^T) Diag(alpha),  B_t = beta k v^T."""
+    k = np.asarray(k, f64)
+    dk = k.shape[0]
+    A = (np.eye(dk) - beta * np.outer(k, k)) @ np.diag(np.exp(np.asarray(log_alpha, f64)))
+    Bm = beta * np.outer(k, np.asarray(v, f64))
+    return A, Bm
+
+
+def compose(later, earlier):
+    """Affine composition: applying ``earlier`` then ``later`` equals
+    (A_l A_e, A_l B_e + B_l)."""
+    A2, B2 = later
+    A1, B1 = earlier
+    return A2 @ A1, A2 @ B1 + B2
+
+
+def recurrent_dense(q, k, v, beta, log_alpha, S0=None):
+    """One head, one sequence: S <- A_t S + B_t with dense A_t, o_t = S_t^T q_t.
+    q, k, log_alpha [T, dk]; v [T, dv]; beta [T]."""
+    T, dk = q.shape
+    dv = v.shape[-1]
+    S = np.zeros((dk, dv), f64) if S0 is None else np.array(S0, f64)
+    o = np.zeros((T, dv), f64)
+    for t in range(T):
+        A, Bm = transition(k[t], beta[t], log_alpha[t], v[t])
+        S = A @ S + Bm
+        o[t] = S.T @ np.asarray(q[t], f64)
+    return o, S
+
+
+def chunked_affine(q, k, v, beta, log_alpha, chunk, S0=None):
+    """One head: the chunked execution the pages describe, in dense form.
+
+    Each chunk's transitions are composed into one (A, B) independently of
+    the incoming state; chunks are then applied in order.  Outputs inside a
+    chunk use the prefix composition up to that token.  Dense d_k x d_k
+    matrices: tiny inputs only.  Returns (o, S_T, boundary states)."""
+    T, dk = q.shape
+    dv = v.shape[-1]
+    S = np.zeros((dk, dv), f64) if S0 is None else np.array(S0, f64)
+    o = np.zeros((T, dv), f64)
+    bounds = []
+    for c0 in range(0, T, chunk):
+        bounds.append(S.copy())
+        acc = (np.eye(dk), np.zeros((dk, dv)))
+        prefix = []
+        for t in range(c0, min(T, c0 + chunk)):
+            acc = compose(transition(k[t], beta[t], log_alpha[t], v[t]), acc)
+            prefix.append(acc)
+        for j, (A, Bm) in enumerate(prefix):
+            o[c0 + j] = (A @ S + Bm).T @ np.asarray(q[c0 + j], f64)
+        A, Bm = prefix[-1]
+        S = A @ S + Bm
+    return o, S, bounds
+
+
+# ----------------------------------------------------- the metric -------
+def rel_err(x, ref):
+    """max |x - ref| / RMS(ref).  If RMS(ref) == 0 the comparison requires
+    exact zeros: 0.0 when x is all zero, else inf."""
+    x = np.asarray(x, f64)
+    ref = np.asarray(ref, f64)
+    rms = np.sqrt(np.mean(ref * ref)) if ref.size else 0.0
+    d = np.max(np.abs(x - ref)) if ref.size else 0.0
+    if rms > 0:
+        return d / rms
+    return 0.0 if d == 0 else float("inf")

@@ -1,0 +1,283 @@
+"""Seeded synthetic inputs for the KDA gated delta-rule recurrence.
+
+This module is shared by the CPU oracle's tests and the GPU path's tests and
+benchmark.  It draws random numbers and shapes them into the inputs the
+recurrence consumes; it performs none of the recurrence's own arithmetic.
+
+Input preparation (the sublayer stages *before* the recurrence, Module 04 §3
+"The sublayer is bigger than the recurrence": Q/K normalisation, decay gate,
+write gate) is done here on the synthetic pre-activations:
+
+* k is L2-normalised per (token, head) in fp32,
+* beta = sigmoid(x),
+* log_alpha = -softplus(x)  (so alpha = exp(log_alpha) lies in (0, 1)).
+
+bf16 workloads are rounded to bf16 with round-to-nearest-even *after* these
+steps; the arrays returned here hold the rounded values widened back to fp32
+(exactly), so every consumer sees identical inputs.
+
+Layouts (row-major, contiguous):
+    q, k       [B, T, H, d_k]
+    v          [B, T, H, d_v]
+    beta       [B, T, H]
+    log_alpha  [B, T, H, d_k]
+    state      [N, H, d_k, d_v]   (N = number of sequences)
+For packed workloads B == 1 and ``cu_seqlens`` (int32, [N+1]) delimits the
+documents along T.
+
+Random stream: numpy ``Generator(PCG64(seed))``; draws are made in fp32 in
+the order q, k, v, beta_raw, gate_raw, then the initial state.  Long inputs
+are drawn in blocks of ``BLOCK_TOKENS`` tokens, each block from its own child
+of ``SeedSequence(seed)``, so host memory stays bounded and any block can be
+regenerated on its own.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+BLOCK_TOKENS = 8192
+
+
+# ---------------------------------------------------------------- bf16 -----
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 -> bf16 (round to nearest, ties to even); return uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    rounding = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + rounding) >> np.uint32(16)).astype(np.uint16)
+
+
+def bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bits to fp32 exactly."""
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """fp32 array whose values are the bf16 (RNE) roundings of ``x``."""
+    return bits_to_f32(bf16_bits(x))
+
+
+# ------------------------------------------------------- activations -------
+def _softplus(x: np.ndarray) -> np.ndarray:
+    # stable: max(x,0) + log1p(exp(-|x|))
+    return np.maximum(x, 0) + np.log1p(np.exp(-np.abs(x)))
+
+
+def _sigmoid(x: np.ndarray) -> np.ndarray:
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def _l2norm(x: np.ndarray) -> np.ndarray:
+    n = np.sqrt(np.sum(x.astype(np.float32) ** 2, axis=-1, keepdims=True))
+    return (x / np.maximum(n, np.float32(1e-12))).astype(np.float32)
+
+
+# ---------------------------------------------------------- container ------
+@dataclasses.dataclass
+class KDAInputs:
+    """One synthetic workload.  All float arrays are fp32 (bf16-exact if
+    ``dtype == 'bf16'``)."""
+
+    name: str
+    dtype: str  # 'f32' or 'bf16' : the element type handed to the kernels
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    beta: np.ndarray
+    log_alpha: np.ndarray
+    initial_state: Optional[np.ndarray]  # fp32 [N,H,dk,dv] or None (zeros)
+    cu_seqlens: Optional[np.ndarray]  # int32 [N+1] or None (B rows)
+    chunk_size: int
+
+    @property
+    def B(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def T(self) -> int:
+        return self.q.shape[1]
+
+    @property
+    def H(self) -> int:
+        return self.q.shape[2]
+
+    @property
+    def d_k(self) -> int:
+        return self.q.shape[3]
+
+    @property
+    def d_v(self) -> int:
+        return self.v.shape[3]
+
+    @property
+    def num_seqs(self) -> int:
+        return self.B if self.cu_seqlens is None else len(self.cu_seqlens) - 1
+
+    def seq_bounds(self):
+        """[(row, start, end)] of every sequence along (B, T)."""
+        if self.cu_seqlens is None:
+            return [(b, 0, self.T) for b in range(self.B)]
+        c = self.cu_seqlens
+        return [(0, int(c[n]), int(c[n + 1])) for n in range(len(c) - 1)]
+
+
+# ------------------------------------------------------------ drawing ------
+def _draw_tokens(rng, B, T, H, dk, dv, gate_mean=0.0):
+    f32 = np.float32
+    q = rng.standard_normal((B, T, H, dk), dtype=f32)
+    k = rng.standard_normal((B, T, H, dk), dtype=f32)
+    v = rng.standard_normal((B, T, H, dv), dtype=f32)
+    beta_raw = rng.standard_normal((B, T, H), dtype=f32)
+    gate_raw = rng.standard_normal((B, T, H, dk), dtype=f32)
+    if gate_mean:
+        gate_raw += f32(gate_mean)
+    k = _l2norm(k)
+    beta = _sigmoid(beta_raw).astype(f32)
+    log_alpha = (-_softplus(gate_raw)).astype(f32)
+    return q, k, v, beta, log_alpha
+
+
+def _finish(name, dtype, q, k, v, beta, log_alpha, state, cu, chunk):
+    if dtype == "bf16":
+        q, k, v, beta, log_alpha = (round_bf16(a) for a in (q, k, v, beta, log_alpha))
+    return KDAInputs(name, dtype, q, k, v, beta, log_alpha, state, cu, chunk)
+
+
+def make_uniform(seed: int, B: int, T: int, H: int, dk: int, dv: int, dtype: str,
+                 chunk: int = 64, state_std: float = 0.0, gate_mean: float = 0.0,
+                 name: str = "custom") -> KDAInputs:
+    """B independent rows of T tokens, typical gates; optional N(0, std^2) state."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q, k, v, beta, la = _draw_tokens(rng, B, T, H, dk, dv, gate_mean)
+    state = None
+    if state_std:
+        state = (rng.standard_normal((B, H, dk, dv), dtype=np.float32) * np.float32(state_std))
+    return _finish(name, dtype, q, k, v, beta, la, state, None, chunk)
+
+
+def make_packed(seed: int, lengths, H: int, dk: int, dv: int, dtype: str, chunk: int = 64,
+                state_std: float = 0.02, name: str = "packed") -> KDAInputs:
+    """Documents of the given lengths concatenated along T (B == 1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    T = int(np.sum(lengths))
+    q, k, v, beta, la = _draw_tokens(rng, 1, T, H, dk, dv)
+    n = len(lengths)
+    state = None
+    if state_std:
+        state = rng.standard_normal((n, H, dk, dv), dtype=np.float32) * np.float32(state_std)
+    cu = np.zeros(n + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))
+    return _finish(name, dtype, q, k, v, beta, la, state, cu, chunk)
+
+
+def _extreme_block(rng, T, H, dk):
+    """Per token: Bernoulli(0.1) selects the token (all heads); selected
+    tokens get log_alpha ~ U[-20, -10] per (head, channel) and beta drawn
+    from {1e-4, 1 - 1e-4} with probability 1/2 each per (token, head)."""
+    sel = rng.random(T) < 0.1
+    la = rng.uniform(-20.0, -10.0, size=(T, H, dk)).astype(np.float32)
+    bsel = rng.random((T, H)) < 0.5
+    b = np.where(bsel, np.float32(1e-4), np.float32(1.0 - 1e-4)).astype(np.float32)
+    return sel, la, b
+
+
+def make_long(seed: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16",
+              chunk: int = 64, extreme: bool = True, name: str = "long") -> KDAInputs:
+    """One long row drawn in BLOCK_TOKENS blocks (child seeds), with the
+    extreme-gate stress pattern when ``extreme``."""
+    f32 = np.float32
+    shape_k = (1, T, H, dk)
+    q = np.empty(shape_k, f32)
+    k = np.empty(shape_k, f32)
+    v = np.empty((1, T, H, dv), f32)
+    beta = np.empty((1, T, H), f32)
+    la = np.empty(shape_k, f32)
+    nblk = (T + BLOCK_TOKENS - 1) // BLOCK_TOKENS
+    children = np.random.SeedSequence(seed).spawn(nblk)
+    for i, ss in enumerate(children):
+        t0, t1 = i * BLOCK_TOKENS, min(T, (i + 1) * BLOCK_TOKENS)
+        rng = np.random.Generator(np.random.PCG64(ss))
+        bq, bk, bv, bb, bla = _draw_tokens(rng, 1, t1 - t0, H, dk, dv)
+        if extreme:
+            sel, xla, xb = _extreme_block(rng, t1 - t0, H, dk)
+            bla[0, sel] = xla[sel]
+            bb[0, sel] = xb[sel]
+        if dtype == "bf16":
+            bq, bk, bv, bb, bla = (round_bf16(a) for a in (bq, bk, bv, bb, bla))
+        q[:, t0:t1], k[:, t0:t1], v[:, t0:t1] = bq, bk, bv
+        beta[:, t0:t1], la[:, t0:t1] = bb, bla
+    return KDAInputs(name, dtype, q, k, v, beta, la, None, None, chunk)
+
+
+# -------------------------------------------------- the five workloads ----
+C4_DOCS = 8
+
+
+def c4_lengths(seed: int = 4):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.integers(512, 8193, size=C4_DOCS).tolist()
+
+
+def workload(idx: int, **over) -> KDAInputs:
+    """The five named workloads (seed = workload index):
+
+    1  tiny fp32: B=1 H=1 T=64 d=16, chunk 16, zero state
+    2  prefill:   B=1 H=16 T=4096 d=128 bf16, chunk 64, zero state
+    3  decode:    see :func:`decode_workload`
+    4  packed:    8 docs, lengths U[512, 8192], H=32 d=128 bf16, chunk 64,
+                  per-document N(0, 0.02^2) state
+    5  long:      B=1 H=32 T=131072 d=128 bf16, chunk 64, 10% extreme gates
+    """
+    if idx == 1:
+        return make_uniform(1, 1, 64, 1, 16, 16, "f32", chunk=16, name="tiny_f32_T64_d16")
+    if idx == 2:
+        return make_uniform(2, 1, over.get("T", 4096), over.get("H", 16), 128, 128, "bf16",
+                            chunk=64, name="prefill_T4096_H16_d128")
+    if idx == 4:
+        lens = over.get("lengths", c4_lengths(4))
+        return make_packed(4, lens, over.get("H", 32), 128, 128, "bf16", chunk=64,
+                           name="packed_8docs_H32_d128")
+    if idx == 5:
+        return make_long(5, over.get("T", 131072), over.get("H", 32), 128, 128, "bf16",
+                         chunk=64, name="long_T131072_H32_d128_extreme")
+    raise ValueError(f"workload {idx}: use decode_workload() for 3")
+
+
+@dataclasses.dataclass
+class DecodeInputs:
+    """``steps`` single-token steps for B sequences (q,k,v,beta,log_alpha have a
+    leading step axis: [steps, B, H, d] / [steps, B, H])."""
+
+    name: str
+    dtype: str
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    beta: np.ndarray
+    log_alpha: np.ndarray
+    initial_state: np.ndarray  # fp32 [B,H,dk,dv]
+
+
+def decode_workload(B: int = 256, H: int = 32, dk: int = 128, dv: int = 128,
+                    steps: int = 64, seed: int = 3, dtype: str = "bf16",
+                    state_std: float = 0.02, name: str = "decode_B256_H32_d128") -> DecodeInputs:
+    """Workload 3: per step fresh q,k,v,beta,alpha (as in workload 1, rounded
+    to bf16); initial state N(0, 0.02^2) fp32, drawn after the token inputs."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    # steps play the role of T with one token per sequence: [steps, B, H, d]
+    q, k, v, beta, la = _draw_tokens(rng, steps, B, H, dk, dv)
+    state = rng.standard_normal((B, H, dk, dv), dtype=np.float32) * np.float32(state_std)
+    if dtype == "bf16":
+        q, k, v, beta, la = (round_bf16(a) for a in (q, k, v, beta, la))
+    return DecodeInputs(name, dtype, q, k, v, beta, la, state)
+
+
+def slow_decay(seed: int, B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16",
+               chunk: int = 64, state_std: float = 0.02) -> KDAInputs:
+    """Supplementary case: log_alpha = -softplus(N(-5, 1)) (alpha ~ 0.99), so
+    state carried across chunk boundaries dominates the outputs."""
+    return make_uniform(seed, B, T, H, dk, dv, dtype, chunk=chunk, state_std=state_std,
+                        gate_mean=-5.0, name="slow_decay")
