@@ -1,0 +1,241 @@
+"""KDA gated delta-rule recurrence on AMD Instinct MI355X (gfx950).
+
+Thin Python binding over ``libkda.so`` (C ABI in ``include/kda.h``): it only
+marshals torch tensors into pointers and sizes, allocates outputs and the
+workspace with torch, and passes torch's current HIP stream.  Every step of
+the computation runs in the library's HIP kernels; there is no CPU fallback —
+if the library is missing or the tensors are not on the GPU these functions
+raise.
+
+    o, S = prefill(q, k, v, beta, log_alpha, initial_state=None,
+                   cu_seqlens=None, chunk_size=64)
+    o = decode_step(q, k, v, beta, log_alpha, state)     # state updated in place
+
+The recurrence (per sequence and head, S is d_k x d_v fp32):
+    S_t = (I - beta_t k_t k_t^T) Diag(exp(log_alpha_t)) S_{t-1} + beta_t k_t v_t^T
+    o_t = S_t^T q_t
+("GLM-5.3-Flash Architecture Mastery", course index, Course Outcomes;
+Module 04 — KDA II, §2: prefill and decode are separate kernel families.)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["prefill", "decode_step", "workspace_bytes", "max_chunks", "lib", "KDAError",
+           "PrefillArgs", "KDA_F32", "KDA_BF16"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+_STATUS_BAD_SEQLENS = 6
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({_status_string(status)})")
+
+
+class PrefillArgs(ctypes.Structure):
+    """Mirror of ``kda_prefill_args`` (include/kda.h)."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+        ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+        ("chunk_size", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("beta", ctypes.c_void_p), ("log_alpha", ctypes.c_void_p),
+        ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_host", ctypes.c_void_p),
+        ("initial_state", ctypes.c_void_p), ("final_state", ctypes.c_void_p),
+        ("chunk_states", ctypes.c_void_p), ("o", ctypes.c_void_p),
+        ("device_status", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded ``libkda.so`` with argument types declared."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                               "(or gated_delta_rule_49_amd/build.py) first")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32 = ctypes.c_void_p, ctypes.c_int32
+        AP = ctypes.POINTER(PrefillArgs)
+        L.kda_prefill_workspace_bytes.argtypes = [AP]
+        L.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
+        L.kda_prefill_max_chunks.argtypes = [AP]
+        L.kda_prefill_max_chunks.restype = ctypes.c_int64
+        L.kda_prefill_chunked.argtypes = [AP, P]
+        L.kda_prefill_chunked.restype = I32
+        L.kda_decode_step.argtypes = [I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P]
+        L.kda_decode_step.restype = I32
+        L.kda_status_string.argtypes = [I32]
+        L.kda_status_string.restype = ctypes.c_char_p
+        L.kda_abi_version.restype = I32
+        _lib = L
+    return _lib
+
+
+def _status_string(s: int) -> str:
+    try:
+        return lib().kda_status_string(int(s)).decode()
+    except Exception:  # pragma: no cover
+        return "?"
+
+
+def _dt(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return KDA_F32
+    if t == torch.bfloat16:
+        return KDA_BF16
+    raise TypeError(f"unsupported dtype {t} (float32 or bfloat16)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU (no CPU path exists)")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensors are on different devices")
+    return dev
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _make_args(q, k, v, beta, log_alpha, cu_seqlens, chunk_size, out_dtype, cu_host=None):
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    a = PrefillArgs()
+    a.B, a.T, a.H, a.d_k, a.d_v = B, T, H, dk, dv
+    a.num_seqs = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    a.chunk_size = chunk_size
+    a.in_dtype = _dt(q.dtype)
+    a.out_dtype = _dt(out_dtype)
+    a.q, a.k, a.v, a.beta, a.log_alpha = (_ptr(x) for x in (q, k, v, beta, log_alpha))
+    a.cu_seqlens = _ptr(cu_seqlens)
+    if cu_host is not None:
+        a.cu_seqlens_host = cu_host.ctypes.data_as(ctypes.c_void_p)
+    return a
+
+
+def workspace_bytes(q, k, v, beta, log_alpha, cu_seqlens=None, chunk_size=64,
+                    out_dtype=torch.float32) -> int:
+    return int(lib().kda_prefill_workspace_bytes(
+        ctypes.byref(_make_args(q, k, v, beta, log_alpha, cu_seqlens, chunk_size, out_dtype))))
+
+
+def max_chunks(q, k, v, beta, log_alpha, cu_seqlens=None, chunk_size=64) -> int:
+    return int(lib().kda_prefill_max_chunks(
+        ctypes.byref(_make_args(q, k, v, beta, log_alpha, cu_seqlens, chunk_size, torch.float32))))
+
+
+def prefill(q, k, v, beta, log_alpha, initial_state=None, output_final_state=True,
+            cu_seqlens=None, chunk_size=64, out_dtype=torch.float32, chunk_states=False,
+            workspace=None, final_state=None, o=None, check_seqlens=False):
+    """Chunked prefill.
+
+    q, k, log_alpha [B,T,H,d_k]; v [B,T,H,d_v]; beta [B,T,H]; all float32 or
+    all bfloat16 on one GPU.  ``cu_seqlens`` (int32 [N+1], B == 1) packs N
+    documents along T.  ``initial_state`` fp32 [N,H,d_k,d_v] or None (zeros).
+    Returns (o, final_state or None) or, with ``chunk_states=True``,
+    (o, final_state, chunk_states) where chunk_states[c] is the state entering
+    global chunk c (documents in order).  ``check_seqlens`` additionally
+    validates cu_seqlens on the host (one device-to-host copy) and raises on a
+    device-side rejection (one synchronisation)."""
+    dev = _check_dev(q, k, v, beta, log_alpha, initial_state, cu_seqlens, workspace, final_state, o)
+    if not (q.dtype == k.dtype == v.dtype == beta.dtype == log_alpha.dtype):
+        raise TypeError("q, k, v, beta, log_alpha must share one dtype")
+    if q.dim() != 4 or k.shape != q.shape or log_alpha.shape != q.shape:
+        raise ValueError("q, k, log_alpha must be [B,T,H,d_k]")
+    B, T, H, dk = q.shape
+    if v.dim() != 4 or v.shape[:3] != q.shape[:3] or beta.shape != q.shape[:3]:
+        raise ValueError("v must be [B,T,H,d_v] and beta [B,T,H]")
+    dv = v.shape[-1]
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if initial_state is not None:
+        if initial_state.dtype != torch.float32 or tuple(initial_state.shape) != (N, H, dk, dv):
+            raise ValueError(f"initial_state must be float32 [{N},{H},{dk},{dv}]")
+    cu_host = None
+    if cu_seqlens is not None and check_seqlens:
+        cu_host = cu_seqlens.cpu().numpy()
+    a = _make_args(q, k, v, beta, log_alpha, cu_seqlens, chunk_size, out_dtype, cu_host)
+    L = lib()
+    need = int(L.kda_prefill_workspace_bytes(ctypes.byref(a)))
+    if need == 0:
+        st = L.kda_prefill_chunked(ctypes.byref(a), None)  # reports why
+        raise KDAError(st, "kda_prefill_chunked")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    cs = None
+    if chunk_states:
+        nmax = int(L.kda_prefill_max_chunks(ctypes.byref(a)))
+        cs = torch.zeros((nmax, H, dk, dv), dtype=torch.float32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev) if check_seqlens else None
+    a.o = _ptr(o)
+    a.initial_state = _ptr(initial_state)
+    a.final_state = _ptr(final_state)
+    a.chunk_states = _ptr(cs)
+    a.device_status = _ptr(status)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    st = L.kda_prefill_chunked(ctypes.byref(a), _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_prefill_chunked")
+    if status is not None and int(status.item()) != 0:
+        raise KDAError(int(status.item()), "kda_prefill_chunked (device check)")
+    if chunk_states:
+        if cu_seqlens is None:
+            nch = B * ((T + chunk_size - 1) // chunk_size)
+        else:
+            lens = (cu_seqlens[1:] - cu_seqlens[:-1]).cpu()
+            nch = int(((lens + chunk_size - 1) // chunk_size).sum())
+        return o, final_state, cs[:nch]
+    return o, final_state
+
+
+def decode_step(q, k, v, beta, log_alpha, state, out_dtype=torch.float32, o=None):
+    """One fused decode step: q, k, log_alpha [B,H,d_k]; v [B,H,d_v];
+    beta [B,H]; state fp32 [B,H,d_k,d_v] updated in place.  Returns o [B,H,d_v]."""
+    dev = _check_dev(q, k, v, beta, log_alpha, state, o)
+    if not (q.dtype == k.dtype == v.dtype == beta.dtype == log_alpha.dtype):
+        raise TypeError("q, k, v, beta, log_alpha must share one dtype")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape[:2] != (B, H) or beta.shape != (B, H):
+        raise ValueError("shape mismatch")
+    if state.dtype != torch.float32 or tuple(state.shape) != (B, H, dk, dv):
+        raise ValueError(f"state must be float32 [{B},{H},{dk},{dv}]")
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=out_dtype, device=dev)
+    st = lib().kda_decode_step(B, H, dk, dv, _dt(q.dtype), _dt(o.dtype), _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(beta), _ptr(log_alpha), _ptr(state), _ptr(o), _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_decode_step")
+    return o

@@ -1,0 +1,140 @@
+// C ABI of libkda (declared in include/kda.h): host-side validation,
+// workspace sizing and dispatch.  No kernel is launched before every
+// argument has been checked; nothing here allocates or synchronises.
+#include "../../include/kda.h"
+#include "kda_launch.hpp"
+
+using namespace kda;
+
+namespace {
+
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
+bool dtype_ok(int t) { return t == KDA_F32 || t == KDA_BF16; }
+
+// shape / dtype / pointer checks that do not need the workspace
+kda_status check_prefill(const kda_prefill_args *a) {
+    if (!a) return KDA_ERR_NULL_ARG;
+    if (a->B < 1 || a->T < 0 || a->H < 1 || a->num_seqs < 0) return KDA_ERR_BAD_SHAPE;
+    if (!dim_ok(a->d_k) || !dim_ok(a->d_v) || !chunk_ok(a->chunk_size)) {
+        // sizes that are positive but not implemented are "unsupported"
+        if (a->d_k < 1 || a->d_v < 1 || a->chunk_size < 1) return KDA_ERR_BAD_SHAPE;
+        return KDA_ERR_UNSUPPORTED;
+    }
+    if (!dtype_ok(a->in_dtype) || !dtype_ok(a->out_dtype)) return KDA_ERR_UNSUPPORTED;
+    if (a->cu_seqlens) {
+        if (a->B != 1 || a->num_seqs < 1) return KDA_ERR_BAD_SHAPE;
+    } else if (a->num_seqs != a->B) {
+        return KDA_ERR_BAD_SHAPE;
+    }
+    if (a->cu_seqlens_host && !a->cu_seqlens) return KDA_ERR_BAD_SHAPE;
+    // element counts must fit the kernels' 32-bit token indexing
+    const int64_t tokens = static_cast<int64_t>(a->B) * a->T;
+    if (tokens * a->H > (static_cast<int64_t>(1) << 31)) return KDA_ERR_UNSUPPORTED;
+    const bool any_tokens = tokens > 0;
+    if (any_tokens && (!a->q || !a->k || !a->v || !a->beta || !a->log_alpha || !a->o))
+        return KDA_ERR_NULL_ARG;
+    if (a->cu_seqlens_host) {
+        const int32_t *c = a->cu_seqlens_host;
+        if (c[0] != 0 || c[a->num_seqs] != a->T) return KDA_ERR_BAD_SEQLENS;
+        for (int n = 0; n < a->num_seqs; ++n)
+            if (c[n + 1] < c[n]) return KDA_ERR_BAD_SEQLENS;
+    }
+    return KDA_OK;
+}
+
+int64_t max_chunks(const kda_prefill_args *a) {
+    const int64_t per_row = (static_cast<int64_t>(a->T) + a->chunk_size - 1) / a->chunk_size;
+    return a->cu_seqlens ? per_row + a->num_seqs : per_row * a->B;
+}
+
+bool use_mfma(const kda_prefill_args *a) {
+    return a->in_dtype == KDA_BF16 && mfma_supported(a->d_k, a->d_v, a->chunk_size);
+}
+
+size_t workspace_for(const kda_prefill_args *a) {
+    size_t bytes = table_bytes(a->num_seqs);
+    if (use_mfma(a))
+        bytes += static_cast<size_t>(max_chunks(a)) * a->H * mfma_block_bytes(a->chunk_size, a->d_k);
+    return bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char *kda_status_string(int32_t s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_NULL_ARG: return "a required pointer is NULL";
+        case KDA_ERR_BAD_SHAPE: return "sizes are inconsistent or out of range";
+        case KDA_ERR_UNSUPPORTED: return "valid but unsupported size or dtype";
+        case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case KDA_ERR_HIP: return "HIP launch failed";
+        case KDA_ERR_BAD_SEQLENS: return "cu_seqlens malformed";
+        default: return "unknown status";
+    }
+}
+
+int64_t kda_prefill_max_chunks(const kda_prefill_args *a) {
+    if (check_prefill(a) != KDA_OK) return 0;
+    return max_chunks(a);
+}
+
+size_t kda_prefill_workspace_bytes(const kda_prefill_args *a) {
+    if (check_prefill(a) != KDA_OK) return 0;
+    return workspace_for(a);
+}
+
+kda_status kda_prefill_chunked(const kda_prefill_args *a, void *hip_stream) {
+    kda_status st = check_prefill(a);
+    if (st != KDA_OK) return st;
+    if (!a->workspace) return KDA_ERR_NULL_ARG;
+    if (reinterpret_cast<uintptr_t>(a->workspace) % kAlign) return KDA_ERR_BAD_SHAPE;
+    if (a->workspace_bytes < workspace_for(a)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+
+    char *ws = static_cast<char *>(a->workspace);
+    PrefillParams p{};
+    p.q = a->q; p.k = a->k; p.v = a->v; p.beta = a->beta; p.log_alpha = a->log_alpha;
+    p.o = a->o;
+    p.initial_state = a->initial_state;
+    p.final_state = a->final_state;
+    p.chunk_states = a->chunk_states;
+    p.cu_seqlens = a->cu_seqlens;
+    p.status = reinterpret_cast<int32_t *>(ws);
+    p.chunk_off = reinterpret_cast<int32_t *>(ws + kAlign);
+    p.user_status = a->device_status;
+    p.B = a->B; p.T = a->T; p.H = a->H; p.dk = a->d_k; p.dv = a->d_v;
+    p.N = a->num_seqs; p.C = a->chunk_size;
+    p.n_chunks_bound = static_cast<int32_t>(max_chunks(a));
+
+    if (p.N == 0) return KDA_OK;
+    hipError_t e = launch_chunk_table(p, s);
+    if (e == hipSuccess) {
+        if (use_mfma(a))
+            e = launch_prefill_mfma(p, ws + table_bytes(p.N), a->out_dtype, s);
+        else
+            e = launch_prefill_f32(p, a->in_dtype, a->out_dtype, s);
+    }
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_decode_step(int32_t B, int32_t H, int32_t d_k, int32_t d_v, int32_t in_dtype,
+                           int32_t out_dtype, const void *q, const void *k, const void *v,
+                           const void *beta, const void *log_alpha, float *state, void *o,
+                           void *hip_stream) {
+    if (B < 0 || H < 1) return KDA_ERR_BAD_SHAPE;
+    if (!dim_ok(d_k) || !dim_ok(d_v)) return (d_k < 1 || d_v < 1) ? KDA_ERR_BAD_SHAPE : KDA_ERR_UNSUPPORTED;
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(B) * H > (static_cast<int64_t>(1) << 31) - 1) return KDA_ERR_UNSUPPORTED;
+    if (B == 0) return KDA_OK;
+    if (!q || !k || !v || !beta || !log_alpha || !state || !o) return KDA_ERR_NULL_ARG;
+    hipError_t e = launch_decode(B, H, d_k, d_v, in_dtype, out_dtype, q, k, v, beta, log_alpha, state, o,
+                                 static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,28 @@
+// Internal host-side launch interface between the C ABI (kda_api.hip) and
+// the kernel translation units.  Arguments are already validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include "kda_prefill_common.hpp"
+
+namespace kda {
+
+// Workspace layout (byte offsets from the workspace base, 256-aligned):
+//   [0, 256)            status word (int32) + padding
+//   [256, 256 + 4(N+1)) chunk_off table, rounded up to 256
+//   then, matrix-core path only, the per-(chunk, head) intermediate blocks.
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline size_t table_bytes(int N) { return kAlign + align_up(sizeof(int32_t) * (static_cast<size_t>(N) + 1)); }
+
+// matrix-core path: bytes of intermediates per (chunk, head)
+size_t mfma_block_bytes(int C, int D);
+bool mfma_supported(int dk, int dv, int C);
+
+hipError_t launch_chunk_table(const PrefillParams &p, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillParams &p, int in_dtype, int out_dtype, hipStream_t s);
+hipError_t launch_prefill_mfma(const PrefillParams &p, void *blocks, int out_dtype, hipStream_t s);
+hipError_t launch_decode(int B, int H, int dk, int dv, int in_dtype, int out_dtype, const void *q,
+                         const void *k, const void *v, const void *beta, const void *log_alpha,
+                         float *state, void *o, hipStream_t s);
+
+}  // namespace kda

@@ -1,0 +1,230 @@
+// Chunked KDA prefill computed entirely in fp32 on the vector ALUs.
+//
+// This is the path for fp32 inputs (the 1e-5 contract needs true fp32
+// arithmetic end to end) and for head sizes the matrix-core path does not
+// cover.  It follows the same chunk decomposition as the matrix-core path:
+// Module 04 — KDA II, §1 "The recurrence has affine form": each chunk's
+// composed transition is independent of the incoming state and is kept in
+// structured form (diagonal decay plus a rank-L correction), never as a dense
+// d_k x d_k matrix.  For a chunk of L tokens with incoming state S, per-channel
+// cumulative log-decay G_r = sum_{i<=r} log_alpha_i and
+//     A_ri = beta_r sum_c k_r[c] k_i[c] exp(G_r[c] - G_i[c])   (i < r)
+//     P_ri =        sum_c q_r[c] k_i[c] exp(G_r[c] - G_i[c])   (i <= r)
+//     T    = (I + A)^-1 Diag(beta)
+//     Delta = T (V - (k * exp(G)) S)          rows are the per-token errors
+//     O     = (q * exp(G)) S + P Delta
+//     S'    = Diag(exp(G_L)) S + (k * exp(G_L - G))^T Delta
+// All exponents are <= 0 (pairs i <= r), so nothing overflows.
+//
+// One workgroup per (sequence, head, BV-column tile of the state): the
+// columns of S evolve independently.  Everything a chunk needs sits in LDS.
+#include "kda_launch.hpp"
+
+namespace kda {
+
+constexpr int F32_THREADS = 256;
+constexpr int F32_BV = 16;
+
+__host__ __device__ inline size_t f32_lds_floats(int C, int dk) {
+    return static_cast<size_t>(C) * dk      // G (base-2 scaled)
+           + static_cast<size_t>(C) * C     // A, then T, then P
+           + static_cast<size_t>(dk) * F32_BV  // S tile
+           + static_cast<size_t>(C) * F32_BV   // X, then Delta
+           + C;                                // beta
+}
+
+template <typename TI, typename TO>
+__global__ void __launch_bounds__(F32_THREADS) prefill_f32_kernel(PrefillParams p) {
+    if (*p.status != 0) return;
+    extern __shared__ float lds[];
+    const int C = p.C, dk = p.dk, dv = p.dv, H = p.H;
+    const int nvt = dv / F32_BV;
+    const int vt = blockIdx.x % nvt;
+    const int h = (blockIdx.x / nvt) % H;
+    const int n = blockIdx.x / (nvt * H);
+    const int v0 = vt * F32_BV;
+    const int tid = threadIdx.x;
+
+    float *G = lds;                 // [C][dk]
+    float *AT = G + C * dk;         // [C][C]
+    float *S = AT + C * C;          // [dk][BV]
+    float *X = S + dk * F32_BV;     // [C][BV]
+    float *bet = X + C * F32_BV;    // [C]
+
+    const TI *q = static_cast<const TI *>(p.q);
+    const TI *k = static_cast<const TI *>(p.k);
+    const TI *v = static_cast<const TI *>(p.v);
+    const TI *beta = static_cast<const TI *>(p.beta);
+    const TI *la = static_cast<const TI *>(p.log_alpha);
+    TO *o = static_cast<TO *>(p.o);
+
+    const SeqRange sr = seq_range(p, n);
+    const int64_t state_off = (static_cast<int64_t>(n) * H + h) * dk * dv;
+    for (int e = tid; e < dk * F32_BV; e += F32_THREADS) {
+        const int c = e / F32_BV, j = e % F32_BV;
+        S[e] = p.initial_state ? p.initial_state[state_off + static_cast<int64_t>(c) * dv + v0 + j] : 0.f;
+    }
+    const int nch = (sr.len + C - 1) / C;
+    const int64_t cbase = p.chunk_off[n];
+    __syncthreads();
+
+    for (int ch = 0; ch < nch; ++ch) {
+        const int64_t t0 = sr.start + static_cast<int64_t>(ch) * C;
+        const int L = min(C, sr.len - ch * C);
+        // token t, head h -> row offsets
+        auto kv = [&](int64_t t) { return (t * H + h); };
+
+        if (p.chunk_states) {
+            float *cs = p.chunk_states + ((cbase + ch) * H + h) * static_cast<int64_t>(dk) * dv;
+            for (int e = tid; e < dk * F32_BV; e += F32_THREADS) {
+                const int c = e / F32_BV, j = e % F32_BV;
+                cs[static_cast<int64_t>(c) * dv + v0 + j] = S[e];
+            }
+        }
+        // 1. cumulative log-decay (base 2), beta; padded rows decay by 1
+        for (int c = tid; c < dk; c += F32_THREADS) {
+            float acc = 0.f;
+            for (int r = 0; r < C; ++r) {
+                if (r < L) acc += io<TI>::ld(la, kv(t0 + r) * dk + c) * kLog2e;
+                G[r * dk + c] = acc;
+            }
+        }
+        for (int r = tid; r < C; r += F32_THREADS) bet[r] = r < L ? io<TI>::ld(beta, kv(t0 + r)) : 0.f;
+        __syncthreads();
+
+        // 2. A (strictly lower, rows scaled by beta)
+        for (int e = tid; e < C * C; e += F32_THREADS) {
+            const int r = e / C, i = e % C;
+            float acc = 0.f;
+            if (i < r && r < L) {
+                const int64_t kr = kv(t0 + r) * dk, ki = kv(t0 + i) * dk;
+                for (int c = 0; c < dk; ++c)
+                    acc += io<TI>::ld(k, kr + c) * io<TI>::ld(k, ki + c) * exp2f(G[r * dk + c] - G[i * dk + c]);
+                acc *= bet[r];
+            }
+            AT[e] = acc;
+        }
+        __syncthreads();
+
+        // 3. T = (I + A)^-1 Diag(beta), row by row, overwriting A in place:
+        //    T[r, :] = beta_r e_r - sum_{i<r} A[r, i] T[i, :]
+        for (int r = 0; r < C; ++r) {
+            float val = 0.f;
+            const int j = tid;
+            if (j < C) {
+                val = (j == r) ? bet[r] : 0.f;
+                for (int i = j; i < r; ++i) val -= AT[r * C + i] * AT[i * C + j];
+            }
+            __syncthreads();
+            if (j < C) AT[r * C + j] = (j <= r) ? val : 0.f;
+            __syncthreads();
+        }
+
+        // 4. X = V - (k * exp(G)) S
+        for (int e = tid; e < C * F32_BV; e += F32_THREADS) {
+            const int r = e / F32_BV, j = e % F32_BV;
+            float acc = 0.f;
+            if (r < L) {
+                const int64_t kr = kv(t0 + r) * dk;
+                for (int c = 0; c < dk; ++c) acc += io<TI>::ld(k, kr + c) * exp2f(G[r * dk + c]) * S[c * F32_BV + j];
+                acc = io<TI>::ld(v, kv(t0 + r) * dv + v0 + j) - acc;
+            }
+            X[e] = acc;
+        }
+        __syncthreads();
+        // 5. Delta = T X (in place through registers)
+        float dreg[(64 * F32_BV + F32_THREADS - 1) / F32_THREADS];
+        {
+            int idx = 0;
+            for (int e = tid; e < C * F32_BV; e += F32_THREADS, ++idx) {
+                const int r = e / F32_BV, j = e % F32_BV;
+                float acc = 0.f;
+                for (int i = 0; i <= r; ++i) acc += AT[r * C + i] * X[i * F32_BV + j];
+                dreg[idx] = acc;
+            }
+        }
+        __syncthreads();
+        {
+            int idx = 0;
+            for (int e = tid; e < C * F32_BV; e += F32_THREADS, ++idx) X[e] = dreg[idx];
+        }
+        __syncthreads();
+
+        // 6. P (inclusive lower) into the A/T buffer
+        for (int e = tid; e < C * C; e += F32_THREADS) {
+            const int r = e / C, i = e % C;
+            float acc = 0.f;
+            if (i <= r && r < L) {
+                const int64_t qr = kv(t0 + r) * dk, ki = kv(t0 + i) * dk;
+                for (int c = 0; c < dk; ++c)
+                    acc += io<TI>::ld(q, qr + c) * io<TI>::ld(k, ki + c) * exp2f(G[r * dk + c] - G[i * dk + c]);
+            }
+            AT[e] = acc;
+        }
+        __syncthreads();
+
+        // 7. O = (q * exp(G)) S + P Delta
+        for (int e = tid; e < C * F32_BV; e += F32_THREADS) {
+            const int r = e / F32_BV, j = e % F32_BV;
+            if (r < L) {
+                const int64_t qr = kv(t0 + r) * dk;
+                float acc = 0.f;
+                for (int c = 0; c < dk; ++c) acc += io<TI>::ld(q, qr + c) * exp2f(G[r * dk + c]) * S[c * F32_BV + j];
+                for (int i = 0; i <= r; ++i) acc += AT[r * C + i] * X[i * F32_BV + j];
+                io<TO>::st(o, kv(t0 + r) * dv + v0 + j, acc);
+            }
+        }
+        // 8. S' = Diag(exp(G_L)) S + (k * exp(G_L - G))^T Delta
+        float sreg[(128 * F32_BV + F32_THREADS - 1) / F32_THREADS];
+        {
+            int idx = 0;
+            for (int e = tid; e < dk * F32_BV; e += F32_THREADS, ++idx) {
+                const int c = e / F32_BV, j = e % F32_BV;
+                const float gl = G[(C - 1) * dk + c];
+                float acc = exp2f(gl) * S[e];
+                for (int r = 0; r < L; ++r)
+                    acc += io<TI>::ld(k, kv(t0 + r) * dk + c) * exp2f(gl - G[r * dk + c]) * X[r * F32_BV + j];
+                sreg[idx] = acc;
+            }
+        }
+        __syncthreads();
+        {
+            int idx = 0;
+            for (int e = tid; e < dk * F32_BV; e += F32_THREADS, ++idx) S[e] = sreg[idx];
+        }
+        __syncthreads();
+    }
+    if (p.final_state) {
+        for (int e = tid; e < dk * F32_BV; e += F32_THREADS) {
+            const int c = e / F32_BV, j = e % F32_BV;
+            p.final_state[state_off + static_cast<int64_t>(c) * dv + v0 + j] = S[e];
+        }
+    }
+}
+
+}  // namespace kda
+
+namespace kda {
+
+namespace {
+template <typename TI, typename TO>
+hipError_t run_f32(const PrefillParams &p, hipStream_t s) {
+    const size_t lds = f32_lds_floats(p.C, p.dk) * sizeof(float);
+    auto kern = prefill_f32_kernel<TI, TO>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    const unsigned grid = static_cast<unsigned>(p.N) * p.H * (p.dv / F32_BV);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(F32_THREADS), lds, s, p);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_prefill_f32(const PrefillParams &p, int in_dtype, int out_dtype, hipStream_t s) {
+    if (in_dtype == 0 && out_dtype == 0) return run_f32<float, float>(p, s);
+    if (in_dtype == 0 && out_dtype == 1) return run_f32<float, bf16_t>(p, s);
+    if (in_dtype == 1 && out_dtype == 0) return run_f32<bf16_t, float>(p, s);
+    return run_f32<bf16_t, bf16_t>(p, s);
+}
+
+}  // namespace kda

@@ -1,0 +1,156 @@
+/*
+ * kda.h — C ABI of libkda: the KDA gated delta-rule recurrence on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (per sequence n and head h; S is d_k x d_v, fp32):
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t ,          alpha_t = exp(log_alpha_t) in (0, 1]^{d_k}
+ *
+ * Closed form and operator order: "GLM-5.3-Flash Architecture Mastery",
+ * course index, Course Outcomes; Module 11 — Correctness as Architecture
+ * Mastery, §2 "The full correctness matrix", KDA row.  Two entry points, one
+ * per request phase (Module 04 — KDA II: Chunked Parallelism & the Full
+ * Sublayer, §2 "Why decode and prefill need different kernels"):
+ *
+ *   kda_prefill_chunked  many tokens per sequence; chunk-parallel: every
+ *                        chunk's composed transition is built independently
+ *                        in structured (diagonal + low-rank) form, then the
+ *                        chunks are applied in order (Module 04, §1 "The
+ *                        recurrence has affine form").
+ *   kda_decode_step      one token per sequence, fused recurrent step, the
+ *                        state updated in place.
+ *
+ * Conventions common to all entry points
+ *   - Pointers marked DEVICE are device memory owned by the caller; the
+ *     library never allocates, frees or synchronises.  Scratch memory for
+ *     prefill is a caller-provided workspace sized by
+ *     kda_prefill_workspace_bytes().
+ *   - Tensors are contiguous, row-major, with the layouts given below.
+ *   - Every argument is validated on the host before the first launch; on an
+ *     error nothing is launched and nothing is written.  After the launches
+ *     a launch failure maps to KDA_ERR_HIP.  Execution is asynchronous on
+ *     the given stream (a hipStream_t passed as void*; NULL = default).
+ *   - No query scale is applied: callers pre-scale q.
+ *   - log_alpha must be <= 0 and all inputs finite; other values are not
+ *     checked and propagate (NaN in, NaN out).
+ *   - The library holds no mutable global state: concurrent calls on
+ *     different streams with disjoint outputs and workspaces are safe.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL_ARG = 1,           /* a required pointer is NULL                 */
+    KDA_ERR_BAD_SHAPE = 2,          /* sizes inconsistent or out of range         */
+    KDA_ERR_UNSUPPORTED = 3,        /* valid but not implemented (dtype, d, C)    */
+    KDA_ERR_WORKSPACE_TOO_SMALL = 4,
+    KDA_ERR_HIP = 5,                /* a HIP launch failed                        */
+    KDA_ERR_BAD_SEQLENS = 6         /* host-visible cu_seqlens are malformed      */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/*
+ * Prefill arguments.  Sequences are either the B rows of a batch
+ * (cu_seqlens == NULL, num_seqs == B) or documents packed along T
+ * (B == 1, cu_seqlens != NULL, num_seqs == len(cu_seqlens) - 1); documents
+ * never share state (Module 11, §2, row "Padding / packing").
+ *
+ *   q, k        DEVICE [B, T, H, d_k]  in_dtype
+ *   v           DEVICE [B, T, H, d_v]  in_dtype
+ *   beta        DEVICE [B, T, H]       in_dtype, expected in [0, 1]
+ *   log_alpha   DEVICE [B, T, H, d_k]  in_dtype, <= 0
+ *   cu_seqlens  DEVICE int32 [num_seqs + 1]: 0 = cu[0] <= cu[1] <= ... <=
+ *               cu[num_seqs] = T.  Checked on the device before any other
+ *               kernel reads it: if malformed, no kernel writes o or any
+ *               state and *device_status (if given) is set to
+ *               KDA_ERR_BAD_SEQLENS.
+ *   cu_seqlens_host  HOST, optional copy of cu_seqlens; when given it is
+ *               validated on the host as well (KDA_ERR_BAD_SEQLENS).
+ *   initial_state DEVICE fp32 [num_seqs, H, d_k, d_v], NULL = zeros.
+ *   final_state DEVICE fp32 [num_seqs, H, d_k, d_v], NULL = not written.
+ *               May alias initial_state (in-place continuation).
+ *   chunk_states DEVICE fp32, NULL = not written: the state ENTERING every
+ *               chunk, documents in order, [sum_n ceil(len_n / C), H, d_k, d_v]
+ *               (the chunk-boundary states of Module 04, §4 "The correctness
+ *               invariant").  Its size is bounded by
+ *               kda_prefill_max_chunks() * H * d_k * d_v floats.
+ *   o           DEVICE [B, T, H, d_v]  out_dtype (fp32 recommended: a bf16
+ *               output alone costs ~2^-9 relative per element).
+ *   device_status DEVICE int32, NULL = not reported; written 0 or an error.
+ *   workspace   DEVICE, >= kda_prefill_workspace_bytes(args), 256-byte aligned.
+ *
+ * Supported: d_k, d_v in {16, 32, 64, 128}; chunk_size in {16, 32, 64};
+ * in_dtype f32 (computed entirely in fp32) or bf16 (matrix-core path with
+ * fp32 state and accumulation, for d_k == d_v in {64, 128}; other sizes use
+ * the fp32 path); out_dtype f32 or bf16.
+ */
+typedef struct kda_prefill_args {
+    int32_t B, T, H, d_k, d_v;
+    int32_t num_seqs;
+    int32_t chunk_size;
+    int32_t in_dtype;              /* kda_dtype */
+    int32_t out_dtype;             /* kda_dtype */
+    const void *q, *k, *v, *beta, *log_alpha;
+    const int32_t *cu_seqlens;
+    const int32_t *cu_seqlens_host;
+    const float *initial_state;
+    float *final_state;
+    float *chunk_states;
+    void *o;
+    int32_t *device_status;
+    void *workspace;
+    size_t workspace_bytes;
+} kda_prefill_args;
+
+/* Workspace bytes the call described by *a needs (0 if a is NULL or
+ * invalid).  Pure host function; depends only on sizes and dtypes. */
+size_t kda_prefill_workspace_bytes(const kda_prefill_args *a);
+
+/* Upper bound on sum_n ceil(len_n / C): ceil(T / C) + num_seqs for packed
+ * input, B * ceil(T / C) otherwise.  Pure host function. */
+int64_t kda_prefill_max_chunks(const kda_prefill_args *a);
+
+/* Chunked prefill over all sequences and heads.  Returns KDA_OK once the
+ * kernels are enqueued on hip_stream. */
+kda_status kda_prefill_chunked(const kda_prefill_args *a, void *hip_stream);
+
+/*
+ * One decode step for B independent sequences (one token each), fused:
+ * the state is read once and written once per (sequence, head)
+ * (Module 04, §2: decode uses a fused recurrent kernel).
+ *
+ *   q, k, log_alpha  DEVICE [B, H, d_k]  in_dtype
+ *   v                DEVICE [B, H, d_v]  in_dtype
+ *   beta             DEVICE [B, H]       in_dtype
+ *   state            DEVICE fp32 [B, H, d_k, d_v], updated in place
+ *   o                DEVICE [B, H, d_v]  out_dtype
+ * Supported: d_k, d_v in {16, 32, 64, 128}; dtypes as for prefill.
+ */
+kda_status kda_decode_step(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
+                           int32_t in_dtype, int32_t out_dtype,
+                           const void *q, const void *k, const void *v,
+                           const void *beta, const void *log_alpha,
+                           float *state, void *o, void *hip_stream);
+
+/* Static description of a status code (never NULL). */
+const char *kda_status_string(int32_t status);
+
+/* KDA_ABI_VERSION of the loaded library. */
+int32_t kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

@@ -1,0 +1,137 @@
+"""The C ABI library loads on any host, exports every function include/kda.h
+declares, and rejects bad arguments on the host before touching a device
+(no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gated_delta_rule_49_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kda.LIB_PATH):
+        from gated_delta_rule_49_amd import build
+        build.build()
+    return kda.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"kda_prefill_chunked", "kda_decode_step", "kda_prefill_workspace_bytes"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in kda.h but not exported"
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.kda_abi_version() == 1
+    for s in range(7):
+        assert L.kda_status_string(s)
+    assert L.kda_status_string(99) == b"unknown status"
+
+
+def test_struct_layout_matches_header(tmp_path):
+    """ctypes mirror == the C compiler's layout of kda_prefill_args."""
+    fields = [f for f, _ in kda.PrefillArgs._fields_]
+    src = tmp_path / "layout.c"
+    body = "".join(f'printf("%zu\\n", offsetof(kda_prefill_args, {f}));' for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "kda.h"\n'
+                   'int main(void){printf("%zu\\n", sizeof(kda_prefill_args));' + body + 'return 0;}\n')
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    want = [ctypes.sizeof(kda.PrefillArgs)] + [getattr(kda.PrefillArgs, f).offset for f in fields]
+    assert got == want
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def base_args(**over):
+    a = kda.PrefillArgs()
+    a.B, a.T, a.H, a.d_k, a.d_v, a.num_seqs, a.chunk_size = 1, 128, 2, 128, 128, 1, 64
+    a.in_dtype, a.out_dtype = 1, 0
+    for f in ("q", "k", "v", "beta", "log_alpha", "o", "workspace"):
+        setattr(a, f, FAKE)
+    for key, val in over.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(workspace=None), 1),
+    (dict(B=0), 2), (dict(H=0), 2), (dict(d_k=0), 2), (dict(num_seqs=2), 2),
+    (dict(d_k=96), 3), (dict(d_v=256), 3), (dict(chunk_size=48), 3), (dict(in_dtype=7), 3),
+    (dict(out_dtype=2), 3),
+    (dict(workspace_bytes=0), 4),
+])
+def test_prefill_host_validation(L, over, status):
+    a = base_args(**over)
+    assert L.kda_prefill_chunked(ctypes.byref(a), None) == status
+
+
+def test_workspace_query_is_pure_and_monotone(L):
+    a = base_args()
+    w1 = L.kda_prefill_workspace_bytes(ctypes.byref(a))
+    a.T = 4096
+    w2 = L.kda_prefill_workspace_bytes(ctypes.byref(a))
+    assert 0 < w1 <= w2
+    assert L.kda_prefill_workspace_bytes(None) == 0
+    assert L.kda_prefill_max_chunks(ctypes.byref(a)) == 64
+
+
+def test_packed_host_seqlens_validation(L):
+    cu_bad = np.array([0, 50, 40, 128], np.int32)
+    a = base_args(num_seqs=3, cu_seqlens=FAKE)
+    a.cu_seqlens_host = cu_bad.ctypes.data_as(ctypes.c_void_p)
+    a.workspace_bytes = L.kda_prefill_workspace_bytes(ctypes.byref(a))
+    assert L.kda_prefill_chunked(ctypes.byref(a), None) == 6
+    cu_end = np.array([0, 50, 60, 127], np.int32)
+    a.cu_seqlens_host = cu_end.ctypes.data_as(ctypes.c_void_p)
+    assert L.kda_prefill_chunked(ctypes.byref(a), None) == 6
+    # packed input requires B == 1
+    b = base_args(B=2, num_seqs=3, cu_seqlens=FAKE)
+    assert L.kda_prefill_chunked(ctypes.byref(b), None) == 2
+    # bound on chunks: ceil(T/C) + N; a malformed host copy makes the query 0
+    assert L.kda_prefill_max_chunks(ctypes.byref(a)) == 0
+    cu_ok = np.array([0, 50, 50, 128], np.int32)
+    a.cu_seqlens_host = cu_ok.ctypes.data_as(ctypes.c_void_p)
+    assert L.kda_prefill_max_chunks(ctypes.byref(a)) == 2 + 3
+
+
+@pytest.mark.parametrize("args,status", [
+    ((4, 2, 128, 128, 1, 0), 1),       # null pointers
+    ((4, 0, 128, 128, 1, 0), 2),
+    ((4, 2, 96, 128, 1, 0), 3),
+    ((4, 2, 128, 128, 3, 0), 3),
+])
+def test_decode_host_validation(L, args, status):
+    assert L.kda_decode_step(*args, None, None, None, None, None, None, None, None) == status
+
+
+def test_decode_empty_batch_is_noop(L):
+    assert L.kda_decode_step(0, 2, 128, 128, 1, 0, None, None, None, None, None, None, None, None) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 4, 1, 16)
+    with pytest.raises(ValueError, match="GPU"):
+        kda.prefill(q, q, q, torch.zeros(1, 4, 1), q)
+    with pytest.raises(ValueError, match="GPU"):
+        kda.decode_step(q[0], q[0], q[0], torch.zeros(1, 4), q[0], torch.zeros(1, 4, 16, 16))
