@@ -1,0 +1,268 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step = one chunked prefill over the prefill workload (chunk table,
+intra-chunk kernel, scan kernel) followed by one fused decode step over the
+decode workload — every stage of the path once.  Inputs are synthetic,
+seeded, generated on the GPU and resident in HBM before timing starts.
+
+Prints ONE JSON line:
+  value        prefill tokens/s (tokens of the prefill workload, all heads)
+               from HIP events around the library call, averaged over steps
+  decode       decode sequence-steps/s, same method
+  roofline     prefill: algorithmic HBM bytes / average call duration vs 8 TB/s
+  cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--workload long|prefill|packed] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s + decode seq-steps/s @H=32,d=128; % MFMA / HBM peak"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+# Algorithmic bytes per (token, head): q, k, v, log_alpha in bf16 (4 x 256 B),
+# beta (2 B), o in fp32 (512 B).
+PREFILL_BYTES_PER_TOKEN_HEAD = 4 * 128 * 2 + 2 + 128 * 4
+# Decode per (sequence, head, step): fp32 state read + write plus the same I/O.
+DECODE_BYTES_PER_SEQ_HEAD = 2 * 128 * 128 * 4 + PREFILL_BYTES_PER_TOKEN_HEAD
+
+
+def chunk_flops_per_token_head(C=64, d=128):
+    """Useful flops of the chunked form per (token, head): Gram A and P
+    (2 C d each, halved by triangularity counted as full here), W and U
+    (2 C d each), and the state-side W S, (q e^G) S, P Delta, K^T Delta:
+    10 C d + 6 d^2 in total."""
+    return 10 * C * d + 6 * d * d
+
+
+class HipEvents:
+    """Minimal ctypes access to hipEvent* so the library can record events on
+    the stream its kernels run on."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            rc = self.lib.hipEventCreate(ctypes.byref(h))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            arr[i] = h
+        return arr
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(out), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(out.value)
+
+
+def prefill_inputs(name, dev):
+    import numpy as np
+    import torch
+    import synth
+    if name == "long":
+        ts = synth.long_tensors(5, 131072, 32, 128, 128, "bf16", True, dev)
+        q, k, v, b, la = (t.to(torch.bfloat16) for t in ts)
+        del ts
+        return dict(workload="long_T131072_H32_d128_extreme", q=q, k=k, v=v, beta=b, log_alpha=la,
+                    init=None, cu=None, cu_host=None, chunk=64)
+    x = synth.workload(2 if name == "prefill" else 4, device=dev)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev, torch.bfloat16)  # noqa: E731
+    init = None if x.initial_state is None else torch.from_numpy(x.initial_state).to(dev)
+    cu = None if x.cu_seqlens is None else torch.from_numpy(x.cu_seqlens).to(dev)
+    return dict(workload=x.name, q=t(x.q), k=t(x.k), v=t(x.v), beta=t(x.beta), log_alpha=t(x.log_alpha),
+                init=init, cu=cu, cu_host=x.cu_seqlens, chunk=x.chunk_size)
+
+
+def cpu_baseline_prefill(P, target_s=12.0):
+    """The fp64 oracle on the first S tokens of every head of the prefill
+    workload (S sized for ~target_s of CPU work)."""
+    import numpy as np
+    from oracle import native
+    q, k, v, b, la = (P[n] for n in ("q", "k", "v", "beta", "log_alpha"))
+    T, H = q.shape[1], q.shape[2]
+    cu = P["cu_host"]
+
+    def host(a, S):
+        return a[:, :S].float().cpu().numpy()
+
+    def run(S):
+        arrs = [host(a, S) for a in (q, k, v, b, la)]
+        init = None
+        cus = None
+        if cu is not None:  # the documents that lie inside the sample
+            ends = [int(e) for e in cu[1:] if e <= S] or [S]
+            S = ends[-1]
+            arrs = [a[:, :S] for a in arrs]
+            cus = np.array([0] + ends, np.int64)
+            if P["init"] is not None:
+                init = P["init"][:len(ends)].cpu().numpy()
+        t = time.perf_counter()
+        native.prefill(*arrs, cu_seqlens=cus, initial_state=init)
+        return time.perf_counter() - t, S
+
+    dt, S = run(min(T, 2048))
+    S2 = int(min(T, max(2048, S * target_s / max(dt, 1e-3))))
+    if S2 > S:
+        dt, S = run(S2)
+    return dict(value=S / dt, unit="tokens/s", cores=native.max_threads(), kind="oracle",
+                sample=f"first {S} of {T} tokens, all {H} heads, fp64 token-by-token recurrence "
+                       f"({dt:.1f} s)")
+
+
+def cpu_baseline_decode(D):
+    from oracle import native
+    import numpy as np
+    B = D["q"].shape[1]
+    args = [D[n][0].float().cpu().numpy()[None] for n in ("q", "k", "v", "beta", "log_alpha")]
+    init = D["state0"].cpu().numpy()
+    t = time.perf_counter()
+    native.prefill(*args, cu_seqlens=np.arange(B + 1), initial_state=init)
+    dt = time.perf_counter() - t
+    return dict(value=B / dt, unit="seq-steps/s", cores=native.max_threads(), kind="oracle",
+                sample=f"one step of all {B} sequences x {D['q'].shape[2]} heads ({dt:.2f} s)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long", choices=["long", "prefill", "packed"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                                   "(the recurrence shards by head or sequence with no exchange)"}))
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_49_amd as kda
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ev = HipEvents()
+    print(f"[bench] generating {args.workload} prefill + decode inputs", file=sys.stderr, flush=True)
+    P = prefill_inputs(args.workload, dev)
+    Bp, T, H, d = P["q"].shape
+    dw = synth.decode_workload(device=dev) if False else None  # host copy not needed
+    g = torch.Generator(device=dev)
+    # decode workload: B=256, H=32, d=128, 64 steps of fresh bf16 inputs
+    from synth.kda_inputs import _draw_tokens, _gen, _state
+    gg = _gen(3, dev)
+    dq, dk_, dv_, db, dla = _draw_tokens(gg, 64, 256, 32, 128, 128, 0.0, dev, True)
+    D = dict(q=dq.to(torch.bfloat16), k=dk_.to(torch.bfloat16), v=dv_.to(torch.bfloat16),
+             beta=db.to(torch.bfloat16), log_alpha=dla.to(torch.bfloat16))
+    D["state0"] = _state(gg, (256, 32, 128, 128), 0.02, dev)
+    del dq, dk_, dv_, db, dla, g, dw
+    state = D["state0"].clone()
+    Bd = D["q"].shape[1]
+
+    # preallocated outputs and workspace (nothing is allocated in the timed loop)
+    ws = torch.empty(kda.workspace_bytes(P["q"], P["k"], P["v"], P["beta"], P["log_alpha"], P["cu"],
+                                         P["chunk"]), dtype=torch.uint8, device=dev)
+    o = torch.empty((Bp, T, H, d), dtype=torch.float32, device=dev)
+    N = Bp if P["cu"] is None else P["cu"].numel() - 1
+    fin = torch.empty((N, H, d, d), dtype=torch.float32, device=dev)
+    od = torch.empty((Bd, 32, 128), dtype=torch.float32, device=dev)
+    n_ev = args.warmup + args.steps
+    pev = ev.create(3 * n_ev)
+    dstart = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    dend = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+
+    def step(i):
+        kda.prefill(P["q"], P["k"], P["v"], P["beta"], P["log_alpha"], initial_state=P["init"],
+                    cu_seqlens=P["cu"], chunk_size=P["chunk"], workspace=ws, o=o, final_state=fin,
+                    timing_events=ctypes.cast(ctypes.byref(pev, 3 * i * ctypes.sizeof(ctypes.c_void_p)),
+                                              ctypes.c_void_p))
+        s = i % 64
+        dstart[i].record()
+        kda.decode_step(D["q"][s], D["k"][s], D["v"][s], D["beta"][s], D["log_alpha"][s], state, o=od)
+        dend[i].record()
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print("[bench] timed steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(args.warmup, n_ev):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    rng = range(args.warmup, n_ev)
+    pre_ms = [ev.ms(pev[3 * i], pev[3 * i + 2]) for i in rng]
+    intra_ms = [ev.ms(pev[3 * i], pev[3 * i + 1]) for i in rng]
+    scan_ms = [ev.ms(pev[3 * i + 1], pev[3 * i + 2]) for i in rng]
+    dec_ms = [dstart[i].elapsed_time(dend[i]) for i in rng]
+    mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    pre, intra, scan, dec = mean(pre_ms), mean(intra_ms), mean(scan_ms), mean(dec_ms)
+
+    tokens = Bp * T
+    value = tokens / (pre * 1e-3)
+    pbytes = tokens * H * PREFILL_BYTES_PER_TOKEN_HEAD
+    if P["init"] is not None:
+        pbytes += 2 * N * H * d * d * 4
+    p_gbs = pbytes / (pre * 1e-3) / 1e9
+    useful_tf = tokens * H * chunk_flops_per_token_head(P["chunk"], d) / (pre * 1e-3) / 1e12
+    dbytes = Bd * 32 * DECODE_BYTES_PER_SEQ_HEAD
+    d_gbs = dbytes / (dec * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": P["workload"], "B": Bp, "T": T, "H": H, "d_k": d, "d_v": d,
+                   "chunk": P["chunk"], "num_seqs": N,
+                   "decode_workload": "decode_B256_H32_d128", "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": p_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": p_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "kda_prefill_chunked (chunk table + intra_kernel + scan_kernel)",
+                     "algorithmic_bytes": pbytes, "avg_ms": pre,
+                     "kernels_ms": {"intra_kernel": intra, "scan_kernel": scan},
+                     "useful_mfma_tflops": useful_tf,
+                     "useful_mfma_frac": useful_tf / BF16_PEAK_TFLOPS},
+        "decode": {"value": Bd / (dec * 1e-3), "unit": "seq-steps/s", "avg_ms": dec,
+                   "roofline": {"bound": "hbm", "achieved": d_gbs, "peak": HBM_PEAK_GBS,
+                                "unit": "GB/s", "frac": d_gbs / HBM_PEAK_GBS, "traffic": None,
+                                "kernel": "decode_step_kernel", "algorithmic_bytes": dbytes}},
+        "prefill_ms": pre,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_prefill(P)
+        out["decode"]["cpu_baseline"] = cpu_baseline_decode(D)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -53,6 +53,7 @@ class PrefillArgs(ctypes.Structure):
         ("chunk_states", ctypes.c_void_p), ("o", ctypes.c_void_p),
         ("device_status", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("timing_events", ctypes.c_void_p),
     ]
 
 
@@ -152,7 +153,7 @@ def max_chunks(q, k, v, beta, log_alpha, cu_seqlens=None, chunk_size=64) -> int:
 
 def prefill(q, k, v, beta, log_alpha, initial_state=None, output_final_state=True,
             cu_seqlens=None, chunk_size=64, out_dtype=torch.float32, chunk_states=False,
-            workspace=None, final_state=None, o=None, check_seqlens=False):
+            workspace=None, final_state=None, o=None, check_seqlens=False, timing_events=None):
     """Chunked prefill.
 
     q, k, log_alpha [B,T,H,d_k]; v [B,T,H,d_v]; beta [B,T,H]; all float32 or
@@ -162,7 +163,9 @@ def prefill(q, k, v, beta, log_alpha, initial_state=None, output_final_state=Tru
     (o, final_state, chunk_states) where chunk_states[c] is the state entering
     global chunk c (documents in order).  ``check_seqlens`` additionally
     validates cu_seqlens on the host (one device-to-host copy) and raises on a
-    device-side rejection (one synchronisation)."""
+    device-side rejection (one synchronisation).  ``timing_events`` (a ctypes
+    pointer to three hipEvent_t) is passed through to the library's
+    profiling hook."""
     dev = _check_dev(q, k, v, beta, log_alpha, initial_state, cu_seqlens, workspace, final_state, o)
     if not (q.dtype == k.dtype == v.dtype == beta.dtype == log_alpha.dtype):
         raise TypeError("q, k, v, beta, log_alpha must share one dtype")
@@ -205,6 +208,7 @@ def prefill(q, k, v, beta, log_alpha, initial_state=None, output_final_state=Tru
     a.device_status = _ptr(status)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = workspace.numel() * workspace.element_size()
+    a.timing_events = timing_events
     st = L.kda_prefill_chunked(ctypes.byref(a), _stream(dev))
     if st != 0:
         raise KDAError(st, "kda_prefill_chunked")

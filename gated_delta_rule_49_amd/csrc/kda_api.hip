@@ -13,7 +13,7 @@ bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
 bool dtype_ok(int t) { return t == KDA_F32 || t == KDA_BF16; }
 
 // shape / dtype / pointer checks that do not need the workspace
-kda_status check_prefill(const kda_prefill_args *a) {
+kda_status check_prefill(const kda_prefill_args *a, bool need_ptrs) {
     if (!a) return KDA_ERR_NULL_ARG;
     if (a->B < 1 || a->T < 0 || a->H < 1 || a->num_seqs < 0) return KDA_ERR_BAD_SHAPE;
     if (!dim_ok(a->d_k) || !dim_ok(a->d_v) || !chunk_ok(a->chunk_size)) {
@@ -31,15 +31,15 @@ kda_status check_prefill(const kda_prefill_args *a) {
     // element counts must fit the kernels' 32-bit token indexing
     const int64_t tokens = static_cast<int64_t>(a->B) * a->T;
     if (tokens * a->H > (static_cast<int64_t>(1) << 31)) return KDA_ERR_UNSUPPORTED;
-    const bool any_tokens = tokens > 0;
-    if (any_tokens && (!a->q || !a->k || !a->v || !a->beta || !a->log_alpha || !a->o))
-        return KDA_ERR_NULL_ARG;
     if (a->cu_seqlens_host) {
         const int32_t *c = a->cu_seqlens_host;
         if (c[0] != 0 || c[a->num_seqs] != a->T) return KDA_ERR_BAD_SEQLENS;
         for (int n = 0; n < a->num_seqs; ++n)
             if (c[n + 1] < c[n]) return KDA_ERR_BAD_SEQLENS;
     }
+    const bool any_tokens = tokens > 0;
+    if (need_ptrs && any_tokens && (!a->q || !a->k || !a->v || !a->beta || !a->log_alpha || !a->o))
+        return KDA_ERR_NULL_ARG;
     return KDA_OK;
 }
 
@@ -79,17 +79,17 @@ const char *kda_status_string(int32_t s) {
 }
 
 int64_t kda_prefill_max_chunks(const kda_prefill_args *a) {
-    if (check_prefill(a) != KDA_OK) return 0;
+    if (check_prefill(a, false) != KDA_OK) return 0;
     return max_chunks(a);
 }
 
 size_t kda_prefill_workspace_bytes(const kda_prefill_args *a) {
-    if (check_prefill(a) != KDA_OK) return 0;
+    if (check_prefill(a, false) != KDA_OK) return 0;
     return workspace_for(a);
 }
 
 kda_status kda_prefill_chunked(const kda_prefill_args *a, void *hip_stream) {
-    kda_status st = check_prefill(a);
+    kda_status st = check_prefill(a, true);
     if (st != KDA_OK) return st;
     if (!a->workspace) return KDA_ERR_NULL_ARG;
     if (reinterpret_cast<uintptr_t>(a->workspace) % kAlign) return KDA_ERR_BAD_SHAPE;
@@ -112,13 +112,18 @@ kda_status kda_prefill_chunked(const kda_prefill_args *a, void *hip_stream) {
     p.n_chunks_bound = static_cast<int32_t>(max_chunks(a));
 
     if (p.N == 0) return KDA_OK;
-    hipError_t e = launch_chunk_table(p, s);
+    hipEvent_t *ev = static_cast<hipEvent_t *>(a->timing_events);
+    hipError_t e = ev ? hipEventRecord(ev[0], s) : hipSuccess;
+    if (e == hipSuccess) e = launch_chunk_table(p, s);
     if (e == hipSuccess) {
         if (use_mfma(a))
-            e = launch_prefill_mfma(p, ws + table_bytes(p.N), a->out_dtype, s);
-        else
+            e = launch_prefill_mfma(p, ws + table_bytes(p.N), a->out_dtype, s, ev ? ev[1] : nullptr);
+        else {
             e = launch_prefill_f32(p, a->in_dtype, a->out_dtype, s);
+            if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);
+        }
     }
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[2], s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -20,7 +20,9 @@ bool mfma_supported(int dk, int dv, int C);
 
 hipError_t launch_chunk_table(const PrefillParams &p, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillParams &p, int in_dtype, int out_dtype, hipStream_t s);
-hipError_t launch_prefill_mfma(const PrefillParams &p, void *blocks, int out_dtype, hipStream_t s);
+// mid_event (nullable) is recorded between the intra-chunk and the scan kernel
+hipError_t launch_prefill_mfma(const PrefillParams &p, void *blocks, int out_dtype, hipStream_t s,
+                               hipEvent_t mid_event);
 hipError_t launch_decode(int B, int H, int dk, int dv, int in_dtype, int out_dtype, const void *q,
                          const void *k, const void *v, const void *beta, const void *log_alpha,
                          float *state, void *o, hipStream_t s);

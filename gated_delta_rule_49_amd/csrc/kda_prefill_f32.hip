@@ -14,7 +14,10 @@
 //     Delta = T (V - (k * exp(G)) S)          rows are the per-token errors
 //     O     = (q * exp(G)) S + P Delta
 //     S'    = Diag(exp(G_L)) S + (k * exp(G_L - G))^T Delta
-// All exponents are <= 0 (pairs i <= r), so nothing overflows.
+// All exponents are <= 0 (pairs i <= r), so nothing overflows.  G is
+// accumulated and held in fp64 and differences are taken in fp64 before one
+// fp32 exp: a cumulative log-decay of magnitude ~50 held in fp32 would put
+// ~1e-5 relative error on every decay factor, the size of the fp32 contract.
 //
 // One workgroup per (sequence, head, BV-column tile of the state): the
 // columns of S evolve independently.  Everything a chunk needs sits in LDS.
@@ -26,7 +29,7 @@ constexpr int F32_THREADS = 256;
 constexpr int F32_BV = 16;
 
 __host__ __device__ inline size_t f32_lds_floats(int C, int dk) {
-    return static_cast<size_t>(C) * dk      // G (base-2 scaled)
+    return 2 * static_cast<size_t>(C) * dk  // G (fp64)
            + static_cast<size_t>(C) * C     // A, then T, then P
            + static_cast<size_t>(dk) * F32_BV  // S tile
            + static_cast<size_t>(C) * F32_BV   // X, then Delta
@@ -45,8 +48,8 @@ __global__ void __launch_bounds__(F32_THREADS) prefill_f32_kernel(PrefillParams 
     const int v0 = vt * F32_BV;
     const int tid = threadIdx.x;
 
-    float *G = lds;                 // [C][dk]
-    float *AT = G + C * dk;         // [C][C]
+    double *G = reinterpret_cast<double *>(lds);  // [C][dk]
+    float *AT = lds + 2 * C * dk;   // [C][C]
     float *S = AT + C * C;          // [dk][BV]
     float *X = S + dk * F32_BV;     // [C][BV]
     float *bet = X + C * F32_BV;    // [C]
@@ -81,11 +84,11 @@ __global__ void __launch_bounds__(F32_THREADS) prefill_f32_kernel(PrefillParams 
                 cs[static_cast<int64_t>(c) * dv + v0 + j] = S[e];
             }
         }
-        // 1. cumulative log-decay (base 2), beta; padded rows decay by 1
+        // 1. cumulative log-decay (fp64), beta; padded rows decay by 1
         for (int c = tid; c < dk; c += F32_THREADS) {
-            float acc = 0.f;
+            double acc = 0.0;
             for (int r = 0; r < C; ++r) {
-                if (r < L) acc += io<TI>::ld(la, kv(t0 + r) * dk + c) * kLog2e;
+                if (r < L) acc += static_cast<double>(io<TI>::ld(la, kv(t0 + r) * dk + c));
                 G[r * dk + c] = acc;
             }
         }
@@ -99,7 +102,8 @@ __global__ void __launch_bounds__(F32_THREADS) prefill_f32_kernel(PrefillParams 
             if (i < r && r < L) {
                 const int64_t kr = kv(t0 + r) * dk, ki = kv(t0 + i) * dk;
                 for (int c = 0; c < dk; ++c)
-                    acc += io<TI>::ld(k, kr + c) * io<TI>::ld(k, ki + c) * exp2f(G[r * dk + c] - G[i * dk + c]);
+                    acc += io<TI>::ld(k, kr + c) * io<TI>::ld(k, ki + c) *
+                           expf(static_cast<float>(G[r * dk + c] - G[i * dk + c]));
                 acc *= bet[r];
             }
             AT[e] = acc;
@@ -126,7 +130,8 @@ __global__ void __launch_bounds__(F32_THREADS) prefill_f32_kernel(PrefillParams 
             float acc = 0.f;
             if (r < L) {
                 const int64_t kr = kv(t0 + r) * dk;
-                for (int c = 0; c < dk; ++c) acc += io<TI>::ld(k, kr + c) * exp2f(G[r * dk + c]) * S[c * F32_BV + j];
+                for (int c = 0; c < dk; ++c)
+                    acc += io<TI>::ld(k, kr + c) * expf(static_cast<float>(G[r * dk + c])) * S[c * F32_BV + j];
                 acc = io<TI>::ld(v, kv(t0 + r) * dv + v0 + j) - acc;
             }
             X[e] = acc;
@@ -157,7 +162,8 @@ __global__ void __launch_bounds__(F32_THREADS) prefill_f32_kernel(PrefillParams 
             if (i <= r && r < L) {
                 const int64_t qr = kv(t0 + r) * dk, ki = kv(t0 + i) * dk;
                 for (int c = 0; c < dk; ++c)
-                    acc += io<TI>::ld(q, qr + c) * io<TI>::ld(k, ki + c) * exp2f(G[r * dk + c] - G[i * dk + c]);
+                    acc += io<TI>::ld(q, qr + c) * io<TI>::ld(k, ki + c) *
+                           expf(static_cast<float>(G[r * dk + c] - G[i * dk + c]));
             }
             AT[e] = acc;
         }
@@ -169,7 +175,8 @@ __global__ void __launch_bounds__(F32_THREADS) prefill_f32_kernel(PrefillParams 
             if (r < L) {
                 const int64_t qr = kv(t0 + r) * dk;
                 float acc = 0.f;
-                for (int c = 0; c < dk; ++c) acc += io<TI>::ld(q, qr + c) * exp2f(G[r * dk + c]) * S[c * F32_BV + j];
+                for (int c = 0; c < dk; ++c)
+                    acc += io<TI>::ld(q, qr + c) * expf(static_cast<float>(G[r * dk + c])) * S[c * F32_BV + j];
                 for (int i = 0; i <= r; ++i) acc += AT[r * C + i] * X[i * F32_BV + j];
                 io<TO>::st(o, kv(t0 + r) * dv + v0 + j, acc);
             }
@@ -180,10 +187,11 @@ __global__ void __launch_bounds__(F32_THREADS) prefill_f32_kernel(PrefillParams 
             int idx = 0;
             for (int e = tid; e < dk * F32_BV; e += F32_THREADS, ++idx) {
                 const int c = e / F32_BV, j = e % F32_BV;
-                const float gl = G[(C - 1) * dk + c];
-                float acc = exp2f(gl) * S[e];
+                const double gl = G[(C - 1) * dk + c];
+                float acc = expf(static_cast<float>(gl)) * S[e];
                 for (int r = 0; r < L; ++r)
-                    acc += io<TI>::ld(k, kv(t0 + r) * dk + c) * exp2f(gl - G[r * dk + c]) * X[r * F32_BV + j];
+                    acc += io<TI>::ld(k, kv(t0 + r) * dk + c) * expf(static_cast<float>(gl - G[r * dk + c])) *
+                           X[r * F32_BV + j];
                 sreg[idx] = acc;
             }
         }

@@ -90,6 +90,11 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *               output alone costs ~2^-9 relative per element).
  *   device_status DEVICE int32, NULL = not reported; written 0 or an error.
  *   workspace   DEVICE, >= kda_prefill_workspace_bytes(args), 256-byte aligned.
+ *   timing_events  HOST, nullable: pointer to 3 hipEvent_t created by the
+ *               caller; recorded on hip_stream before the first kernel
+ *               (the chunk table), between the intra-chunk and the scan kernel
+ *               (after the single kernel on the fp32 path) and after the
+ *               last kernel.  A profiling hook; costs nothing when NULL.
  *
  * Supported: d_k, d_v in {16, 32, 64, 128}; chunk_size in {16, 32, 64};
  * in_dtype f32 (computed entirely in fp32) or bf16 (matrix-core path with
@@ -112,6 +117,7 @@ typedef struct kda_prefill_args {
     int32_t *device_status;
     void *workspace;
     size_t workspace_bytes;
+    void *timing_events;
 } kda_prefill_args;
 
 /* Workspace bytes the call described by *a needs (0 if a is NULL or

@@ -25,11 +25,13 @@ Layouts (row-major, contiguous):
 For packed workloads B == 1 and ``cu_seqlens`` (int32, [N+1]) delimits the
 documents along T.
 
-Random stream: numpy ``Generator(PCG64(seed))``; draws are made in fp32 in
-the order q, k, v, beta_raw, gate_raw, then the initial state.  Long inputs
-are drawn in blocks of ``BLOCK_TOKENS`` tokens, each block from its own child
-of ``SeedSequence(seed)``, so host memory stays bounded and any block can be
-regenerated on its own.
+Random stream: torch's generator on the device given (``device="cpu"`` by
+default; large workloads are drawn on the GPU, which is much faster — the
+same seed gives different, equally valid, inputs on a different device
+type).  Draws are made in fp32 in the order q, k, v, beta_raw, gate_raw,
+then the initial state.  Long inputs are drawn in blocks of ``BLOCK_TOKENS``
+tokens with seeds ``seed * 100003 + block`` so any block can be regenerated on
+its own.  Results are returned as host numpy arrays.
 """
 from __future__ import annotations
 
@@ -37,6 +39,7 @@ import dataclasses
 from typing import Optional
 
 import numpy as np
+import torch
 
 BLOCK_TOKENS = 8192
 
@@ -61,18 +64,14 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
 
 
 # ------------------------------------------------------- activations -------
-def _softplus(x: np.ndarray) -> np.ndarray:
-    # stable: max(x,0) + log1p(exp(-|x|))
-    return np.maximum(x, 0) + np.log1p(np.exp(-np.abs(x)))
+def _gen(seed: int, device):
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
 
 
-def _sigmoid(x: np.ndarray) -> np.ndarray:
-    return 1.0 / (1.0 + np.exp(-x))
-
-
-def _l2norm(x: np.ndarray) -> np.ndarray:
-    n = np.sqrt(np.sum(x.astype(np.float32) ** 2, axis=-1, keepdims=True))
-    return (x / np.maximum(n, np.float32(1e-12))).astype(np.float32)
+def _to_np(t):
+    return t.detach().to("cpu").numpy()
 
 
 # ---------------------------------------------------------- container ------
@@ -125,91 +124,97 @@ class KDAInputs:
 
 
 # ------------------------------------------------------------ drawing ------
-def _draw_tokens(rng, B, T, H, dk, dv, gate_mean=0.0):
-    f32 = np.float32
-    q = rng.standard_normal((B, T, H, dk), dtype=f32)
-    k = rng.standard_normal((B, T, H, dk), dtype=f32)
-    v = rng.standard_normal((B, T, H, dv), dtype=f32)
-    beta_raw = rng.standard_normal((B, T, H), dtype=f32)
-    gate_raw = rng.standard_normal((B, T, H, dk), dtype=f32)
+def _draw_tokens(g, B, T, H, dk, dv, gate_mean=0.0, device="cpu", bf16=False):
+    """Token inputs as torch fp32 tensors on ``device``."""
+    kw = dict(generator=g, device=device, dtype=torch.float32)
+    q = torch.randn((B, T, H, dk), **kw)
+    k = torch.randn((B, T, H, dk), **kw)
+    v = torch.randn((B, T, H, dv), **kw)
+    beta_raw = torch.randn((B, T, H), **kw)
+    gate_raw = torch.randn((B, T, H, dk), **kw)
     if gate_mean:
-        gate_raw += f32(gate_mean)
-    k = _l2norm(k)
-    beta = _sigmoid(beta_raw).astype(f32)
-    log_alpha = (-_softplus(gate_raw)).astype(f32)
-    return q, k, v, beta, log_alpha
+        gate_raw += gate_mean
+    k = k / torch.clamp(torch.linalg.vector_norm(k, dim=-1, keepdim=True), min=1e-12)
+    beta = torch.sigmoid(beta_raw)
+    log_alpha = -torch.nn.functional.softplus(gate_raw)
+    out = [q, k, v, beta, log_alpha]
+    if bf16:
+        out = [t.to(torch.bfloat16).to(torch.float32) for t in out]
+    return out
 
 
-def _finish(name, dtype, q, k, v, beta, log_alpha, state, cu, chunk):
-    if dtype == "bf16":
-        q, k, v, beta, log_alpha = (round_bf16(a) for a in (q, k, v, beta, log_alpha))
-    return KDAInputs(name, dtype, q, k, v, beta, log_alpha, state, cu, chunk)
+def _state(g, shape, std, device):
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std
 
 
 def make_uniform(seed: int, B: int, T: int, H: int, dk: int, dv: int, dtype: str,
                  chunk: int = 64, state_std: float = 0.0, gate_mean: float = 0.0,
-                 name: str = "custom") -> KDAInputs:
+                 name: str = "custom", device="cpu") -> KDAInputs:
     """B independent rows of T tokens, typical gates; optional N(0, std^2) state."""
-    rng = np.random.Generator(np.random.PCG64(seed))
-    q, k, v, beta, la = _draw_tokens(rng, B, T, H, dk, dv, gate_mean)
-    state = None
-    if state_std:
-        state = (rng.standard_normal((B, H, dk, dv), dtype=np.float32) * np.float32(state_std))
-    return _finish(name, dtype, q, k, v, beta, la, state, None, chunk)
+    g = _gen(seed, device)
+    q, k, v, beta, la = _draw_tokens(g, B, T, H, dk, dv, gate_mean, device, dtype == "bf16")
+    state = _to_np(_state(g, (B, H, dk, dv), state_std, device)) if state_std else None
+    return KDAInputs(name, dtype, *(_to_np(t) for t in (q, k, v, beta, la)), state, None, chunk)
 
 
 def make_packed(seed: int, lengths, H: int, dk: int, dv: int, dtype: str, chunk: int = 64,
-                state_std: float = 0.02, name: str = "packed") -> KDAInputs:
+                state_std: float = 0.02, name: str = "packed", device="cpu") -> KDAInputs:
     """Documents of the given lengths concatenated along T (B == 1)."""
-    rng = np.random.Generator(np.random.PCG64(seed))
+    g = _gen(seed, device)
     T = int(np.sum(lengths))
-    q, k, v, beta, la = _draw_tokens(rng, 1, T, H, dk, dv)
+    q, k, v, beta, la = _draw_tokens(g, 1, T, H, dk, dv, 0.0, device, dtype == "bf16")
     n = len(lengths)
-    state = None
-    if state_std:
-        state = rng.standard_normal((n, H, dk, dv), dtype=np.float32) * np.float32(state_std)
+    state = _to_np(_state(g, (n, H, dk, dv), state_std, device)) if state_std else None
     cu = np.zeros(n + 1, dtype=np.int32)
     cu[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))
-    return _finish(name, dtype, q, k, v, beta, la, state, cu, chunk)
+    return KDAInputs(name, dtype, *(_to_np(t) for t in (q, k, v, beta, la)), state, cu, chunk)
 
 
-def _extreme_block(rng, T, H, dk):
+def _extreme_block(g, T, H, dk, device):
     """Per token: Bernoulli(0.1) selects the token (all heads); selected
     tokens get log_alpha ~ U[-20, -10] per (head, channel) and beta drawn
     from {1e-4, 1 - 1e-4} with probability 1/2 each per (token, head)."""
-    sel = rng.random(T) < 0.1
-    la = rng.uniform(-20.0, -10.0, size=(T, H, dk)).astype(np.float32)
-    bsel = rng.random((T, H)) < 0.5
-    b = np.where(bsel, np.float32(1e-4), np.float32(1.0 - 1e-4)).astype(np.float32)
+    kw = dict(generator=g, device=device, dtype=torch.float32)
+    sel = torch.rand((T,), **kw) < 0.1
+    la = torch.rand((T, H, dk), **kw) * 10.0 - 20.0
+    bsel = torch.rand((T, H), **kw) < 0.5
+    b = torch.where(bsel, torch.tensor(1e-4, device=device), torch.tensor(1.0 - 1e-4, device=device))
     return sel, la, b
 
 
-def make_long(seed: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16",
-              chunk: int = 64, extreme: bool = True, name: str = "long") -> KDAInputs:
-    """One long row drawn in BLOCK_TOKENS blocks (child seeds), with the
-    extreme-gate stress pattern when ``extreme``."""
-    f32 = np.float32
-    shape_k = (1, T, H, dk)
-    q = np.empty(shape_k, f32)
-    k = np.empty(shape_k, f32)
-    v = np.empty((1, T, H, dv), f32)
-    beta = np.empty((1, T, H), f32)
-    la = np.empty(shape_k, f32)
+def long_tensors(seed: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16",
+                 extreme: bool = True, device="cpu"):
+    """[q, k, v, beta, log_alpha] of one long row as torch fp32 tensors on
+    ``device`` (bf16-exact if dtype == 'bf16'), drawn in BLOCK_TOKENS blocks
+    with seed ``seed * 100003 + block``; with ``extreme`` the stress pattern
+    of :func:`_extreme_block` is applied per block."""
+    shapes = [(1, T, H, dk), (1, T, H, dk), (1, T, H, dv), (1, T, H), (1, T, H, dk)]
+    out = [torch.empty(sh, dtype=torch.float32, device=device) for sh in shapes]
     nblk = (T + BLOCK_TOKENS - 1) // BLOCK_TOKENS
-    children = np.random.SeedSequence(seed).spawn(nblk)
-    for i, ss in enumerate(children):
+    for i in range(nblk):
         t0, t1 = i * BLOCK_TOKENS, min(T, (i + 1) * BLOCK_TOKENS)
-        rng = np.random.Generator(np.random.PCG64(ss))
-        bq, bk, bv, bb, bla = _draw_tokens(rng, 1, t1 - t0, H, dk, dv)
+        g = _gen(seed * 100003 + i, device)
+        bq, bk, bv, bb, bla = _draw_tokens(g, 1, t1 - t0, H, dk, dv, 0.0, device, False)
         if extreme:
-            sel, xla, xb = _extreme_block(rng, t1 - t0, H, dk)
+            sel, xla, xb = _extreme_block(g, t1 - t0, H, dk, device)
             bla[0, sel] = xla[sel]
             bb[0, sel] = xb[sel]
+        parts = [bq, bk, bv, bb, bla]
         if dtype == "bf16":
-            bq, bk, bv, bb, bla = (round_bf16(a) for a in (bq, bk, bv, bb, bla))
-        q[:, t0:t1], k[:, t0:t1], v[:, t0:t1] = bq, bk, bv
-        beta[:, t0:t1], la[:, t0:t1] = bb, bla
-    return KDAInputs(name, dtype, q, k, v, beta, la, None, None, chunk)
+            parts = [t.to(torch.bfloat16).to(torch.float32) for t in parts]
+        for dst, src in zip(out, parts):
+            dst[:, t0:t1] = src
+    return out
+
+
+def make_long(seed: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16",
+              chunk: int = 64, extreme: bool = True, name: str = "long", device="cpu") -> KDAInputs:
+    """One long row (see :func:`long_tensors`) as host arrays."""
+    ts = long_tensors(seed, T, H, dk, dv, dtype, extreme, device)
+    arrs = []
+    while ts:
+        arrs.append(_to_np(ts.pop(0)))  # frees each device tensor as it is copied
+    return KDAInputs(name, dtype, *arrs, None, None, chunk)
 
 
 # -------------------------------------------------- the five workloads ----
@@ -217,11 +222,12 @@ C4_DOCS = 8
 
 
 def c4_lengths(seed: int = 4):
+    """8 lengths uniform on [512, 8192] (numpy PCG64, so identical on every host)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     return rng.integers(512, 8193, size=C4_DOCS).tolist()
 
 
-def workload(idx: int, **over) -> KDAInputs:
+def workload(idx: int, device="cpu", **over) -> KDAInputs:
     """The five named workloads (seed = workload index):
 
     1  tiny fp32: B=1 H=1 T=64 d=16, chunk 16, zero state
@@ -232,17 +238,18 @@ def workload(idx: int, **over) -> KDAInputs:
     5  long:      B=1 H=32 T=131072 d=128 bf16, chunk 64, 10% extreme gates
     """
     if idx == 1:
-        return make_uniform(1, 1, 64, 1, 16, 16, "f32", chunk=16, name="tiny_f32_T64_d16")
+        return make_uniform(1, 1, 64, 1, 16, 16, "f32", chunk=16, name="tiny_f32_T64_d16",
+                            device=device)
     if idx == 2:
         return make_uniform(2, 1, over.get("T", 4096), over.get("H", 16), 128, 128, "bf16",
-                            chunk=64, name="prefill_T4096_H16_d128")
+                            chunk=64, name="prefill_T4096_H16_d128", device=device)
     if idx == 4:
         lens = over.get("lengths", c4_lengths(4))
         return make_packed(4, lens, over.get("H", 32), 128, 128, "bf16", chunk=64,
-                           name="packed_8docs_H32_d128")
+                           name="packed_8docs_H32_d128", device=device)
     if idx == 5:
         return make_long(5, over.get("T", 131072), over.get("H", 32), 128, 128, "bf16",
-                         chunk=64, name="long_T131072_H32_d128_extreme")
+                         chunk=64, name="long_T131072_H32_d128_extreme", device=device)
     raise ValueError(f"workload {idx}: use decode_workload() for 3")
 
 
@@ -263,21 +270,20 @@ class DecodeInputs:
 
 def decode_workload(B: int = 256, H: int = 32, dk: int = 128, dv: int = 128,
                     steps: int = 64, seed: int = 3, dtype: str = "bf16",
-                    state_std: float = 0.02, name: str = "decode_B256_H32_d128") -> DecodeInputs:
+                    state_std: float = 0.02, name: str = "decode_B256_H32_d128",
+                    device="cpu") -> DecodeInputs:
     """Workload 3: per step fresh q,k,v,beta,alpha (as in workload 1, rounded
     to bf16); initial state N(0, 0.02^2) fp32, drawn after the token inputs."""
-    rng = np.random.Generator(np.random.PCG64(seed))
+    g = _gen(seed, device)
     # steps play the role of T with one token per sequence: [steps, B, H, d]
-    q, k, v, beta, la = _draw_tokens(rng, steps, B, H, dk, dv)
-    state = rng.standard_normal((B, H, dk, dv), dtype=np.float32) * np.float32(state_std)
-    if dtype == "bf16":
-        q, k, v, beta, la = (round_bf16(a) for a in (q, k, v, beta, la))
-    return DecodeInputs(name, dtype, q, k, v, beta, la, state)
+    q, k, v, beta, la = _draw_tokens(g, steps, B, H, dk, dv, 0.0, device, dtype == "bf16")
+    state = _state(g, (B, H, dk, dv), state_std, device)
+    return DecodeInputs(name, dtype, *(_to_np(t) for t in (q, k, v, beta, la, state)))
 
 
 def slow_decay(seed: int, B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16",
-               chunk: int = 64, state_std: float = 0.02) -> KDAInputs:
+               chunk: int = 64, state_std: float = 0.02, device="cpu") -> KDAInputs:
     """Supplementary case: log_alpha = -softplus(N(-5, 1)) (alpha ~ 0.99), so
     state carried across chunk boundaries dominates the outputs."""
     return make_uniform(seed, B, T, H, dk, dv, dtype, chunk=chunk, state_std=state_std,
-                        gate_mean=-5.0, name="slow_decay")
+                        gate_mean=-5.0, name="slow_decay", device=device)

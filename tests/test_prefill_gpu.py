@@ -17,8 +17,9 @@ pytestmark = pytest.mark.gpu
 def check(x, chunk=None, name="", tol=None, boundaries=True):
     chunk = chunk or x.chunk_size
     q, k, v, b, la, init, cu = dev_tensors(x)
-    o, S, cs = kda.prefill(q, k, v, b, la, initial_state=init, cu_seqlens=cu, chunk_size=chunk,
-                           chunk_states=boundaries, check_seqlens=cu is not None)
+    res = kda.prefill(q, k, v, b, la, initial_state=init, cu_seqlens=cu, chunk_size=chunk,
+                      chunk_states=boundaries, check_seqlens=cu is not None)
+    o, S, cs = res if boundaries else (*res, None)
     o_ref, S_ref, cs_ref = native.prefill(x.q, x.k, x.v, x.beta, x.log_alpha, x.cu_seqlens,
                                           x.initial_state, chunk=chunk, want_chunk_states=boundaries)
     tol = tol or TOL[x.dtype]
@@ -97,3 +98,110 @@ def test_malformed_seqlens_write_nothing():
     torch.cuda.synchronize()
     assert int(status.item()) == 6
     assert bool((o == 7.0).all()) and bool((fs == 7.0).all())
+
+
+# --------------------------------------------------- matrix-core path ----
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("T", [1, 37, 100, 200])
+def test_bf16_mfma_chunks_and_ragged_tails(D, chunk, T):
+    x = synth.make_uniform(400 + T + D, 2, T, 2, D, D, "bf16", chunk=chunk, state_std=0.3)
+    check(x, name="mfma")
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_bf16_mfma_slow_decay_boundaries(chunk):
+    """alpha ~ 0.99 with an N(0, 0.02^2) state: carried state dominates, so a
+    chunk-boundary mistake cannot hide behind fast forgetting."""
+    x = synth.slow_decay(17, 1, 1000, 2, 128, 128, "bf16", chunk=chunk)
+    check(x, name="mfma slow decay")
+
+
+def test_bf16_mfma_extreme_gates():
+    """10% of tokens with log alpha in [-20, -10] and beta in {1e-4, 1}: the
+    factorised diagonal Gram blocks overflow fp32 and take the exact path."""
+    x = synth.make_long(55, 2048, 4, 128, 128, "bf16", chunk=64)
+    check(x, name="mfma extreme")
+
+
+def test_bf16_mfma_packed_docs_with_empty_and_tiny():
+    x = synth.make_packed(18, [70, 0, 1, 64, 129, 5], 3, 128, 128, "bf16", chunk=64)
+    check(x, name="mfma packed")
+
+
+def test_bf16_mfma_bf16_output():
+    x = synth.make_uniform(19, 1, 300, 2, 128, 128, "bf16", chunk=64, state_std=0.1)
+    q, k, v, b, la, init, _ = dev_tensors(x)
+    o, S = kda.prefill(q, k, v, b, la, initial_state=init, out_dtype=torch.bfloat16)
+    assert o.dtype == torch.bfloat16
+    o_ref, S_ref, _ = native.prefill(x.q, x.k, x.v, x.beta, x.log_alpha, None, x.initial_state)
+    d = np.abs(o.float().cpu().numpy() - o_ref)
+    rms = np.sqrt(np.mean(o_ref ** 2))
+    assert np.all(d <= 2e-2 * rms + 2.0 ** -8 * np.abs(o_ref))
+    assert err(S, S_ref) <= 2e-2
+
+
+def test_prefill_workload_T4096_H16():
+    """B=1 H=16 T=4096 d=128 bf16, chunk 64, zero state: outputs, final state
+    and all 64 boundary states per head."""
+    check(synth.workload(2), name="prefill workload")
+
+
+def test_packed_workload_8docs_H32():
+    """8 documents, lengths U[512, 8192], H=32, d=128, per-document state:
+    outputs and final states (boundary states are covered above)."""
+    x = synth.workload(4, device="cuda")
+    check(x, name="packed workload", boundaries=False)
+
+
+def test_long_workload_T131072_H32_sampled_heads_and_continuation():
+    """T=131072 H=32 d=128 with 10% extreme gates.  The GPU runs all heads in
+    one pass and as 4 continuation calls of 32768 tokens; the oracle checks
+    two heads over the whole length; the single pass and the continuation
+    must agree (bitwise expected: chunk boundaries coincide)."""
+    x = synth.workload(5, device="cuda")
+    q, k, v, b, la, _, _ = dev_tensors(x)
+    o, S = kda.prefill(q, k, v, b, la)
+    S_run = None
+    outs = []
+    for i in range(4):
+        sl = slice(i * 32768, (i + 1) * 32768)
+        oi, S_run = kda.prefill(q[:, sl].contiguous(), k[:, sl].contiguous(), v[:, sl].contiguous(),
+                                b[:, sl].contiguous(), la[:, sl].contiguous(), initial_state=S_run)
+        outs.append(oi)
+    oc = torch.cat(outs, dim=1)
+    e_cont = dict(o=err(oc, o.double().cpu().numpy()), S=err(S_run, S.double().cpu().numpy()))
+    bitwise = bool(torch.equal(oc, o)) and bool(torch.equal(S_run, S))
+    report("long continuation vs single pass", bitwise=float(bitwise), **e_cont)
+    assert e_cont["o"] <= 2e-2 and e_cont["S"] <= 2e-2
+    heads = [0, 31]
+    sub = lambda a: np.ascontiguousarray(a[:, :, heads])  # noqa: E731
+    o_ref, S_ref, _ = native.prefill(sub(x.q), sub(x.k), sub(x.v), sub(x.beta), sub(x.log_alpha))
+    eo = err(o[:, :, heads], o_ref)
+    es = err(S[:, heads], S_ref)
+    report("long T=131072 heads 0,31", o=eo, S=es)
+    assert eo <= 2e-2 and es <= 2e-2
+
+
+def test_mfma_packed_equals_separate_and_is_deterministic():
+    lens = [200, 64, 1, 129]
+    x = synth.make_packed(20, lens, 2, 128, 128, "bf16", chunk=64)
+    q, k, v, b, la, init, cu = dev_tensors(x)
+    o, S = kda.prefill(q, k, v, b, la, initial_state=init, cu_seqlens=cu)
+    o2, S2 = kda.prefill(q, k, v, b, la, initial_state=init, cu_seqlens=cu)
+    assert torch.equal(o, o2) and torch.equal(S, S2), "run-to-run results differ"
+    c = x.cu_seqlens
+    for n in range(len(lens)):
+        sl = slice(int(c[n]), int(c[n + 1]))
+        on, Sn = kda.prefill(q[:, sl].contiguous(), k[:, sl].contiguous(), v[:, sl].contiguous(),
+                             b[:, sl].contiguous(), la[:, sl].contiguous(), initial_state=init[n:n + 1].contiguous())
+        assert torch.equal(on, o[:, sl]), f"document {n}: packed output differs from separate"
+        assert torch.equal(Sn, S[n:n + 1]), f"document {n}: packed state differs from separate"
+
+
+def test_mfma_power_of_two_homogeneity():
+    x = synth.make_uniform(21, 1, 150, 2, 128, 128, "bf16", chunk=64, state_std=0.2)
+    q, k, v, b, la, init, _ = dev_tensors(x)
+    o, S = kda.prefill(q, k, v, b, la, initial_state=init)
+    o2, S2 = kda.prefill(q, k, 2 * v, b, la, initial_state=2 * init)
+    assert torch.equal(o2, 2 * o) and torch.equal(S2, 2 * S)
