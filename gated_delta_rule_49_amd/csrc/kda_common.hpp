@@ -33,11 +33,9 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// round to nearest, ties to even (finite inputs)
+// round to nearest, ties to even (the hardware conversion, v_cvt_pk_bf16_f32)
 __device__ __forceinline__ bf16_t f32_to_bf16(float x) {
-    uint32_t u = __float_as_uint(x);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return static_cast<bf16_t>(u >> 16);
+    return __builtin_bit_cast(bf16_t, static_cast<__bf16>(x));
 }
 
 __device__ __forceinline__ __bf16 bits_as_bf16(bf16_t b) {

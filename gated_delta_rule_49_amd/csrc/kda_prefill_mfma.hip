@@ -81,323 +81,612 @@ __device__ __forceinline__ uint2 pack4(const bf16_t *s) {
     return r;
 }
 
+// persistent intra-chunk grid: one workgroup per CU of an MI355X (256 CUs)
+constexpr int kIntraGrid = 256;
+
 // log2-domain threshold for factorising a diagonal Gram block
 constexpr float kDiagSpanMax = 100.f;
 
 // ------------------------------------------------------------------ K1 --
+// LDS plan of the intra-chunk kernel (bytes).  Rows are padded so that the
+// 16 lanes of a fragment that read 16 consecutive rows hit distinct banks.
 template <int C, int D>
-__global__ void __launch_bounds__(256) intra_kernel(PrefillParams p, char *__restrict__ blocks) {
-    using Y = Lay<C, D>;
-    constexpr int CP = Y::CP;
-    if (*p.status != 0) return;
-    const int x = blockIdx.x;
-    const int h = blockIdx.y;
-    const int H = p.H;
-    if (x >= p.chunk_off[p.N]) return;
-    const int n = chunk_to_seq(p.chunk_off, p.N, x);
+struct IntraLds {
+    static constexpr int CP = Lay<C, D>::CP;
+    static constexpr int RK = D + 8;       // bf16 row stride of [token][channel]
+    static constexpr int RT = CP + 16;     // bf16 row stride of [channel][token] (octets XOR-swizzled)
+    static constexpr int RTF = CP + 8;     // bf16 row stride of the T fragments
+    static constexpr int RG = D + 4;       // fp32 row stride of G
+    static constexpr int RA = CP + 4;      // fp32 row stride of A and X
+    static constexpr int NPART = 512 / D;  // cumsum: token ranges per channel
+    static constexpr size_t SK = 0;                                   // k   [CP][RK] bf16
+    static constexpr size_t SQ = SK + CP * RK * 2;                    // q   [CP][RK] bf16
+    static constexpr size_t SA = SQ + CP * RK * 2;                    // A   [CP][RA] f32
+    static constexpr size_t SKT = SA + CP * RA * 4;                   // k^T [D][RT] bf16
+    static constexpr size_t SVT = SKT + D * RT * 2;                   // v^T [D][RT] bf16
+    static constexpr size_t SG = SVT + D * RT * 2;                    // G   [CP][RG] f32 (log2 units)
+    static constexpr size_t ST = SG + CP * RG * 4;                    // X = (I+A)^-1 [CP][RA] f32
+    static constexpr size_t SB = ST + CP * RA * 4;                    // beta [CP]
+    static constexpr size_t SP = SB + CP * 4;                         // cumsum partials [NPART][D]
+    static constexpr size_t END = SP + NPART * D * 4;
+    // after the Gram phase q and A are dead: the T fragments reuse [SQ, SKT)
+    // when they fit there, else they get their own region
+    static constexpr bool REUSE = 3 * CP * RTF * 2 <= SKT - SQ;
+    static constexpr size_t TB = REUSE ? SQ : END;                    // T   bf16 [CP][RTF]
+    static constexpr size_t TH = TB + CP * RTF * 2;                   // hi
+    static constexpr size_t TL = TH + CP * RTF * 2;                   // lo
+    static constexpr size_t BYTES = REUSE ? END : TL + CP * RTF * 2;
+    static constexpr int OMASK = CP / 8 - 1;
+    // element offset of (channel, token) in a transposed [channel][token]
+    // array: token octets are XOR-swizzled by the channel octet so that the
+    // staging writes and the fragment reads spread over the banks
+    __device__ static __forceinline__ int tpos(int ch, int tok) {
+        return ch * RT + ((((tok >> 3) ^ (ch >> 3)) & OMASK) << 3) + (tok & 7);
+    }
+    // raw inputs prefetched per thread
+    static constexpr int NVEC = CP * D / 8;                           // 16-byte vectors per array
+    static constexpr int NV = (NVEC + 511) / 512;
+    static constexpr int RP = CP / NPART;
+};
+
+// One thread's share of a (chunk, head)'s raw inputs, held in registers so
+// the next item's loads are in flight while the current one is computed.
+template <int C, int D>
+struct IntraRaw {
+    using M = IntraLds<C, D>;
+    uint4 k[M::NV], v[M::NV], q[M::NV];
+    float g[M::RP];
+    float beta;
+
+    __device__ __forceinline__ void load(const PrefillParams &p, int64_t t0, int L, int h, int tid) {
+        const bf16_t *Kg = static_cast<const bf16_t *>(p.k);
+        const bf16_t *Vg = static_cast<const bf16_t *>(p.v);
+        const bf16_t *Qg = static_cast<const bf16_t *>(p.q);
+        const bf16_t *Ag = static_cast<const bf16_t *>(p.log_alpha);
+        const bf16_t *Bg = static_cast<const bf16_t *>(p.beta);
+        const int H = p.H;
+#pragma unroll
+        for (int u = 0; u < M::NV; ++u) {
+            const int e = tid + 512 * u;
+            const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
+            k[u] = v[u] = q[u] = make_uint4(0, 0, 0, 0);
+            if (e < M::NVEC && r < L) {
+                const int64_t off = ((t0 + r) * H + h) * D + c8;
+                k[u] = *reinterpret_cast<const uint4 *>(Kg + off);
+                v[u] = *reinterpret_cast<const uint4 *>(Vg + off);
+                q[u] = *reinterpret_cast<const uint4 *>(Qg + off);
+            }
+        }
+        const int ch = tid % D, part = tid / D;
+#pragma unroll
+        for (int j = 0; j < M::RP; ++j) {
+            const int r = part * M::RP + j;
+            g[j] = r < L ? bf16_to_f32(Ag[((t0 + r) * H + h) * D + ch]) : 0.f;
+        }
+        beta = (tid < L) ? bf16_to_f32(Bg[(t0 + tid) * H + h]) : 0.f;
+    }
+};
+
+// (chunk, head) work item -> chunk-local coordinates
+struct IntraItem {
+    int x, h, L;
+    int64_t t0;
+};
+
+template <int C>
+__device__ __forceinline__ IntraItem intra_item(const PrefillParams &p, int item) {
+    IntraItem it;
+    it.x = item / p.H;
+    it.h = item % p.H;
+    const int n = chunk_to_seq(p.chunk_off, p.N, it.x);
     const SeqRange sr = seq_range(p, n);
-    const int cidx = x - p.chunk_off[n];
-    const int64_t t0 = sr.start + static_cast<int64_t>(cidx) * C;
-    const int L = min(C, sr.len - cidx * C);
-    char *blk = blocks + (static_cast<size_t>(x) * H + h) * Y::BYTES;
+    const int cidx = it.x - p.chunk_off[n];
+    it.t0 = sr.start + static_cast<int64_t>(cidx) * C;
+    it.L = min(C, sr.len - cidx * C);
+    return it;
+}
 
-    __shared__ __attribute__((aligned(16))) bf16_t sk[CP][D];
-    __shared__ __attribute__((aligned(16))) bf16_t sv[CP][D];
-    __shared__ __attribute__((aligned(16))) float sG[CP][D];   // base-2 cumulative log-decay
-    __shared__ __attribute__((aligned(16))) float sA[CP][CP];
-    __shared__ __attribute__((aligned(16))) float sT[CP][CP];  // (I + A)^-1 (beta applied on use)
-    __shared__ float sbeta[CP];
+// Persistent: each workgroup walks work items item = blockIdx.x + i * gridDim.x
+// (item = chunk * H + head).
+template <int C, int D>
+__global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__restrict__ blocks) {
+    using Y = Lay<C, D>;
+    using M = IntraLds<C, D>;
+    constexpr int CP = Y::CP;
+    constexpr int NPAIR = Y::NMT * (Y::NMT + 1) / 2;
+    if (*p.status != 0) return;
+    const int H = p.H;
+    const int nitems = p.chunk_off[p.N] * H;
 
-    const bf16_t *Kg = static_cast<const bf16_t *>(p.k);
-    const bf16_t *Vg = static_cast<const bf16_t *>(p.v);
-    const bf16_t *Qg = static_cast<const bf16_t *>(p.q);
-    const bf16_t *Ag = static_cast<const bf16_t *>(p.log_alpha);
-    const bf16_t *Bg = static_cast<const bf16_t *>(p.beta);
+    __shared__ __attribute__((aligned(16))) char smem[M::BYTES];
+    auto SK = reinterpret_cast<bf16_t(*)[M::RK]>(smem + M::SK);
+    auto SQ = reinterpret_cast<bf16_t(*)[M::RK]>(smem + M::SQ);
+    auto SA = reinterpret_cast<float(*)[M::RA]>(smem + M::SA);
+    bf16_t *SKT = reinterpret_cast<bf16_t *>(smem + M::SKT);
+    bf16_t *SVT = reinterpret_cast<bf16_t *>(smem + M::SVT);
+    auto SG = reinterpret_cast<float(*)[M::RG]>(smem + M::SG);
+    auto SX = reinterpret_cast<float(*)[M::RA]>(smem + M::ST);
+    auto SBETA = reinterpret_cast<float *>(smem + M::SB);
+    auto SPART = reinterpret_cast<float(*)[D]>(smem + M::SP);
+    auto TB = reinterpret_cast<bf16_t(*)[M::RTF]>(smem + M::TB);
+    auto TH = reinterpret_cast<bf16_t(*)[M::RTF]>(smem + M::TH);
+    auto TL = reinterpret_cast<bf16_t(*)[M::RTF]>(smem + M::TL);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, li = lane & 15;
 
-    // ---- 1. stage k, v (zero beyond L), gate cumsum, beta; clear A, T
-    for (int e = tid; e < CP * D / 8; e += 256) {
-        const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
-        uint4 kk = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-        if (r < L) {
-            const int64_t off = ((t0 + r) * H + h) * D + c8;
-            kk = *reinterpret_cast<const uint4 *>(Kg + off);
-            vv = *reinterpret_cast<const uint4 *>(Vg + off);
-        }
-        *reinterpret_cast<uint4 *>(&sk[r][c8]) = kk;
-        *reinterpret_cast<uint4 *>(&sv[r][c8]) = vv;
-    }
-    for (int e = tid; e < CP * CP; e += 256) {
-        (&sA[0][0])[e] = 0.f;
-        (&sT[0][0])[e] = 0.f;
-    }
-    for (int ch = tid; ch < D; ch += 256) {
-        float acc = 0.f;
-        for (int r = 0; r < CP; ++r) {
-            if (r < L) acc += bf16_to_f32(Ag[((t0 + r) * H + h) * D + ch]) * kLog2e;
-            sG[r][ch] = acc;
-        }
-    }
-    for (int r = tid; r < CP; r += 256) sbeta[r] = r < L ? bf16_to_f32(Bg[(t0 + r) * H + h]) : 0.f;
-    __syncthreads();
+    IntraRaw<C, D> raw;
+    int item = blockIdx.x;
+    if (item >= nitems) return;
+    IntraItem it = intra_item<C>(p, item);
+    raw.load(p, it.t0, it.L, it.h, tid);
 
-    // ---- 2. Gram blocks: wave a computes row block a (rows 16a..16a+15)
-    //      as transposed tiles A^T(b,a), P^T(b,a) for column blocks b <= a.
-    if (wave < Y::NMT) {
-        const int a = wave;
-        const int r = 16 * a + li;  // row (token) this lane feeds as B operand
-        float span = 0.f;
-        for (int ch = lane; ch < D; ch += 64) {
-            const float gm = a > 0 ? sG[16 * a - 1][ch] : 0.f;
-            span = fmaxf(span, gm - sG[16 * a + 15][ch]);
-        }
-        const bool diag_mfma = wave_max(span) <= kDiagSpanMax;
+    for (; item < nitems; item += gridDim.x) {
+        const int L = it.L;
+        char *blk = blocks + (static_cast<size_t>(it.x) * H + it.h) * Y::BYTES;
 
-        f32x4 accA[Y::NMT], accP[Y::NMT];
+        // ---- 1. stage k, q (natural) and k^T, v^T (transposed, swizzled),
+        //         zero beyond L; gate cumsum: thread (channel, token range)
+        //         sums its range, range totals are combined through LDS.
 #pragma unroll
-        for (int b = 0; b < Y::NMT; ++b) {
-            accA[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-            accP[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int ks = 0; ks < Y::KSD; ++ks) {
-            const int c0 = 32 * ks + 8 * g;
-            float gm[8];
-            frag8 krh, krl, qrh, qrl;
-            const uint4 kraw = *reinterpret_cast<const uint4 *>(&sk[r][c0]);
-            uint4 qraw = make_uint4(0, 0, 0, 0);
-            if (r < L) qraw = *reinterpret_cast<const uint4 *>(Qg + ((t0 + r) * H + h) * D + c0);
-            const bf16_t *kr = reinterpret_cast<const bf16_t *>(&kraw);
-            const bf16_t *qr = reinterpret_cast<const bf16_t *>(&qraw);
+        for (int u = 0; u < M::NV; ++u) {
+            const int e = tid + 512 * u;
+            if (e >= M::NVEC) continue;
+            const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
+            *reinterpret_cast<uint4 *>(&SK[r][c8]) = raw.k[u];
+            *reinterpret_cast<uint4 *>(&SQ[r][c8]) = raw.q[u];
+            const bf16_t *kb = reinterpret_cast<const bf16_t *>(&raw.k[u]);
+            const bf16_t *vb = reinterpret_cast<const bf16_t *>(&raw.v[u]);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                gm[j] = a > 0 ? sG[16 * a - 1][c0 + j] : 0.f;
-                const float rf = fast_exp2(sG[r][c0 + j] - gm[j]);
-                split_bf16(bf16_to_f32(kr[j]) * rf, krh.s[j], krl.s[j]);
-                split_bf16(bf16_to_f32(qr[j]) * rf, qrh.s[j], qrl.s[j]);
-            }
-#pragma unroll
-            for (int b = 0; b < Y::NMT; ++b) {
-                if (b > a || (b == a && !diag_mfma)) continue;
-                const int i = 16 * b + li;
-                frag8 kih, kil;
-                const uint4 kiraw = *reinterpret_cast<const uint4 *>(&sk[i][c0]);
-                const bf16_t *ki = reinterpret_cast<const bf16_t *>(&kiraw);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float cf = fast_exp2(gm[j] - sG[i][c0 + j]);
-                    split_bf16(bf16_to_f32(ki[j]) * cf, kih.s[j], kil.s[j]);
-                }
-                accA[b] = mfma16(kih.v, krh.v, accA[b]);
-                accA[b] = mfma16(kih.v, krl.v, accA[b]);
-                accA[b] = mfma16(kil.v, krh.v, accA[b]);
-                accP[b] = mfma16(kih.v, qrh.v, accP[b]);
-                accP[b] = mfma16(kih.v, qrl.v, accP[b]);
-                accP[b] = mfma16(kil.v, qrh.v, accP[b]);
+                SKT[M::tpos(c8 + j, r)] = kb[j];
+                SVT[M::tpos(c8 + j, r)] = vb[j];
             }
         }
-        if (!diag_mfma) {
-            // exact pairwise diagonal block: lane holds (i = 16a + 4g + j, r)
-            float ea[4] = {0.f, 0.f, 0.f, 0.f}, ep[4] = {0.f, 0.f, 0.f, 0.f};
-            const bool rvalid = r < L;
-            for (int ch = 0; ch < D; ++ch) {
-                const float gr = sG[r][ch];
-                const float kr_ = bf16_to_f32(sk[r][ch]);
-                const float qr_ = rvalid ? bf16_to_f32(Qg[((t0 + r) * H + h) * D + ch]) : 0.f;
+        if (tid < CP) SBETA[tid] = raw.beta;
+        for (int e = tid; e < CP * M::RA; e += 512) {
+            (&SA[0][0])[e] = 0.f;
+            (&SX[0][0])[e] = 0.f;
+        }
+        const int cch = tid % D, part = tid / D;
+        float gv[M::RP];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int i = 16 * a + 4 * g + j;
-                    if (i <= r) {
-                        const float f = bf16_to_f32(sk[i][ch]) * fast_exp2(gr - sG[i][ch]);
-                        ea[j] += kr_ * f;
-                        ep[j] += qr_ * f;
-                    }
+        for (int j = 0; j < M::RP; ++j) gv[j] = raw.g[j];
+#pragma unroll
+        for (int j = 1; j < M::RP; ++j) gv[j] += gv[j - 1];
+        SPART[part][cch] = gv[M::RP - 1];
+        // the next item's raw inputs: loads in flight during this item
+        const int next = item + gridDim.x;
+        IntraItem itn = it;
+        if (next < nitems) {
+            itn = intra_item<C>(p, next);
+            raw.load(p, itn.t0, itn.L, itn.h, tid);
+        }
+        __syncthreads();
+        {
+            float off = 0.f;
+            for (int q2 = 0; q2 < part; ++q2) off += SPART[q2][cch];
+#pragma unroll
+            for (int j = 0; j < M::RP; ++j) SG[part * M::RP + j][cch] = (off + gv[j]) * kLog2e;
+        }
+        __syncthreads();
+
+        // ---- 2. Gram blocks A^T(b,a), P^T(b,a) for b <= a, one block pair
+        //         per wave at a time.  Factors around reference row
+        //         m = 16a - 1: rows (<= 1) e^{G_r - G_m}, columns e^{G_m - G_i}.
+        for (int pi = wave; pi < NPAIR; pi += 8) {
+            int a = 0, rem = pi;
+            while (rem > a) { rem -= a + 1; ++a; }
+            const int b = rem;
+            const int r = 16 * a + li;
+            bool fact = true;
+            if (a == b) {
+                float span = 0.f;
+                for (int ch = lane; ch < D; ch += 64) {
+                    const float gm = a > 0 ? SG[16 * a - 1][ch] : 0.f;
+                    span = fmaxf(span, gm - SG[16 * a + 15][ch]);
                 }
+                fact = wave_max(span) <= kDiagSpanMax;
             }
+            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = accA;
+            if (fact) {
+                const int i = 16 * b + li;
 #pragma unroll
-            for (int b = 0; b < Y::NMT; ++b)
-                if (b == a) {
+                for (int ks = 0; ks < Y::KSD; ++ks) {
+                    const int c0 = 32 * ks + 8 * g;
+                    const uint4 kraw = *reinterpret_cast<const uint4 *>(&SK[r][c0]);
+                    const uint4 qraw = *reinterpret_cast<const uint4 *>(&SQ[r][c0]);
+                    const uint4 kiraw = *reinterpret_cast<const uint4 *>(&SK[i][c0]);
+                    const bf16_t *kr = reinterpret_cast<const bf16_t *>(&kraw);
+                    const bf16_t *qr = reinterpret_cast<const bf16_t *>(&qraw);
+                    const bf16_t *ki = reinterpret_cast<const bf16_t *>(&kiraw);
+                    frag8 krh, krl, qrh, qrl, kih, kil;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float gm = a > 0 ? SG[16 * a - 1][c0 + j] : 0.f;
+                        const float rf = fast_exp2(SG[r][c0 + j] - gm);
+                        const float cf = fast_exp2(gm - SG[i][c0 + j]);
+                        split_bf16(bf16_to_f32(kr[j]) * rf, krh.s[j], krl.s[j]);
+                        split_bf16(bf16_to_f32(qr[j]) * rf, qrh.s[j], qrl.s[j]);
+                        split_bf16(bf16_to_f32(ki[j]) * cf, kih.s[j], kil.s[j]);
+                    }
+                    accA = mfma16(kih.v, krh.v, accA);
+                    accA = mfma16(kih.v, krl.v, accA);
+                    accA = mfma16(kil.v, krh.v, accA);
+                    accP = mfma16(kih.v, qrh.v, accP);
+                    accP = mfma16(kih.v, qrl.v, accP);
+                    accP = mfma16(kil.v, qrh.v, accP);
+                }
+            } else {
+                // exact pairwise diagonal block: lane holds (i = 16a + 4g + j, r)
+                for (int ch = 0; ch < D; ++ch) {
+                    const float gr = SG[r][ch];
+                    const float kr_ = bf16_to_f32(SK[r][ch]);
+                    const float qr_ = bf16_to_f32(SQ[r][ch]);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        accA[b][j] = ea[j];
-                        accP[b][j] = ep[j];
+                        const int i = 16 * a + 4 * g + j;
+                        if (i <= r) {
+                            const float f = bf16_to_f32(SK[i][ch]) * fast_exp2(gr - SG[i][ch]);
+                            accA[j] += kr_ * f;
+                            accP[j] += qr_ * f;
+                        }
                     }
                 }
-        }
-        // A (rows scaled by beta_r, strictly lower) -> LDS; P -> workspace
-        const float br = sbeta[r];
-#pragma unroll
-        for (int b = 0; b < Y::NMT; ++b) {
-            if (b > a) continue;
+            }
+            // A (rows scaled by beta_r, strictly lower) -> LDS; P -> workspace
+            const float br = SBETA[r];
+            f32x4 av;
             bf16_t ph[4], pl[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int i = 16 * b + 4 * g + j;
-                sA[r][i] = (i < r) ? accA[b][j] * br : 0.f;
-                split_bf16((i <= r) ? accP[b][j] : 0.f, ph[j], pl[j]);
+                av[j] = (i < r) ? accA[j] * br : 0.f;
+                split_bf16((i <= r) ? accP[j] : 0.f, ph[j], pl[j]);
             }
+            *reinterpret_cast<f32x4 *>(&SA[r][16 * b + 4 * g]) = av;
             const size_t fo = ((static_cast<size_t>(a) * Y::KSC + b / 2) * 64 + lane) * 16 + (b & 1) * 8;
             *reinterpret_cast<uint2 *>(blk + Y::PH + fo) = pack4(ph);
             *reinterpret_cast<uint2 *>(blk + Y::PL + fo) = pack4(pl);
-            if (b == a && (b & 1) == 0) {  // upper half of the same k step is zero
+            if (b == a && (b & 1) == 0) {  // the upper half of this k step is zero
                 *reinterpret_cast<uint2 *>(blk + Y::PH + fo + 8) = make_uint2(0, 0);
                 *reinterpret_cast<uint2 *>(blk + Y::PL + fo + 8) = make_uint2(0, 0);
             }
         }
-    }
-    __syncthreads();
 
-    // ---- 3. X = (I + A)^-1 by blocked forward substitution (fp32 VALU)
-    if (wave < Y::NMT && li == lane) {  // lanes 0..15: column jj of diagonal block a
-        const int a = wave, jj = li, base = 16 * a;
-        float xc[16];
+        // ---- 2b. q e^G (scan A-operand order), (k e^{G_L - G})^T, e^{G_L}
+        for (int f = wave; f < Y::NMT * Y::KSD + Y::NDT * Y::KSC; f += 8) {
+            frag8 hi, lo;
+            size_t dst_h, dst_l;
+            if (f < Y::NMT * Y::KSD) {
+                const int mt = f / Y::KSD, ks = f % Y::KSD;
+                const int r = 16 * mt + li;
+                const int cA = 32 * ks + 4 * g, cB = cA + 16;
+                const uint2 q0 = *reinterpret_cast<const uint2 *>(&SQ[r][cA]);
+                const uint2 q1 = *reinterpret_cast<const uint2 *>(&SQ[r][cB]);
+                const f32x4 g0 = *reinterpret_cast<const f32x4 *>(&SG[r][cA]);
+                const f32x4 g1 = *reinterpret_cast<const f32x4 *>(&SG[r][cB]);
+                const bf16_t *qa = reinterpret_cast<const bf16_t *>(&q0);
+                const bf16_t *qb = reinterpret_cast<const bf16_t *>(&q1);
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            float s = (rr == jj) ? 1.f : 0.f;
+                for (int j = 0; j < 4; ++j) {
+                    split_bf16(bf16_to_f32(qa[j]) * fast_exp2(g0[j]), hi.s[j], lo.s[j]);
+                    split_bf16(bf16_to_f32(qb[j]) * fast_exp2(g1[j]), hi.s[4 + j], lo.s[4 + j]);
+                }
+                const size_t fo = (static_cast<size_t>(f) * 64 + lane) * 16;
+                dst_h = Y::QH + fo;
+                dst_l = Y::QL + fo;
+            } else {
+                const int f2 = f - Y::NMT * Y::KSD;
+                const int mt = f2 / Y::KSC, ks = f2 % Y::KSC;
+                const int ch = 16 * mt + li;
+                const float gl = SG[C - 1][ch];
+                const int iA = 32 * ks + 4 * g, iB = iA + 16;
+                const uint2 k0 = *reinterpret_cast<const uint2 *>(&SKT[M::tpos(ch, iA)]);
+                const uint2 k1 = *reinterpret_cast<const uint2 *>(&SKT[M::tpos(ch, iB)]);
+                const bf16_t *ka = reinterpret_cast<const bf16_t *>(&k0);
+                const bf16_t *kb = reinterpret_cast<const bf16_t *>(&k1);
 #pragma unroll
-            for (int i = 0; i < rr; ++i)
-                if (i >= jj) s -= sA[base + rr][base + i] * xc[i];
-            xc[rr] = (rr >= jj) ? s : 0.f;
+                for (int j = 0; j < 4; ++j) {
+                    split_bf16(bf16_to_f32(ka[j]) * fast_exp2(gl - SG[iA + j][ch]), hi.s[j], lo.s[j]);
+                    split_bf16(bf16_to_f32(kb[j]) * fast_exp2(gl - SG[iB + j][ch]), hi.s[4 + j], lo.s[4 + j]);
+                }
+                const size_t fo = (static_cast<size_t>(f2) * 64 + lane) * 16;
+                dst_h = Y::KBH + fo;
+                dst_l = Y::KBL + fo;
+            }
+            st16(blk + dst_h, hi.u);
+            st16(blk + dst_l, lo.u);
         }
+        if (tid < D) reinterpret_cast<float *>(blk + Y::GAM)[tid] = fast_exp2(SG[C - 1][tid]);
+        __syncthreads();
+
+        // ---- 3. X = (I + A)^-1 by blocked forward substitution (fp32 VALU).
+        //         Diagonal blocks: lane jj owns column jj; row rr of A_aa is
+        //         read as four broadcast 16-byte loads.
+        if (wave < Y::NMT && lane < 16) {
+            const int a = wave, jj = lane, base = 16 * a;
+            float xc[16];
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) sT[base + rr][base + jj] = xc[rr];
-    }
-    __syncthreads();
+            for (int rr = 0; rr < 16; ++rr) {
+                float arow[16];
 #pragma unroll
-    for (int lev = 1; lev < Y::NMT; ++lev) {
-        // block (a, b) with a - b = lev handled by wave b
-        const bool act = wave < Y::NMT - lev;
-        const int b = wave, a = wave + lev;
-        const int rr = lane >> 2, cc0 = (lane & 3) * 4;
-        float y[4] = {0.f, 0.f, 0.f, 0.f};
-        if (act) {
-            for (int c = b; c < a; ++c)
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const f32x4 t = *reinterpret_cast<const f32x4 *>(&SA[base + rr][base + 4 * q4]);
 #pragma unroll
-                for (int kk = 0; kk < 16; ++kk) {
-                    const float av = sA[16 * a + rr][16 * c + kk];
+                    for (int j = 0; j < 4; ++j) arow[4 * q4 + j] = t[j];
+                }
+                float s0 = (rr == jj) ? 1.f : 0.f, s1 = 0.f;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) y[q] += av * sT[16 * c + kk][16 * b + cc0 + q];
+                for (int i = 0; i < rr; ++i) {
+                    const float t = (i >= jj) ? arow[i] * xc[i] : 0.f;
+                    if (i & 1) s1 -= t; else s0 -= t;
+                }
+                xc[rr] = (rr >= jj) ? s0 + s1 : 0.f;
+            }
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) SX[base + rr][base + jj] = xc[rr];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int lev = 1; lev < Y::NMT; ++lev) {
+            // block (a, b), a - b = lev, handled by wave b
+            const bool act = wave < Y::NMT - lev;
+            const int b = wave, a = wave + lev;
+            const int rr = lane >> 2, cc0 = (lane & 3) * 4;
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
+            if (act) {
+                for (int c = b; c < a; ++c)
+#pragma unroll
+                    for (int kk = 0; kk < 16; ++kk)
+                        y += SA[16 * a + rr][16 * c + kk] *
+                             *reinterpret_cast<const f32x4 *>(&SX[16 * c + kk][16 * b + cc0]);
+                *reinterpret_cast<f32x4 *>(&SX[16 * a + rr][16 * b + cc0]) = y;
+            }
+            __syncthreads();
+            f32x4 xo = {0.f, 0.f, 0.f, 0.f};
+            if (act) {
+#pragma unroll
+                for (int kk = 0; kk < 16; ++kk)
+                    xo -= SX[16 * a + rr][16 * a + kk] *
+                          *reinterpret_cast<const f32x4 *>(&SX[16 * a + kk][16 * b + cc0]);
+            }
+            __syncthreads();
+            if (act) *reinterpret_cast<f32x4 *>(&SX[16 * a + rr][16 * b + cc0]) = xo;
+            __syncthreads();
+        }
+
+        // ---- 3b. T = X Diag(beta) as MFMA operands: bf16, and hi/lo (q, A dead)
+        for (int e = tid; e < CP * CP / 4; e += 512) {
+            const int r = e / (CP / 4), i4 = (e % (CP / 4)) * 4;
+            const f32x4 xv = *reinterpret_cast<const f32x4 *>(&SX[r][i4]);
+            bf16_t tb[4], th[4], tl[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float t = xv[j] * SBETA[i4 + j];
+                tb[j] = f32_to_bf16(t);
+                split_bf16(t, th[j], tl[j]);
+            }
+            *reinterpret_cast<uint2 *>(&TB[r][i4]) = pack4(tb);
+            *reinterpret_cast<uint2 *>(&TH[r][i4]) = pack4(th);
+            *reinterpret_cast<uint2 *>(&TL[r][i4]) = pack4(tl);
+        }
+        __syncthreads();
+
+        // ---- 4. W^T = (k e^G)^T T^T (bf16) per channel tile; U = T V (T split)
+        //         per value tile.  Items: NDT W tiles then NDT U tiles.
+        for (int wi = wave; wi < 2 * Y::NDT; wi += 8) {
+            const bool isW = wi < Y::NDT;
+            const int ct = isW ? wi : wi - Y::NDT;
+            const int ch = 16 * ct + li;
+            f32x4 acc[Y::NMT];
+#pragma unroll
+            for (int tt = 0; tt < Y::NMT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s2 = 0; s2 < Y::KSC; ++s2) {
+                const int i0 = 32 * s2 + 8 * g;
+                frag8 opk;  // W: (k e^G)^T, channel row ch, tokens i0..i0+7; U: V^T
+                if (isW) {
+                    const uint4 kraw = *reinterpret_cast<const uint4 *>(&SKT[M::tpos(ch, i0)]);
+                    const bf16_t *kk = reinterpret_cast<const bf16_t *>(&kraw);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        opk.s[j] = f32_to_bf16(bf16_to_f32(kk[j]) * fast_exp2(SG[i0 + j][ch]));
+                } else {
+                    opk.u = *reinterpret_cast<const uint4 *>(&SVT[M::tpos(ch, i0)]);
                 }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) sT[16 * a + rr][16 * b + cc0 + q] = y[q];
-        }
-        __syncthreads();
-        float xo[4] = {0.f, 0.f, 0.f, 0.f};
-        if (act) {
-#pragma unroll
-            for (int kk = 0; kk < 16; ++kk) {
-                const float xa = sT[16 * a + rr][16 * a + kk];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) xo[q] -= xa * sT[16 * a + kk][16 * b + cc0 + q];
-            }
-        }
-        __syncthreads();
-        if (act) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) sT[16 * a + rr][16 * b + cc0 + q] = xo[q];
-        }
-        __syncthreads();
-    }
-
-    // ---- 4. W^T = (k e^G)^T T^T  (bf16)  and  U = T V  (T split)
-    //      T[r][i] = X[r][i] * beta_i.  Wave w: channel tiles ct = w, w+4, ...
-    for (int ct = wave; ct < Y::NDT; ct += 4) {
-        const int ch = 16 * ct + li;
-        f32x4 accW[Y::NMT], accU[Y::NMT];
-#pragma unroll
-        for (int tt = 0; tt < Y::NMT; ++tt) {
-            accW[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            accU[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int s = 0; s < Y::KSC; ++s) {
-            frag8 kt, vb;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int i = 32 * s + 8 * g + j;
-                kt.s[j] = f32_to_bf16(bf16_to_f32(sk[i][ch]) * fast_exp2(sG[i][ch]));
-                vb.s[j] = sv[i][ch];
+                for (int tt = 0; tt < Y::NMT; ++tt) {
+                    if (32 * s2 > 16 * tt + 15) continue;
+                    const int r = 16 * tt + li;
+                    if (isW) {
+                        frag8 tb;
+                        tb.u = *reinterpret_cast<const uint4 *>(&TB[r][i0]);
+                        acc[tt] = mfma16(opk.v, tb.v, acc[tt]);   // rows: channels, cols: tokens
+                    } else {
+                        frag8 th, tl;
+                        th.u = *reinterpret_cast<const uint4 *>(&TH[r][i0]);
+                        tl.u = *reinterpret_cast<const uint4 *>(&TL[r][i0]);
+                        acc[tt] = mfma16(th.v, opk.v, acc[tt]);   // rows: tokens, cols: channels
+                        acc[tt] = mfma16(tl.v, opk.v, acc[tt]);
+                    }
+                }
             }
 #pragma unroll
             for (int tt = 0; tt < Y::NMT; ++tt) {
-                if (32 * s > 16 * tt + 15) continue;
-                const int r = 16 * tt + li;
-                frag8 tb, th, tl;
+                if (isW) {
+                    bf16_t wb[4];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int i = 32 * s + 8 * g + j;
-                    const float tv = sT[r][i] * sbeta[i];
-                    tb.s[j] = f32_to_bf16(tv);
-                    split_bf16(tv, th.s[j], tl.s[j]);
+                    for (int j = 0; j < 4; ++j) wb[j] = f32_to_bf16(acc[tt][j]);
+                    const size_t fo = ((static_cast<size_t>(tt) * Y::KSD + ct / 2) * 64 + lane) * 16 + (ct & 1) * 8;
+                    *reinterpret_cast<uint2 *>(blk + Y::W + fo) = pack4(wb);
+                } else {
+                    *reinterpret_cast<f32x4 *>(blk + Y::U + ((static_cast<size_t>(tt) * Y::NDT + ct) * 64 + lane) * 16) =
+                        acc[tt];
                 }
-                accW[tt] = mfma16(kt.v, tb.v, accW[tt]);  // rows: channels, cols: tokens
-                accU[tt] = mfma16(th.v, vb.v, accU[tt]);  // rows: tokens, cols: channels
-                accU[tt] = mfma16(tl.v, vb.v, accU[tt]);
             }
         }
-#pragma unroll
-        for (int tt = 0; tt < Y::NMT; ++tt) {
-            bf16_t wb[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) wb[j] = f32_to_bf16(accW[tt][j]);
-            const size_t fo = ((static_cast<size_t>(tt) * Y::KSD + ct / 2) * 64 + lane) * 16 + (ct & 1) * 8;
-            *reinterpret_cast<uint2 *>(blk + Y::W + fo) = pack4(wb);
-            *reinterpret_cast<f32x4 *>(blk + Y::U + ((static_cast<size_t>(tt) * Y::NDT + ct) * 64 + lane) * 16) =
-                accU[tt];
-        }
+        __syncthreads();  // LDS is restaged by the next item
+        it = itn;
     }
-
-    // ---- 5. q e^G (split, scan A-operand order), (k e^{G_L - G})^T (split), e^{G_L}
-    for (int f = wave; f < Y::NMT * Y::KSD; f += 4) {
-        const int mt = f / Y::KSD, ks = f % Y::KSD;
-        const int r = 16 * mt + li;
-        frag8 hi, lo;
-        uint2 q0 = make_uint2(0, 0), q1 = make_uint2(0, 0);
-        if (r < L) {
-            const bf16_t *qp = Qg + ((t0 + r) * H + h) * D + 32 * ks + 4 * g;
-            q0 = *reinterpret_cast<const uint2 *>(qp);
-            q1 = *reinterpret_cast<const uint2 *>(qp + 16);
-        }
-        const bf16_t *qa = reinterpret_cast<const bf16_t *>(&q0);
-        const bf16_t *qb = reinterpret_cast<const bf16_t *>(&q1);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int ch = 32 * ks + kperm(g, j);
-            const float qv = bf16_to_f32(j < 4 ? qa[j] : qb[j - 4]);
-            split_bf16(qv * fast_exp2(sG[r][ch]), hi.s[j], lo.s[j]);
-        }
-        const size_t fo = (static_cast<size_t>(f) * 64 + lane) * 16;
-        st16(blk + Y::QH + fo, hi.u);
-        st16(blk + Y::QL + fo, lo.u);
-    }
-    for (int f = wave; f < Y::NDT * Y::KSC; f += 4) {
-        const int mt = f / Y::KSC, ks = f % Y::KSC;
-        const int ch = 16 * mt + li;
-        const float gl = sG[C - 1][ch];
-        frag8 hi, lo;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int i = 32 * ks + kperm(g, j);
-            split_bf16(bf16_to_f32(sk[i][ch]) * fast_exp2(gl - sG[i][ch]), hi.s[j], lo.s[j]);
-        }
-        const size_t fo = (static_cast<size_t>(f) * 64 + lane) * 16;
-        st16(blk + Y::KBH + fo, hi.u);
-        st16(blk + Y::KBL + fo, lo.u);
-    }
-    for (int ch = tid; ch < D; ch += 256)
-        reinterpret_cast<float *>(blk + Y::GAM)[ch] = fast_exp2(sG[C - 1][ch]);
 }
 
 // ------------------------------------------------------------------ K2 --
+// Everything one wave of the scan reads from a chunk's workspace block.
+template <int C, int D>
+struct ScanOps {
+    using Y = Lay<C, D>;
+    static constexpr int NW = D / 32;
+    static constexpr int OWN = (Y::NMT + NW - 1) / NW;
+    frag8 w[Y::NMT], qh[Y::NMT], ql[Y::NMT];   // token tile mt, channel step = wave
+    f32x4 u[OWN];                               // owned token tiles, this column tile
+    frag8 ph[OWN][Y::KSC], pl[OWN][Y::KSC];    // owned token tiles x token steps
+    frag8 kh[2][Y::KSC], kl[2][Y::KSC];        // the wave's two channel tiles x token steps
+    f32x4 gam[2];
+
+    __device__ __forceinline__ void load(const char *blk, int wv, int nt, int lane) {
+        const int g = lane >> 4;
+#pragma unroll
+        for (int mt = 0; mt < Y::NMT; ++mt) {
+            const size_t fo = ((static_cast<size_t>(mt) * Y::KSD + wv) * 64 + lane) * 16;
+            w[mt].u = ld16(blk + Y::W + fo);
+            qh[mt].u = ld16(blk + Y::QH + fo);
+            ql[mt].u = ld16(blk + Y::QL + fo);
+        }
+#pragma unroll
+        for (int uu = 0; uu < OWN; ++uu) {
+            const int mt = wv + uu * NW;
+            if (mt >= Y::NMT) continue;
+            u[uu] = ldf4(blk + Y::U + ((static_cast<size_t>(mt) * Y::NDT + nt) * 64 + lane) * 16);
+#pragma unroll
+            for (int st = 0; st < Y::KSC; ++st) {
+                if (32 * st > 16 * mt + 15) continue;
+                const size_t fo = ((static_cast<size_t>(mt) * Y::KSC + st) * 64 + lane) * 16;
+                ph[uu][st].u = ld16(blk + Y::PH + fo);
+                pl[uu][st].u = ld16(blk + Y::PL + fo);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+#pragma unroll
+            for (int st = 0; st < Y::KSC; ++st) {
+                const size_t fo = ((static_cast<size_t>(2 * wv + i) * Y::KSC + st) * 64 + lane) * 16;
+                kh[i][st].u = ld16(blk + Y::KBH + fo);
+                kl[i][st].u = ld16(blk + Y::KBL + fo);
+            }
+            gam[i] = ldf4(blk + Y::GAM + (32 * wv + 16 * i + 4 * g) * sizeof(float));
+        }
+    }
+};
+
+template <int C, int D>
+struct ScanShared {
+    using Y = Lay<C, D>;
+    f32x4 red[2][D / 32][Y::NMT][64];
+    uint4 dls[Y::NMT][64];
+};
+
+// One chunk of the scan for one wave: consumes the operands in `op` and
+// updates the state tiles S in place.
+template <int C, int D, typename TO>
+__device__ __forceinline__ void scan_chunk(const ScanOps<C, D> &op, f32x4 (&S)[2], ScanShared<C, D> &sh,
+                                           const PrefillParams &p, int64_t x, int64_t t0, int L, int h,
+                                           int w, int nt, int lane) {
+    using Y = Lay<C, D>;
+    constexpr int NW = D / 32;
+    constexpr int OWN = ScanOps<C, D>::OWN;
+    const int g = lane >> 4, li = lane & 15;
+    const int col = 16 * nt + li;
+    const int H = p.H;
+    if (p.chunk_states) {
+        float *cs = p.chunk_states + (x * H + h) * static_cast<int64_t>(D) * D;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cs[static_cast<int64_t>(32 * w + 16 * i + 4 * g + j) * D + col] = S[i][j];
+    }
+    // (a) this wave's state rows as a B operand, hi/lo
+    frag8 sh_, sl_;
+    acc2_to_split(S[0], S[1], sh_, sl_);
+    // (b) partial W S and (q e^G) S over this wave's 32 channels
+#pragma unroll
+    for (int mt = 0; mt < Y::NMT; ++mt) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        sh.red[0][w][mt][lane] = mfma16(op.w[mt].v, sh_.v, z);
+        f32x4 pq = mfma16(op.qh[mt].v, sh_.v, z);
+        pq = mfma16(op.qh[mt].v, sl_.v, pq);
+        pq = mfma16(op.ql[mt].v, sh_.v, pq);
+        sh.red[1][w][mt][lane] = pq;
+    }
+    __syncthreads();
+    // (c) reduce the owned token tiles: Delta = U - sum_w W S
+    f32x4 oq[OWN];
+#pragma unroll
+    for (int uu = 0; uu < OWN; ++uu) {
+        const int mt = w + uu * NW;
+        if (mt >= Y::NMT) continue;
+        f32x4 d = op.u[uu];
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+            d -= sh.red[0][ww][mt][lane];
+            acc += sh.red[1][ww][mt][lane];
+        }
+        oq[uu] = acc;
+        bf16_t hi[4], lo[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) split_bf16(d[j], hi[j], lo[j]);
+        const uint2 ph = pack4(hi), pl = pack4(lo);
+        sh.dls[mt][lane] = make_uint4(ph.x, ph.y, pl.x, pl.y);
+    }
+    __syncthreads();
+    // (d) Delta as B operands, one per 32-token step
+    frag8 dh[Y::KSC], dl[Y::KSC];
+#pragma unroll
+    for (int st = 0; st < Y::KSC; ++st) {
+        const uint4 a0 = sh.dls[2 * st][lane];
+        const uint4 a1 = (2 * st + 1 < Y::NMT) ? sh.dls[2 * st + 1][lane] : make_uint4(0, 0, 0, 0);
+        dh[st].u = make_uint4(a0.x, a0.y, a1.x, a1.y);
+        dl[st].u = make_uint4(a0.z, a0.w, a1.z, a1.w);
+    }
+    // (e) outputs of the owned token tiles: O = (q e^G) S + P Delta
+    TO *o = static_cast<TO *>(p.o);
+#pragma unroll
+    for (int uu = 0; uu < OWN; ++uu) {
+        const int mt = w + uu * NW;
+        if (mt >= Y::NMT) continue;
+        f32x4 acc = oq[uu];
+#pragma unroll
+        for (int st = 0; st < Y::KSC; ++st) {
+            if (32 * st > 16 * mt + 15) continue;
+            acc = mfma16(op.ph[uu][st].v, dh[st].v, acc);
+            acc = mfma16(op.ph[uu][st].v, dl[st].v, acc);
+            acc = mfma16(op.pl[uu][st].v, dh[st].v, acc);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int tok = 16 * mt + 4 * g + j;
+            if (tok < L) io<TO>::st(o, ((t0 + tok) * H + h) * D + col, acc[j]);
+        }
+    }
+    // (f) state: S = e^{G_L} S + (k e^{G_L - G})^T Delta
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        S[i] *= op.gam[i];
+#pragma unroll
+        for (int st = 0; st < Y::KSC; ++st) {
+            S[i] = mfma16(op.kh[i][st].v, dh[st].v, S[i]);
+            S[i] = mfma16(op.kh[i][st].v, dl[st].v, S[i]);
+            S[i] = mfma16(op.kl[i][st].v, dh[st].v, S[i]);
+        }
+    }
+}
+
 template <int C, int D, typename TO>
 __global__ void __launch_bounds__(64 * (D / 32)) scan_kernel(PrefillParams p, const char *__restrict__ blocks) {
     using Y = Lay<C, D>;
-    constexpr int NW = D / 32;    // waves; wave w owns state rows [32w, 32w + 32)
     constexpr int NVT = D / 16;   // 16-column state tiles per head
-    constexpr int OWN = (Y::NMT + NW - 1) / NW;  // token tiles reduced per wave
     if (*p.status != 0) return;
     // XCD-aware order: the NVT column tiles of one (sequence, head) share
     // blockIdx % 8, hence one XCD and its L2.
@@ -414,10 +703,8 @@ __global__ void __launch_bounds__(64 * (D / 32)) scan_kernel(PrefillParams p, co
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int g = lane >> 4, li = lane & 15;
     const int col = 16 * nt + li;
-    TO *o = static_cast<TO *>(p.o);
 
-    __shared__ f32x4 red[2][NW][Y::NMT][64];
-    __shared__ uint4 dls[Y::NMT][64];
+    __shared__ ScanShared<C, D> sh;
 
     const int64_t soff = (static_cast<int64_t>(n) * H + h) * D * D;
     f32x4 S[2];
@@ -429,109 +716,22 @@ __global__ void __launch_bounds__(64 * (D / 32)) scan_kernel(PrefillParams p, co
             S[i][j] = p.initial_state ? p.initial_state[soff + static_cast<int64_t>(row) * D + col] : 0.f;
         }
 
-    for (int c = 0; c < nch; ++c) {
-        const int64_t x = cbase + c;
-        const char *blk = blocks + (static_cast<size_t>(x) * H + h) * Y::BYTES;
-        const int64_t t0 = sr.start + static_cast<int64_t>(c) * C;
-        const int L = min(C, sr.len - c * C);
-        if (p.chunk_states) {
-            float *cs = p.chunk_states + (x * H + h) * static_cast<int64_t>(D) * D;
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    cs[static_cast<int64_t>(32 * w + 16 * i + 4 * g + j) * D + col] = S[i][j];
-        }
-        // (a) state rows of this wave as a B operand, hi/lo
-        frag8 sh, sl;
-        acc2_to_split(S[0], S[1], sh, sl);
-        // (b) partial W S and (q e^G) S over this wave's 32 channels
-#pragma unroll
-        for (int mt = 0; mt < Y::NMT; ++mt) {
-            const size_t fo = ((static_cast<size_t>(mt) * Y::KSD + w) * 64 + lane) * 16;
-            frag8 wf, qh, ql;
-            wf.u = ld16(blk + Y::W + fo);
-            qh.u = ld16(blk + Y::QH + fo);
-            ql.u = ld16(blk + Y::QL + fo);
-            f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            red[0][w][mt][lane] = mfma16(wf.v, sh.v, z);
-            f32x4 pq = mfma16(qh.v, sh.v, z);
-            pq = mfma16(qh.v, sl.v, pq);
-            pq = mfma16(ql.v, sh.v, pq);
-            red[1][w][mt][lane] = pq;
-        }
-        __syncthreads();
-        // (c) reduce the token tiles this wave owns: Delta = U - sum W S
-        f32x4 oq[OWN];
-#pragma unroll
-        for (int u = 0; u < OWN; ++u) {
-            const int mt = w + u * NW;
-            if (mt >= Y::NMT) continue;
-            f32x4 d = ldf4(blk + Y::U + ((static_cast<size_t>(mt) * Y::NDT + nt) * 64 + lane) * 16);
-            f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) {
-                d -= red[0][ww][mt][lane];
-                s += red[1][ww][mt][lane];
-            }
-            oq[u] = s;
-            frag8 dd;
-            bf16_t hi[4], lo[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) split_bf16(d[j], hi[j], lo[j]);
-            const uint2 ph = pack4(hi), pl = pack4(lo);
-            dls[mt][lane] = make_uint4(ph.x, ph.y, pl.x, pl.y);
-        }
-        __syncthreads();
-        // (d) Delta as B operands, one per 32-token k step
-        frag8 dh[Y::KSC], dl[Y::KSC];
-#pragma unroll
-        for (int s = 0; s < Y::KSC; ++s) {
-            const uint4 t0v = dls[2 * s][lane];
-            const uint4 t1v = (2 * s + 1 < Y::NMT) ? dls[2 * s + 1][lane] : make_uint4(0, 0, 0, 0);
-            dh[s].u = make_uint4(t0v.x, t0v.y, t1v.x, t1v.y);
-            dl[s].u = make_uint4(t0v.z, t0v.w, t1v.z, t1v.w);
-        }
-        // (e) outputs of the owned token tiles: O = (q e^G) S + P Delta
-#pragma unroll
-        for (int u = 0; u < OWN; ++u) {
-            const int mt = w + u * NW;
-            if (mt >= Y::NMT) continue;
-            f32x4 acc = oq[u];
-#pragma unroll
-            for (int s = 0; s < Y::KSC; ++s) {
-                if (32 * s > 16 * mt + 15) continue;
-                const size_t fo = ((static_cast<size_t>(mt) * Y::KSC + s) * 64 + lane) * 16;
-                frag8 ph, pl;
-                ph.u = ld16(blk + Y::PH + fo);
-                pl.u = ld16(blk + Y::PL + fo);
-                acc = mfma16(ph.v, dh[s].v, acc);
-                acc = mfma16(ph.v, dl[s].v, acc);
-                acc = mfma16(pl.v, dh[s].v, acc);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int tok = 16 * mt + 4 * g + j;
-                if (tok < L) io<TO>::st(o, ((t0 + tok) * H + h) * D + col, acc[j]);
-            }
-        }
-        // (f) state: S = e^{G_L} S + (k e^{G_L - G})^T Delta
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int mtc = 2 * w + i;
-            const f32x4 gam = ldf4(blk + Y::GAM + (32 * w + 16 * i + 4 * g) * sizeof(float));
-            S[i] *= gam;
-#pragma unroll
-            for (int s = 0; s < Y::KSC; ++s) {
-                const size_t fo = ((static_cast<size_t>(mtc) * Y::KSC + s) * 64 + lane) * 16;
-                frag8 kh, kl;
-                kh.u = ld16(blk + Y::KBH + fo);
-                kl.u = ld16(blk + Y::KBL + fo);
-                S[i] = mfma16(kh.v, dh[s].v, S[i]);
-                S[i] = mfma16(kh.v, dl[s].v, S[i]);
-                S[i] = mfma16(kl.v, dh[s].v, S[i]);
-            }
-        }
+    auto blk_of = [&](int c) {
+        return blocks + (static_cast<size_t>(cbase + c) * H + h) * Y::BYTES;
+    };
+    // Two operand buffers: chunk c+1's loads are in flight while chunk c is
+    // computed, so the memory latency of the workspace is hidden behind the
+    // chunk's matrix work.
+    ScanOps<C, D> b0, b1;
+    if (nch > 0) b0.load(blk_of(0), w, nt, lane);
+    for (int c = 0; c < nch; c += 2) {
+        if (c + 1 < nch) b1.load(blk_of(c + 1), w, nt, lane);
+        scan_chunk<C, D, TO>(b0, S, sh, p, cbase + c, sr.start + static_cast<int64_t>(c) * C,
+                             min(C, sr.len - c * C), h, w, nt, lane);
+        if (c + 1 >= nch) break;
+        if (c + 2 < nch) b0.load(blk_of(c + 2), w, nt, lane);
+        scan_chunk<C, D, TO>(b1, S, sh, p, cbase + c + 1, sr.start + static_cast<int64_t>(c + 1) * C,
+                             min(C, sr.len - (c + 1) * C), h, w, nt, lane);
     }
     if (p.final_state) {
 #pragma unroll
@@ -561,7 +761,9 @@ bool mfma_supported(int dk, int dv, int C) {
 namespace {
 template <int C, int D, typename TO>
 hipError_t run_mfma(const PrefillParams &p, char *blocks, hipStream_t s, hipEvent_t mid) {
-    hipLaunchKernelGGL((intra_kernel<C, D>), dim3(p.n_chunks_bound, p.H), dim3(256), 0, s, p, blocks);
+    const int items = p.n_chunks_bound * p.H;  // upper bound; the kernel reads the exact count
+    const int igrid = items < kIntraGrid ? items : kIntraGrid;
+    hipLaunchKernelGGL((intra_kernel<C, D>), dim3(igrid), dim3(512), 0, s, p, blocks);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && mid) e = hipEventRecord(mid, s);
     if (e != hipSuccess) return e;
