@@ -134,9 +134,12 @@ struct IntraLds {
 template <int C, int D>
 struct IntraRaw {
     using M = IntraLds<C, D>;
+    // Raw bits only, loaded from rows clamped into [0, L): nothing here
+    // depends on the loaded values, so the loads stay in flight until the
+    // next item stages them (rows >= L are zeroed there).
     uint4 k[M::NV], v[M::NV], q[M::NV];
-    float g[M::RP];
-    float beta;
+    uint32_t g[M::RP];
+    uint32_t beta;
 
     __device__ __forceinline__ void load(const PrefillParams &p, int64_t t0, int L, int h, int tid) {
         const bf16_t *Kg = static_cast<const bf16_t *>(p.k);
@@ -147,23 +150,20 @@ struct IntraRaw {
         const int H = p.H;
 #pragma unroll
         for (int u = 0; u < M::NV; ++u) {
-            const int e = tid + 512 * u;
-            const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
-            k[u] = v[u] = q[u] = make_uint4(0, 0, 0, 0);
-            if (e < M::NVEC && r < L) {
-                const int64_t off = ((t0 + r) * H + h) * D + c8;
-                k[u] = *reinterpret_cast<const uint4 *>(Kg + off);
-                v[u] = *reinterpret_cast<const uint4 *>(Vg + off);
-                q[u] = *reinterpret_cast<const uint4 *>(Qg + off);
-            }
+            const int e = min(tid + 512 * u, M::NVEC - 1);
+            const int r = min(e / (D / 8), L - 1), c8 = (e % (D / 8)) * 8;
+            const int64_t off = ((t0 + r) * H + h) * D + c8;
+            k[u] = *reinterpret_cast<const uint4 *>(Kg + off);
+            v[u] = *reinterpret_cast<const uint4 *>(Vg + off);
+            q[u] = *reinterpret_cast<const uint4 *>(Qg + off);
         }
         const int ch = tid % D, part = tid / D;
 #pragma unroll
         for (int j = 0; j < M::RP; ++j) {
-            const int r = part * M::RP + j;
-            g[j] = r < L ? bf16_to_f32(Ag[((t0 + r) * H + h) * D + ch]) : 0.f;
+            const int r = min(part * M::RP + j, L - 1);
+            g[j] = Ag[((t0 + r) * H + h) * D + ch];
         }
-        beta = (tid < L) ? bf16_to_f32(Bg[(t0 + tid) * H + h]) : 0.f;
+        beta = Bg[(t0 + min(tid, L - 1)) * H + h];
     }
 };
 
@@ -234,17 +234,20 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
             const int e = tid + 512 * u;
             if (e >= M::NVEC) continue;
             const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
-            *reinterpret_cast<uint4 *>(&SK[r][c8]) = raw.k[u];
-            *reinterpret_cast<uint4 *>(&SQ[r][c8]) = raw.q[u];
-            const bf16_t *kb = reinterpret_cast<const bf16_t *>(&raw.k[u]);
-            const bf16_t *vb = reinterpret_cast<const bf16_t *>(&raw.v[u]);
+            const bool live = r < L;
+            const uint4 z = make_uint4(0, 0, 0, 0);
+            const uint4 kv = live ? raw.k[u] : z, vv = live ? raw.v[u] : z, qv = live ? raw.q[u] : z;
+            *reinterpret_cast<uint4 *>(&SK[r][c8]) = kv;
+            *reinterpret_cast<uint4 *>(&SQ[r][c8]) = qv;
+            const bf16_t *kb = reinterpret_cast<const bf16_t *>(&kv);
+            const bf16_t *vb = reinterpret_cast<const bf16_t *>(&vv);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 SKT[M::tpos(c8 + j, r)] = kb[j];
                 SVT[M::tpos(c8 + j, r)] = vb[j];
             }
         }
-        if (tid < CP) SBETA[tid] = raw.beta;
+        if (tid < CP) SBETA[tid] = tid < L ? bf16_to_f32(static_cast<bf16_t>(raw.beta)) : 0.f;
         for (int e = tid; e < CP * M::RA; e += 512) {
             (&SA[0][0])[e] = 0.f;
             (&SX[0][0])[e] = 0.f;
@@ -252,7 +255,8 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
         const int cch = tid % D, part = tid / D;
         float gv[M::RP];
 #pragma unroll
-        for (int j = 0; j < M::RP; ++j) gv[j] = raw.g[j];
+        for (int j = 0; j < M::RP; ++j)
+            gv[j] = (part * M::RP + j < L) ? bf16_to_f32(static_cast<bf16_t>(raw.g[j])) : 0.f;
 #pragma unroll
         for (int j = 1; j < M::RP; ++j) gv[j] += gv[j - 1];
         SPART[part][cch] = gv[M::RP - 1];
@@ -319,18 +323,34 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
                     accP = mfma16(kil.v, qrh.v, accP);
                 }
             } else {
-                // exact pairwise diagonal block: lane holds (i = 16a + 4g + j, r)
-                for (int ch = 0; ch < D; ++ch) {
-                    const float gr = SG[r][ch];
-                    const float kr_ = bf16_to_f32(SK[r][ch]);
-                    const float qr_ = bf16_to_f32(SQ[r][ch]);
+                // exact pairwise diagonal block: lane holds (i = 16a + 4g + j, r);
+                // eight channels per step, all operands as 16-byte LDS reads
+#pragma unroll 2
+                for (int c8 = 0; c8 < D; c8 += 8) {
+                    const uint4 kr8 = *reinterpret_cast<const uint4 *>(&SK[r][c8]);
+                    const uint4 qr8 = *reinterpret_cast<const uint4 *>(&SQ[r][c8]);
+                    const f32x4 gr0 = *reinterpret_cast<const f32x4 *>(&SG[r][c8]);
+                    const f32x4 gr1 = *reinterpret_cast<const f32x4 *>(&SG[r][c8 + 4]);
+                    const bf16_t *krb = reinterpret_cast<const bf16_t *>(&kr8);
+                    const bf16_t *qrb = reinterpret_cast<const bf16_t *>(&qr8);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int i = 16 * a + 4 * g + j;
+                        const uint4 ki8 = *reinterpret_cast<const uint4 *>(&SK[i][c8]);
+                        const f32x4 gi0 = *reinterpret_cast<const f32x4 *>(&SG[i][c8]);
+                        const f32x4 gi1 = *reinterpret_cast<const f32x4 *>(&SG[i][c8 + 4]);
+                        const bf16_t *kib = reinterpret_cast<const bf16_t *>(&ki8);
+                        float sa = 0.f, sp = 0.f;
+#pragma unroll
+                        for (int c = 0; c < 8; ++c) {
+                            const float gd = (c < 4 ? gr0[c] : gr1[c - 4]) - (c < 4 ? gi0[c] : gi1[c - 4]);
+                            const float f = bf16_to_f32(kib[c]) * fast_exp2(fminf(gd, 0.f));
+                            sa += bf16_to_f32(krb[c]) * f;
+                            sp += bf16_to_f32(qrb[c]) * f;
+                        }
                         if (i <= r) {
-                            const float f = bf16_to_f32(SK[i][ch]) * fast_exp2(gr - SG[i][ch]);
-                            accA[j] += kr_ * f;
-                            accP[j] += qr_ * f;
+                            accA[j] += sa;
+                            accP[j] += sp;
                         }
                     }
                 }
@@ -355,8 +375,11 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
             }
         }
 
-        // ---- 2b. q e^G (scan A-operand order), (k e^{G_L - G})^T, e^{G_L}
-        for (int f = wave; f < Y::NMT * Y::KSD + Y::NDT * Y::KSC; f += 8) {
+        // ---- 2b. q e^G (scan A-operand order), (k e^{G_L - G})^T, e^{G_L}.
+        //      Waves that had two Gram block pairs sit this out.
+        constexpr int NTWO = NPAIR > 8 ? NPAIR - 8 : 0;  // waves 0..NTWO-1 did two pairs
+        constexpr int N2B = 8 - NTWO;
+        for (int f = wave - NTWO; wave >= NTWO && f < Y::NMT * Y::KSD + Y::NDT * Y::KSC; f += N2B) {
             frag8 hi, lo;
             size_t dst_h, dst_l;
             if (f < Y::NMT * Y::KSD) {
@@ -429,33 +452,38 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
             for (int rr = 0; rr < 16; ++rr) SX[base + rr][base + jj] = xc[rr];
         }
         __syncthreads();
-#pragma unroll
-        for (int lev = 1; lev < Y::NMT; ++lev) {
-            // block (a, b), a - b = lev, handled by wave b
-            const bool act = wave < Y::NMT - lev;
-            const int b = wave, a = wave + lev;
+        // Off-diagonal blocks, one column block b per wave, top to bottom:
+        //   X_ab = -X_aa sum_{c=b}^{a-1} A_ac X_cb   (a > b)
+        // Only this wave writes column block b; X_aa and A come from the
+        // previous phase, so no barrier is needed between the steps (the
+        // wave's own LDS writes are ordered before its later reads).
+        if (wave < Y::NMT - 1) {
+            const int b = wave;
             const int rr = lane >> 2, cc0 = (lane & 3) * 4;
-            f32x4 y = {0.f, 0.f, 0.f, 0.f};
-            if (act) {
+            for (int a = b + 1; a < Y::NMT; ++a) {
+                f32x4 y = {0.f, 0.f, 0.f, 0.f};
                 for (int c = b; c < a; ++c)
 #pragma unroll
                     for (int kk = 0; kk < 16; ++kk)
                         y += SA[16 * a + rr][16 * c + kk] *
                              *reinterpret_cast<const f32x4 *>(&SX[16 * c + kk][16 * b + cc0]);
+                // y -> LDS scratch (row block a of column b, not yet final)
                 *reinterpret_cast<f32x4 *>(&SX[16 * a + rr][16 * b + cc0]) = y;
-            }
-            __syncthreads();
-            f32x4 xo = {0.f, 0.f, 0.f, 0.f};
-            if (act) {
+                __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): y visible to the wave
+                __builtin_amdgcn_wave_barrier();
+                f32x4 xo = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < 16; ++kk)
                     xo -= SX[16 * a + rr][16 * a + kk] *
                           *reinterpret_cast<const f32x4 *>(&SX[16 * a + kk][16 * b + cc0]);
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+                __builtin_amdgcn_wave_barrier();
+                *reinterpret_cast<f32x4 *>(&SX[16 * a + rr][16 * b + cc0]) = xo;
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+                __builtin_amdgcn_wave_barrier();
             }
-            __syncthreads();
-            if (act) *reinterpret_cast<f32x4 *>(&SX[16 * a + rr][16 * b + cc0]) = xo;
-            __syncthreads();
         }
+        __syncthreads();
 
         // ---- 3b. T = X Diag(beta) as MFMA operands: bf16, and hi/lo (q, A dead)
         for (int e = tid; e < CP * CP / 4; e += 512) {
