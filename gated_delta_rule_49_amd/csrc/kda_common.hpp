@@ -92,4 +92,15 @@ __device__ __forceinline__ void acc2_to_bf16(const f32x4 &t0, const f32x4 &t1, f
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() is a
+// workgroup-scope fence over all memory, so it waits for every outstanding
+// global load and store of the wave (s_waitcnt vmcnt(0)); kernels whose
+// waves exchange data only through LDS use this instead so that prefetched
+// loads and workspace stores stay in flight across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace kda

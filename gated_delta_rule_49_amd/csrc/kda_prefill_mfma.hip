@@ -267,14 +267,14 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
             itn = intra_item<C>(p, next);
             raw.load(p, itn.t0, itn.L, itn.h, tid);
         }
-        __syncthreads();
+        lds_barrier();
         {
             float off = 0.f;
             for (int q2 = 0; q2 < part; ++q2) off += SPART[q2][cch];
 #pragma unroll
             for (int j = 0; j < M::RP; ++j) SG[part * M::RP + j][cch] = (off + gv[j]) * kLog2e;
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- 2. Gram blocks A^T(b,a), P^T(b,a) for b <= a, one block pair
         //         per wave at a time.  Factors around reference row
@@ -423,7 +423,7 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
             st16(blk + dst_l, lo.u);
         }
         if (tid < D) reinterpret_cast<float *>(blk + Y::GAM)[tid] = fast_exp2(SG[C - 1][tid]);
-        __syncthreads();
+        lds_barrier();
 
         // ---- 3. X = (I + A)^-1 by blocked forward substitution (fp32 VALU).
         //         Diagonal blocks: lane jj owns column jj; row rr of A_aa is
@@ -451,7 +451,7 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) SX[base + rr][base + jj] = xc[rr];
         }
-        __syncthreads();
+        lds_barrier();
         // Off-diagonal blocks, one column block b per wave, top to bottom:
         //   X_ab = -X_aa sum_{c=b}^{a-1} A_ac X_cb   (a > b)
         // Only this wave writes column block b; X_aa and A come from the
@@ -483,7 +483,7 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
                 __builtin_amdgcn_wave_barrier();
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- 3b. T = X Diag(beta) as MFMA operands: bf16, and hi/lo (q, A dead)
         for (int e = tid; e < CP * CP / 4; e += 512) {
@@ -500,7 +500,7 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
             *reinterpret_cast<uint2 *>(&TH[r][i4]) = pack4(th);
             *reinterpret_cast<uint2 *>(&TL[r][i4]) = pack4(tl);
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- 4. W^T = (k e^G)^T T^T (bf16) per channel tile; U = T V (T split)
         //         per value tile.  Items: NDT W tiles then NDT U tiles.
@@ -555,26 +555,22 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
                 }
             }
         }
-        __syncthreads();  // LDS is restaged by the next item
+        lds_barrier();  // LDS is restaged by the next item
         it = itn;
     }
 }
 
 // ------------------------------------------------------------------ K2 --
-// Everything one wave of the scan reads from a chunk's workspace block.
+// What one wave of the scan reads from a chunk's workspace block, in two
+// groups: the operands of the first products (W and q e^G, needed as soon as
+// the chunk starts; prefetched one chunk ahead) and the rest (needed only
+// after the two exchanges through LDS; requested when the chunk starts).
 template <int C, int D>
-struct ScanOps {
+struct ScanEarly {
     using Y = Lay<C, D>;
-    static constexpr int NW = D / 32;
-    static constexpr int OWN = (Y::NMT + NW - 1) / NW;
     frag8 w[Y::NMT], qh[Y::NMT], ql[Y::NMT];   // token tile mt, channel step = wave
-    f32x4 u[OWN];                               // owned token tiles, this column tile
-    frag8 ph[OWN][Y::KSC], pl[OWN][Y::KSC];    // owned token tiles x token steps
-    frag8 kh[2][Y::KSC], kl[2][Y::KSC];        // the wave's two channel tiles x token steps
-    f32x4 gam[2];
 
-    __device__ __forceinline__ void load(const char *blk, int wv, int nt, int lane) {
-        const int g = lane >> 4;
+    __device__ __forceinline__ void load(const char *blk, int wv, int lane) {
 #pragma unroll
         for (int mt = 0; mt < Y::NMT; ++mt) {
             const size_t fo = ((static_cast<size_t>(mt) * Y::KSD + wv) * 64 + lane) * 16;
@@ -582,6 +578,23 @@ struct ScanOps {
             qh[mt].u = ld16(blk + Y::QH + fo);
             ql[mt].u = ld16(blk + Y::QL + fo);
         }
+    }
+};
+
+template <int C, int D>
+struct ScanLate {
+    using Y = Lay<C, D>;
+    static constexpr int NW = D / 32;
+    static constexpr int OWN = (Y::NMT + NW - 1) / NW;
+    f32x4 gam[2];
+    f32x4 u[OWN];                               // owned token tiles, this column tile
+    frag8 ph[OWN][Y::KSC], pl[OWN][Y::KSC];    // owned token tiles x token steps
+    frag8 kh[2][Y::KSC], kl[2][Y::KSC];        // the wave's two channel tiles x token steps
+
+    __device__ __forceinline__ void load(const char *blk, int wv, int nt, int lane) {
+        const int g = lane >> 4;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) gam[i] = ldf4(blk + Y::GAM + (32 * wv + 16 * i + 4 * g) * sizeof(float));
 #pragma unroll
         for (int uu = 0; uu < OWN; ++uu) {
             const int mt = wv + uu * NW;
@@ -603,7 +616,6 @@ struct ScanOps {
                 kh[i][st].u = ld16(blk + Y::KBH + fo);
                 kl[i][st].u = ld16(blk + Y::KBL + fo);
             }
-            gam[i] = ldf4(blk + Y::GAM + (32 * wv + 16 * i + 4 * g) * sizeof(float));
         }
     }
 };
@@ -618,12 +630,12 @@ struct ScanShared {
 // One chunk of the scan for one wave: consumes the operands in `op` and
 // updates the state tiles S in place.
 template <int C, int D, typename TO>
-__device__ __forceinline__ void scan_chunk(const ScanOps<C, D> &op, f32x4 (&S)[2], ScanShared<C, D> &sh,
-                                           const PrefillParams &p, int64_t x, int64_t t0, int L, int h,
-                                           int w, int nt, int lane) {
+__device__ __forceinline__ void scan_chunk(const ScanEarly<C, D> &ope, const ScanLate<C, D> &op, f32x4 (&S)[2],
+                                           ScanShared<C, D> &sh, const PrefillParams &p, int64_t x,
+                                           int64_t t0, int L, int h, int w, int nt, int lane) {
     using Y = Lay<C, D>;
     constexpr int NW = D / 32;
-    constexpr int OWN = ScanOps<C, D>::OWN;
+    constexpr int OWN = ScanLate<C, D>::OWN;
     const int g = lane >> 4, li = lane & 15;
     const int col = 16 * nt + li;
     const int H = p.H;
@@ -641,13 +653,13 @@ __device__ __forceinline__ void scan_chunk(const ScanOps<C, D> &op, f32x4 (&S)[2
 #pragma unroll
     for (int mt = 0; mt < Y::NMT; ++mt) {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        sh.red[0][w][mt][lane] = mfma16(op.w[mt].v, sh_.v, z);
-        f32x4 pq = mfma16(op.qh[mt].v, sh_.v, z);
-        pq = mfma16(op.qh[mt].v, sl_.v, pq);
-        pq = mfma16(op.ql[mt].v, sh_.v, pq);
+        sh.red[0][w][mt][lane] = mfma16(ope.w[mt].v, sh_.v, z);
+        f32x4 pq = mfma16(ope.qh[mt].v, sh_.v, z);
+        pq = mfma16(ope.qh[mt].v, sl_.v, pq);
+        pq = mfma16(ope.ql[mt].v, sh_.v, pq);
         sh.red[1][w][mt][lane] = pq;
     }
-    __syncthreads();
+    lds_barrier();
     // (c) reduce the owned token tiles: Delta = U - sum_w W S
     f32x4 oq[OWN];
 #pragma unroll
@@ -668,7 +680,7 @@ __device__ __forceinline__ void scan_chunk(const ScanOps<C, D> &op, f32x4 (&S)[2
         const uint2 ph = pack4(hi), pl = pack4(lo);
         sh.dls[mt][lane] = make_uint4(ph.x, ph.y, pl.x, pl.y);
     }
-    __syncthreads();
+    lds_barrier();
     // (d) Delta as B operands, one per 32-token step
     frag8 dh[Y::KSC], dl[Y::KSC];
 #pragma unroll
@@ -747,19 +759,26 @@ __global__ void __launch_bounds__(64 * (D / 32)) scan_kernel(PrefillParams p, co
     auto blk_of = [&](int c) {
         return blocks + (static_cast<size_t>(cbase + c) * H + h) * Y::BYTES;
     };
-    // Two operand buffers: chunk c+1's loads are in flight while chunk c is
-    // computed, so the memory latency of the workspace is hidden behind the
-    // chunk's matrix work.
-    ScanOps<C, D> b0, b1;
-    if (nch > 0) b0.load(blk_of(0), w, nt, lane);
-    for (int c = 0; c < nch; c += 2) {
-        if (c + 1 < nch) b1.load(blk_of(c + 1), w, nt, lane);
-        scan_chunk<C, D, TO>(b0, S, sh, p, cbase + c, sr.start + static_cast<int64_t>(c) * C,
-                             min(C, sr.len - c * C), h, w, nt, lane);
-        if (c + 1 >= nch) break;
-        if (c + 2 < nch) b0.load(blk_of(c + 2), w, nt, lane);
-        scan_chunk<C, D, TO>(b1, S, sh, p, cbase + c + 1, sr.start + static_cast<int64_t>(c + 1) * C,
-                             min(C, sr.len - (c + 1) * C), h, w, nt, lane);
+    // Per chunk c: its late operands are requested first, then chunk c+1's
+    // first operands, then chunk c is computed.  vmcnt retires in order, so
+    // waiting for chunk c's operands never waits for the prefetch behind
+    // them; the prefetch is unconditional (clamped chunk index) and the
+    // barriers order LDS only, so nothing else forces it to complete early.
+    ScanEarly<C, D> e0, e1;
+    ScanLate<C, D> lt;
+    if (nch > 0) {
+        e0.load(blk_of(0), w, lane);
+        for (int c = 0; c < nch; c += 2) {
+            lt.load(blk_of(c), w, nt, lane);
+            e1.load(blk_of(min(c + 1, nch - 1)), w, lane);
+            scan_chunk<C, D, TO>(e0, lt, S, sh, p, cbase + c, sr.start + static_cast<int64_t>(c) * C,
+                                 min(C, sr.len - c * C), h, w, nt, lane);
+            if (c + 1 >= nch) break;
+            lt.load(blk_of(c + 1), w, nt, lane);
+            e0.load(blk_of(min(c + 2, nch - 1)), w, lane);
+            scan_chunk<C, D, TO>(e1, lt, S, sh, p, cbase + c + 1, sr.start + static_cast<int64_t>(c + 1) * C,
+                                 min(C, sr.len - (c + 1) * C), h, w, nt, lane);
+        }
     }
     if (p.final_state) {
 #pragma unroll
