@@ -14,11 +14,21 @@ Prints ONE JSON line:
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload long|prefill|packed] [--no-cpu-baseline]
+       python bench.py --summarize DIR    per-kernel means of a rocprofv3 CSV run
+       python bench.py --copy-calibration one 1 GiB device copy (counter scale)
+
+`roofline.traffic` is filled from profiles/traffic.json (HBM bytes per call
+measured with rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by the same counters
+on a plain 1 GiB copy) when the kernel sources still hash to the recorded
+value, else null.
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import ctypes
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -43,6 +53,69 @@ def chunk_flops_per_token_head(C=64, d=128):
     (2 C d each), and the state-side W S, (q e^G) S, P Delta, K^T Delta:
     10 C d + 6 d^2 in total."""
     return 10 * C * d + 6 * d * d
+
+
+def kernel_sources_sha() -> str:
+    """sha256 over the HIP sources of libkda (what the counters were taken on)."""
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "gated_delta_rule_49_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(d, "*.hip")) + glob.glob(os.path.join(d, "*.hpp"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(key):
+    """HBM bytes per call for `key` from profiles/traffic.json, or None if the
+    record is missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sources_sha") != kernel_sources_sha() or key not in rec.get("calls", {}):
+        return None
+    c = rec["calls"][key]
+    return c["fetch_kib"] * 1024 * rec["fetch_scale"] + c["write_kib"] * 1024 * rec["write_scale"]
+
+
+def summarize(root):
+    """Per-kernel means of rocprofv3 --output-format csv results under root."""
+    for f in glob.glob(os.path.join(root, "**", "*kernel_stats.csv"), recursive=True):
+        print(f"# kernel stats ({os.path.basename(f)})")
+        print("| kernel | calls | average | total |\n|---|---|---|---|")
+        other = [0, 0.0]
+        for row in csv.DictReader(open(f)):
+            if "kda::" not in row["Name"]:  # input generation and copies
+                other[0] += int(row["Calls"])
+                other[1] += float(row["TotalDurationNs"])
+                continue
+            print(f"| {row['Name'].split('(')[0]} | {row['Calls']} | "
+                  f"{float(row['AverageNs']) / 1e3:.1f} us | {float(row['TotalDurationNs']) / 1e6:.3f} ms |")
+        print(f"| (other kernels: input generation, copies) | {other[0]} | | {other[1] / 1e6:.3f} ms |")
+    acc = {}
+    for f in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            name = row["Kernel_Name"]
+            if "kda::" not in name and "copyBuffer" not in name:
+                continue
+            acc.setdefault((name.split("(")[0], row["Counter_Name"]), []).append(float(row["Counter_Value"]))
+    if acc:
+        print("# counters (mean per dispatch)")
+        print("| kernel | counter | dispatches | mean |\n|---|---|---|---|")
+        for (k, c), v in sorted(acc.items()):
+            print(f"| {k} | {c} | {len(v)} | {sum(v) / len(v):.6g} |")
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 28  # floats: 1 GiB
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print("copied 3 x 1 GiB device to device")
 
 
 class HipEvents:
@@ -148,7 +221,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long", choices=["long", "prefill", "packed"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize", metavar="DIR")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
                                    "(the recurrence shards by head or sequence with no exchange)"}))
@@ -245,7 +326,7 @@ def main():
                    "chunk": P["chunk"], "num_seqs": N,
                    "decode_workload": "decode_B256_H32_d128", "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": p_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": p_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "frac": p_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(f"prefill_{args.workload}"),
                      "kernel": "kda_prefill_chunked (chunk table + intra_kernel + scan_kernel)",
                      "algorithmic_bytes": pbytes, "avg_ms": pre,
                      "kernels_ms": {"intra_kernel": intra, "scan_kernel": scan},
@@ -253,7 +334,8 @@ def main():
                      "useful_mfma_frac": useful_tf / BF16_PEAK_TFLOPS},
         "decode": {"value": Bd / (dec * 1e-3), "unit": "seq-steps/s", "avg_ms": dec,
                    "roofline": {"bound": "hbm", "achieved": d_gbs, "peak": HBM_PEAK_GBS,
-                                "unit": "GB/s", "frac": d_gbs / HBM_PEAK_GBS, "traffic": None,
+                                "unit": "GB/s", "frac": d_gbs / HBM_PEAK_GBS,
+                                "traffic": measured_traffic("decode"),
                                 "kernel": "decode_step_kernel", "algorithmic_bytes": dbytes}},
         "prefill_ms": pre,
     }

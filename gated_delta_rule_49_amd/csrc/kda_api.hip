@@ -53,7 +53,7 @@ bool use_mfma(const kda_prefill_args *a) {
 }
 
 size_t workspace_for(const kda_prefill_args *a) {
-    size_t bytes = table_bytes(a->num_seqs);
+    size_t bytes = table_bytes(a->num_seqs, max_chunks(a));
     if (use_mfma(a))
         bytes += static_cast<size_t>(max_chunks(a)) * a->H * mfma_block_bytes(a->chunk_size, a->d_k);
     return bytes;
@@ -106,6 +106,7 @@ kda_status kda_prefill_chunked(const kda_prefill_args *a, void *hip_stream) {
     p.cu_seqlens = a->cu_seqlens;
     p.status = reinterpret_cast<int32_t *>(ws);
     p.chunk_off = reinterpret_cast<int32_t *>(ws + kAlign);
+    p.chunk_info = reinterpret_cast<const int4 *>(ws + kAlign + chunk_off_bytes(a->num_seqs));
     p.user_status = a->device_status;
     p.B = a->B; p.T = a->T; p.H = a->H; p.dk = a->d_k; p.dv = a->d_v;
     p.N = a->num_seqs; p.C = a->chunk_size;
@@ -117,7 +118,8 @@ kda_status kda_prefill_chunked(const kda_prefill_args *a, void *hip_stream) {
     if (e == hipSuccess) e = launch_chunk_table(p, s);
     if (e == hipSuccess) {
         if (use_mfma(a))
-            e = launch_prefill_mfma(p, ws + table_bytes(p.N), a->out_dtype, s, ev ? ev[1] : nullptr);
+            e = launch_prefill_mfma(p, ws + table_bytes(p.N, p.n_chunks_bound), a->out_dtype, s,
+                                    ev ? ev[1] : nullptr);
         else {
             e = launch_prefill_f32(p, a->in_dtype, a->out_dtype, s);
             if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);

@@ -9,10 +9,14 @@ namespace kda {
 // Workspace layout (byte offsets from the workspace base, 256-aligned):
 //   [0, 256)            status word (int32) + padding
 //   [256, 256 + 4(N+1)) chunk_off table, rounded up to 256
+//   then chunk_info, 16 bytes per chunk (up to the chunk bound), rounded up
 //   then, matrix-core path only, the per-(chunk, head) intermediate blocks.
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
-inline size_t table_bytes(int N) { return kAlign + align_up(sizeof(int32_t) * (static_cast<size_t>(N) + 1)); }
+inline size_t chunk_off_bytes(int N) { return align_up(sizeof(int32_t) * (static_cast<size_t>(N) + 1)); }
+inline size_t table_bytes(int N, int64_t n_chunks_bound) {
+    return kAlign + chunk_off_bytes(N) + align_up(16 * static_cast<size_t>(n_chunks_bound));
+}
 
 // matrix-core path: bytes of intermediates per (chunk, head)
 size_t mfma_block_bytes(int C, int D);

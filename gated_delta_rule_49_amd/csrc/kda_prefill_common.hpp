@@ -12,6 +12,7 @@ struct PrefillParams {
     float *chunk_states;
     const int32_t *cu_seqlens;   // device, may be null (B rows of T tokens)
     const int32_t *chunk_off;    // device [N+1] first chunk of each sequence (workspace)
+    const int4 *chunk_info;      // device [chunks] (token start lo, hi, length, sequence) (workspace)
     int32_t *status;             // device, workspace word: 0 = inputs valid
     int32_t *user_status;        // device, optional mirror of *status
     int32_t B, T, H, dk, dv, N, C;

@@ -98,7 +98,8 @@ struct IntraLds {
     static constexpr int RTF = CP + 8;     // bf16 row stride of the T fragments
     static constexpr int RG = D + 4;       // fp32 row stride of G
     static constexpr int RA = CP + 4;      // fp32 row stride of A and X
-    static constexpr int NPART = 512 / D;  // cumsum: token ranges per channel
+    static constexpr int CPW = D / 8;      // cumsum: channels per wave
+    static constexpr int NSEG = 64 / CPW;  // cumsum: token segments per channel
     static constexpr size_t SK = 0;                                   // k   [CP][RK] bf16
     static constexpr size_t SQ = SK + CP * RK * 2;                    // q   [CP][RK] bf16
     static constexpr size_t SA = SQ + CP * RK * 2;                    // A   [CP][RA] f32
@@ -107,8 +108,7 @@ struct IntraLds {
     static constexpr size_t SG = SVT + D * RT * 2;                    // G   [CP][RG] f32 (log2 units)
     static constexpr size_t ST = SG + CP * RG * 4;                    // X = (I+A)^-1 [CP][RA] f32
     static constexpr size_t SB = ST + CP * RA * 4;                    // beta [CP]
-    static constexpr size_t SP = SB + CP * 4;                         // cumsum partials [NPART][D]
-    static constexpr size_t END = SP + NPART * D * 4;
+    static constexpr size_t END = SB + CP * 4;
     // after the Gram phase q and A are dead: the T fragments reuse [SQ, SKT)
     // when they fit there, else they get their own region
     static constexpr bool REUSE = 3 * CP * RTF * 2 <= SKT - SQ;
@@ -126,7 +126,7 @@ struct IntraLds {
     // raw inputs prefetched per thread
     static constexpr int NVEC = CP * D / 8;                           // 16-byte vectors per array
     static constexpr int NV = (NVEC + 511) / 512;
-    static constexpr int RP = CP / NPART;
+    static constexpr int RS = CP / NSEG;                              // rows per cumsum segment
 };
 
 // One thread's share of a (chunk, head)'s raw inputs, held in registers so
@@ -137,9 +137,18 @@ struct IntraRaw {
     // Raw bits only, loaded from rows clamped into [0, L): nothing here
     // depends on the loaded values, so the loads stay in flight until the
     // next item stages them (rows >= L are zeroed there).
-    uint4 k[M::NV], v[M::NV], q[M::NV];
-    uint32_t g[M::RP];
+    typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;  // one 128-bit register tuple
+    u32x4 k[M::NV], v[M::NV], q[M::NV], a[M::NV];
     uint32_t beta;
+
+    // Marks the loaded registers as redefined here, so that nothing derived
+    // from them is scheduled before this point (which would wait for the
+    // loads right after they are issued).
+    __device__ __forceinline__ void settle() {
+#pragma unroll
+        for (int u = 0; u < M::NV; ++u) asm volatile("" : "+v"(k[u]), "+v"(v[u]), "+v"(q[u]), "+v"(a[u]));
+        asm volatile("" : "+v"(beta));
+    }
 
     __device__ __forceinline__ void load(const PrefillParams &p, int64_t t0, int L, int h, int tid) {
         const bf16_t *Kg = static_cast<const bf16_t *>(p.k);
@@ -153,17 +162,43 @@ struct IntraRaw {
             const int e = min(tid + 512 * u, M::NVEC - 1);
             const int r = min(e / (D / 8), L - 1), c8 = (e % (D / 8)) * 8;
             const int64_t off = ((t0 + r) * H + h) * D + c8;
-            k[u] = *reinterpret_cast<const uint4 *>(Kg + off);
-            v[u] = *reinterpret_cast<const uint4 *>(Vg + off);
-            q[u] = *reinterpret_cast<const uint4 *>(Qg + off);
-        }
-        const int ch = tid % D, part = tid / D;
-#pragma unroll
-        for (int j = 0; j < M::RP; ++j) {
-            const int r = min(part * M::RP + j, L - 1);
-            g[j] = Ag[((t0 + r) * H + h) * D + ch];
+            k[u] = *reinterpret_cast<const u32x4 *>(Kg + off);
+            v[u] = *reinterpret_cast<const u32x4 *>(Vg + off);
+            q[u] = *reinterpret_cast<const u32x4 *>(Qg + off);
+            a[u] = *reinterpret_cast<const u32x4 *>(Ag + off);
         }
         beta = Bg[(t0 + min(tid, L - 1)) * H + h];
+    }
+};
+
+// A wave's W and U tiles of the previous item, held until they are stored.
+// Wave w computes W channel tile w (if w < D/16) and U value tile
+// (w >= D/16 ? w : w + 8) - D/16 (if that is < D/16).
+template <int C, int D>
+struct IntraPend {
+    using Y = Lay<C, D>;
+    uint2 w[Y::NMT];
+    f32x4 u[Y::NMT];
+    char *blk;
+
+    __device__ __forceinline__ void flush(int wave, int lane) {
+        if (blk == nullptr) return;
+        if (wave < Y::NDT) {
+            const int ct = wave;
+#pragma unroll
+            for (int tt = 0; tt < Y::NMT; ++tt) {
+                const size_t fo = ((static_cast<size_t>(tt) * Y::KSD + ct / 2) * 64 + lane) * 16 + (ct & 1) * 8;
+                *reinterpret_cast<uint2 *>(blk + Y::W + fo) = w[tt];
+            }
+        }
+        const int wi = wave >= Y::NDT ? wave : wave + 8;
+        if (wi < 2 * Y::NDT) {
+            const int ct = wi - Y::NDT;
+#pragma unroll
+            for (int tt = 0; tt < Y::NMT; ++tt)
+                *reinterpret_cast<f32x4 *>(blk + Y::U + ((static_cast<size_t>(tt) * Y::NDT + ct) * 64 + lane) * 16) = u[tt];
+        }
+        blk = nullptr;
     }
 };
 
@@ -173,17 +208,31 @@ struct IntraItem {
     int64_t t0;
 };
 
-template <int C>
-__device__ __forceinline__ IntraItem intra_item(const PrefillParams &p, int item) {
+__device__ __forceinline__ IntraItem intra_item(int item, int H, const int4 &ci) {
     IntraItem it;
-    it.x = item / p.H;
-    it.h = item % p.H;
-    const int n = chunk_to_seq(p.chunk_off, p.N, it.x);
-    const SeqRange sr = seq_range(p, n);
-    const int cidx = it.x - p.chunk_off[n];
-    it.t0 = sr.start + static_cast<int64_t>(cidx) * C;
-    it.L = min(C, sr.len - cidx * C);
+    it.x = item / H;
+    it.h = item % H;
+    it.t0 = static_cast<int64_t>(static_cast<uint32_t>(ci.x)) | (static_cast<int64_t>(ci.y) << 32);
+    it.L = ci.z;
     return it;
+}
+
+// Gram work plan: the block pair (a, b <= a) that wave group grp (0..3)
+// handles in its u-th slot, as a * 8 + b, or -1.  With four row blocks the ten
+// pairs are dealt 3, 3, 2, 2 so that each SIMD (waves w and w + 4) carries five
+// half-pairs:  g0 (3,3) (3,2) (3,1) | g1 (3,0) (2,2) (2,1) | g2 (2,0) (1,1) |
+// g3 (1,0) (0,0).  One byte per group, 0xff = none.
+template <int NB>
+__device__ __forceinline__ int gram_pair(int grp, int u) {
+    uint32_t w;
+    if (NB == 4)
+        w = u == 0 ? 0x0810181bu : u == 1 ? 0x0009121au : 0xffff1119u;
+    else if (NB == 2)
+        w = u == 0 ? 0xff000809u : 0xffffffffu;  // g0 (1,1) | g1 (1,0) | g2 (0,0)
+    else
+        w = u == 0 ? 0xffffff00u : 0xffffffffu;  // g0 (0,0)
+    const int code = static_cast<int>((w >> (8 * grp)) & 0xffu);
+    return code == 0xff ? -1 : code;
 }
 
 // Persistent: each workgroup walks work items item = blockIdx.x + i * gridDim.x
@@ -193,7 +242,7 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
     using Y = Lay<C, D>;
     using M = IntraLds<C, D>;
     constexpr int CP = Y::CP;
-    constexpr int NPAIR = Y::NMT * (Y::NMT + 1) / 2;
+    constexpr int KH = Y::KSD / 2;  // channel k-steps per Gram half
     if (*p.status != 0) return;
     const int H = p.H;
     const int nitems = p.chunk_off[p.N] * H;
@@ -207,126 +256,193 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
     auto SG = reinterpret_cast<float(*)[M::RG]>(smem + M::SG);
     auto SX = reinterpret_cast<float(*)[M::RA]>(smem + M::ST);
     auto SBETA = reinterpret_cast<float *>(smem + M::SB);
-    auto SPART = reinterpret_cast<float(*)[D]>(smem + M::SP);
     auto TB = reinterpret_cast<bf16_t(*)[M::RTF]>(smem + M::TB);
     auto TH = reinterpret_cast<bf16_t(*)[M::RTF]>(smem + M::TH);
     auto TL = reinterpret_cast<bf16_t(*)[M::RTF]>(smem + M::TL);
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4, li = lane & 15;
-
+    if (static_cast<int>(blockIdx.x) >= nitems) return;
     IntraRaw<C, D> raw;
-    int item = blockIdx.x;
-    if (item >= nitems) return;
-    IntraItem it = intra_item<C>(p, item);
-    raw.load(p, it.t0, it.L, it.h, tid);
+    IntraItem it{};
+    int4 nci = p.chunk_info[blockIdx.x / H];  // coordinates of the next item
+    IntraPend<C, D> pend;
+    pend.blk = nullptr;
 
-    for (; item < nitems; item += gridDim.x) {
+    // Pass i computes item_i and loads the raw inputs of item_{i+1}; the first
+    // pass (item < 0) only loads.  A single load site keeps the prefetched
+    // registers in place across the loop instead of being copied (a copy
+    // would wait for the loads).
+    for (int item = static_cast<int>(blockIdx.x) - static_cast<int>(gridDim.x);; item += gridDim.x) {
+        // The thread index is made opaque for each item so that the compiler
+        // recomputes per-thread addresses inside the loop instead of keeping
+        // dozens of them live (and spilled) across the whole kernel.
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int g = lane >> 4, li = lane & 15;
         const int L = it.L;
+        const int next = item + static_cast<int>(gridDim.x);
+        const bool live = item >= 0;
         char *blk = blocks + (static_cast<size_t>(it.x) * H + it.h) * Y::BYTES;
+        // (the wait for this load coincides with the staging's wait for the
+        // prefetched inputs, which were issued before it)
+        const IntraItem itn = intra_item(next, H, make_int4(__builtin_amdgcn_readfirstlane(nci.x),
+                                                            __builtin_amdgcn_readfirstlane(nci.y),
+                                                            __builtin_amdgcn_readfirstlane(nci.z), 0));
+        const int kh = wave & 1, grp = wave >> 1;
+        f32x4 accA[3], accP[3];
+        int pab[3];
 
-        // ---- 1. stage k, q (natural) and k^T, v^T (transposed, swizzled),
-        //         zero beyond L; gate cumsum: thread (channel, token range)
-        //         sums its range, range totals are combined through LDS.
+        if (live) {
+            raw.settle();
+            // ---- 1. stage k, q (natural), k^T, v^T (transposed, swizzled) and
+            //         log alpha (fp32, natural; becomes G in place), zero beyond L;
+            //         then the gate cumsum, one wave per D/8 channels: lane
+            //         (channel, token segment) sums its segment and the segment
+            //         offsets come from a scan across lanes.
 #pragma unroll
-        for (int u = 0; u < M::NV; ++u) {
-            const int e = tid + 512 * u;
-            if (e >= M::NVEC) continue;
-            const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
-            const bool live = r < L;
-            const uint4 z = make_uint4(0, 0, 0, 0);
-            const uint4 kv = live ? raw.k[u] : z, vv = live ? raw.v[u] : z, qv = live ? raw.q[u] : z;
-            *reinterpret_cast<uint4 *>(&SK[r][c8]) = kv;
-            *reinterpret_cast<uint4 *>(&SQ[r][c8]) = qv;
-            const bf16_t *kb = reinterpret_cast<const bf16_t *>(&kv);
-            const bf16_t *vb = reinterpret_cast<const bf16_t *>(&vv);
+            for (int u = 0; u < M::NV; ++u) {
+                const int e = tid + 512 * u;
+                if (e >= M::NVEC) continue;
+                const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
+                const bool live = r < L;
+                using u32x4 = typename IntraRaw<C, D>::u32x4;
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                const u32x4 kv = live ? raw.k[u] : z, vv = live ? raw.v[u] : z, qv = live ? raw.q[u] : z;
+                const u32x4 av = live ? raw.a[u] : z;
+                *reinterpret_cast<u32x4 *>(&SK[r][c8]) = kv;
+                *reinterpret_cast<u32x4 *>(&SQ[r][c8]) = qv;
+                // 32-bit word operations on the raw registers (element j of a
+                // vector is the low (j even) or high (j odd) half of word j / 2)
+                const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+                const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+                const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                SKT[M::tpos(c8 + j, r)] = kb[j];
-                SVT[M::tpos(c8 + j, r)] = vb[j];
-            }
-        }
-        if (tid < CP) SBETA[tid] = tid < L ? bf16_to_f32(static_cast<bf16_t>(raw.beta)) : 0.f;
-        for (int e = tid; e < CP * M::RA; e += 512) {
-            (&SA[0][0])[e] = 0.f;
-            (&SX[0][0])[e] = 0.f;
-        }
-        const int cch = tid % D, part = tid / D;
-        float gv[M::RP];
-#pragma unroll
-        for (int j = 0; j < M::RP; ++j)
-            gv[j] = (part * M::RP + j < L) ? bf16_to_f32(static_cast<bf16_t>(raw.g[j])) : 0.f;
-#pragma unroll
-        for (int j = 1; j < M::RP; ++j) gv[j] += gv[j - 1];
-        SPART[part][cch] = gv[M::RP - 1];
-        // the next item's raw inputs: loads in flight during this item
-        const int next = item + gridDim.x;
-        IntraItem itn = it;
-        if (next < nitems) {
-            itn = intra_item<C>(p, next);
-            raw.load(p, itn.t0, itn.L, itn.h, tid);
-        }
-        lds_barrier();
-        {
-            float off = 0.f;
-            for (int q2 = 0; q2 < part; ++q2) off += SPART[q2][cch];
-#pragma unroll
-            for (int j = 0; j < M::RP; ++j) SG[part * M::RP + j][cch] = (off + gv[j]) * kLog2e;
-        }
-        lds_barrier();
-
-        // ---- 2. Gram blocks A^T(b,a), P^T(b,a) for b <= a, one block pair
-        //         per wave at a time.  Factors around reference row
-        //         m = 16a - 1: rows (<= 1) e^{G_r - G_m}, columns e^{G_m - G_i}.
-        for (int pi = wave; pi < NPAIR; pi += 8) {
-            int a = 0, rem = pi;
-            while (rem > a) { rem -= a + 1; ++a; }
-            const int b = rem;
-            const int r = 16 * a + li;
-            bool fact = true;
-            if (a == b) {
-                float span = 0.f;
-                for (int ch = lane; ch < D; ch += 64) {
-                    const float gm = a > 0 ? SG[16 * a - 1][ch] : 0.f;
-                    span = fmaxf(span, gm - SG[16 * a + 15][ch]);
+                for (int j2 = 0; j2 < 4; ++j2) {
+                    SKT[M::tpos(c8 + 2 * j2, r)] = static_cast<bf16_t>(kw[j2] & 0xffffu);
+                    SKT[M::tpos(c8 + 2 * j2 + 1, r)] = static_cast<bf16_t>(kw[j2] >> 16);
+                    SVT[M::tpos(c8 + 2 * j2, r)] = static_cast<bf16_t>(vw[j2] & 0xffffu);
+                    SVT[M::tpos(c8 + 2 * j2 + 1, r)] = static_cast<bf16_t>(vw[j2] >> 16);
                 }
-                fact = wave_max(span) <= kDiagSpanMax;
+                *reinterpret_cast<f32x4 *>(&SG[r][c8]) =
+                    f32x4{__uint_as_float(aw[0] << 16), __uint_as_float(aw[0] & 0xffff0000u),
+                          __uint_as_float(aw[1] << 16), __uint_as_float(aw[1] & 0xffff0000u)};
+                *reinterpret_cast<f32x4 *>(&SG[r][c8 + 4]) =
+                    f32x4{__uint_as_float(aw[2] << 16), __uint_as_float(aw[2] & 0xffff0000u),
+                          __uint_as_float(aw[3] << 16), __uint_as_float(aw[3] & 0xffff0000u)};
             }
-            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = accA;
-            if (fact) {
-                const int i = 16 * b + li;
+            if (tid < CP) SBETA[tid] = tid < L ? bf16_to_f32(static_cast<bf16_t>(raw.beta)) : 0.f;
+            lds_barrier();
+            pend.flush(wave, lane);  // the previous item's W and U tiles
+            {
+                const int chl = lane % M::CPW, seg = lane / M::CPW;
+                const int ch = wave * M::CPW + chl;
+                float gv[M::RS];
 #pragma unroll
-                for (int ks = 0; ks < Y::KSD; ++ks) {
-                    const int c0 = 32 * ks + 8 * g;
-                    const uint4 kraw = *reinterpret_cast<const uint4 *>(&SK[r][c0]);
-                    const uint4 qraw = *reinterpret_cast<const uint4 *>(&SQ[r][c0]);
-                    const uint4 kiraw = *reinterpret_cast<const uint4 *>(&SK[i][c0]);
-                    const bf16_t *kr = reinterpret_cast<const bf16_t *>(&kraw);
-                    const bf16_t *qr = reinterpret_cast<const bf16_t *>(&qraw);
-                    const bf16_t *ki = reinterpret_cast<const bf16_t *>(&kiraw);
-                    frag8 krh, krl, qrh, qrl, kih, kil;
+                for (int j = 0; j < M::RS; ++j) gv[j] = SG[seg * M::RS + j][ch];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float gm = a > 0 ? SG[16 * a - 1][c0 + j] : 0.f;
-                        const float rf = fast_exp2(SG[r][c0 + j] - gm);
-                        const float cf = fast_exp2(gm - SG[i][c0 + j]);
-                        split_bf16(bf16_to_f32(kr[j]) * rf, krh.s[j], krl.s[j]);
-                        split_bf16(bf16_to_f32(qr[j]) * rf, qrh.s[j], qrl.s[j]);
-                        split_bf16(bf16_to_f32(ki[j]) * cf, kih.s[j], kil.s[j]);
+                for (int j = 1; j < M::RS; ++j) gv[j] += gv[j - 1];
+                float t = gv[M::RS - 1];
+#pragma unroll
+                for (int o = M::CPW; o < 64; o <<= 1) {
+                    const float n = __shfl_up(t, o);
+                    if (lane >= o) t += n;
+                }
+                const float off = t - gv[M::RS - 1];
+#pragma unroll
+                for (int j = 0; j < M::RS; ++j) SG[seg * M::RS + j][ch] = (off + gv[j]) * kLog2e;
+            }
+            lds_barrier();
+
+            // ---- 2. Gram blocks A^T(b,a), P^T(b,a) for b <= a.  Work unit =
+            //         (block pair, half of the channels): wave w = kh + 2 grp takes
+            //         channel half kh of the pairs in group grp (gram_pair), so every
+            //         SIMD gets the same number of units and a wave reuses its row
+            //         operands across the pairs of one row block.  Factors around
+            //         reference row m = 16a - 1: rows (<= 1) e^{G_r - G_m}, columns
+            //         e^{G_m - G_i}.  Half 1 leaves its partial sums in LDS (A in SA,
+            //         P in SX) and half 0 adds them and finalises.
+            bool exact[3];
+            {
+                float kr32[KH][8], qr32[KH][8];  // row operands, fp32
+                int cur_a = -1;
+#pragma unroll
+                for (int u = 0; u < 3; ++u) {
+                    const int code = gram_pair<Y::NMT>(grp, u);
+                    pab[u] = code;
+                    exact[u] = false;
+                    accA[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    accP[u] = accA[u];
+                    if (code < 0) continue;
+                    const int a = code >> 3, b = code & 7;
+                    const int r = 16 * a + li;
+                    if (a == b) {
+                        float span = 0.f;
+                        if (lane < 32 * KH) {
+                            const int ch = 32 * KH * kh + lane;
+                            const float gm = a > 0 ? SG[16 * a - 1][ch] : 0.f;
+                            span = gm - SG[16 * a + 15][ch];
+                        }
+                        exact[u] = wave_max(span) > kDiagSpanMax;
+                        if (exact[u]) continue;  // done pair by pair below
                     }
-                    accA = mfma16(kih.v, krh.v, accA);
-                    accA = mfma16(kih.v, krl.v, accA);
-                    accA = mfma16(kil.v, krh.v, accA);
-                    accP = mfma16(kih.v, qrh.v, accP);
-                    accP = mfma16(kih.v, qrl.v, accP);
-                    accP = mfma16(kil.v, qrh.v, accP);
+                    if (a != cur_a) {  // row operands of block a, this channel half
+#pragma unroll
+                        for (int s2 = 0; s2 < KH; ++s2) {
+                            const int c0 = 32 * (KH * kh + s2) + 8 * g;
+                            const uint4 kraw = *reinterpret_cast<const uint4 *>(&SK[r][c0]);
+                            const uint4 qraw = *reinterpret_cast<const uint4 *>(&SQ[r][c0]);
+                            const bf16_t *kr = reinterpret_cast<const bf16_t *>(&kraw);
+                            const bf16_t *qr = reinterpret_cast<const bf16_t *>(&qraw);
+                            const f32x4 gr0 = *reinterpret_cast<const f32x4 *>(&SG[r][c0]);
+                            const f32x4 gr1 = *reinterpret_cast<const f32x4 *>(&SG[r][c0 + 4]);
+                            f32x4 gm0 = {0.f, 0.f, 0.f, 0.f}, gm1 = gm0;
+                            if (a > 0) {
+                                gm0 = *reinterpret_cast<const f32x4 *>(&SG[16 * a - 1][c0]);
+                                gm1 = *reinterpret_cast<const f32x4 *>(&SG[16 * a - 1][c0 + 4]);
+                            }
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) {
+                                const float rf = fast_exp2(j < 4 ? gr0[j] - gm0[j] : gr1[j - 4] - gm1[j - 4]);
+                                kr32[s2][j] = bf16_to_f32(kr[j]) * rf;
+                                qr32[s2][j] = bf16_to_f32(qr[j]) * rf;
+                            }
+                        }
+                        cur_a = a;
+                    }
+                    const int i = 16 * b + li;
+#pragma unroll
+                    for (int s2 = 0; s2 < KH; ++s2) {
+                        const int c0 = 32 * (KH * kh + s2) + 8 * g;
+                        const uint4 kiraw = *reinterpret_cast<const uint4 *>(&SK[i][c0]);
+                        const bf16_t *ki = reinterpret_cast<const bf16_t *>(&kiraw);
+                        const f32x4 gi0 = *reinterpret_cast<const f32x4 *>(&SG[i][c0]);
+                        const f32x4 gi1 = *reinterpret_cast<const f32x4 *>(&SG[i][c0 + 4]);
+                        f32x4 gm0 = {0.f, 0.f, 0.f, 0.f}, gm1 = gm0;
+                        if (a > 0) {
+                            gm0 = *reinterpret_cast<const f32x4 *>(&SG[16 * a - 1][c0]);
+                            gm1 = *reinterpret_cast<const f32x4 *>(&SG[16 * a - 1][c0 + 4]);
+                        }
+                        // fp32 matrix cores, four channels per step: in step j lane
+                        // group g contributes channel c0 + j of its row / column
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const float cf = fast_exp2(j < 4 ? gm0[j] - gi0[j] : gm1[j - 4] - gi1[j - 4]);
+                            const float kc = bf16_to_f32(ki[j]) * cf;
+                            accA[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(kc, kr32[s2][j], accA[u], 0, 0, 0);
+                            accP[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(kc, qr32[s2][j], accP[u], 0, 0, 0);
+                        }
+                    }
                 }
-            } else {
-                // exact pairwise diagonal block: lane holds (i = 16a + 4g + j, r);
-                // eight channels per step, all operands as 16-byte LDS reads
-#pragma unroll 2
-                for (int c8 = 0; c8 < D; c8 += 8) {
+            }
+            // Diagonal blocks whose decay is too steep to factorise in this
+            // channel half, exactly, pair by pair: lane holds (i = 16a + 4g + j, r).
+#pragma unroll
+            for (int u = 0; u < 3; ++u) {
+                if (!exact[u]) continue;
+                const int a = pab[u] >> 3;
+                const int r = 16 * a + li;
+#pragma unroll 1
+                for (int c8 = 32 * KH * kh; c8 < 32 * KH * (kh + 1); c8 += 8) {
                     const uint4 kr8 = *reinterpret_cast<const uint4 *>(&SK[r][c8]);
                     const uint4 qr8 = *reinterpret_cast<const uint4 *>(&SQ[r][c8]);
                     const f32x4 gr0 = *reinterpret_cast<const f32x4 *>(&SG[r][c8]);
@@ -349,215 +465,256 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
                             sp += bf16_to_f32(qrb[c]) * f;
                         }
                         if (i <= r) {
-                            accA[j] += sa;
-                            accP[j] += sp;
+                            accA[u][j] += sa;
+                            accP[u][j] += sp;
                         }
                     }
                 }
             }
-            // A (rows scaled by beta_r, strictly lower) -> LDS; P -> workspace
-            const float br = SBETA[r];
-            f32x4 av;
-            bf16_t ph[4], pl[4];
+            if (kh == 1) {  // partial sums -> LDS; the same lanes of half 0 read them
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int i = 16 * b + 4 * g + j;
-                av[j] = (i < r) ? accA[j] * br : 0.f;
-                split_bf16((i <= r) ? accP[j] : 0.f, ph[j], pl[j]);
-            }
-            *reinterpret_cast<f32x4 *>(&SA[r][16 * b + 4 * g]) = av;
-            const size_t fo = ((static_cast<size_t>(a) * Y::KSC + b / 2) * 64 + lane) * 16 + (b & 1) * 8;
-            *reinterpret_cast<uint2 *>(blk + Y::PH + fo) = pack4(ph);
-            *reinterpret_cast<uint2 *>(blk + Y::PL + fo) = pack4(pl);
-            if (b == a && (b & 1) == 0) {  // the upper half of this k step is zero
-                *reinterpret_cast<uint2 *>(blk + Y::PH + fo + 8) = make_uint2(0, 0);
-                *reinterpret_cast<uint2 *>(blk + Y::PL + fo + 8) = make_uint2(0, 0);
-            }
-        }
-
-        // ---- 2b. q e^G (scan A-operand order), (k e^{G_L - G})^T, e^{G_L}.
-        //      Waves that had two Gram block pairs sit this out.
-        constexpr int NTWO = NPAIR > 8 ? NPAIR - 8 : 0;  // waves 0..NTWO-1 did two pairs
-        constexpr int N2B = 8 - NTWO;
-        for (int f = wave - NTWO; wave >= NTWO && f < Y::NMT * Y::KSD + Y::NDT * Y::KSC; f += N2B) {
-            frag8 hi, lo;
-            size_t dst_h, dst_l;
-            if (f < Y::NMT * Y::KSD) {
-                const int mt = f / Y::KSD, ks = f % Y::KSD;
-                const int r = 16 * mt + li;
-                const int cA = 32 * ks + 4 * g, cB = cA + 16;
-                const uint2 q0 = *reinterpret_cast<const uint2 *>(&SQ[r][cA]);
-                const uint2 q1 = *reinterpret_cast<const uint2 *>(&SQ[r][cB]);
-                const f32x4 g0 = *reinterpret_cast<const f32x4 *>(&SG[r][cA]);
-                const f32x4 g1 = *reinterpret_cast<const f32x4 *>(&SG[r][cB]);
-                const bf16_t *qa = reinterpret_cast<const bf16_t *>(&q0);
-                const bf16_t *qb = reinterpret_cast<const bf16_t *>(&q1);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    split_bf16(bf16_to_f32(qa[j]) * fast_exp2(g0[j]), hi.s[j], lo.s[j]);
-                    split_bf16(bf16_to_f32(qb[j]) * fast_exp2(g1[j]), hi.s[4 + j], lo.s[4 + j]);
+                for (int u = 0; u < 3; ++u) {
+                    if (pab[u] < 0) continue;
+                    const int a = pab[u] >> 3, b = pab[u] & 7;
+                    const int r = 16 * a + li;
+                    *reinterpret_cast<f32x4 *>(&SA[r][16 * b + 4 * g]) = accA[u];
+                    *reinterpret_cast<f32x4 *>(&SX[r][16 * b + 4 * g]) = accP[u];
                 }
-                const size_t fo = (static_cast<size_t>(f) * 64 + lane) * 16;
-                dst_h = Y::QH + fo;
-                dst_l = Y::QL + fo;
-            } else {
-                const int f2 = f - Y::NMT * Y::KSD;
-                const int mt = f2 / Y::KSC, ks = f2 % Y::KSC;
-                const int ch = 16 * mt + li;
-                const float gl = SG[C - 1][ch];
-                const int iA = 32 * ks + 4 * g, iB = iA + 16;
-                const uint2 k0 = *reinterpret_cast<const uint2 *>(&SKT[M::tpos(ch, iA)]);
-                const uint2 k1 = *reinterpret_cast<const uint2 *>(&SKT[M::tpos(ch, iB)]);
-                const bf16_t *ka = reinterpret_cast<const bf16_t *>(&k0);
-                const bf16_t *kb = reinterpret_cast<const bf16_t *>(&k1);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    split_bf16(bf16_to_f32(ka[j]) * fast_exp2(gl - SG[iA + j][ch]), hi.s[j], lo.s[j]);
-                    split_bf16(bf16_to_f32(kb[j]) * fast_exp2(gl - SG[iB + j][ch]), hi.s[4 + j], lo.s[4 + j]);
-                }
-                const size_t fo = (static_cast<size_t>(f2) * 64 + lane) * 16;
-                dst_h = Y::KBH + fo;
-                dst_l = Y::KBL + fo;
             }
-            st16(blk + dst_h, hi.u);
-            st16(blk + dst_l, lo.u);
-        }
-        if (tid < D) reinterpret_cast<float *>(blk + Y::GAM)[tid] = fast_exp2(SG[C - 1][tid]);
-        lds_barrier();
-
-        // ---- 3. X = (I + A)^-1 by blocked forward substitution (fp32 VALU).
-        //         Diagonal blocks: lane jj owns column jj; row rr of A_aa is
-        //         read as four broadcast 16-byte loads.
-        if (wave < Y::NMT && lane < 16) {
-            const int a = wave, jj = lane, base = 16 * a;
-            float xc[16];
+            lds_barrier();
+            if (kh == 0) {
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                float arow[16];
+                for (int u = 0; u < 3; ++u) {
+                    const int code = pab[u];
+                    if (code < 0) continue;
+                    const int a = code >> 3, b = code & 7;
+                    const int r = 16 * a + li;
+                    const f32x4 pa = *reinterpret_cast<const f32x4 *>(&SA[r][16 * b + 4 * g]);
+                    const f32x4 pp = *reinterpret_cast<const f32x4 *>(&SX[r][16 * b + 4 * g]);
+                    // A (rows scaled by beta_r, strictly lower) -> LDS; P -> workspace
+                    const float br = SBETA[r];
+                    f32x4 av;
+                    bf16_t ph[4], pl[4];
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const f32x4 t = *reinterpret_cast<const f32x4 *>(&SA[base + rr][base + 4 * q4]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) arow[4 * q4 + j] = t[j];
-                }
-                float s0 = (rr == jj) ? 1.f : 0.f, s1 = 0.f;
-#pragma unroll
-                for (int i = 0; i < rr; ++i) {
-                    const float t = (i >= jj) ? arow[i] * xc[i] : 0.f;
-                    if (i & 1) s1 -= t; else s0 -= t;
-                }
-                xc[rr] = (rr >= jj) ? s0 + s1 : 0.f;
-            }
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) SX[base + rr][base + jj] = xc[rr];
-        }
-        lds_barrier();
-        // Off-diagonal blocks, one column block b per wave, top to bottom:
-        //   X_ab = -X_aa sum_{c=b}^{a-1} A_ac X_cb   (a > b)
-        // Only this wave writes column block b; X_aa and A come from the
-        // previous phase, so no barrier is needed between the steps (the
-        // wave's own LDS writes are ordered before its later reads).
-        if (wave < Y::NMT - 1) {
-            const int b = wave;
-            const int rr = lane >> 2, cc0 = (lane & 3) * 4;
-            for (int a = b + 1; a < Y::NMT; ++a) {
-                f32x4 y = {0.f, 0.f, 0.f, 0.f};
-                for (int c = b; c < a; ++c)
-#pragma unroll
-                    for (int kk = 0; kk < 16; ++kk)
-                        y += SA[16 * a + rr][16 * c + kk] *
-                             *reinterpret_cast<const f32x4 *>(&SX[16 * c + kk][16 * b + cc0]);
-                // y -> LDS scratch (row block a of column b, not yet final)
-                *reinterpret_cast<f32x4 *>(&SX[16 * a + rr][16 * b + cc0]) = y;
-                __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): y visible to the wave
-                __builtin_amdgcn_wave_barrier();
-                f32x4 xo = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < 16; ++kk)
-                    xo -= SX[16 * a + rr][16 * a + kk] *
-                          *reinterpret_cast<const f32x4 *>(&SX[16 * a + kk][16 * b + cc0]);
-                __builtin_amdgcn_s_waitcnt(0xc07f);
-                __builtin_amdgcn_wave_barrier();
-                *reinterpret_cast<f32x4 *>(&SX[16 * a + rr][16 * b + cc0]) = xo;
-                __builtin_amdgcn_s_waitcnt(0xc07f);
-                __builtin_amdgcn_wave_barrier();
-            }
-        }
-        lds_barrier();
-
-        // ---- 3b. T = X Diag(beta) as MFMA operands: bf16, and hi/lo (q, A dead)
-        for (int e = tid; e < CP * CP / 4; e += 512) {
-            const int r = e / (CP / 4), i4 = (e % (CP / 4)) * 4;
-            const f32x4 xv = *reinterpret_cast<const f32x4 *>(&SX[r][i4]);
-            bf16_t tb[4], th[4], tl[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float t = xv[j] * SBETA[i4 + j];
-                tb[j] = f32_to_bf16(t);
-                split_bf16(t, th[j], tl[j]);
-            }
-            *reinterpret_cast<uint2 *>(&TB[r][i4]) = pack4(tb);
-            *reinterpret_cast<uint2 *>(&TH[r][i4]) = pack4(th);
-            *reinterpret_cast<uint2 *>(&TL[r][i4]) = pack4(tl);
-        }
-        lds_barrier();
-
-        // ---- 4. W^T = (k e^G)^T T^T (bf16) per channel tile; U = T V (T split)
-        //         per value tile.  Items: NDT W tiles then NDT U tiles.
-        for (int wi = wave; wi < 2 * Y::NDT; wi += 8) {
-            const bool isW = wi < Y::NDT;
-            const int ct = isW ? wi : wi - Y::NDT;
-            const int ch = 16 * ct + li;
-            f32x4 acc[Y::NMT];
-#pragma unroll
-            for (int tt = 0; tt < Y::NMT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s2 = 0; s2 < Y::KSC; ++s2) {
-                const int i0 = 32 * s2 + 8 * g;
-                frag8 opk;  // W: (k e^G)^T, channel row ch, tokens i0..i0+7; U: V^T
-                if (isW) {
-                    const uint4 kraw = *reinterpret_cast<const uint4 *>(&SKT[M::tpos(ch, i0)]);
-                    const bf16_t *kk = reinterpret_cast<const bf16_t *>(&kraw);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        opk.s[j] = f32_to_bf16(bf16_to_f32(kk[j]) * fast_exp2(SG[i0 + j][ch]));
-                } else {
-                    opk.u = *reinterpret_cast<const uint4 *>(&SVT[M::tpos(ch, i0)]);
-                }
-#pragma unroll
-                for (int tt = 0; tt < Y::NMT; ++tt) {
-                    if (32 * s2 > 16 * tt + 15) continue;
-                    const int r = 16 * tt + li;
-                    if (isW) {
-                        frag8 tb;
-                        tb.u = *reinterpret_cast<const uint4 *>(&TB[r][i0]);
-                        acc[tt] = mfma16(opk.v, tb.v, acc[tt]);   // rows: channels, cols: tokens
-                    } else {
-                        frag8 th, tl;
-                        th.u = *reinterpret_cast<const uint4 *>(&TH[r][i0]);
-                        tl.u = *reinterpret_cast<const uint4 *>(&TL[r][i0]);
-                        acc[tt] = mfma16(th.v, opk.v, acc[tt]);   // rows: tokens, cols: channels
-                        acc[tt] = mfma16(tl.v, opk.v, acc[tt]);
+                    for (int j = 0; j < 4; ++j) {
+                        const int i = 16 * b + 4 * g + j;
+                        av[j] = (i < r) ? (accA[u][j] + pa[j]) * br : 0.f;
+                        split_bf16((i <= r) ? accP[u][j] + pp[j] : 0.f, ph[j], pl[j]);
+                    }
+                    *reinterpret_cast<f32x4 *>(&SA[r][16 * b + 4 * g]) = av;
+                    const size_t fo = ((static_cast<size_t>(a) * Y::KSC + b / 2) * 64 + lane) * 16 + (b & 1) * 8;
+                    *reinterpret_cast<uint2 *>(blk + Y::PH + fo) = pack4(ph);
+                    *reinterpret_cast<uint2 *>(blk + Y::PL + fo) = pack4(pl);
+                    if (b == a && (b & 1) == 0) {  // the upper half of this k step is zero
+                        *reinterpret_cast<uint2 *>(blk + Y::PH + fo + 8) = make_uint2(0, 0);
+                        *reinterpret_cast<uint2 *>(blk + Y::PL + fo + 8) = make_uint2(0, 0);
                     }
                 }
             }
+        }  // live
+        // the next item's raw inputs: loads in flight during the rest of this
+        // item (issued after the Gram phase, whose registers they would crowd)
+        if (next < nitems) raw.load(p, itn.t0, itn.L, itn.h, tid);
+        if (live) {
+            lds_barrier();
+
+            if (wave == 0) {
+                // ---- 3. X = (I + A)^-1 (fp32), all on wave 0 while the other
+                //         waves build the scan operands (2b).
+                // Diagonal blocks: lane (a = lane / 16, jj = lane % 16) owns
+                // column jj of X_aa; row rr of A_aa is four broadcast 16-byte reads.
+                {
+                    const int a = lane >> 4, jj = lane & 15, base = 16 * a;
+                    if (a < Y::NMT) {
+                        float xc[16];
 #pragma unroll
-            for (int tt = 0; tt < Y::NMT; ++tt) {
-                if (isW) {
-                    bf16_t wb[4];
+                        for (int rr = 0; rr < 16; ++rr) {
+                            float arow[16];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) wb[j] = f32_to_bf16(acc[tt][j]);
-                    const size_t fo = ((static_cast<size_t>(tt) * Y::KSD + ct / 2) * 64 + lane) * 16 + (ct & 1) * 8;
-                    *reinterpret_cast<uint2 *>(blk + Y::W + fo) = pack4(wb);
-                } else {
-                    *reinterpret_cast<f32x4 *>(blk + Y::U + ((static_cast<size_t>(tt) * Y::NDT + ct) * 64 + lane) * 16) =
-                        acc[tt];
+                            for (int q4 = 0; q4 < 4; ++q4) {
+                                const f32x4 t = *reinterpret_cast<const f32x4 *>(&SA[base + rr][base + 4 * q4]);
+#pragma unroll
+                                for (int j = 0; j < 4; ++j) arow[4 * q4 + j] = t[j];
+                            }
+                            float s0 = (rr == jj) ? 1.f : 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+                            for (int i = 0; i < rr; ++i) {
+                                const float t = (i >= jj) ? arow[i] * xc[i] : 0.f;
+                                if ((i & 3) == 0) s0 -= t;
+                                else if ((i & 3) == 1) s1 -= t;
+                                else if ((i & 3) == 2) s2 -= t;
+                                else s3 -= t;
+                            }
+                            xc[rr] = (rr >= jj) ? (s0 + s1) + (s2 + s3) : 0.f;
+                        }
+#pragma unroll
+                        for (int rr = 0; rr < 16; ++rr) SX[base + rr][base + jj] = xc[rr];
+                    }
+                }
+                __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+                __builtin_amdgcn_wave_barrier();
+                // Off-diagonal blocks by levels d = a - b on fp32 matrix cores:
+                //   X_ab = -X_aa sum_{c=b}^{a-1} A_ac X_cb
+                // 16x16x16 products as four v_mfma_f32_16x16x4_f32; in step s lane
+                // (g, li) supplies k = 4g + s, so an A operand is one 16-byte row
+                // read and a product's accumulator is, register for register, the
+                // B operand of the next product.
+#pragma unroll
+                for (int d = 1; d < Y::NMT; ++d) {
+#pragma unroll
+                    for (int b = 0; b + d < Y::NMT; ++b) {
+                        const int a = b + d;
+                        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int c = b; c < a; ++c) {
+                            const f32x4 av = *reinterpret_cast<const f32x4 *>(&SA[16 * a + li][16 * c + 4 * g]);
+#pragma unroll
+                            for (int s2 = 0; s2 < 4; ++s2)
+                                y = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s2], SX[16 * c + 4 * g + s2][16 * b + li], y,
+                                                                         0, 0, 0);
+                        }
+                        const f32x4 xa = *reinterpret_cast<const f32x4 *>(&SX[16 * a + li][16 * a + 4 * g]);
+                        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int s2 = 0; s2 < 4; ++s2) z = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[s2], y[s2], z, 0, 0, 0);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) SX[16 * a + 4 * g + j][16 * b + li] = -z[j];
+                    }
+                    __builtin_amdgcn_s_waitcnt(0xc07f);
+                    __builtin_amdgcn_wave_barrier();
+                }
+            } else {
+                // ---- 2b. q e^G (scan A-operand order), (k e^{G_L - G})^T, e^{G_L}
+                constexpr int NF = Y::NMT * Y::KSD + Y::NDT * Y::KSC;
+                for (int f = wave - 1; f < NF; f += 7) {
+                    frag8 hi, lo;
+                    size_t dst_h, dst_l;
+                    if (f < Y::NMT * Y::KSD) {
+                        const int mt = f / Y::KSD, ks = f % Y::KSD;
+                        const int r = 16 * mt + li;
+                        const int cA = 32 * ks + 4 * g, cB = cA + 16;
+                        const uint2 q0 = *reinterpret_cast<const uint2 *>(&SQ[r][cA]);
+                        const uint2 q1 = *reinterpret_cast<const uint2 *>(&SQ[r][cB]);
+                        const f32x4 g0 = *reinterpret_cast<const f32x4 *>(&SG[r][cA]);
+                        const f32x4 g1 = *reinterpret_cast<const f32x4 *>(&SG[r][cB]);
+                        const bf16_t *qa = reinterpret_cast<const bf16_t *>(&q0);
+                        const bf16_t *qb = reinterpret_cast<const bf16_t *>(&q1);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            split_bf16(bf16_to_f32(qa[j]) * fast_exp2(g0[j]), hi.s[j], lo.s[j]);
+                            split_bf16(bf16_to_f32(qb[j]) * fast_exp2(g1[j]), hi.s[4 + j], lo.s[4 + j]);
+                        }
+                        const size_t fo = (static_cast<size_t>(f) * 64 + lane) * 16;
+                        dst_h = Y::QH + fo;
+                        dst_l = Y::QL + fo;
+                    } else {
+                        const int f2 = f - Y::NMT * Y::KSD;
+                        const int mt = f2 / Y::KSC, ks = f2 % Y::KSC;
+                        const int ch = 16 * mt + li;
+                        const float gl = SG[C - 1][ch];
+                        const int iA = 32 * ks + 4 * g, iB = iA + 16;
+                        const uint2 k0 = *reinterpret_cast<const uint2 *>(&SKT[M::tpos(ch, iA)]);
+                        const uint2 k1 = *reinterpret_cast<const uint2 *>(&SKT[M::tpos(ch, iB)]);
+                        const bf16_t *ka = reinterpret_cast<const bf16_t *>(&k0);
+                        const bf16_t *kb = reinterpret_cast<const bf16_t *>(&k1);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            split_bf16(bf16_to_f32(ka[j]) * fast_exp2(gl - SG[iA + j][ch]), hi.s[j], lo.s[j]);
+                            split_bf16(bf16_to_f32(kb[j]) * fast_exp2(gl - SG[iB + j][ch]), hi.s[4 + j], lo.s[4 + j]);
+                        }
+                        const size_t fo = (static_cast<size_t>(f2) * 64 + lane) * 16;
+                        dst_h = Y::KBH + fo;
+                        dst_l = Y::KBL + fo;
+                    }
+                    st16(blk + dst_h, hi.u);
+                    st16(blk + dst_l, lo.u);
+                }
+                if (tid - 64 < D) reinterpret_cast<float *>(blk + Y::GAM)[tid - 64] = fast_exp2(SG[C - 1][tid - 64]);
+            }
+            lds_barrier();
+
+            // ---- 3b. T = X Diag(beta) as MFMA operands: bf16, and hi/lo (q, A dead)
+            for (int e = tid; e < CP * CP / 4; e += 512) {
+                const int r = e / (CP / 4), i4 = (e % (CP / 4)) * 4;
+                // X is only defined on the lower block triangle of the C x C part
+                const bool live = r < C && (i4 >> 4) <= (r >> 4);
+                const f32x4 xv = live ? *reinterpret_cast<const f32x4 *>(&SX[r][i4]) : f32x4{0.f, 0.f, 0.f, 0.f};
+                bf16_t tb[4], th[4], tl[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float t = xv[j] * SBETA[i4 + j];
+                    tb[j] = f32_to_bf16(t);
+                    split_bf16(t, th[j], tl[j]);
+                }
+                *reinterpret_cast<uint2 *>(&TB[r][i4]) = pack4(tb);
+                *reinterpret_cast<uint2 *>(&TH[r][i4]) = pack4(th);
+                *reinterpret_cast<uint2 *>(&TL[r][i4]) = pack4(tl);
+            }
+            lds_barrier();
+
+            // ---- 4. W^T = (k e^G)^T T^T (bf16) per channel tile; U = T V (T split)
+            //         per value tile.  Items: NDT W tiles then NDT U tiles.
+            pend.blk = blk;
+            for (int wi = wave; wi < 2 * Y::NDT; wi += 8) {
+                const bool isW = wi < Y::NDT;
+                const int ct = isW ? wi : wi - Y::NDT;
+                const int ch = 16 * ct + li;
+                f32x4 acc[Y::NMT];
+#pragma unroll
+                for (int tt = 0; tt < Y::NMT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s2 = 0; s2 < Y::KSC; ++s2) {
+                    const int i0 = 32 * s2 + 8 * g;
+                    frag8 opk;  // W: (k e^G)^T, channel row ch, tokens i0..i0+7; U: V^T
+                    if (isW) {
+                        const uint4 kraw = *reinterpret_cast<const uint4 *>(&SKT[M::tpos(ch, i0)]);
+                        const bf16_t *kk = reinterpret_cast<const bf16_t *>(&kraw);
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            opk.s[j] = f32_to_bf16(bf16_to_f32(kk[j]) * fast_exp2(SG[i0 + j][ch]));
+                    } else {
+                        opk.u = *reinterpret_cast<const uint4 *>(&SVT[M::tpos(ch, i0)]);
+                    }
+#pragma unroll
+                    for (int tt = 0; tt < Y::NMT; ++tt) {
+                        if (32 * s2 > 16 * tt + 15) continue;
+                        const int r = 16 * tt + li;
+                        if (isW) {
+                            frag8 tb;
+                            tb.u = *reinterpret_cast<const uint4 *>(&TB[r][i0]);
+                            acc[tt] = mfma16(opk.v, tb.v, acc[tt]);   // rows: channels, cols: tokens
+                        } else {
+                            frag8 th, tl;
+                            th.u = *reinterpret_cast<const uint4 *>(&TH[r][i0]);
+                            tl.u = *reinterpret_cast<const uint4 *>(&TL[r][i0]);
+                            acc[tt] = mfma16(th.v, opk.v, acc[tt]);   // rows: tokens, cols: channels
+                            acc[tt] = mfma16(tl.v, opk.v, acc[tt]);
+                        }
+                    }
+                }
+                // stored after the next item's staging (or at exit), so that the
+                // staging's wait for its prefetched inputs does not also wait for
+                // these stores to complete
+#pragma unroll
+                for (int tt = 0; tt < Y::NMT; ++tt) {
+                    if (isW) {
+                        bf16_t wb[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) wb[j] = f32_to_bf16(acc[tt][j]);
+                        pend.w[tt] = pack4(wb);
+                    } else {
+                        pend.u[tt] = acc[tt];
+                    }
                 }
             }
-        }
-        lds_barrier();  // LDS is restaged by the next item
+            lds_barrier();  // LDS is restaged by the next item
+        }  // live
+        if (next >= nitems) break;
         it = itn;
+        const int after = next + static_cast<int>(gridDim.x);
+        nci = after < nitems ? p.chunk_info[after / H] : make_int4(0, 0, 1, 0);
     }
+    pend.flush(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6), threadIdx.x & 63);
 }
 
 // ------------------------------------------------------------------ K2 --

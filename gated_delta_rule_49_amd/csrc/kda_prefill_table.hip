@@ -3,7 +3,9 @@
 
 namespace kda {
 
-// Chunk table: chunk_off[n] = sum_{m < n} ceil(len_m / C).  With packed
+// Chunk table: chunk_off[n] = sum_{m < n} ceil(len_m / C), and per chunk x
+// chunk_info[x] = (first token low 32 bits, high 32 bits, length, sequence)
+// so that a kernel walking chunks reads its coordinates with one load.  With packed
 // input also validates cu_seqlens (0 = cu[0] <= ... <= cu[N] = T) and writes
 // the verdict to *status (and *user_status); every later kernel reads
 // *status first and does nothing if it is non-zero, so malformed offsets are
@@ -47,9 +49,22 @@ __global__ void __launch_bounds__(1024) chunk_table_kernel(PrefillParams p) {
         int32_t len = p.cu_seqlens ? p.cu_seqlens[n + 1] - p.cu_seqlens[n] : p.T;
         run += len > 0 ? (len + p.C - 1) / p.C : 0;
     }
+    if (tid == 1023) off[N] = s_sum[1023];
+    const int32_t total = s_sum[1023];
+    const bool bad = s_bad || total > p.n_chunks_bound;
+    __syncthreads();  // chunk_off visible to the whole workgroup
+    if (!bad) {
+        int4 *info = const_cast<int4 *>(p.chunk_info);
+        for (int x = tid; x < total; x += 1024) {
+            const int n = chunk_to_seq(off, N, x);
+            const SeqRange sr = seq_range(p, n);
+            const int c = x - off[n];
+            const int64_t t0 = sr.start + static_cast<int64_t>(c) * p.C;
+            info[x] = make_int4(static_cast<int32_t>(t0 & 0xffffffff), static_cast<int32_t>(t0 >> 32),
+                                min(p.C, sr.len - c * p.C), n);
+        }
+    }
     if (tid == 1023) {
-        off[N] = s_sum[1023];
-        const int32_t bad = s_bad || s_sum[1023] > p.n_chunks_bound;
         *p.status = bad ? 6 /* KDA_ERR_BAD_SEQLENS */ : 0;
         if (p.user_status) *p.user_status = bad ? 6 : 0;
     }
