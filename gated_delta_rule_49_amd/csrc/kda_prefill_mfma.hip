@@ -718,62 +718,72 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
 }
 
 // ------------------------------------------------------------------ K2 --
-// What one wave of the scan reads from a chunk's workspace block, in two
-// groups: the operands of the first products (W and q e^G, needed as soon as
-// the chunk starts; prefetched one chunk ahead) and the rest (needed only
-// after the two exchanges through LDS; requested when the chunk starts).
+// One wave's operands for one chunk, read from the chunk's workspace block in
+// MFMA register order as 128-bit register tuples.  Wave w owns state rows
+// [32w, 32w + 32): channel k-step w of the W S and (q e^G) S products and
+// channel tiles 2w, 2w + 1 of the state update; it also finishes the output
+// token tiles w, w + D/32, ...
 template <int C, int D>
-struct ScanEarly {
-    using Y = Lay<C, D>;
-    frag8 w[Y::NMT], qh[Y::NMT], ql[Y::NMT];   // token tile mt, channel step = wave
-
-    __device__ __forceinline__ void load(const char *blk, int wv, int lane) {
-#pragma unroll
-        for (int mt = 0; mt < Y::NMT; ++mt) {
-            const size_t fo = ((static_cast<size_t>(mt) * Y::KSD + wv) * 64 + lane) * 16;
-            w[mt].u = ld16(blk + Y::W + fo);
-            qh[mt].u = ld16(blk + Y::QH + fo);
-            ql[mt].u = ld16(blk + Y::QL + fo);
-        }
-    }
-};
-
-template <int C, int D>
-struct ScanLate {
+struct ScanOps {
     using Y = Lay<C, D>;
     static constexpr int NW = D / 32;
     static constexpr int OWN = (Y::NMT + NW - 1) / NW;
+    typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+    u32x4 w[Y::NMT], qh[Y::NMT], ql[Y::NMT];   // token tile mt, channel step = wave
+    u32x4 kh[2][Y::KSC], kl[2][Y::KSC];       // the wave's two channel tiles x token steps
+    u32x4 ph[OWN][Y::KSC], pl[OWN][Y::KSC];   // owned token tiles x token steps
+    f32x4 u[OWN];                             // owned token tiles, this column tile
     f32x4 gam[2];
-    f32x4 u[OWN];                               // owned token tiles, this column tile
-    frag8 ph[OWN][Y::KSC], pl[OWN][Y::KSC];    // owned token tiles x token steps
-    frag8 kh[2][Y::KSC], kl[2][Y::KSC];        // the wave's two channel tiles x token steps
 
-    __device__ __forceinline__ void load(const char *blk, int wv, int nt, int lane) {
-        const int g = lane >> 4;
+    // blk: the chunk's block (uniform); lane16 = 16 * lane.  Four parts, so
+    // that the requests can be spread over the previous chunk's computation.
+    __device__ __forceinline__ void load(int part, const char *blk, uint32_t lane16, int wv, int nt, int g) {
+        auto at = [&](size_t off) { return reinterpret_cast<const u32x4 *>(blk + off + lane16); };
+        if (part == 0) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) gam[i] = ldf4(blk + Y::GAM + (32 * wv + 16 * i + 4 * g) * sizeof(float));
+            for (int mt = 0; mt < Y::NMT; ++mt) {
+                const size_t fo = (static_cast<size_t>(mt) * Y::KSD + wv) * Y::FRAG;
+                w[mt] = *at(Y::W + fo);
+                qh[mt] = *at(Y::QH + fo);
+                ql[mt] = *at(Y::QL + fo);
+            }
+        } else if (part == 1) {
 #pragma unroll
-        for (int uu = 0; uu < OWN; ++uu) {
-            const int mt = wv + uu * NW;
-            if (mt >= Y::NMT) continue;
-            u[uu] = ldf4(blk + Y::U + ((static_cast<size_t>(mt) * Y::NDT + nt) * 64 + lane) * 16);
+            for (int uu = 0; uu < OWN; ++uu) {
+                const int mt = wv + uu * NW;
+                if (mt >= Y::NMT) continue;
+                u[uu] = __builtin_bit_cast(f32x4, *at(Y::U + (static_cast<size_t>(mt) * Y::NDT + nt) * Y::FRAG));
+            }
 #pragma unroll
-            for (int st = 0; st < Y::KSC; ++st) {
-                if (32 * st > 16 * mt + 15) continue;
-                const size_t fo = ((static_cast<size_t>(mt) * Y::KSC + st) * 64 + lane) * 16;
-                ph[uu][st].u = ld16(blk + Y::PH + fo);
-                pl[uu][st].u = ld16(blk + Y::PL + fo);
+            for (int i = 0; i < 2; ++i)
+                gam[i] = *reinterpret_cast<const f32x4 *>(blk + Y::GAM + (32 * wv + 16 * i + 4 * g) * sizeof(float));
+        } else if (part == 2) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int st = 0; st < Y::KSC; ++st) {
+                    const size_t fo = (static_cast<size_t>(2 * wv + i) * Y::KSC + st) * Y::FRAG;
+                    kh[i][st] = *at(Y::KBH + fo);
+                    kl[i][st] = *at(Y::KBL + fo);
+                }
+        } else {
+#pragma unroll
+            for (int uu = 0; uu < OWN; ++uu) {
+                const int mt = wv + uu * NW;
+                if (mt >= Y::NMT) continue;
+#pragma unroll
+                for (int st = 0; st < Y::KSC; ++st) {
+                    if (32 * st > 16 * mt + 15) continue;  // zero above the diagonal
+                    const size_t fo = (static_cast<size_t>(mt) * Y::KSC + st) * Y::FRAG;
+                    ph[uu][st] = *at(Y::PH + fo);
+                    pl[uu][st] = *at(Y::PL + fo);
+                }
             }
         }
+    }
+    __device__ __forceinline__ void load(const char *blk, uint32_t lane16, int wv, int nt, int g) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-#pragma unroll
-            for (int st = 0; st < Y::KSC; ++st) {
-                const size_t fo = ((static_cast<size_t>(2 * wv + i) * Y::KSC + st) * 64 + lane) * 16;
-                kh[i][st].u = ld16(blk + Y::KBH + fo);
-                kl[i][st].u = ld16(blk + Y::KBL + fo);
-            }
-        }
+        for (int part = 0; part < 4; ++part) load(part, blk, lane16, wv, nt, g);
     }
 };
 
@@ -784,15 +794,20 @@ struct ScanShared {
     uint4 dls[Y::NMT][64];
 };
 
+__device__ __forceinline__ bf16x8 as_bf16x8(const ScanOps<64, 128>::u32x4 &u) { return __builtin_bit_cast(bf16x8, u); }
+
 // One chunk of the scan for one wave: consumes the operands in `op` and
 // updates the state tiles S in place.
+// The next chunk's operands are requested into `nx` in four parts between
+// the phases, so that the transfers overlap this chunk's computation.
 template <int C, int D, typename TO>
-__device__ __forceinline__ void scan_chunk(const ScanEarly<C, D> &ope, const ScanLate<C, D> &op, f32x4 (&S)[2],
-                                           ScanShared<C, D> &sh, const PrefillParams &p, int64_t x,
-                                           int64_t t0, int L, int h, int w, int nt, int lane) {
+__device__ __forceinline__ void scan_chunk(const ScanOps<C, D> &op, ScanOps<C, D> &nx, const char *nblk,
+                                           uint32_t lane16, f32x4 (&S)[2], ScanShared<C, D> &sh,
+                                           const PrefillParams &p, int64_t x, int64_t t0, int L, int h, int w,
+                                           int nt, int lane) {
     using Y = Lay<C, D>;
     constexpr int NW = D / 32;
-    constexpr int OWN = ScanLate<C, D>::OWN;
+    constexpr int OWN = ScanOps<C, D>::OWN;
     const int g = lane >> 4, li = lane & 15;
     const int col = 16 * nt + li;
     const int H = p.H;
@@ -806,16 +821,19 @@ __device__ __forceinline__ void scan_chunk(const ScanEarly<C, D> &ope, const Sca
     // (a) this wave's state rows as a B operand, hi/lo
     frag8 sh_, sl_;
     acc2_to_split(S[0], S[1], sh_, sl_);
-    // (b) partial W S and (q e^G) S over this wave's 32 channels
+    // (b) partial W S (W and S both rounded to bf16: the product only reaches
+    //     the outputs through Delta's first-order term) and (q e^G) S over this
+    //     wave's 32 channels
 #pragma unroll
     for (int mt = 0; mt < Y::NMT; ++mt) {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        sh.red[0][w][mt][lane] = mfma16(ope.w[mt].v, sh_.v, z);
-        f32x4 pq = mfma16(ope.qh[mt].v, sh_.v, z);
-        pq = mfma16(ope.qh[mt].v, sl_.v, pq);
-        pq = mfma16(ope.ql[mt].v, sh_.v, pq);
+        sh.red[0][w][mt][lane] = mfma16(as_bf16x8(op.w[mt]), sh_.v, z);
+        f32x4 pq = mfma16(as_bf16x8(op.qh[mt]), sh_.v, z);
+        pq = mfma16(as_bf16x8(op.qh[mt]), sl_.v, pq);
+        pq = mfma16(as_bf16x8(op.ql[mt]), sh_.v, pq);
         sh.red[1][w][mt][lane] = pq;
     }
+    nx.load(0, nblk, lane16, w, nt, g);
     lds_barrier();
     // (c) reduce the owned token tiles: Delta = U - sum_w W S
     f32x4 oq[OWN];
@@ -837,6 +855,7 @@ __device__ __forceinline__ void scan_chunk(const ScanEarly<C, D> &ope, const Sca
         const uint2 ph = pack4(hi), pl = pack4(lo);
         sh.dls[mt][lane] = make_uint4(ph.x, ph.y, pl.x, pl.y);
     }
+    nx.load(1, nblk, lane16, w, nt, g);
     lds_barrier();
     // (d) Delta as B operands, one per 32-token step
     frag8 dh[Y::KSC], dl[Y::KSC];
@@ -847,7 +866,20 @@ __device__ __forceinline__ void scan_chunk(const ScanEarly<C, D> &ope, const Sca
         dh[st].u = make_uint4(a0.x, a0.y, a1.x, a1.y);
         dl[st].u = make_uint4(a0.z, a0.w, a1.z, a1.w);
     }
-    // (e) outputs of the owned token tiles: O = (q e^G) S + P Delta
+    // (e) state: S = e^{G_L} S + (k e^{G_L - G})^T Delta  (first: it carries
+    //     the dependency into the next chunk)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        S[i] *= op.gam[i];
+#pragma unroll
+        for (int st = 0; st < Y::KSC; ++st) {
+            S[i] = mfma16(as_bf16x8(op.kh[i][st]), dh[st].v, S[i]);
+            S[i] = mfma16(as_bf16x8(op.kh[i][st]), dl[st].v, S[i]);
+            S[i] = mfma16(as_bf16x8(op.kl[i][st]), dh[st].v, S[i]);
+        }
+    }
+    nx.load(2, nblk, lane16, w, nt, g);
+    // (f) outputs of the owned token tiles: O = (q e^G) S + P Delta
     TO *o = static_cast<TO *>(p.o);
 #pragma unroll
     for (int uu = 0; uu < OWN; ++uu) {
@@ -857,9 +889,9 @@ __device__ __forceinline__ void scan_chunk(const ScanEarly<C, D> &ope, const Sca
 #pragma unroll
         for (int st = 0; st < Y::KSC; ++st) {
             if (32 * st > 16 * mt + 15) continue;
-            acc = mfma16(op.ph[uu][st].v, dh[st].v, acc);
-            acc = mfma16(op.ph[uu][st].v, dl[st].v, acc);
-            acc = mfma16(op.pl[uu][st].v, dh[st].v, acc);
+            acc = mfma16(as_bf16x8(op.ph[uu][st]), dh[st].v, acc);
+            acc = mfma16(as_bf16x8(op.ph[uu][st]), dl[st].v, acc);
+            acc = mfma16(as_bf16x8(op.pl[uu][st]), dh[st].v, acc);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -867,17 +899,7 @@ __device__ __forceinline__ void scan_chunk(const ScanEarly<C, D> &ope, const Sca
             if (tok < L) io<TO>::st(o, ((t0 + tok) * H + h) * D + col, acc[j]);
         }
     }
-    // (f) state: S = e^{G_L} S + (k e^{G_L - G})^T Delta
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        S[i] *= op.gam[i];
-#pragma unroll
-        for (int st = 0; st < Y::KSC; ++st) {
-            S[i] = mfma16(op.kh[i][st].v, dh[st].v, S[i]);
-            S[i] = mfma16(op.kh[i][st].v, dl[st].v, S[i]);
-            S[i] = mfma16(op.kl[i][st].v, dh[st].v, S[i]);
-        }
-    }
+    nx.load(3, nblk, lane16, w, nt, g);
 }
 
 template <int C, int D, typename TO>
@@ -897,7 +919,7 @@ __global__ void __launch_bounds__(64 * (D / 32)) scan_kernel(PrefillParams p, co
     const SeqRange sr = seq_range(p, n);
     const int nch = (sr.len + C - 1) / C;
     const int64_t cbase = p.chunk_off[n];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, li = lane & 15;
     const int col = 16 * nt + li;
 
@@ -916,26 +938,38 @@ __global__ void __launch_bounds__(64 * (D / 32)) scan_kernel(PrefillParams p, co
     auto blk_of = [&](int c) {
         return blocks + (static_cast<size_t>(cbase + c) * H + h) * Y::BYTES;
     };
-    // Per chunk c: its late operands are requested first, then chunk c+1's
-    // first operands, then chunk c is computed.  vmcnt retires in order, so
-    // waiting for chunk c's operands never waits for the prefetch behind
-    // them; the prefetch is unconditional (clamped chunk index) and the
-    // barriers order LDS only, so nothing else forces it to complete early.
-    ScanEarly<C, D> e0, e1;
-    ScanLate<C, D> lt;
+    // Every operand of chunk c + 1 is requested while chunk c is computed
+    // (two buffers, alternating); chunk indices are clamped, so every load is
+    // inside the sequence's blocks.  Waves exchange data through LDS only.
+    // L2 warm-up: while chunk c is computed, the column tiles of the head
+    // together touch every 128-byte line of chunk c + kWarmAhead's block (one
+    // dword per line, this workgroup's eighth), so that block is in L2 before
+    // its operands are requested; the loaded word is only consumed (without
+    // instructions) one chunk later, so the wait for it is free.
+    constexpr int kWarmAhead = 2;
+    constexpr int kLines = static_cast<int>(Y::BYTES / 128);
+    constexpr int kSlots = NVT * (D / 32) * 64;  // lanes of all the head's workgroups
+    const uint32_t warm_off = static_cast<uint32_t>(((nt * (D / 32) + w) * 64 + lane) * kLines / kSlots) * 128u;
+    uint32_t warm = 0;
+    auto warm_up = [&](int c) {
+        asm volatile("" ::"v"(warm));
+        warm = *reinterpret_cast<const uint32_t *>(blk_of(min(c + kWarmAhead, nch - 1)) + warm_off);
+    };
+    ScanOps<C, D> A, B;
     if (nch > 0) {
-        e0.load(blk_of(0), w, lane);
+        const uint32_t lane16 = 16u * lane;
+        A.load(blk_of(0), lane16, w, nt, g);
         for (int c = 0; c < nch; c += 2) {
-            lt.load(blk_of(c), w, nt, lane);
-            e1.load(blk_of(min(c + 1, nch - 1)), w, lane);
-            scan_chunk<C, D, TO>(e0, lt, S, sh, p, cbase + c, sr.start + static_cast<int64_t>(c) * C,
-                                 min(C, sr.len - c * C), h, w, nt, lane);
+            warm_up(c);
+            scan_chunk<C, D, TO>(A, B, blk_of(min(c + 1, nch - 1)), lane16, S, sh, p, cbase + c,
+                                 sr.start + static_cast<int64_t>(c) * C, min(C, sr.len - c * C), h, w, nt, lane);
             if (c + 1 >= nch) break;
-            lt.load(blk_of(c + 1), w, nt, lane);
-            e0.load(blk_of(min(c + 2, nch - 1)), w, lane);
-            scan_chunk<C, D, TO>(e1, lt, S, sh, p, cbase + c + 1, sr.start + static_cast<int64_t>(c + 1) * C,
-                                 min(C, sr.len - (c + 1) * C), h, w, nt, lane);
+            warm_up(c + 1);
+            scan_chunk<C, D, TO>(B, A, blk_of(min(c + 2, nch - 1)), lane16, S, sh, p, cbase + c + 1,
+                                 sr.start + static_cast<int64_t>(c + 1) * C, min(C, sr.len - (c + 1) * C), h, w,
+                                 nt, lane);
         }
+        asm volatile("" ::"v"(warm));
     }
     if (p.final_state) {
 #pragma unroll
