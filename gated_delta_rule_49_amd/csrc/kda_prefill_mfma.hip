@@ -84,8 +84,10 @@ __device__ __forceinline__ uint2 pack4(const bf16_t *s) {
 // persistent intra-chunk grid: one workgroup per CU of an MI355X (256 CUs)
 constexpr int kIntraGrid = 256;
 
-// log2-domain threshold for factorising a diagonal Gram block
-constexpr float kDiagSpanMax = 100.f;
+// Diagonal Gram blocks are factorised around the midpoint of their own decay
+// (both factors within 2^(+-span/2)); beyond this span (log2 units) they are
+// computed pair by pair instead.
+constexpr float kDiagSpanMax = 200.f;
 
 // ------------------------------------------------------------------ K1 --
 // LDS plan of the intra-chunk kernel (bytes).  Rows are padded so that the
@@ -357,13 +359,16 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
             //         (block pair, half of the channels): wave w = kh + 2 grp takes
             //         channel half kh of the pairs in group grp (gram_pair), so every
             //         SIMD gets the same number of units and a wave reuses its row
-            //         operands across the pairs of one row block.  Factors around
+            //         operands across the pairs of one row block.  Operands are
+            //         split into bf16 hi + lo (three MFMA passes, ~16 bits; fp32
+            //         matrix cores cost ~5x the matrix time and measured slower).
+            //         Factors around
             //         reference row m = 16a - 1: rows (<= 1) e^{G_r - G_m}, columns
             //         e^{G_m - G_i}.  Half 1 leaves its partial sums in LDS (A in SA,
             //         P in SX) and half 0 adds them and finalises.
             bool exact[3];
             {
-                float kr32[KH][8], qr32[KH][8];  // row operands, fp32
+                frag8 krh[KH], krl[KH], qrh[KH], qrl[KH];
                 int cur_a = -1;
 #pragma unroll
                 for (int u = 0; u < 3; ++u) {
@@ -384,6 +389,40 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
                         }
                         exact[u] = wave_max(span) > kDiagSpanMax;
                         if (exact[u]) continue;  // done pair by pair below
+                        // Factorise around c = (G_m + G_{16a+15}) / 2 per channel:
+                        // rows e^{G_r - c}, columns e^{c - G_i}, both within
+                        // 2^(+-span/2) and kept in fp32 (fp32 matrix cores: no
+                        // hi/lo split).  Rows and columns are the same 16 tokens,
+                        // so a lane builds both operands of its own token.
+#pragma unroll
+                        for (int s2 = 0; s2 < KH; ++s2) {
+                            const int c0 = 32 * (KH * kh + s2) + 8 * g;
+                            const uint4 kraw = *reinterpret_cast<const uint4 *>(&SK[r][c0]);
+                            const uint4 qraw = *reinterpret_cast<const uint4 *>(&SQ[r][c0]);
+                            const bf16_t *kr = reinterpret_cast<const bf16_t *>(&kraw);
+                            const bf16_t *qr = reinterpret_cast<const bf16_t *>(&qraw);
+                            const f32x4 gr0 = *reinterpret_cast<const f32x4 *>(&SG[r][c0]);
+                            const f32x4 gr1 = *reinterpret_cast<const f32x4 *>(&SG[r][c0 + 4]);
+                            const f32x4 ge0 = *reinterpret_cast<const f32x4 *>(&SG[16 * a + 15][c0]);
+                            const f32x4 ge1 = *reinterpret_cast<const f32x4 *>(&SG[16 * a + 15][c0 + 4]);
+                            f32x4 gm0 = {0.f, 0.f, 0.f, 0.f}, gm1 = gm0;
+                            if (a > 0) {
+                                gm0 = *reinterpret_cast<const f32x4 *>(&SG[16 * a - 1][c0]);
+                                gm1 = *reinterpret_cast<const f32x4 *>(&SG[16 * a - 1][c0 + 4]);
+                            }
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) {
+                                const float gr = j < 4 ? gr0[j] : gr1[j - 4];
+                                const float cmid = 0.5f * ((j < 4 ? gm0[j] : gm1[j - 4]) + (j < 4 ? ge0[j] : ge1[j - 4]));
+                                const float kv = bf16_to_f32(kr[j]);
+                                const float rf = fast_exp2(gr - cmid), cf = fast_exp2(cmid - gr);
+                                // step j: lane group g contributes channel c0 + j
+                                accA[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv * cf, kv * rf, accA[u], 0, 0, 0);
+                                accP[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv * cf, bf16_to_f32(qr[j]) * rf, accP[u],
+                                                                               0, 0, 0);
+                            }
+                        }
+                        continue;
                     }
                     if (a != cur_a) {  // row operands of block a, this channel half
 #pragma unroll
@@ -403,8 +442,8 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
 #pragma unroll
                             for (int j = 0; j < 8; ++j) {
                                 const float rf = fast_exp2(j < 4 ? gr0[j] - gm0[j] : gr1[j - 4] - gm1[j - 4]);
-                                kr32[s2][j] = bf16_to_f32(kr[j]) * rf;
-                                qr32[s2][j] = bf16_to_f32(qr[j]) * rf;
+                                split_bf16(bf16_to_f32(kr[j]) * rf, krh[s2].s[j], krl[s2].s[j]);
+                                split_bf16(bf16_to_f32(qr[j]) * rf, qrh[s2].s[j], qrl[s2].s[j]);
                             }
                         }
                         cur_a = a;
@@ -422,15 +461,18 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
                             gm0 = *reinterpret_cast<const f32x4 *>(&SG[16 * a - 1][c0]);
                             gm1 = *reinterpret_cast<const f32x4 *>(&SG[16 * a - 1][c0 + 4]);
                         }
-                        // fp32 matrix cores, four channels per step: in step j lane
-                        // group g contributes channel c0 + j of its row / column
+                        frag8 kih, kil;
 #pragma unroll
                         for (int j = 0; j < 8; ++j) {
                             const float cf = fast_exp2(j < 4 ? gm0[j] - gi0[j] : gm1[j - 4] - gi1[j - 4]);
-                            const float kc = bf16_to_f32(ki[j]) * cf;
-                            accA[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(kc, kr32[s2][j], accA[u], 0, 0, 0);
-                            accP[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(kc, qr32[s2][j], accP[u], 0, 0, 0);
+                            split_bf16(bf16_to_f32(ki[j]) * cf, kih.s[j], kil.s[j]);
                         }
+                        accA[u] = mfma16(kih.v, krh[s2].v, accA[u]);
+                        accA[u] = mfma16(kih.v, krl[s2].v, accA[u]);
+                        accA[u] = mfma16(kil.v, krh[s2].v, accA[u]);
+                        accP[u] = mfma16(kih.v, qrh[s2].v, accP[u]);
+                        accP[u] = mfma16(kih.v, qrl[s2].v, accP[u]);
+                        accP[u] = mfma16(kil.v, qrh[s2].v, accP[u]);
                     }
                 }
             }
