@@ -110,7 +110,8 @@ struct IntraLds {
     static constexpr size_t SG = SVT + D * RT * 2;                    // G   [CP][RG] f32 (log2 units)
     static constexpr size_t ST = SG + CP * RG * 4;                    // X = (I+A)^-1 [CP][RA] f32
     static constexpr size_t SB = ST + CP * RA * 4;                    // beta [CP]
-    static constexpr size_t END = SB + CP * 4;
+    static constexpr size_t SCNT = SB + CP * 4;                       // work counter (int)
+    static constexpr size_t END = SCNT + 16;
     // after the Gram phase q and A are dead: the T fragments reuse [SQ, SKT)
     // when they fit there, else they get their own region
     static constexpr bool REUSE = 3 * CP * RTF * 2 <= SKT - SQ;
@@ -217,6 +218,36 @@ __device__ __forceinline__ IntraItem intra_item(int item, int H, const int4 &ci)
     it.t0 = static_cast<int64_t>(static_cast<uint32_t>(ci.x)) | (static_cast<int64_t>(ci.y) << 32);
     it.L = ci.z;
     return it;
+}
+
+// P Q for 16 x 16 fp32 matrices held in accumulator layout (lane l: rows
+// 4(l/16) + j, column l % 16), with P given transposed: four
+// v_mfma_f32_16x16x4_f32 steps, step s taking k = 4(l/16) + s, so the A value
+// of lane l is P[l%16][4(l/16)+s] = pt[s] and the B value is q[s].
+__device__ __forceinline__ f32x4 mm16(const f32x4 &pt, const f32x4 &q) {
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(pt[s], q[s], c, 0, 0, 0);
+    return c;
+}
+
+// (I + N)^-1 for a strictly lower 16 x 16 N (nilpotent): with M = -N,
+// (I + M)(I + M^2)(I + M^4)(I + M^8), four levels of 16 x 16 products on
+// fp32 matrix cores.  n and nt are N and N^T in accumulator layout; returns
+// the inverse in accumulator layout (exactly zero above the diagonal).
+__device__ __forceinline__ f32x4 unit_lower_inverse16(const f32x4 &n, const f32x4 &nt, int lane) {
+    const int g = lane >> 4, li = lane & 15;
+    const f32x4 m = -n, mt = -nt;
+    const f32x4 m2 = mm16(mt, m), m2t = mm16(m, mt);
+    const f32x4 m3 = mm16(mt, m2), m3t = mm16(m2, mt);
+    const f32x4 m4 = mm16(m2t, m2), m4t = mm16(m2, m2t);
+    const f32x4 m8 = mm16(m4t, m4);
+    f32x4 id;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) id[j] = (4 * g + j == li) ? 1.f : 0.f;
+    const f32x4 r1 = id + m + m2 + m3, r1t = id + mt + m2t + m3t;  // (I + M)(I + M^2)
+    const f32x4 r2 = r1 + mm16(r1t, m4), r2t = r1t + mm16(m4, r1t);  // ... (I + M^4)
+    return r2 + mm16(r2t, m8);                                          // ... (I + M^8)
 }
 
 // Gram work plan: the block pair (a, b <= a) that wave group grp (0..3)
@@ -333,6 +364,8 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
                           __uint_as_float(aw[3] << 16), __uint_as_float(aw[3] & 0xffff0000u)};
             }
             if (tid < CP) SBETA[tid] = tid < L ? bf16_to_f32(static_cast<bf16_t>(raw.beta)) : 0.f;
+            // fragments 0 .. 7 - C/16 go to the waves that do not invert a diagonal block
+            if (tid == 0) *reinterpret_cast<int *>(smem + M::SCNT) = 8 - Y::NMT;
             lds_barrier();
             pend.flush(wave, lane);  // the previous item's W and U tiles
             {
@@ -560,118 +593,101 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
         if (live) {
             lds_barrier();
 
-            if (wave == 0) {
-                // ---- 3. X = (I + A)^-1 (fp32), all on wave 0 while the other
-                //         waves build the scan operands (2b).
-                // Diagonal blocks: lane (a = lane / 16, jj = lane % 16) owns
-                // column jj of X_aa; row rr of A_aa is four broadcast 16-byte reads.
-                {
-                    const int a = lane >> 4, jj = lane & 15, base = 16 * a;
-                    if (a < Y::NMT) {
-                        float xc[16];
+            // ---- 2b (any idle wave). One scan-operand fragment: q e^G in the
+            //      scan's A-operand order, or (k e^{G_L - G})^T, as bf16 hi/lo.
+            constexpr int NF = Y::NMT * Y::KSD + Y::NDT * Y::KSC;
+            auto operand_fragment = [&](int f) {
+                frag8 hi, lo;
+                size_t dst_h, dst_l;
+                if (f < Y::NMT * Y::KSD) {
+                    const int mt = f / Y::KSD, ks = f % Y::KSD;
+                    const int r = 16 * mt + li;
+                    const int cA = 32 * ks + 4 * g, cB = cA + 16;
+                    const uint2 q0 = *reinterpret_cast<const uint2 *>(&SQ[r][cA]);
+                    const uint2 q1 = *reinterpret_cast<const uint2 *>(&SQ[r][cB]);
+                    const f32x4 g0 = *reinterpret_cast<const f32x4 *>(&SG[r][cA]);
+                    const f32x4 g1 = *reinterpret_cast<const f32x4 *>(&SG[r][cB]);
+                    const bf16_t *qa = reinterpret_cast<const bf16_t *>(&q0);
+                    const bf16_t *qb = reinterpret_cast<const bf16_t *>(&q1);
 #pragma unroll
-                        for (int rr = 0; rr < 16; ++rr) {
-                            float arow[16];
-#pragma unroll
-                            for (int q4 = 0; q4 < 4; ++q4) {
-                                const f32x4 t = *reinterpret_cast<const f32x4 *>(&SA[base + rr][base + 4 * q4]);
-#pragma unroll
-                                for (int j = 0; j < 4; ++j) arow[4 * q4 + j] = t[j];
-                            }
-                            float s0 = (rr == jj) ? 1.f : 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-                            for (int i = 0; i < rr; ++i) {
-                                const float t = (i >= jj) ? arow[i] * xc[i] : 0.f;
-                                if ((i & 3) == 0) s0 -= t;
-                                else if ((i & 3) == 1) s1 -= t;
-                                else if ((i & 3) == 2) s2 -= t;
-                                else s3 -= t;
-                            }
-                            xc[rr] = (rr >= jj) ? (s0 + s1) + (s2 + s3) : 0.f;
-                        }
-#pragma unroll
-                        for (int rr = 0; rr < 16; ++rr) SX[base + rr][base + jj] = xc[rr];
+                    for (int j = 0; j < 4; ++j) {
+                        split_bf16(bf16_to_f32(qa[j]) * fast_exp2(g0[j]), hi.s[j], lo.s[j]);
+                        split_bf16(bf16_to_f32(qb[j]) * fast_exp2(g1[j]), hi.s[4 + j], lo.s[4 + j]);
                     }
-                }
-                __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-                __builtin_amdgcn_wave_barrier();
-                // Off-diagonal blocks by levels d = a - b on fp32 matrix cores:
-                //   X_ab = -X_aa sum_{c=b}^{a-1} A_ac X_cb
-                // 16x16x16 products as four v_mfma_f32_16x16x4_f32; in step s lane
-                // (g, li) supplies k = 4g + s, so an A operand is one 16-byte row
-                // read and a product's accumulator is, register for register, the
-                // B operand of the next product.
+                    const size_t fo = (static_cast<size_t>(f) * 64 + lane) * 16;
+                    dst_h = Y::QH + fo;
+                    dst_l = Y::QL + fo;
+                } else {
+                    const int f2 = f - Y::NMT * Y::KSD;
+                    const int mt = f2 / Y::KSC, ks = f2 % Y::KSC;
+                    const int ch = 16 * mt + li;
+                    const float gl = SG[C - 1][ch];
+                    const int iA = 32 * ks + 4 * g, iB = iA + 16;
+                    const uint2 k0 = *reinterpret_cast<const uint2 *>(&SKT[M::tpos(ch, iA)]);
+                    const uint2 k1 = *reinterpret_cast<const uint2 *>(&SKT[M::tpos(ch, iB)]);
+                    const bf16_t *ka = reinterpret_cast<const bf16_t *>(&k0);
+                    const bf16_t *kb = reinterpret_cast<const bf16_t *>(&k1);
 #pragma unroll
-                for (int d = 1; d < Y::NMT; ++d) {
-#pragma unroll
-                    for (int b = 0; b + d < Y::NMT; ++b) {
-                        const int a = b + d;
-                        f32x4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int c = b; c < a; ++c) {
-                            const f32x4 av = *reinterpret_cast<const f32x4 *>(&SA[16 * a + li][16 * c + 4 * g]);
-#pragma unroll
-                            for (int s2 = 0; s2 < 4; ++s2)
-                                y = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s2], SX[16 * c + 4 * g + s2][16 * b + li], y,
-                                                                         0, 0, 0);
-                        }
-                        const f32x4 xa = *reinterpret_cast<const f32x4 *>(&SX[16 * a + li][16 * a + 4 * g]);
-                        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int s2 = 0; s2 < 4; ++s2) z = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[s2], y[s2], z, 0, 0, 0);
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) SX[16 * a + 4 * g + j][16 * b + li] = -z[j];
+                    for (int j = 0; j < 4; ++j) {
+                        split_bf16(bf16_to_f32(ka[j]) * fast_exp2(gl - SG[iA + j][ch]), hi.s[j], lo.s[j]);
+                        split_bf16(bf16_to_f32(kb[j]) * fast_exp2(gl - SG[iB + j][ch]), hi.s[4 + j], lo.s[4 + j]);
                     }
-                    __builtin_amdgcn_s_waitcnt(0xc07f);
-                    __builtin_amdgcn_wave_barrier();
+                    const size_t fo = (static_cast<size_t>(f2) * 64 + lane) * 16;
+                    dst_h = Y::KBH + fo;
+                    dst_l = Y::KBL + fo;
                 }
-            } else {
-                // ---- 2b. q e^G (scan A-operand order), (k e^{G_L - G})^T, e^{G_L}
-                constexpr int NF = Y::NMT * Y::KSD + Y::NDT * Y::KSC;
-                for (int f = wave - 1; f < NF; f += 7) {
-                    frag8 hi, lo;
-                    size_t dst_h, dst_l;
-                    if (f < Y::NMT * Y::KSD) {
-                        const int mt = f / Y::KSD, ks = f % Y::KSD;
-                        const int r = 16 * mt + li;
-                        const int cA = 32 * ks + 4 * g, cB = cA + 16;
-                        const uint2 q0 = *reinterpret_cast<const uint2 *>(&SQ[r][cA]);
-                        const uint2 q1 = *reinterpret_cast<const uint2 *>(&SQ[r][cB]);
-                        const f32x4 g0 = *reinterpret_cast<const f32x4 *>(&SG[r][cA]);
-                        const f32x4 g1 = *reinterpret_cast<const f32x4 *>(&SG[r][cB]);
-                        const bf16_t *qa = reinterpret_cast<const bf16_t *>(&q0);
-                        const bf16_t *qb = reinterpret_cast<const bf16_t *>(&q1);
+                st16(blk + dst_h, hi.u);
+                st16(blk + dst_l, lo.u);
+            };
+
+            // ---- 3. X = (I + A)^-1 in fp32 on matrix cores.  (a) wave a < C/16
+            //         inverts diagonal block a while the other waves take one
+            //         operand fragment each; (b) wave b < C/16 - 1 walks block
+            //         column b down, X_ab = -X_aa sum_{c=b}^{a-1} A_ac X_cb, one
+            //         product chain per term; every wave then takes the remaining
+            //         fragments from a counter in LDS.
+            f32x4 xdiag = {0.f, 0.f, 0.f, 0.f};
+            if (wave < Y::NMT) {
+                const int base = 16 * wave;
+                f32x4 n, nt;
+                nt = *reinterpret_cast<const f32x4 *>(&SA[base + li][base + 4 * g]);
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            split_bf16(bf16_to_f32(qa[j]) * fast_exp2(g0[j]), hi.s[j], lo.s[j]);
-                            split_bf16(bf16_to_f32(qb[j]) * fast_exp2(g1[j]), hi.s[4 + j], lo.s[4 + j]);
-                        }
-                        const size_t fo = (static_cast<size_t>(f) * 64 + lane) * 16;
-                        dst_h = Y::QH + fo;
-                        dst_l = Y::QL + fo;
-                    } else {
-                        const int f2 = f - Y::NMT * Y::KSD;
-                        const int mt = f2 / Y::KSC, ks = f2 % Y::KSC;
-                        const int ch = 16 * mt + li;
-                        const float gl = SG[C - 1][ch];
-                        const int iA = 32 * ks + 4 * g, iB = iA + 16;
-                        const uint2 k0 = *reinterpret_cast<const uint2 *>(&SKT[M::tpos(ch, iA)]);
-                        const uint2 k1 = *reinterpret_cast<const uint2 *>(&SKT[M::tpos(ch, iB)]);
-                        const bf16_t *ka = reinterpret_cast<const bf16_t *>(&k0);
-                        const bf16_t *kb = reinterpret_cast<const bf16_t *>(&k1);
+                for (int j = 0; j < 4; ++j) n[j] = SA[base + 4 * g + j][base + li];
+                xdiag = unit_lower_inverse16(n, nt, lane);
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            split_bf16(bf16_to_f32(ka[j]) * fast_exp2(gl - SG[iA + j][ch]), hi.s[j], lo.s[j]);
-                            split_bf16(bf16_to_f32(kb[j]) * fast_exp2(gl - SG[iB + j][ch]), hi.s[4 + j], lo.s[4 + j]);
-                        }
-                        const size_t fo = (static_cast<size_t>(f2) * 64 + lane) * 16;
-                        dst_h = Y::KBH + fo;
-                        dst_l = Y::KBL + fo;
+                for (int j = 0; j < 4; ++j) SX[base + 4 * g + j][base + li] = xdiag[j];
+            } else if (wave - Y::NMT < NF) {
+                operand_fragment(wave - Y::NMT);
+            }
+            lds_barrier();
+            if (wave < Y::NMT - 1) {
+                const int b = wave;
+                f32x4 xcol[Y::NMT];  // X_cb, c >= b, accumulator layout
+#pragma unroll
+                for (int c = 0; c < Y::NMT; ++c) xcol[c] = xdiag;
+#pragma unroll
+                for (int a = 1; a < Y::NMT; ++a) {
+                    if (a <= b) continue;
+                    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int c = 0; c < Y::NMT - 1; ++c) {
+                        if (c < b || c >= a) continue;
+                        y += mm16(*reinterpret_cast<const f32x4 *>(&SA[16 * a + li][16 * c + 4 * g]), xcol[c]);
                     }
-                    st16(blk + dst_h, hi.u);
-                    st16(blk + dst_l, lo.u);
+                    const f32x4 z = mm16(*reinterpret_cast<const f32x4 *>(&SX[16 * a + li][16 * a + 4 * g]), y);
+                    xcol[a] = -z;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) SX[16 * a + 4 * g + j][16 * b + li] = -z[j];
                 }
-                if (tid - 64 < D) reinterpret_cast<float *>(blk + Y::GAM)[tid - 64] = fast_exp2(SG[C - 1][tid - 64]);
+            }
+            if (tid >= 512 - D) reinterpret_cast<float *>(blk + Y::GAM)[tid - (512 - D)] = fast_exp2(SG[C - 1][tid - (512 - D)]);
+            int *cnt = reinterpret_cast<int *>(smem + M::SCNT);
+            for (;;) {
+                int f = 0;
+                if (lane == 0) f = atomicAdd(cnt, 1);
+                f = __shfl(f, 0);
+                if (f >= NF) break;
+                operand_fragment(f);
             }
             lds_barrier();
 
