@@ -39,7 +39,7 @@ def _load():
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
         lib.kda_oracle_prefill.argtypes = [I64, P, I64, I64, I64, I64, P, P, P, P, P, P, P, P,
-                                           I64, P, ctypes.c_int]
+                                           I64, P, ctypes.c_int, ctypes.c_int]
         lib.kda_oracle_prefill.restype = ctypes.c_int
         lib.kda_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -55,11 +55,12 @@ def _ptr(a):
 
 
 def prefill(q, k, v, beta, log_alpha, cu_seqlens=None, initial_state=None, chunk=0,
-            want_chunk_states=False, nthreads=0):
+            want_chunk_states=False, nthreads=0, prologue_flags=0):
     """Run the C oracle.  Arrays as in ``reference.prefill`` (q [B,T,H,dk] ...).
     Rows of a batch are treated as separate sequences (B > 1 requires
-    cu_seqlens is None).  Returns (o [B,T,H,dv], final [N,H,dk,dv], chunk_states
-    or None), all fp64."""
+    cu_seqlens is None).  ``prologue_flags`` as in ``reference.prologue``.
+    Returns (o [B,T,H,dv], final [N,H,dk,dv], chunk_states or None), all
+    fp64."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     f32 = np.float32
@@ -86,13 +87,13 @@ def prefill(q, k, v, beta, log_alpha, cu_seqlens=None, initial_state=None, chunk
         cs = np.zeros((nch, H, dk, dv), np.float64)
     rc = _load().kda_oracle_prefill(N, _ptr(cu), B * T, H, dk, dv, _ptr(qq), _ptr(kk), _ptr(vv),
                                     _ptr(bb), _ptr(gg), _ptr(init), _ptr(final), _ptr(o),
-                                    int(chunk), _ptr(cs), int(nthreads))
+                                    int(chunk), _ptr(cs), int(nthreads), int(prologue_flags))
     if rc != 0:
         raise RuntimeError(f"kda_oracle_prefill failed: {rc}")
     return o.reshape(B, T, H, dv), final, cs
 
 
-def decode_steps(q, k, v, beta, log_alpha, initial_state, nthreads=0):
+def decode_steps(q, k, v, beta, log_alpha, initial_state, nthreads=0, prologue_flags=0):
     """Token-by-token trajectory of B independent sequences over ``steps``
     single-token steps: q [steps,B,H,dk] ...  Returns (o [steps,B,H,dv],
     states [steps,B,H,dk,dv]) in fp64, the state after every step."""
@@ -105,7 +106,7 @@ def decode_steps(q, k, v, beta, log_alpha, initial_state, nthreads=0):
         # B sequences of one token each, one packed call
         o, S, _ = prefill(q[s][None], k[s][None], v[s][None], beta[s][None], log_alpha[s][None],
                           cu_seqlens=np.arange(B + 1, dtype=np.int64), initial_state=S,
-                          nthreads=nthreads)
+                          nthreads=nthreads, prologue_flags=prologue_flags)
         outs[s] = o[0]
         states[s] = S
     return outs, states

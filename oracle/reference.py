@@ -43,6 +43,53 @@ import numpy as np
 f64 = np.float64
 
 
+# ---------------------------------------------------------- prologue ----
+# The stages that run just before the recurrence in the executed sublayer:
+# Q/K normalisation, a decay gate that produces alpha and a write gate that
+# produces beta (Module 04 — KDA II, §3 "The sublayer is bigger than the
+# recurrence").  The pages name the stages but give no formulas; the forms
+# below are the ones the workload descriptions use for their inputs (k "then
+# L2-normalised", beta = sigmoid(x), alpha = exp(-softplus(x))).  Reading for
+# the norm: x / sqrt(sum x^2 + eps) with eps = 1e-6, so a zero vector stays
+# zero instead of becoming NaN.
+PRO_GATE_SOFTPLUS = 1   # log_alpha holds x; the gate is log alpha = -softplus(x)
+PRO_BETA_SIGMOID = 2    # beta holds x; beta = sigmoid(x)
+PRO_QK_L2NORM = 4       # q and k are L2-normalised over d_k per (token, head)
+QK_NORM_EPS = 1e-6
+
+
+def softplus(x):
+    """log(1 + e^x), evaluated without overflow: max(x, 0) + log1p(e^-|x|)."""
+    x = np.asarray(x, f64)
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+
+
+def sigmoid(x):
+    """1 / (1 + e^-x), evaluated without overflow on either side."""
+    x = np.asarray(x, f64)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def l2norm(x, eps=QK_NORM_EPS):
+    """x / sqrt(sum over the last axis of x^2 + eps)."""
+    x = np.asarray(x, f64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
+def prologue(q, k, beta, log_alpha, flags):
+    """Apply the selected pre-recurrence stages (flags: PRO_* bits) in fp64.
+    Returns (q, k, beta, log_alpha) as the recurrence consumes them."""
+    q, k, beta, log_alpha = (np.asarray(a, f64) for a in (q, k, beta, log_alpha))
+    if flags & PRO_QK_L2NORM:
+        q, k = l2norm(q), l2norm(k)
+    if flags & PRO_BETA_SIGMOID:
+        beta = sigmoid(beta)
+    if flags & PRO_GATE_SOFTPLUS:
+        log_alpha = -softplus(log_alpha)
+    return q, k, beta, log_alpha
+
+
 # ------------------------------------------------------- one token ------
 def step(S, q, k, v, beta, log_alpha):
     """One token of the recurrence, batched over any leading axes.
@@ -76,15 +123,17 @@ def recurrent(q, k, v, beta, log_alpha, S0=None, snap_every=0):
     return o, S, snaps
 
 
-def prefill(q, k, v, beta, log_alpha, cu_seqlens=None, initial_state=None, snap_every=0):
+def prefill(q, k, v, beta, log_alpha, cu_seqlens=None, initial_state=None, snap_every=0, prologue_flags=0):
     """Batched / packed driver.  Layouts as the kernels': q [B,T,H,dk] ...;
     with ``cu_seqlens`` (B == 1) every document starts from its own state
     (``initial_state[n]`` or zeros) and shares nothing with its neighbours.
+    ``prologue_flags`` (PRO_* bits) says which inputs are pre-activations.
 
     Returns (o [B,T,H,dv] fp64, final [N,H,dk,dv] fp64, snaps) where snaps is
     the concatenation over documents of the state entering each chunk."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
+    q, k, beta, log_alpha = prologue(q, k, beta, log_alpha, prologue_flags)
     if cu_seqlens is None:
         seqs = [(b, 0, T) for b in range(B)]
     else:

@@ -90,6 +90,9 @@ class KDAInputs:
     initial_state: Optional[np.ndarray]  # fp32 [N,H,dk,dv] or None (zeros)
     cu_seqlens: Optional[np.ndarray]  # int32 [N+1] or None (B rows)
     chunk_size: int
+    # non-zero: q, k, beta, log_alpha hold the raw pre-activations of the
+    # stages before the recurrence (bit 1 gate, bit 2 beta, bit 4 q/k norm)
+    prologue: int = 0
 
     @property
     def B(self) -> int:
@@ -155,6 +158,23 @@ def make_uniform(seed: int, B: int, T: int, H: int, dk: int, dv: int, dtype: str
     q, k, v, beta, la = _draw_tokens(g, B, T, H, dk, dv, gate_mean, device, dtype == "bf16")
     state = _to_np(_state(g, (B, H, dk, dv), state_std, device)) if state_std else None
     return KDAInputs(name, dtype, *(_to_np(t) for t in (q, k, v, beta, la)), state, None, chunk)
+
+
+def make_preact(seed: int, B: int, T: int, H: int, dk: int, dv: int, dtype: str,
+                chunk: int = 64, state_std: float = 0.0, name: str = "preact",
+                device="cpu") -> KDAInputs:
+    """Raw pre-activations for the fused prologue: q, k, v, beta_raw and
+    gate_raw ~ N(0, 1) drawn in the same order as the other workloads, but
+    with no normalisation, sigmoid or softplus applied (``prologue == 7``)."""
+    g = _gen(seed, device)
+    kw = dict(generator=g, device=device, dtype=torch.float32)
+    out = [torch.randn((B, T, H, dk), **kw), torch.randn((B, T, H, dk), **kw),
+           torch.randn((B, T, H, dv), **kw), torch.randn((B, T, H), **kw),
+           torch.randn((B, T, H, dk), **kw)]
+    if dtype == "bf16":
+        out = [t.to(torch.bfloat16).to(torch.float32) for t in out]
+    state = _to_np(_state(g, (B, H, dk, dv), state_std, device)) if state_std else None
+    return KDAInputs(name, dtype, *(_to_np(t) for t in out), state, None, chunk, prologue=7)
 
 
 def make_packed(seed: int, lengths, H: int, dk: int, dv: int, dtype: str, chunk: int = 64,
