@@ -10,6 +10,12 @@ raise.
     o, S = prefill(q, k, v, beta, log_alpha, initial_state=None,
                    cu_seqlens=None, chunk_size=64)
     o = decode_step(q, k, v, beta, log_alpha, state)     # state updated in place
+    o, S, per_token = decode(q, k, v, beta, log_alpha, state)   # m tokens per sequence
+
+``prologue`` (prefill and decode) fuses the stages that precede the
+recurrence: PROLOGUE_GATE_SOFTPLUS (log_alpha holds x, log alpha =
+-softplus(x)), PROLOGUE_BETA_SIGMOID (beta holds x, beta = sigmoid(x)),
+PROLOGUE_QK_L2NORM (q, k divided by sqrt(sum x^2 + 1e-6)), or PROLOGUE_ALL.
 
 The recurrence (per sequence and head, S is d_k x d_v fp32):
     S_t = (I - beta_t k_t k_t^T) Diag(exp(log_alpha_t)) S_{t-1} + beta_t k_t v_t^T
@@ -24,13 +30,16 @@ import os
 
 import torch
 
-__all__ = ["prefill", "decode_step", "workspace_bytes", "max_chunks", "lib", "KDAError",
-           "PrefillArgs", "KDA_F32", "KDA_BF16"]
+__all__ = ["prefill", "decode_step", "decode", "workspace_bytes", "max_chunks", "lib", "KDAError",
+           "PrefillArgs", "DecodeArgs", "KDA_F32", "KDA_BF16", "PROLOGUE_GATE_SOFTPLUS",
+           "PROLOGUE_BETA_SIGMOID", "PROLOGUE_QK_L2NORM", "PROLOGUE_ALL"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkda.so")
 
 KDA_F32, KDA_BF16 = 0, 1
+PROLOGUE_GATE_SOFTPLUS, PROLOGUE_BETA_SIGMOID, PROLOGUE_QK_L2NORM = 1, 2, 4
+PROLOGUE_ALL = 7
 _STATUS_BAD_SEQLENS = 6
 
 
@@ -54,6 +63,20 @@ class PrefillArgs(ctypes.Structure):
         ("device_status", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("timing_events", ctypes.c_void_p),
+        ("prologue", ctypes.c_uint32),
+    ]
+
+
+class DecodeArgs(ctypes.Structure):
+    """Mirror of ``kda_decode_args`` (include/kda.h)."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+        ("n_tokens", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("prologue", ctypes.c_uint32),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("beta", ctypes.c_void_p), ("log_alpha", ctypes.c_void_p),
+        ("initial_state", ctypes.c_void_p), ("final_state", ctypes.c_void_p),
+        ("token_states", ctypes.c_void_p), ("o", ctypes.c_void_p),
     ]
 
 
@@ -78,6 +101,8 @@ def lib():
         L.kda_prefill_chunked.restype = I32
         L.kda_decode_step.argtypes = [I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P]
         L.kda_decode_step.restype = I32
+        L.kda_decode.argtypes = [ctypes.POINTER(DecodeArgs), P]
+        L.kda_decode.restype = I32
         L.kda_status_string.argtypes = [I32]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_abi_version.restype = I32
@@ -124,7 +149,7 @@ def _stream(dev):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
-def _make_args(q, k, v, beta, log_alpha, cu_seqlens, chunk_size, out_dtype, cu_host=None):
+def _make_args(q, k, v, beta, log_alpha, cu_seqlens, chunk_size, out_dtype, cu_host=None, prologue=0):
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     a = PrefillArgs()
@@ -137,6 +162,7 @@ def _make_args(q, k, v, beta, log_alpha, cu_seqlens, chunk_size, out_dtype, cu_h
     a.cu_seqlens = _ptr(cu_seqlens)
     if cu_host is not None:
         a.cu_seqlens_host = cu_host.ctypes.data_as(ctypes.c_void_p)
+    a.prologue = int(prologue)
     return a
 
 
@@ -153,7 +179,8 @@ def max_chunks(q, k, v, beta, log_alpha, cu_seqlens=None, chunk_size=64) -> int:
 
 def prefill(q, k, v, beta, log_alpha, initial_state=None, output_final_state=True,
             cu_seqlens=None, chunk_size=64, out_dtype=torch.float32, chunk_states=False,
-            workspace=None, final_state=None, o=None, check_seqlens=False, timing_events=None):
+            workspace=None, final_state=None, o=None, check_seqlens=False, timing_events=None,
+            prologue=0):
     """Chunked prefill.
 
     q, k, log_alpha [B,T,H,d_k]; v [B,T,H,d_v]; beta [B,T,H]; all float32 or
@@ -165,7 +192,8 @@ def prefill(q, k, v, beta, log_alpha, initial_state=None, output_final_state=Tru
     validates cu_seqlens on the host (one device-to-host copy) and raises on a
     device-side rejection (one synchronisation).  ``timing_events`` (a ctypes
     pointer to three hipEvent_t) is passed through to the library's
-    profiling hook."""
+    profiling hook.  ``prologue``: PROLOGUE_* bits (which inputs are
+    pre-activations)."""
     dev = _check_dev(q, k, v, beta, log_alpha, initial_state, cu_seqlens, workspace, final_state, o)
     if not (q.dtype == k.dtype == v.dtype == beta.dtype == log_alpha.dtype):
         raise TypeError("q, k, v, beta, log_alpha must share one dtype")
@@ -184,7 +212,7 @@ def prefill(q, k, v, beta, log_alpha, initial_state=None, output_final_state=Tru
     cu_host = None
     if cu_seqlens is not None and check_seqlens:
         cu_host = cu_seqlens.cpu().numpy()
-    a = _make_args(q, k, v, beta, log_alpha, cu_seqlens, chunk_size, out_dtype, cu_host)
+    a = _make_args(q, k, v, beta, log_alpha, cu_seqlens, chunk_size, out_dtype, cu_host, prologue)
     L = lib()
     need = int(L.kda_prefill_workspace_bytes(ctypes.byref(a)))
     if need == 0:
@@ -243,3 +271,42 @@ def decode_step(q, k, v, beta, log_alpha, state, out_dtype=torch.float32, o=None
     if st != 0:
         raise KDAError(st, "kda_decode_step")
     return o
+
+
+def decode(q, k, v, beta, log_alpha, state, out_dtype=torch.float32, update_state=True,
+           token_states=False, prologue=0, o=None, final_state=None):
+    """m consecutive tokens per sequence in one launch (multi-token decode /
+    speculative verification).
+
+    q, k, log_alpha [B,m,H,d_k]; v [B,m,H,d_v]; beta [B,m,H]; state fp32
+    [B,H,d_k,d_v], the state before the first token.  With ``update_state``
+    the state after the last token is written back into ``state`` (else into
+    ``final_state`` if given, else nowhere, keeping ``state`` for a rollback).
+    ``token_states=True`` also returns the state after every token,
+    [B,m,H,d_k,d_v].  Returns (o [B,m,H,d_v], final state or None,
+    token states or None)."""
+    dev = _check_dev(q, k, v, beta, log_alpha, state, o, final_state)
+    if not (q.dtype == k.dtype == v.dtype == beta.dtype == log_alpha.dtype):
+        raise TypeError("q, k, v, beta, log_alpha must share one dtype")
+    if q.dim() != 4 or k.shape != q.shape or log_alpha.shape != q.shape:
+        raise ValueError("q, k, log_alpha must be [B,m,H,d_k]")
+    B, m, H, dk = q.shape
+    if v.dim() != 4 or v.shape[:3] != q.shape[:3] or beta.shape != q.shape[:3]:
+        raise ValueError("v must be [B,m,H,d_v] and beta [B,m,H]")
+    dv = v.shape[-1]
+    if state.dtype != torch.float32 or tuple(state.shape) != (B, H, dk, dv):
+        raise ValueError(f"state must be float32 [{B},{H},{dk},{dv}]")
+    if o is None:
+        o = torch.empty((B, m, H, dv), dtype=out_dtype, device=dev)
+    if update_state:
+        final_state = state
+    ts = torch.empty((B, m, H, dk, dv), dtype=torch.float32, device=dev) if token_states else None
+    a = DecodeArgs()
+    a.B, a.H, a.d_k, a.d_v, a.n_tokens = B, H, dk, dv, m
+    a.in_dtype, a.out_dtype, a.prologue = _dt(q.dtype), _dt(o.dtype), int(prologue)
+    a.q, a.k, a.v, a.beta, a.log_alpha = (_ptr(x) for x in (q, k, v, beta, log_alpha))
+    a.initial_state, a.final_state, a.token_states, a.o = _ptr(state), _ptr(final_state), _ptr(ts), _ptr(o)
+    st = lib().kda_decode(ctypes.byref(a), _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_decode")
+    return o, final_state, ts

@@ -11,6 +11,7 @@ namespace {
 bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
 bool dtype_ok(int t) { return t == KDA_F32 || t == KDA_BF16; }
+bool prologue_ok(uint32_t f) { return (f & ~static_cast<uint32_t>(KDA_PROLOGUE_ALL)) == 0; }
 
 // shape / dtype / pointer checks that do not need the workspace
 kda_status check_prefill(const kda_prefill_args *a, bool need_ptrs) {
@@ -22,6 +23,7 @@ kda_status check_prefill(const kda_prefill_args *a, bool need_ptrs) {
         return KDA_ERR_UNSUPPORTED;
     }
     if (!dtype_ok(a->in_dtype) || !dtype_ok(a->out_dtype)) return KDA_ERR_UNSUPPORTED;
+    if (!prologue_ok(a->prologue)) return KDA_ERR_UNSUPPORTED;
     if (a->cu_seqlens) {
         if (a->B != 1 || a->num_seqs < 1) return KDA_ERR_BAD_SHAPE;
     } else if (a->num_seqs != a->B) {
@@ -111,6 +113,7 @@ kda_status kda_prefill_chunked(const kda_prefill_args *a, void *hip_stream) {
     p.B = a->B; p.T = a->T; p.H = a->H; p.dk = a->d_k; p.dv = a->d_v;
     p.N = a->num_seqs; p.C = a->chunk_size;
     p.n_chunks_bound = static_cast<int32_t>(max_chunks(a));
+    p.prologue = a->prologue;
 
     if (p.N == 0) return KDA_OK;
     hipEvent_t *ev = static_cast<hipEvent_t *>(a->timing_events);
@@ -133,14 +136,28 @@ kda_status kda_decode_step(int32_t B, int32_t H, int32_t d_k, int32_t d_v, int32
                            int32_t out_dtype, const void *q, const void *k, const void *v,
                            const void *beta, const void *log_alpha, float *state, void *o,
                            void *hip_stream) {
-    if (B < 0 || H < 1) return KDA_ERR_BAD_SHAPE;
-    if (!dim_ok(d_k) || !dim_ok(d_v)) return (d_k < 1 || d_v < 1) ? KDA_ERR_BAD_SHAPE : KDA_ERR_UNSUPPORTED;
-    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_UNSUPPORTED;
-    if (static_cast<int64_t>(B) * H > (static_cast<int64_t>(1) << 31) - 1) return KDA_ERR_UNSUPPORTED;
-    if (B == 0) return KDA_OK;
-    if (!q || !k || !v || !beta || !log_alpha || !state || !o) return KDA_ERR_NULL_ARG;
-    hipError_t e = launch_decode(B, H, d_k, d_v, in_dtype, out_dtype, q, k, v, beta, log_alpha, state, o,
-                                 static_cast<hipStream_t>(hip_stream));
+    kda_decode_args a{};
+    a.B = B; a.H = H; a.d_k = d_k; a.d_v = d_v; a.n_tokens = 1;
+    a.in_dtype = in_dtype; a.out_dtype = out_dtype; a.prologue = 0;
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.log_alpha = log_alpha;
+    a.initial_state = state; a.final_state = state; a.token_states = nullptr; a.o = o;
+    return kda_decode(&a, hip_stream);
+}
+
+kda_status kda_decode(const kda_decode_args *a, void *hip_stream) {
+    if (!a) return KDA_ERR_NULL_ARG;
+    if (a->B < 0 || a->H < 1 || a->n_tokens < 1) return KDA_ERR_BAD_SHAPE;
+    if (!dim_ok(a->d_k) || !dim_ok(a->d_v)) return (a->d_k < 1 || a->d_v < 1) ? KDA_ERR_BAD_SHAPE : KDA_ERR_UNSUPPORTED;
+    if (!dtype_ok(a->in_dtype) || !dtype_ok(a->out_dtype)) return KDA_ERR_UNSUPPORTED;
+    if (!prologue_ok(a->prologue)) return KDA_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(a->B) * a->n_tokens * a->H > (static_cast<int64_t>(1) << 31) - 1)
+        return KDA_ERR_UNSUPPORTED;
+    if (a->B == 0) return KDA_OK;
+    if (!a->q || !a->k || !a->v || !a->beta || !a->log_alpha || !a->initial_state || !a->o)
+        return KDA_ERR_NULL_ARG;
+    hipError_t e = launch_decode(a->B, a->H, a->n_tokens, a->d_k, a->d_v, a->in_dtype, a->out_dtype, a->prologue,
+                                 a->q, a->k, a->v, a->beta, a->log_alpha, a->initial_state, a->final_state,
+                                 a->token_states, a->o, static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

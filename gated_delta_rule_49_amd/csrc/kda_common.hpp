@@ -92,6 +92,34 @@ __device__ __forceinline__ void acc2_to_bf16(const f32x4 &t0, const f32x4 &t1, f
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ------------------------------------------------------------ prologue ----
+// Stages that precede the recurrence in the executed sublayer (Module 04 —
+// KDA II, §3 "The sublayer is bigger than the recurrence"), fused into the
+// kernels when the matching bit is set; the argument then holds the
+// pre-activation x.
+constexpr uint32_t kProGate = 1u;    // log alpha = -softplus(x)
+constexpr uint32_t kProBeta = 2u;    // beta = sigmoid(x)
+constexpr uint32_t kProQKNorm = 4u;  // q, k / sqrt(sum x^2 + kQKNormEps)
+constexpr float kQKNormEps = 1e-6f;
+
+// log(1 + e^x) = max(x, 0) + log1p(e^-|x|) on the hardware exp2 / log2, with
+// log1p(y) = log(u) * y / (u - 1), u = 1 + y, which cancels the rounding of u
+// (a few ulp; no overflow for any x).
+__device__ __forceinline__ float softplus_f32(float x) {
+    const float y = fast_exp2(-fabsf(x) * kLog2e);
+    const float u = 1.f + y;
+    const float l1p = (u == 1.f) ? y : __builtin_amdgcn_logf(u) * 0.6931471805599453f * y *
+                                           __builtin_amdgcn_rcpf(u - 1.f);
+    return fmaxf(x, 0.f) + l1p;
+}
+
+// 1 / (1 + e^-x) without overflow on either side
+__device__ __forceinline__ float sigmoid_f32(float x) {
+    const float e = fast_exp2(-fabsf(x) * kLog2e);
+    const float r = 1.f / (1.f + e);
+    return x >= 0.f ? r : e * r;
+}
+
 // Workgroup barrier that orders LDS only.  __syncthreads() is a
 // workgroup-scope fence over all memory, so it waits for every outstanding
 // global load and store of the wave (s_waitcnt vmcnt(0)); kernels whose

@@ -1,17 +1,23 @@
-// Fused single-token KDA decode step (Module 04 — KDA II, §2 "Why decode and
-// prefill need different kernels": decode applies one recurrent step to a
-// state already resident in memory).
+// Fused KDA decode (Module 04 — KDA II, §2 "Why decode and prefill need
+// different kernels": decode applies recurrent steps to a state already
+// resident in memory), for m >= 1 consecutive tokens per sequence in one
+// launch (multi-token decode / speculative verification: Module 11, §2, row
+// "Serving state").
 //
-// Per (sequence b, head h), with a = exp(log_alpha) and S the fp32 state:
+// Per (sequence b, head h) and token, with a = exp(log_alpha) and S the fp32
+// state:
 //     p = S^T (a * k),  r = S^T (a * q),  kappa = k . q
 //     delta = beta (v - p)
 //     o = r + kappa * delta               (= S_t^T q_t, post-update state)
 //     S <- a * S + k delta^T              (= (I - beta k k^T) Diag(a) S + beta k v^T)
-// The state is HBM-bound: it is read once into registers, reduced along d_k,
-// and written once.  One workgroup per (b, h); the column space of S is
-// split across lanes in float4 groups (16-byte coalesced rows) and the row
-// space across row groups; the d_k reductions run lane-to-lane inside a wave
-// (DPP/permute via __shfl_xor) and across waves through LDS.
+// With the q/k norm, k and q are 1/|k|, 1/|q| times the inputs: the sums
+// over rows are taken on the inputs and scaled once.
+// The state is HBM-bound: it is read once into registers, the m tokens are
+// applied there, and it is written once (plus once per token when the
+// per-token states are requested).  One workgroup per (b, h); the column
+// space of S is split across lanes in float4 groups (16-byte coalesced rows)
+// and the row space across row groups; the d_k reductions run lane-to-lane
+// inside a wave (__shfl_xor) and across waves through LDS.
 #include "kda_launch.hpp"
 
 namespace kda {
@@ -26,105 +32,158 @@ struct DecodeShape {
     static constexpr int RG_PER_WAVE = 64 / TPR;            // row groups in a wave
 };
 
-template <int DK, int DV, typename TI, typename TO>
-__global__ void __launch_bounds__((DecodeShape<DK, DV>::NT))
-decode_step_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__restrict__ v,
-                   const TI *__restrict__ beta, const TI *__restrict__ log_alpha,
-                   float *__restrict__ state, TO *__restrict__ o, int H) {
+// Arguments of one launch: m consecutive tokens per sequence.
+struct DecodeParams {
+    const void *q, *k, *v, *beta, *log_alpha;  // [B, m, H, d] / [B, m, H]
+    const float *state_in;                     // [B, H, DK, DV]
+    float *state_out;                          // nullable; may alias state_in
+    float *token_states;                       // nullable; [B, m, H, DK, DV]
+    void *o;                                   // [B, m, H, DV]
+    int H, m;
+    uint32_t prologue;                         // kPro* bits
+};
+
+// MULTI = false: the single-token launch (m == 1, no per-token states), a
+// straight-line kernel without the token loop.
+template <int DK, int DV, typename TI, typename TO, bool MULTI>
+__global__ void __launch_bounds__((DecodeShape<DK, DV>::NT)) decode_kernel(DecodeParams p) {
     using Sh = DecodeShape<DK, DV>;
     const int bh = blockIdx.x;
+    const int b = bh / p.H, h = bh % p.H;
     const int tid = threadIdx.x;
     const int c4 = tid % Sh::TPR;   // column group: columns 4*c4 .. 4*c4+3
     const int rg = tid / Sh::TPR;   // row group: rows rg + RG*i
+    const int wave = tid / 64;
+    const int lane = tid % 64;
+    const TI *q = static_cast<const TI *>(p.q);
+    const TI *k = static_cast<const TI *>(p.k);
+    const TI *v = static_cast<const TI *>(p.v);
+    const TI *beta = static_cast<const TI *>(p.beta);
+    const TI *la = static_cast<const TI *>(p.log_alpha);
+    TO *o = static_cast<TO *>(p.o);
 
     __shared__ float s_a[DK], s_k[DK], s_q[DK], s_ak[DK], s_aq[DK];
     __shared__ float s_red[2][Sh::NW > 1 ? Sh::NW : 1][DV];
-    __shared__ float s_kappa;
+    __shared__ float s_kappa, s_nk, s_nq;
 
-    const int64_t vecoff = static_cast<int64_t>(bh) * DK;
-    for (int i = tid; i < DK; i += Sh::NT) {
-        const float a = __expf(io<TI>::ld(log_alpha, vecoff + i));
-        const float kk = io<TI>::ld(k, vecoff + i);
-        const float qq = io<TI>::ld(q, vecoff + i);
-        s_a[i] = a;
-        s_k[i] = kk;
-        s_q[i] = qq;
-        s_ak[i] = a * kk;
-        s_aq[i] = a * qq;
-    }
-    __syncthreads();
-    if (tid < 64) {
-        float kq = 0.f;
-        for (int i = tid; i < DK; i += 64) kq += s_k[i] * s_q[i];
-        for (int m = 32; m >= 1; m >>= 1) kq += __shfl_xor(kq, m);
-        if (tid == 0) s_kappa = kq;
-    }
-
-    // load this thread's rows of S (float4 each) and reduce p, r partials
-    float4 *S4 = reinterpret_cast<float4 *>(state + static_cast<int64_t>(bh) * DK * DV);
+    // this thread's rows of S (float4 each), held in registers for all m tokens
+    const int64_t soff = static_cast<int64_t>(bh) * DK * DV;
+    const float4 *S4 = reinterpret_cast<const float4 *>(p.state_in + soff);
     float4 sv[Sh::RPT];
-    float p[4] = {0.f, 0.f, 0.f, 0.f}, r[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < Sh::RPT; ++i) {
-        const int row = rg + Sh::RG * i;
-        sv[i] = S4[row * (DV / 4) + c4];
-    }
+    for (int i = 0; i < Sh::RPT; ++i) sv[i] = S4[(rg + Sh::RG * i) * (DV / 4) + c4];
+
+    const int m = MULTI ? p.m : 1;
+    for (int t = 0; t < m; ++t) {
+        const int64_t tok = (static_cast<int64_t>(b) * m + t) * p.H + h;  // row of [B, m, H]
+        if (t > 0) __syncthreads();  // the previous token's readers of s_* are done
+        const int64_t vecoff = tok * DK;
+        for (int i = tid; i < DK; i += Sh::NT) {
+            const float x = io<TI>::ld(la, vecoff + i);
+            // alpha = exp(log alpha); with the gate prologue exp(-softplus(x)) = 1 / (1 + e^x)
+            const float a = (p.prologue & kProGate) ? sigmoid_f32(-x) : __expf(x);
+            const float kk = io<TI>::ld(k, vecoff + i);
+            const float qq = io<TI>::ld(q, vecoff + i);
+            s_a[i] = a;
+            s_k[i] = kk;
+            s_q[i] = qq;
+            s_ak[i] = a * kk;
+            s_aq[i] = a * qq;
+        }
+        __syncthreads();
+        if (wave == 0) {  // kappa = k.q and, with the norm, 1/|k| and 1/|q|
+            float kq = 0.f, k2 = 0.f, q2 = 0.f;
+            for (int i = lane; i < DK; i += 64) {
+                const float kk = s_k[i], qq = s_q[i];
+                kq += kk * qq;
+                k2 += kk * kk;
+                q2 += qq * qq;
+            }
 #pragma unroll
-    for (int i = 0; i < Sh::RPT; ++i) {
-        const int row = rg + Sh::RG * i;
-        const float ak = s_ak[row], aq = s_aq[row];
-        p[0] += sv[i].x * ak; p[1] += sv[i].y * ak; p[2] += sv[i].z * ak; p[3] += sv[i].w * ak;
-        r[0] += sv[i].x * aq; r[1] += sv[i].y * aq; r[2] += sv[i].z * aq; r[3] += sv[i].w * aq;
-    }
-    // reduce across the row groups inside the wave (lane bits >= log2(TPR))
+            for (int m = 32; m >= 1; m >>= 1) {
+                kq += __shfl_xor(kq, m);
+                k2 += __shfl_xor(k2, m);
+                q2 += __shfl_xor(q2, m);
+            }
+            if (lane == 0) {
+                float nk = 1.f, nq = 1.f;
+                if (p.prologue & kProQKNorm) {
+                    nk = 1.f / __builtin_sqrtf(k2 + kQKNormEps);
+                    nq = 1.f / __builtin_sqrtf(q2 + kQKNormEps);
+                }
+                s_nk = nk;
+                s_nq = nq;
+                s_kappa = kq * nk * nq;
+            }
+        }
+
+        // partial p = S^T (a k), r = S^T (a q) over this thread's rows
+        float pr[4] = {0.f, 0.f, 0.f, 0.f}, rr[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int m = Sh::TPR; m < 64 && m < Sh::NT; m <<= 1) {
+        for (int i = 0; i < Sh::RPT; ++i) {
+            const int row = rg + Sh::RG * i;
+            const float ak = s_ak[row], aq = s_aq[row];
+            pr[0] += sv[i].x * ak; pr[1] += sv[i].y * ak; pr[2] += sv[i].z * ak; pr[3] += sv[i].w * ak;
+            rr[0] += sv[i].x * aq; rr[1] += sv[i].y * aq; rr[2] += sv[i].z * aq; rr[3] += sv[i].w * aq;
+        }
+        // reduce across the row groups inside the wave (lane bits >= log2(TPR))
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            p[j] += __shfl_xor(p[j], m);
-            r[j] += __shfl_xor(r[j], m);
+        for (int m = Sh::TPR; m < 64 && m < Sh::NT; m <<= 1) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pr[j] += __shfl_xor(pr[j], m);
+                rr[j] += __shfl_xor(rr[j], m);
+            }
+        }
+        if (lane < Sh::TPR) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                s_red[0][wave][4 * c4 + j] = pr[j];
+                s_red[1][wave][4 * c4 + j] = rr[j];
+            }
+        }
+        __syncthreads();
+        // every thread needs delta for its 4 columns: sum the wave partials
+        float pt[4] = {0.f, 0.f, 0.f, 0.f}, rt[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < Sh::NW; ++w) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pt[j] += s_red[0][w][4 * c4 + j];
+                rt[j] += s_red[1][w][4 * c4 + j];
+            }
+        }
+        const float nk = s_nk, nq = s_nq;
+        float bt = io<TI>::ld(beta, tok);
+        if (p.prologue & kProBeta) bt = sigmoid_f32(bt);
+        const int64_t voff = tok * DV + 4 * c4;
+        float delta[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) delta[j] = bt * (io<TI>::ld(v, voff + j) - pt[j] * nk);
+        if (rg == 0) {
+            const float kappa = s_kappa;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) io<TO>::st(o, voff + j, rt[j] * nq + kappa * delta[j]);
+        }
+#pragma unroll
+        for (int i = 0; i < Sh::RPT; ++i) {
+            const int row = rg + Sh::RG * i;
+            const float a = s_a[row], kk = s_k[row] * nk;
+            sv[i].x = a * sv[i].x + kk * delta[0];
+            sv[i].y = a * sv[i].y + kk * delta[1];
+            sv[i].z = a * sv[i].z + kk * delta[2];
+            sv[i].w = a * sv[i].w + kk * delta[3];
+        }
+        if (MULTI && p.token_states) {
+            float4 *T4 = reinterpret_cast<float4 *>(p.token_states + tok * DK * DV);
+#pragma unroll
+            for (int i = 0; i < Sh::RPT; ++i) T4[(rg + Sh::RG * i) * (DV / 4) + c4] = sv[i];
         }
     }
-    const int wave = tid / 64;
-    const int lane = tid % 64;
-    if (lane < Sh::TPR) {
+    if (p.state_out) {
+        float4 *O4 = reinterpret_cast<float4 *>(p.state_out + soff);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            s_red[0][wave][4 * c4 + j] = p[j];
-            s_red[1][wave][4 * c4 + j] = r[j];
-        }
-    }
-    __syncthreads();
-    // every thread needs delta for its 4 columns: sum the wave partials
-    float pt[4] = {0.f, 0.f, 0.f, 0.f}, rt[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < Sh::NW; ++w) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            pt[j] += s_red[0][w][4 * c4 + j];
-            rt[j] += s_red[1][w][4 * c4 + j];
-        }
-    }
-    const float b = io<TI>::ld(beta, bh);
-    const int64_t voff = static_cast<int64_t>(bh) * DV + 4 * c4;
-    float delta[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) delta[j] = b * (io<TI>::ld(v, voff + j) - pt[j]);
-    if (rg == 0) {
-        const float kappa = s_kappa;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) io<TO>::st(o, voff + j, rt[j] + kappa * delta[j]);
-    }
-#pragma unroll
-    for (int i = 0; i < Sh::RPT; ++i) {
-        const int row = rg + Sh::RG * i;
-        const float a = s_a[row], kk = s_k[row];
-        float4 s = sv[i];
-        s.x = a * s.x + kk * delta[0];
-        s.y = a * s.y + kk * delta[1];
-        s.z = a * s.z + kk * delta[2];
-        s.w = a * s.w + kk * delta[3];
-        S4[row * (DV / 4) + c4] = s;
+        for (int i = 0; i < Sh::RPT; ++i) O4[(rg + Sh::RG * i) * (DV / 4) + c4] = sv[i];
     }
 }
 
@@ -134,47 +193,44 @@ namespace kda {
 
 namespace {
 template <int DK, int DV, typename TI, typename TO>
-hipError_t run_decode(int B, int H, const void *q, const void *k, const void *v, const void *beta,
-                      const void *la, float *state, void *o, hipStream_t s) {
+hipError_t run_decode(const DecodeParams &p, int B, hipStream_t s) {
     using Sh = DecodeShape<DK, DV>;
-    hipLaunchKernelGGL((decode_step_kernel<DK, DV, TI, TO>), dim3(static_cast<unsigned>(B) * H),
-                       dim3(Sh::NT), 0, s, static_cast<const TI *>(q), static_cast<const TI *>(k),
-                       static_cast<const TI *>(v), static_cast<const TI *>(beta),
-                       static_cast<const TI *>(la), state, static_cast<TO *>(o), H);
+    const dim3 grid(static_cast<unsigned>(B) * p.H), block(Sh::NT);
+    if (p.m == 1 && !p.token_states)
+        hipLaunchKernelGGL((decode_kernel<DK, DV, TI, TO, false>), grid, block, 0, s, p);
+    else
+        hipLaunchKernelGGL((decode_kernel<DK, DV, TI, TO, true>), grid, block, 0, s, p);
     return hipGetLastError();
 }
 
 template <int DK, int DV>
-hipError_t run_decode_dt(int B, int H, int in_dt, int out_dt, const void *q, const void *k,
-                         const void *v, const void *beta, const void *la, float *state, void *o,
-                         hipStream_t s) {
-    if (in_dt == 0 && out_dt == 0) return run_decode<DK, DV, float, float>(B, H, q, k, v, beta, la, state, o, s);
-    if (in_dt == 0 && out_dt == 1) return run_decode<DK, DV, float, bf16_t>(B, H, q, k, v, beta, la, state, o, s);
-    if (in_dt == 1 && out_dt == 0) return run_decode<DK, DV, bf16_t, float>(B, H, q, k, v, beta, la, state, o, s);
-    return run_decode<DK, DV, bf16_t, bf16_t>(B, H, q, k, v, beta, la, state, o, s);
+hipError_t run_decode_dt(const DecodeParams &p, int B, int in_dt, int out_dt, hipStream_t s) {
+    if (in_dt == 0 && out_dt == 0) return run_decode<DK, DV, float, float>(p, B, s);
+    if (in_dt == 0 && out_dt == 1) return run_decode<DK, DV, float, bf16_t>(p, B, s);
+    if (in_dt == 1 && out_dt == 0) return run_decode<DK, DV, bf16_t, float>(p, B, s);
+    return run_decode<DK, DV, bf16_t, bf16_t>(p, B, s);
 }
 
 template <int DK>
-hipError_t run_decode_dv(int B, int H, int dv, int in_dt, int out_dt, const void *q, const void *k,
-                         const void *v, const void *beta, const void *la, float *state, void *o,
-                         hipStream_t s) {
+hipError_t run_decode_dv(const DecodeParams &p, int B, int dv, int in_dt, int out_dt, hipStream_t s) {
     switch (dv) {
-        case 16: return run_decode_dt<DK, 16>(B, H, in_dt, out_dt, q, k, v, beta, la, state, o, s);
-        case 32: return run_decode_dt<DK, 32>(B, H, in_dt, out_dt, q, k, v, beta, la, state, o, s);
-        case 64: return run_decode_dt<DK, 64>(B, H, in_dt, out_dt, q, k, v, beta, la, state, o, s);
-        default: return run_decode_dt<DK, 128>(B, H, in_dt, out_dt, q, k, v, beta, la, state, o, s);
+        case 16: return run_decode_dt<DK, 16>(p, B, in_dt, out_dt, s);
+        case 32: return run_decode_dt<DK, 32>(p, B, in_dt, out_dt, s);
+        case 64: return run_decode_dt<DK, 64>(p, B, in_dt, out_dt, s);
+        default: return run_decode_dt<DK, 128>(p, B, in_dt, out_dt, s);
     }
 }
 }  // namespace
 
-hipError_t launch_decode(int B, int H, int dk, int dv, int in_dtype, int out_dtype, const void *q,
-                         const void *k, const void *v, const void *beta, const void *log_alpha,
-                         float *state, void *o, hipStream_t s) {
+hipError_t launch_decode(int B, int H, int m, int dk, int dv, int in_dtype, int out_dtype, uint32_t prologue,
+                         const void *q, const void *k, const void *v, const void *beta, const void *log_alpha,
+                         const float *state_in, float *state_out, float *token_states, void *o, hipStream_t s) {
+    DecodeParams p{q, k, v, beta, log_alpha, state_in, state_out, token_states, o, H, m, prologue};
     switch (dk) {
-        case 16: return run_decode_dv<16>(B, H, dv, in_dtype, out_dtype, q, k, v, beta, log_alpha, state, o, s);
-        case 32: return run_decode_dv<32>(B, H, dv, in_dtype, out_dtype, q, k, v, beta, log_alpha, state, o, s);
-        case 64: return run_decode_dv<64>(B, H, dv, in_dtype, out_dtype, q, k, v, beta, log_alpha, state, o, s);
-        default: return run_decode_dv<128>(B, H, dv, in_dtype, out_dtype, q, k, v, beta, log_alpha, state, o, s);
+        case 16: return run_decode_dv<16>(p, B, dv, in_dtype, out_dtype, s);
+        case 32: return run_decode_dv<32>(p, B, dv, in_dtype, out_dtype, s);
+        case 64: return run_decode_dv<64>(p, B, dv, in_dtype, out_dtype, s);
+        default: return run_decode_dv<128>(p, B, dv, in_dtype, out_dtype, s);
     }
 }
 

@@ -27,8 +27,10 @@ hipError_t launch_prefill_f32(const PrefillParams &p, int in_dtype, int out_dtyp
 // mid_event (nullable) is recorded between the intra-chunk and the scan kernel
 hipError_t launch_prefill_mfma(const PrefillParams &p, void *blocks, int out_dtype, hipStream_t s,
                                hipEvent_t mid_event);
-hipError_t launch_decode(int B, int H, int dk, int dv, int in_dtype, int out_dtype, const void *q,
-                         const void *k, const void *v, const void *beta, const void *log_alpha,
-                         float *state, void *o, hipStream_t s);
+// m tokens per sequence; state_out and token_states nullable, state_out may
+// alias state_in
+hipError_t launch_decode(int B, int H, int m, int dk, int dv, int in_dtype, int out_dtype, uint32_t prologue,
+                         const void *q, const void *k, const void *v, const void *beta, const void *log_alpha,
+                         const float *state_in, float *state_out, float *token_states, void *o, hipStream_t s);
 
 }  // namespace kda

@@ -17,6 +17,7 @@ struct PrefillParams {
     int32_t *user_status;        // device, optional mirror of *status
     int32_t B, T, H, dk, dv, N, C;
     int32_t n_chunks_bound;      // grid bound on the total number of chunks
+    uint32_t prologue;           // kPro* bits: which inputs are pre-activations
 };
 
 // Token range of sequence n: tokens [start, start + len) of the flattened

@@ -33,7 +33,7 @@ __host__ __device__ inline size_t f32_lds_floats(int C, int dk) {
            + static_cast<size_t>(C) * C     // A, then T, then P
            + static_cast<size_t>(dk) * F32_BV  // S tile
            + static_cast<size_t>(C) * F32_BV   // X, then Delta
-           + C;                                // beta
+           + 3 * static_cast<size_t>(C);       // beta, 1/|k|, 1/|q|
 }
 
 template <typename TI, typename TO>
@@ -53,6 +53,8 @@ __global__ void __launch_bounds__(F32_THREADS) prefill_f32_kernel(PrefillParams 
     float *S = AT + C * C;          // [dk][BV]
     float *X = S + dk * F32_BV;     // [C][BV]
     float *bet = X + C * F32_BV;    // [C]
+    float *nk = bet + C;            // [C] 1/|k_r| (1 without the q/k norm)
+    float *nq = nk + C;             // [C] 1/|q_r|
 
     const TI *q = static_cast<const TI *>(p.q);
     const TI *k = static_cast<const TI *>(p.k);
@@ -84,15 +86,40 @@ __global__ void __launch_bounds__(F32_THREADS) prefill_f32_kernel(PrefillParams 
                 cs[static_cast<int64_t>(c) * dv + v0 + j] = S[e];
             }
         }
-        // 1. cumulative log-decay (fp64), beta; padded rows decay by 1
+        // 1. cumulative log-decay (fp64), beta, q/k norms; padded rows decay by 1.
+        //    Prologue (pre-activations): log alpha = -softplus(x), beta =
+        //    sigmoid(x), 1/|.| = 1/sqrt(sum x^2 + eps), in fp32.
         for (int c = tid; c < dk; c += F32_THREADS) {
             double acc = 0.0;
             for (int r = 0; r < C; ++r) {
-                if (r < L) acc += static_cast<double>(io<TI>::ld(la, kv(t0 + r) * dk + c));
+                if (r < L) {
+                    float g = io<TI>::ld(la, kv(t0 + r) * dk + c);
+                    if (p.prologue & kProGate) g = -(fmaxf(g, 0.f) + log1pf(expf(-fabsf(g))));
+                    acc += static_cast<double>(g);
+                }
                 G[r * dk + c] = acc;
             }
         }
-        for (int r = tid; r < C; r += F32_THREADS) bet[r] = r < L ? io<TI>::ld(beta, kv(t0 + r)) : 0.f;
+        for (int r = tid; r < C; r += F32_THREADS) {
+            float b = 0.f, ik = 1.f, iq = 1.f;
+            if (r < L) {
+                b = io<TI>::ld(beta, kv(t0 + r));
+                if (p.prologue & kProBeta) b = 1.f / (1.f + expf(-b));
+                if (p.prologue & kProQKNorm) {
+                    float sk = 0.f, sq = 0.f;
+                    for (int c = 0; c < dk; ++c) {
+                        const float x = io<TI>::ld(k, kv(t0 + r) * dk + c), y = io<TI>::ld(q, kv(t0 + r) * dk + c);
+                        sk += x * x;
+                        sq += y * y;
+                    }
+                    ik = 1.f / sqrtf(sk + kQKNormEps);
+                    iq = 1.f / sqrtf(sq + kQKNormEps);
+                }
+            }
+            bet[r] = b;
+            nk[r] = ik;
+            nq[r] = iq;
+        }
         __syncthreads();
 
         // 2. A (strictly lower, rows scaled by beta)
@@ -104,7 +131,7 @@ __global__ void __launch_bounds__(F32_THREADS) prefill_f32_kernel(PrefillParams 
                 for (int c = 0; c < dk; ++c)
                     acc += io<TI>::ld(k, kr + c) * io<TI>::ld(k, ki + c) *
                            expf(static_cast<float>(G[r * dk + c] - G[i * dk + c]));
-                acc *= bet[r];
+                acc *= bet[r] * nk[r] * nk[i];
             }
             AT[e] = acc;
         }
@@ -132,7 +159,7 @@ __global__ void __launch_bounds__(F32_THREADS) prefill_f32_kernel(PrefillParams 
                 const int64_t kr = kv(t0 + r) * dk;
                 for (int c = 0; c < dk; ++c)
                     acc += io<TI>::ld(k, kr + c) * expf(static_cast<float>(G[r * dk + c])) * S[c * F32_BV + j];
-                acc = io<TI>::ld(v, kv(t0 + r) * dv + v0 + j) - acc;
+                acc = io<TI>::ld(v, kv(t0 + r) * dv + v0 + j) - acc * nk[r];
             }
             X[e] = acc;
         }
@@ -164,6 +191,7 @@ __global__ void __launch_bounds__(F32_THREADS) prefill_f32_kernel(PrefillParams 
                 for (int c = 0; c < dk; ++c)
                     acc += io<TI>::ld(q, qr + c) * io<TI>::ld(k, ki + c) *
                            expf(static_cast<float>(G[r * dk + c] - G[i * dk + c]));
+                acc *= nq[r] * nk[i];
             }
             AT[e] = acc;
         }
@@ -177,6 +205,7 @@ __global__ void __launch_bounds__(F32_THREADS) prefill_f32_kernel(PrefillParams 
                 float acc = 0.f;
                 for (int c = 0; c < dk; ++c)
                     acc += io<TI>::ld(q, qr + c) * expf(static_cast<float>(G[r * dk + c])) * S[c * F32_BV + j];
+                acc *= nq[r];
                 for (int i = 0; i <= r; ++i) acc += AT[r * C + i] * X[i * F32_BV + j];
                 io<TO>::st(o, kv(t0 + r) * dv + v0 + j, acc);
             }
@@ -190,7 +219,7 @@ __global__ void __launch_bounds__(F32_THREADS) prefill_f32_kernel(PrefillParams 
                 const double gl = G[(C - 1) * dk + c];
                 float acc = expf(static_cast<float>(gl)) * S[e];
                 for (int r = 0; r < L; ++r)
-                    acc += io<TI>::ld(k, kv(t0 + r) * dk + c) * expf(static_cast<float>(gl - G[r * dk + c])) *
+                    acc += io<TI>::ld(k, kv(t0 + r) * dk + c) * nk[r] * expf(static_cast<float>(gl - G[r * dk + c])) *
                            X[r * F32_BV + j];
                 sreg[idx] = acc;
             }

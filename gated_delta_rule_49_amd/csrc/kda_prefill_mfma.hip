@@ -110,7 +110,9 @@ struct IntraLds {
     static constexpr size_t SG = SVT + D * RT * 2;                    // G   [CP][RG] f32 (log2 units)
     static constexpr size_t ST = SG + CP * RG * 4;                    // X = (I+A)^-1 [CP][RA] f32
     static constexpr size_t SB = ST + CP * RA * 4;                    // beta [CP]
-    static constexpr size_t SCNT = SB + CP * 4;                       // work counter (int)
+    static constexpr size_t SNK = SB + CP * 4;                        // 1/|k_r| [CP] (1 without the norm)
+    static constexpr size_t SNQ = SNK + CP * 4;                       // 1/|q_r| [CP]
+    static constexpr size_t SCNT = SNQ + CP * 4;                      // work counter (int)
     static constexpr size_t END = SCNT + 16;
     // after the Gram phase q and A are dead: the T fragments reuse [SQ, SKT)
     // when they fit there, else they get their own region
@@ -289,6 +291,8 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
     auto SG = reinterpret_cast<float(*)[M::RG]>(smem + M::SG);
     auto SX = reinterpret_cast<float(*)[M::RA]>(smem + M::ST);
     auto SBETA = reinterpret_cast<float *>(smem + M::SB);
+    auto SNK = reinterpret_cast<float *>(smem + M::SNK);
+    auto SNQ = reinterpret_cast<float *>(smem + M::SNQ);
     auto TB = reinterpret_cast<bf16_t(*)[M::RTF]>(smem + M::TB);
     auto TH = reinterpret_cast<bf16_t(*)[M::RTF]>(smem + M::TH);
     auto TL = reinterpret_cast<bf16_t(*)[M::RTF]>(smem + M::TL);
@@ -356,14 +360,51 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
                     SVT[M::tpos(c8 + 2 * j2, r)] = static_cast<bf16_t>(vw[j2] & 0xffffu);
                     SVT[M::tpos(c8 + 2 * j2 + 1, r)] = static_cast<bf16_t>(vw[j2] >> 16);
                 }
-                *reinterpret_cast<f32x4 *>(&SG[r][c8]) =
-                    f32x4{__uint_as_float(aw[0] << 16), __uint_as_float(aw[0] & 0xffff0000u),
-                          __uint_as_float(aw[1] << 16), __uint_as_float(aw[1] & 0xffff0000u)};
-                *reinterpret_cast<f32x4 *>(&SG[r][c8 + 4]) =
-                    f32x4{__uint_as_float(aw[2] << 16), __uint_as_float(aw[2] & 0xffff0000u),
-                          __uint_as_float(aw[3] << 16), __uint_as_float(aw[3] & 0xffff0000u)};
+                f32x4 g0 = {__uint_as_float(aw[0] << 16), __uint_as_float(aw[0] & 0xffff0000u),
+                            __uint_as_float(aw[1] << 16), __uint_as_float(aw[1] & 0xffff0000u)};
+                f32x4 g1 = {__uint_as_float(aw[2] << 16), __uint_as_float(aw[2] & 0xffff0000u),
+                            __uint_as_float(aw[3] << 16), __uint_as_float(aw[3] & 0xffff0000u)};
+                if (p.prologue & kProGate) {  // rows beyond L hold x = 0: zeroed below by live
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        g0[j] = live ? -softplus_f32(g0[j]) : 0.f;
+                        g1[j] = live ? -softplus_f32(g1[j]) : 0.f;
+                    }
+                }
+                *reinterpret_cast<f32x4 *>(&SG[r][c8]) = g0;
+                *reinterpret_cast<f32x4 *>(&SG[r][c8 + 4]) = g1;
+                // 1 / |k_r|, 1 / |q_r| (1 without the norm): the D/8 lanes of
+                // row r are consecutive, so the sum of squares is a butterfly
+                // over them
+                float nk = 1.f, nq = 1.f;
+                if (p.prologue & kProQKNorm) {
+                    const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+                    float sk = 0.f, sq = 0.f;
+#pragma unroll
+                    for (int j2 = 0; j2 < 4; ++j2) {
+                        const float k0 = __uint_as_float(kw[j2] << 16), k1 = __uint_as_float(kw[j2] & 0xffff0000u);
+                        const float q0 = __uint_as_float(qw[j2] << 16), q1 = __uint_as_float(qw[j2] & 0xffff0000u);
+                        sk += k0 * k0 + k1 * k1;
+                        sq += q0 * q0 + q1 * q1;
+                    }
+#pragma unroll
+                    for (int o = 1; o < D / 8; o <<= 1) {
+                        sk += __shfl_xor(sk, o);
+                        sq += __shfl_xor(sq, o);
+                    }
+                    nk = 1.f / __builtin_sqrtf(sk + kQKNormEps);
+                    nq = 1.f / __builtin_sqrtf(sq + kQKNormEps);
+                }
+                if (c8 == 0) {
+                    SNK[r] = nk;
+                    SNQ[r] = nq;
+                }
             }
-            if (tid < CP) SBETA[tid] = tid < L ? bf16_to_f32(static_cast<bf16_t>(raw.beta)) : 0.f;
+            if (tid < CP) {
+                float b = bf16_to_f32(static_cast<bf16_t>(raw.beta));
+                if (p.prologue & kProBeta) b = sigmoid_f32(b);
+                SBETA[tid] = tid < L ? b : 0.f;
+            }
             // fragments 0 .. 7 - C/16 go to the waves that do not invert a diagonal block
             if (tid == 0) *reinterpret_cast<int *>(smem + M::SCNT) = 8 - Y::NMT;
             lds_barrier();
@@ -567,14 +608,17 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
                     const f32x4 pa = *reinterpret_cast<const f32x4 *>(&SA[r][16 * b + 4 * g]);
                     const f32x4 pp = *reinterpret_cast<const f32x4 *>(&SX[r][16 * b + 4 * g]);
                     // A (rows scaled by beta_r, strictly lower) -> LDS; P -> workspace
-                    const float br = SBETA[r];
+                    // rows scaled by beta_r; the q/k norms enter as 1/|k_r| 1/|k_i|
+                    // (A) and 1/|q_r| 1/|k_i| (P)
+                    const float ar = SBETA[r] * SNK[r], pr = SNQ[r];
+                    const f32x4 nki = *reinterpret_cast<const f32x4 *>(&SNK[16 * b + 4 * g]);
                     f32x4 av;
                     bf16_t ph[4], pl[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int i = 16 * b + 4 * g + j;
-                        av[j] = (i < r) ? (accA[u][j] + pa[j]) * br : 0.f;
-                        split_bf16((i <= r) ? accP[u][j] + pp[j] : 0.f, ph[j], pl[j]);
+                        av[j] = (i < r) ? (accA[u][j] + pa[j]) * ar * nki[j] : 0.f;
+                        split_bf16((i <= r) ? (accP[u][j] + pp[j]) * pr * nki[j] : 0.f, ph[j], pl[j]);
                     }
                     *reinterpret_cast<f32x4 *>(&SA[r][16 * b + 4 * g]) = av;
                     const size_t fo = ((static_cast<size_t>(a) * Y::KSC + b / 2) * 64 + lane) * 16 + (b & 1) * 8;
@@ -609,10 +653,11 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
                     const f32x4 g1 = *reinterpret_cast<const f32x4 *>(&SG[r][cB]);
                     const bf16_t *qa = reinterpret_cast<const bf16_t *>(&q0);
                     const bf16_t *qb = reinterpret_cast<const bf16_t *>(&q1);
+                    const float nq = SNQ[r];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        split_bf16(bf16_to_f32(qa[j]) * fast_exp2(g0[j]), hi.s[j], lo.s[j]);
-                        split_bf16(bf16_to_f32(qb[j]) * fast_exp2(g1[j]), hi.s[4 + j], lo.s[4 + j]);
+                        split_bf16(bf16_to_f32(qa[j]) * nq * fast_exp2(g0[j]), hi.s[j], lo.s[j]);
+                        split_bf16(bf16_to_f32(qb[j]) * nq * fast_exp2(g1[j]), hi.s[4 + j], lo.s[4 + j]);
                     }
                     const size_t fo = (static_cast<size_t>(f) * 64 + lane) * 16;
                     dst_h = Y::QH + fo;
@@ -627,10 +672,13 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
                     const uint2 k1 = *reinterpret_cast<const uint2 *>(&SKT[M::tpos(ch, iB)]);
                     const bf16_t *ka = reinterpret_cast<const bf16_t *>(&k0);
                     const bf16_t *kb = reinterpret_cast<const bf16_t *>(&k1);
+                    const f32x4 nka = *reinterpret_cast<const f32x4 *>(&SNK[iA]);
+                    const f32x4 nkb = *reinterpret_cast<const f32x4 *>(&SNK[iB]);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        split_bf16(bf16_to_f32(ka[j]) * fast_exp2(gl - SG[iA + j][ch]), hi.s[j], lo.s[j]);
-                        split_bf16(bf16_to_f32(kb[j]) * fast_exp2(gl - SG[iB + j][ch]), hi.s[4 + j], lo.s[4 + j]);
+                        split_bf16(bf16_to_f32(ka[j]) * nka[j] * fast_exp2(gl - SG[iA + j][ch]), hi.s[j], lo.s[j]);
+                        split_bf16(bf16_to_f32(kb[j]) * nkb[j] * fast_exp2(gl - SG[iB + j][ch]), hi.s[4 + j],
+                                   lo.s[4 + j]);
                     }
                     const size_t fo = (static_cast<size_t>(f2) * 64 + lane) * 16;
                     dst_h = Y::KBH + fo;
@@ -701,7 +749,7 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const float t = xv[j] * SBETA[i4 + j];
-                    tb[j] = f32_to_bf16(t);
+                    tb[j] = f32_to_bf16(t * SNK[i4 + j]);  // W = T Diag(1/|k|) (k e^G)
                     split_bf16(t, th[j], tl[j]);
                 }
                 *reinterpret_cast<uint2 *>(&TB[r][i4]) = pack4(tb);

@@ -20,6 +20,14 @@
  *                        recurrence has affine form").
  *   kda_decode_step      one token per sequence, fused recurrent step, the
  *                        state updated in place.
+ *   kda_decode           m >= 1 tokens per sequence in one launch (multi-token
+ *                        decode / speculative verification), the state read
+ *                        once and written once, optionally the state after
+ *                        every token for rollback (Module 11, §2 "The full
+ *                        correctness matrix", row "Serving state").
+ *
+ * Both families can fuse the stages that run just before the recurrence
+ * (KDA_PROLOGUE_* flags below).
  *
  * Conventions common to all entry points
  *   - Pointers marked DEVICE are device memory owned by the caller; the
@@ -47,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum {
     KDA_OK = 0,
@@ -60,6 +68,28 @@ typedef enum {
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/*
+ * Prologue flags (the `prologue` field of the argument structs).  The
+ * executed sublayer runs Q/K normalisation, a learned decay gate producing
+ * alpha and a learned write gate producing beta just before the recurrence
+ * (Module 04 — KDA II, §3 "The sublayer is bigger than the recurrence");
+ * each flag fuses one of them into the kernels, so that the argument holds
+ * the pre-activation x instead of the value:
+ *   GATE_SOFTPLUS  log_alpha holds x; the kernels use log alpha = -softplus(x)
+ *                  = -log(1 + e^x) (alpha = 1 / (1 + e^x)), computed in fp32.
+ *   BETA_SIGMOID   beta holds x; beta = 1 / (1 + e^-x).
+ *   QK_L2NORM      q and k are divided by sqrt(sum_c x_c^2 + 1e-6) over their
+ *                  d_k channels, per (token, head), in fp32 (the inputs are
+ *                  not rounded again after the division).
+ * The pages name the stages without formulas; these are the forms the
+ * workload descriptions apply to their inputs.  Unknown bits are
+ * KDA_ERR_UNSUPPORTED.
+ */
+#define KDA_PROLOGUE_GATE_SOFTPLUS 1u
+#define KDA_PROLOGUE_BETA_SIGMOID 2u
+#define KDA_PROLOGUE_QK_L2NORM 4u
+#define KDA_PROLOGUE_ALL 7u
 
 /*
  * Prefill arguments.  Sequences are either the B rows of a batch
@@ -95,6 +125,7 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *               (the chunk table), between the intra-chunk and the scan kernel
  *               (after the single kernel on the fp32 path) and after the
  *               last kernel.  A profiling hook; costs nothing when NULL.
+ *   prologue    KDA_PROLOGUE_* bits, 0 = q, k, beta, log_alpha used as given.
  *
  * Supported: d_k, d_v in {16, 32, 64, 128}; chunk_size in {16, 32, 64};
  * in_dtype f32 (computed entirely in fp32) or bf16 (matrix-core path with
@@ -118,6 +149,7 @@ typedef struct kda_prefill_args {
     void *workspace;
     size_t workspace_bytes;
     void *timing_events;
+    uint32_t prologue;
 } kda_prefill_args;
 
 /* Workspace bytes the call described by *a needs (0 if a is NULL or
@@ -149,6 +181,47 @@ kda_status kda_decode_step(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
                            const void *q, const void *k, const void *v,
                            const void *beta, const void *log_alpha,
                            float *state, void *o, void *hip_stream);
+
+/*
+ * m >= 1 consecutive tokens for each of B independent sequences in one
+ * launch: multi-token decode and speculative verification, where a rejected
+ * suffix must be rolled back to the state after the last accepted token
+ * (Module 11, §2 "The full correctness matrix", row "Serving state"; the
+ * course index's module list, Module 08 "Vision, MTP, and Hybrid Serving
+ * State", on why a rollback must restore the recurrent state).
+ * Per (sequence, head) the state is read once, the m tokens are applied in
+ * order in registers, and the results are written once; the fused step is
+ * the same as kda_decode_step's.
+ *
+ *   q, k, log_alpha  DEVICE [B, m, H, d_k]  in_dtype
+ *   v                DEVICE [B, m, H, d_v]  in_dtype
+ *   beta             DEVICE [B, m, H]       in_dtype
+ *   initial_state    DEVICE fp32 [B, H, d_k, d_v]: the state before token 0.
+ *   final_state      DEVICE fp32 [B, H, d_k, d_v], NULL = not written: the
+ *                    state after token m - 1.  May alias initial_state (in
+ *                    place); leave it NULL to keep initial_state for a
+ *                    rollback to zero accepted tokens.
+ *   token_states     DEVICE fp32 [B, m, H, d_k, d_v], NULL = not written:
+ *                    the state after every token (m x the state traffic).
+ *   o                DEVICE [B, m, H, d_v]  out_dtype; o[b, j] uses the
+ *                    state after token j.
+ *   prologue         KDA_PROLOGUE_* bits.
+ * Supported: d_k, d_v in {16, 32, 64, 128}; 1 <= m; B * m * H < 2^31.
+ */
+typedef struct kda_decode_args {
+    int32_t B, H, d_k, d_v;
+    int32_t n_tokens;
+    int32_t in_dtype;              /* kda_dtype */
+    int32_t out_dtype;             /* kda_dtype */
+    uint32_t prologue;
+    const void *q, *k, *v, *beta, *log_alpha;
+    const float *initial_state;
+    float *final_state;
+    float *token_states;
+    void *o;
+} kda_decode_args;
+
+kda_status kda_decode(const kda_decode_args *a, void *hip_stream);
 
 /* Static description of a status code (never NULL). */
 const char *kda_status_string(int32_t status);

@@ -162,19 +162,29 @@ def make_uniform(seed: int, B: int, T: int, H: int, dk: int, dv: int, dtype: str
 
 def make_preact(seed: int, B: int, T: int, H: int, dk: int, dv: int, dtype: str,
                 chunk: int = 64, state_std: float = 0.0, name: str = "preact",
-                device="cpu") -> KDAInputs:
-    """Raw pre-activations for the fused prologue: q, k, v, beta_raw and
-    gate_raw ~ N(0, 1) drawn in the same order as the other workloads, but
-    with no normalisation, sigmoid or softplus applied (``prologue == 7``)."""
+                device="cpu", prologue: int = 7) -> KDAInputs:
+    """Inputs for the fused prologue: q, k, v, beta_raw and gate_raw ~ N(0, 1)
+    drawn in the same order as the other workloads.  The stages selected by
+    ``prologue`` (bit 1 gate, bit 2 beta, bit 4 q/k norm) are left as raw
+    pre-activations; the others are applied here as for the other workloads
+    (k normalised, beta = sigmoid, log alpha = -softplus), so that the
+    recurrence always sees keys of unit norm and gates in range."""
     g = _gen(seed, device)
     kw = dict(generator=g, device=device, dtype=torch.float32)
-    out = [torch.randn((B, T, H, dk), **kw), torch.randn((B, T, H, dk), **kw),
-           torch.randn((B, T, H, dv), **kw), torch.randn((B, T, H), **kw),
-           torch.randn((B, T, H, dk), **kw)]
+    q, k, v, beta, la = (torch.randn((B, T, H, dk), **kw), torch.randn((B, T, H, dk), **kw),
+                         torch.randn((B, T, H, dv), **kw), torch.randn((B, T, H), **kw),
+                         torch.randn((B, T, H, dk), **kw))
+    if not prologue & 4:
+        k = k / torch.clamp(torch.linalg.vector_norm(k, dim=-1, keepdim=True), min=1e-12)
+    if not prologue & 2:
+        beta = torch.sigmoid(beta)
+    if not prologue & 1:
+        la = -torch.nn.functional.softplus(la)
+    out = [q, k, v, beta, la]
     if dtype == "bf16":
         out = [t.to(torch.bfloat16).to(torch.float32) for t in out]
     state = _to_np(_state(g, (B, H, dk, dv), state_std, device)) if state_std else None
-    return KDAInputs(name, dtype, *(_to_np(t) for t in out), state, None, chunk, prologue=7)
+    return KDAInputs(name, dtype, *(_to_np(t) for t in out), state, None, chunk, prologue=prologue)
 
 
 def make_packed(seed: int, lengths, H: int, dk: int, dv: int, dtype: str, chunk: int = 64,

@@ -30,32 +30,34 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert {"kda_prefill_chunked", "kda_decode_step", "kda_prefill_workspace_bytes"} <= set(names)
+    assert {"kda_prefill_chunked", "kda_decode_step", "kda_decode", "kda_prefill_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in kda.h but not exported"
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.kda_abi_version() == 1
+    assert L.kda_abi_version() == 2
     for s in range(7):
         assert L.kda_status_string(s)
     assert L.kda_status_string(99) == b"unknown status"
 
 
-def test_struct_layout_matches_header(tmp_path):
-    """ctypes mirror == the C compiler's layout of kda_prefill_args."""
-    fields = [f for f, _ in kda.PrefillArgs._fields_]
+@pytest.mark.parametrize("cname,cls", [("kda_prefill_args", kda.PrefillArgs),
+                                       ("kda_decode_args", kda.DecodeArgs)])
+def test_struct_layout_matches_header(tmp_path, cname, cls):
+    """ctypes mirror == the C compiler's layout of the argument structs."""
+    fields = [f for f, _ in cls._fields_]
     src = tmp_path / "layout.c"
-    body = "".join(f'printf("%zu\\n", offsetof(kda_prefill_args, {f}));' for f in fields)
+    body = "".join(f'printf("%zu\\n", offsetof({cname}, {f}));' for f in fields)
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "kda.h"\n'
-                   'int main(void){printf("%zu\\n", sizeof(kda_prefill_args));' + body + 'return 0;}\n')
+                   f'int main(void){{printf("%zu\\n", sizeof({cname}));' + body + 'return 0;}\n')
     exe = tmp_path / "layout"
     import subprocess
     subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
                    check=True)
     got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
                                           check=True).stdout.split()]
-    want = [ctypes.sizeof(kda.PrefillArgs)] + [getattr(kda.PrefillArgs, f).offset for f in fields]
+    want = [ctypes.sizeof(cls)] + [getattr(cls, f).offset for f in fields]
     assert got == want
 
 
@@ -77,7 +79,7 @@ def base_args(**over):
     (dict(q=None), 1), (dict(o=None), 1), (dict(workspace=None), 1),
     (dict(B=0), 2), (dict(H=0), 2), (dict(d_k=0), 2), (dict(num_seqs=2), 2),
     (dict(d_k=96), 3), (dict(d_v=256), 3), (dict(chunk_size=48), 3), (dict(in_dtype=7), 3),
-    (dict(out_dtype=2), 3),
+    (dict(out_dtype=2), 3), (dict(prologue=8), 3), (dict(prologue=0x80000000), 3),
     (dict(workspace_bytes=0), 4),
 ])
 def test_prefill_host_validation(L, over, status):
@@ -122,6 +124,31 @@ def test_packed_host_seqlens_validation(L):
 ])
 def test_decode_host_validation(L, args, status):
     assert L.kda_decode_step(*args, None, None, None, None, None, None, None, None) == status
+
+
+def decode_args(**over):
+    a = kda.DecodeArgs()
+    a.B, a.H, a.d_k, a.d_v, a.n_tokens, a.in_dtype, a.out_dtype = 4, 2, 128, 128, 3, 1, 0
+    for f in ("q", "k", "v", "beta", "log_alpha", "initial_state", "o"):
+        setattr(a, f, FAKE)
+    for key, val in over.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), 1), (dict(initial_state=None), 1), (dict(o=None), 1),
+    (dict(H=0), 2), (dict(n_tokens=0), 2), (dict(B=-1), 2),
+    (dict(d_k=96), 3), (dict(in_dtype=4), 3), (dict(prologue=16), 3),
+    (dict(B=1 << 20, n_tokens=1 << 10, H=4), 3),
+])
+def test_multi_token_decode_host_validation(L, over, status):
+    assert L.kda_decode(ctypes.byref(decode_args(**over)), None) == status
+
+
+def test_multi_token_decode_empty_batch_and_null_args(L):
+    assert L.kda_decode(ctypes.byref(decode_args(B=0, q=None)), None) == 0
+    assert L.kda_decode(None, None) == 1
 
 
 def test_decode_empty_batch_is_noop(L):
