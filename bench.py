@@ -13,6 +13,10 @@ Prints ONE JSON line:
                the decode step inside each timed step is reported beside it
   roofline     prefill: algorithmic HBM bytes / average call duration vs 8 TB/s,
                and vs what a plain 512 MiB device copy reaches in the same run
+  prologue     the same prefill from raw pre-activations (softplus decay gate,
+               sigmoid write gate and q/k L2 norm fused into the kernels)
+  decode_multi 4 tokens per sequence per launch (multi-token decode), with
+               and without the per-token states written for rollback
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -217,6 +221,24 @@ def cpu_baseline_decode(D):
                 sample=f"one step of all {B} sequences x {D['q'].shape[2]} heads ({dt:.2f} s)")
 
 
+def _decode_into(kda, mt, state, om, tsb):
+    """kda.decode writing the per-token states into a preallocated buffer
+    (the binding allocates them otherwise)."""
+    a = kda.DecodeArgs()
+    B, m, H, d = mt["q"].shape
+    a.B, a.H, a.d_k, a.d_v, a.n_tokens = B, H, d, d, m
+    a.in_dtype, a.out_dtype, a.prologue = kda.KDA_BF16, kda.KDA_F32, 0
+    a.q, a.k, a.v, a.beta, a.log_alpha = (ctypes.c_void_p(mt[n].data_ptr())
+                                          for n in ("q", "k", "v", "beta", "log_alpha"))
+    a.initial_state = a.final_state = ctypes.c_void_p(state.data_ptr())
+    a.token_states = ctypes.c_void_p(tsb.data_ptr())
+    a.o = ctypes.c_void_p(om.data_ptr())
+    import torch
+    st = kda.lib().kda_decode(ctypes.byref(a), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if st != 0:
+        raise kda.KDAError(st, "kda_decode")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -323,6 +345,57 @@ def main():
         copy_gbs = max(copy_gbs, 2 * csrc.numel() * 4 / (ca.elapsed_time(cb) / 10 * 1e-3) / 1e9)
     del csrc, cdst
 
+    # Prefill from pre-activations: the same shapes, q, k, v, beta_raw,
+    # gate_raw ~ N(0, 1) (bf16), every prologue stage fused.
+    print("[bench] fused prologue", file=sys.stderr, flush=True)
+    pro = None
+    if Bp == 1 and P["cu"] is None:
+        from synth.kda_inputs import preact_tensors
+        xq, xk, xv, xb, xg = preact_tensors(_gen(5, dev), 1, T, H, d, d, "bf16", dev)
+        pro_ms = []
+        for i in range(1 + args.warmup):
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record()
+            kda.prefill(xq, xk, xv, xb, xg, chunk_size=P["chunk"], workspace=ws, o=o, final_state=fin,
+                        prologue=kda.PROLOGUE_ALL)
+            b_.record()
+            torch.cuda.synchronize()
+            pro_ms.append(a_.elapsed_time(b_))
+        del xq, xk, xv, xb, xg
+        pro = min(pro_ms[1:]) if len(pro_ms) > 1 else pro_ms[0]
+
+    # Multi-token decode: 4 tokens per sequence per launch over the decode
+    # workload's shapes (B=256, H=32, d=128), 16 launches back to back.
+    print("[bench] multi-token decode", file=sys.stderr, flush=True)
+    M_TOK = 4
+    mt = {n: D[n][:M_TOK].transpose(0, 1).contiguous() for n in ("q", "k", "v", "beta", "log_alpha")}
+    om = torch.empty((Bd, M_TOK, 32, 128), dtype=torch.float32, device=dev)
+    tsb = torch.empty((Bd, M_TOK, 32, 128, 128), dtype=torch.float32, device=dev)
+    multi = {}
+    for with_states in (False, True):
+        def launch():
+            kda.decode(mt["q"], mt["k"], mt["v"], mt["beta"], mt["log_alpha"], state, o=om,
+                       token_states=False) if not with_states else \
+                _decode_into(kda, mt, state, om, tsb)
+        launch()
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        for _ in range(16):
+            launch()
+        b_.record()
+        torch.cuda.synchronize()
+        ms = a_.elapsed_time(b_) / 16
+        nbytes = Bd * 32 * (2 * 128 * 128 * 4 + M_TOK * PREFILL_BYTES_PER_TOKEN_HEAD)
+        if with_states:
+            nbytes += Bd * 32 * M_TOK * 128 * 128 * 4
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        multi["with_token_states" if with_states else "state_only"] = {
+            "value": Bd * M_TOK / (ms * 1e-3), "unit": "seq-token-steps/s", "avg_ms": ms,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "frac_of_achievable": None, "algorithmic_bytes": nbytes,
+                         "kernel": "decode_kernel (m = 4)"}}
+    del tsb, om, mt
+
     rng = range(args.warmup, n_ev)
     pre_ms = [ev.ms(pev[3 * i], pev[3 * i + 2]) for i in rng]
     intra_ms = [ev.ms(pev[3 * i], pev[3 * i + 1]) for i in rng]
@@ -373,9 +446,22 @@ def main():
                                 "unit": "GB/s", "frac": d_gbs / HBM_PEAK_GBS,
                                 "achievable_copy_gbs": copy_gbs, "frac_of_achievable": d_gbs / copy_gbs,
                                 "traffic": measured_traffic("decode"),
-                                "kernel": "decode_step_kernel", "algorithmic_bytes": dbytes}},
+                                "kernel": "decode_kernel (m = 1)", "algorithmic_bytes": dbytes}},
         "prefill_ms": pre,
     }
+    if pro is not None:
+        pro_bytes = tokens * H * PREFILL_BYTES_PER_TOKEN_HEAD
+        out["prologue"] = {"value": tokens / (pro * 1e-3), "unit": "tokens/s", "avg_ms": pro,
+                           "overhead_vs_plain": pro / pre - 1.0,
+                           "stages": "log alpha = -softplus(x), beta = sigmoid(x), q/k L2 norm",
+                           "inputs": "q, k, v, beta_raw, gate_raw ~ N(0,1) bf16, same shapes",
+                           "roofline": {"bound": "hbm", "achieved": pro_bytes / (pro * 1e-3) / 1e9,
+                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                        "frac": pro_bytes / (pro * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                        "algorithmic_bytes": pro_bytes}}
+    for v_ in multi.values():
+        v_["roofline"]["frac_of_achievable"] = v_["roofline"]["achieved"] / copy_gbs
+    out["decode_multi"] = dict(tokens_per_launch=M_TOK, **multi)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline_prefill(P)

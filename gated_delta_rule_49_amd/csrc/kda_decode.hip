@@ -44,10 +44,15 @@ struct DecodeParams {
 };
 
 // MULTI = false: the single-token launch (m == 1, no per-token states), a
-// straight-line kernel without the token loop.
+// straight-line kernel without the token loop.  MULTI = true stages the
+// inputs of up to MG tokens at once, so that the token loop itself waits on
+// no global load.
 template <int DK, int DV, typename TI, typename TO, bool MULTI>
-__global__ void __launch_bounds__((DecodeShape<DK, DV>::NT)) decode_kernel(DecodeParams p) {
+__global__ void __launch_bounds__((DecodeShape<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(sizeof(TO) == 4 ? 4 : 3)))
+decode_kernel(DecodeParams p) {
     using Sh = DecodeShape<DK, DV>;
+    constexpr int MG = MULTI ? 8 : 1;   // tokens staged per group
+    constexpr int NRED = Sh::NW > 1 ? Sh::NW : 1;
     const int bh = blockIdx.x;
     const int b = bh / p.H, h = bh % p.H;
     const int tid = threadIdx.x;
@@ -62,9 +67,12 @@ __global__ void __launch_bounds__((DecodeShape<DK, DV>::NT)) decode_kernel(Decod
     const TI *la = static_cast<const TI *>(p.log_alpha);
     TO *o = static_cast<TO *>(p.o);
 
-    __shared__ float s_a[DK], s_k[DK], s_q[DK], s_ak[DK], s_aq[DK];
-    __shared__ float s_red[2][Sh::NW > 1 ? Sh::NW : 1][DV];
-    __shared__ float s_kappa, s_nk, s_nq;
+    __shared__ float s_a[MG][DK], s_k[MG][DK], s_q[MG][DK], s_ak[MG][DK], s_aq[MG][DK];
+    __shared__ float s_v[MG][DV], s_b[MG];
+    __shared__ float s_kappa[MG], s_nk[MG], s_nq[MG];
+    // wave partials of p and r, double-buffered over tokens so that one
+    // barrier per token suffices
+    __shared__ float s_red[MULTI ? 2 : 1][2][NRED][DV];
 
     // this thread's rows of S (float4 each), held in registers for all m tokens
     const int64_t soff = static_cast<int64_t>(bh) * DK * DV;
@@ -74,36 +82,50 @@ __global__ void __launch_bounds__((DecodeShape<DK, DV>::NT)) decode_kernel(Decod
     for (int i = 0; i < Sh::RPT; ++i) sv[i] = S4[(rg + Sh::RG * i) * (DV / 4) + c4];
 
     const int m = MULTI ? p.m : 1;
-    for (int t = 0; t < m; ++t) {
-        const int64_t tok = (static_cast<int64_t>(b) * m + t) * p.H + h;  // row of [B, m, H]
-        if (t > 0) __syncthreads();  // the previous token's readers of s_* are done
-        const int64_t vecoff = tok * DK;
-        for (int i = tid; i < DK; i += Sh::NT) {
-            const float x = io<TI>::ld(la, vecoff + i);
+    int par = 0;
+    for (int t0 = 0; t0 < m; t0 += MG) {
+        const int nt = MULTI ? min(MG, m - t0) : 1;
+        const int64_t tok0 = (static_cast<int64_t>(b) * m + t0) * p.H + h;  // row of [B, m, H]
+        if (t0 > 0) __syncthreads();  // the previous group's readers of s_* are done
+        // stage the group's token vectors
+        for (int idx = tid; idx < nt * DK; idx += Sh::NT) {
+            const int t = idx / DK, i = idx % DK;
+            const int64_t off = (tok0 + static_cast<int64_t>(t) * p.H) * DK + i;
+            const float x = io<TI>::ld(la, off);
             // alpha = exp(log alpha); with the gate prologue exp(-softplus(x)) = 1 / (1 + e^x)
             const float a = (p.prologue & kProGate) ? sigmoid_f32(-x) : __expf(x);
-            const float kk = io<TI>::ld(k, vecoff + i);
-            const float qq = io<TI>::ld(q, vecoff + i);
-            s_a[i] = a;
-            s_k[i] = kk;
-            s_q[i] = qq;
-            s_ak[i] = a * kk;
-            s_aq[i] = a * qq;
+            const float kk = io<TI>::ld(k, off);
+            const float qq = io<TI>::ld(q, off);
+            s_a[t][i] = a;
+            s_k[t][i] = kk;
+            s_q[t][i] = qq;
+            s_ak[t][i] = a * kk;
+            s_aq[t][i] = a * qq;
+        }
+        for (int idx = tid; idx < nt * DV; idx += Sh::NT) {
+            const int t = idx / DV, j = idx % DV;
+            s_v[t][j] = io<TI>::ld(v, (tok0 + static_cast<int64_t>(t) * p.H) * DV + j);
+        }
+        if (tid < nt) {
+            float bt = io<TI>::ld(beta, tok0 + static_cast<int64_t>(tid) * p.H);
+            if (p.prologue & kProBeta) bt = sigmoid_f32(bt);
+            s_b[tid] = bt;
         }
         __syncthreads();
-        if (wave == 0) {  // kappa = k.q and, with the norm, 1/|k| and 1/|q|
+        // kappa = k.q and, with the norm, 1/|k| and 1/|q|: one wave per token
+        for (int t = wave; t < nt; t += Sh::NW) {
             float kq = 0.f, k2 = 0.f, q2 = 0.f;
             for (int i = lane; i < DK; i += 64) {
-                const float kk = s_k[i], qq = s_q[i];
+                const float kk = s_k[t][i], qq = s_q[t][i];
                 kq += kk * qq;
                 k2 += kk * kk;
                 q2 += qq * qq;
             }
 #pragma unroll
-            for (int m = 32; m >= 1; m >>= 1) {
-                kq += __shfl_xor(kq, m);
-                k2 += __shfl_xor(k2, m);
-                q2 += __shfl_xor(q2, m);
+            for (int msk = 32; msk >= 1; msk >>= 1) {
+                kq += __shfl_xor(kq, msk);
+                k2 += __shfl_xor(k2, msk);
+                q2 += __shfl_xor(q2, msk);
             }
             if (lane == 0) {
                 float nk = 1.f, nq = 1.f;
@@ -111,73 +133,74 @@ __global__ void __launch_bounds__((DecodeShape<DK, DV>::NT)) decode_kernel(Decod
                     nk = 1.f / __builtin_sqrtf(k2 + kQKNormEps);
                     nq = 1.f / __builtin_sqrtf(q2 + kQKNormEps);
                 }
-                s_nk = nk;
-                s_nq = nq;
-                s_kappa = kq * nk * nq;
+                s_nk[t] = nk;
+                s_nq[t] = nq;
+                s_kappa[t] = kq * nk * nq;
             }
         }
 
-        // partial p = S^T (a k), r = S^T (a q) over this thread's rows
-        float pr[4] = {0.f, 0.f, 0.f, 0.f}, rr[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < nt; ++t, par ^= MULTI ? 1 : 0) {
+            const int64_t tok = tok0 + static_cast<int64_t>(t) * p.H;
+            // partial p = S^T (a k), r = S^T (a q) over this thread's rows
+            float pr[4] = {0.f, 0.f, 0.f, 0.f}, rr[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < Sh::RPT; ++i) {
-            const int row = rg + Sh::RG * i;
-            const float ak = s_ak[row], aq = s_aq[row];
-            pr[0] += sv[i].x * ak; pr[1] += sv[i].y * ak; pr[2] += sv[i].z * ak; pr[3] += sv[i].w * ak;
-            rr[0] += sv[i].x * aq; rr[1] += sv[i].y * aq; rr[2] += sv[i].z * aq; rr[3] += sv[i].w * aq;
-        }
-        // reduce across the row groups inside the wave (lane bits >= log2(TPR))
-#pragma unroll
-        for (int m = Sh::TPR; m < 64 && m < Sh::NT; m <<= 1) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                pr[j] += __shfl_xor(pr[j], m);
-                rr[j] += __shfl_xor(rr[j], m);
+            for (int i = 0; i < Sh::RPT; ++i) {
+                const int row = rg + Sh::RG * i;
+                const float ak = s_ak[t][row], aq = s_aq[t][row];
+                pr[0] += sv[i].x * ak; pr[1] += sv[i].y * ak; pr[2] += sv[i].z * ak; pr[3] += sv[i].w * ak;
+                rr[0] += sv[i].x * aq; rr[1] += sv[i].y * aq; rr[2] += sv[i].z * aq; rr[3] += sv[i].w * aq;
             }
-        }
-        if (lane < Sh::TPR) {
+            // reduce across the row groups inside the wave (lane bits >= log2(TPR))
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                s_red[0][wave][4 * c4 + j] = pr[j];
-                s_red[1][wave][4 * c4 + j] = rr[j];
+            for (int msk = Sh::TPR; msk < 64 && msk < Sh::NT; msk <<= 1) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pr[j] += __shfl_xor(pr[j], msk);
+                    rr[j] += __shfl_xor(rr[j], msk);
+                }
             }
-        }
-        __syncthreads();
-        // every thread needs delta for its 4 columns: sum the wave partials
-        float pt[4] = {0.f, 0.f, 0.f, 0.f}, rt[4] = {0.f, 0.f, 0.f, 0.f};
+            if (lane < Sh::TPR) {
 #pragma unroll
-        for (int w = 0; w < Sh::NW; ++w) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                pt[j] += s_red[0][w][4 * c4 + j];
-                rt[j] += s_red[1][w][4 * c4 + j];
+                for (int j = 0; j < 4; ++j) {
+                    s_red[par][0][wave][4 * c4 + j] = pr[j];
+                    s_red[par][1][wave][4 * c4 + j] = rr[j];
+                }
             }
-        }
-        const float nk = s_nk, nq = s_nq;
-        float bt = io<TI>::ld(beta, tok);
-        if (p.prologue & kProBeta) bt = sigmoid_f32(bt);
-        const int64_t voff = tok * DV + 4 * c4;
-        float delta[4];
+            __syncthreads();
+            // every thread needs delta for its 4 columns: sum the wave partials
+            float pt[4] = {0.f, 0.f, 0.f, 0.f}, rt[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) delta[j] = bt * (io<TI>::ld(v, voff + j) - pt[j] * nk);
-        if (rg == 0) {
-            const float kappa = s_kappa;
+            for (int w = 0; w < Sh::NW; ++w) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) io<TO>::st(o, voff + j, rt[j] * nq + kappa * delta[j]);
-        }
+                for (int j = 0; j < 4; ++j) {
+                    pt[j] += s_red[par][0][w][4 * c4 + j];
+                    rt[j] += s_red[par][1][w][4 * c4 + j];
+                }
+            }
+            const float nk = s_nk[t], nq = s_nq[t], bt = s_b[t];
+            const int64_t voff = tok * DV + 4 * c4;
+            float delta[4];
 #pragma unroll
-        for (int i = 0; i < Sh::RPT; ++i) {
-            const int row = rg + Sh::RG * i;
-            const float a = s_a[row], kk = s_k[row] * nk;
-            sv[i].x = a * sv[i].x + kk * delta[0];
-            sv[i].y = a * sv[i].y + kk * delta[1];
-            sv[i].z = a * sv[i].z + kk * delta[2];
-            sv[i].w = a * sv[i].w + kk * delta[3];
-        }
-        if (MULTI && p.token_states) {
-            float4 *T4 = reinterpret_cast<float4 *>(p.token_states + tok * DK * DV);
+            for (int j = 0; j < 4; ++j) delta[j] = bt * (s_v[t][4 * c4 + j] - pt[j] * nk);
+            if (rg == 0) {
+                const float kappa = s_kappa[t];
 #pragma unroll
-            for (int i = 0; i < Sh::RPT; ++i) T4[(rg + Sh::RG * i) * (DV / 4) + c4] = sv[i];
+                for (int j = 0; j < 4; ++j) io<TO>::st(o, voff + j, rt[j] * nq + kappa * delta[j]);
+            }
+#pragma unroll
+            for (int i = 0; i < Sh::RPT; ++i) {
+                const int row = rg + Sh::RG * i;
+                const float a = s_a[t][row], kk = s_k[t][row] * nk;
+                sv[i].x = a * sv[i].x + kk * delta[0];
+                sv[i].y = a * sv[i].y + kk * delta[1];
+                sv[i].z = a * sv[i].z + kk * delta[2];
+                sv[i].w = a * sv[i].w + kk * delta[3];
+            }
+            if (MULTI && p.token_states) {
+                float4 *T4 = reinterpret_cast<float4 *>(p.token_states + tok * DK * DV);
+#pragma unroll
+                for (int i = 0; i < Sh::RPT; ++i) T4[(rg + Sh::RG * i) * (DV / 4) + c4] = sv[i];
+            }
         }
     }
     if (p.state_out) {

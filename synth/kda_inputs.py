@@ -170,6 +170,16 @@ def make_preact(seed: int, B: int, T: int, H: int, dk: int, dv: int, dtype: str,
     (k normalised, beta = sigmoid, log alpha = -softplus), so that the
     recurrence always sees keys of unit norm and gates in range."""
     g = _gen(seed, device)
+    out = preact_tensors(g, B, T, H, dk, dv, dtype, device, prologue)
+    if dtype == "bf16":
+        out = [t.to(torch.float32) for t in out]
+    state = _to_np(_state(g, (B, H, dk, dv), state_std, device)) if state_std else None
+    return KDAInputs(name, dtype, *(_to_np(t) for t in out), state, None, chunk, prologue=prologue)
+
+
+def preact_tensors(g, B, T, H, dk, dv, dtype="bf16", device="cpu", prologue=7):
+    """The token draws of ``make_preact`` as torch tensors on ``device``
+    (bf16 tensors for dtype 'bf16'), for benchmarks that keep them there."""
     kw = dict(generator=g, device=device, dtype=torch.float32)
     q, k, v, beta, la = (torch.randn((B, T, H, dk), **kw), torch.randn((B, T, H, dk), **kw),
                          torch.randn((B, T, H, dv), **kw), torch.randn((B, T, H), **kw),
@@ -182,9 +192,8 @@ def make_preact(seed: int, B: int, T: int, H: int, dk: int, dv: int, dtype: str,
         la = -torch.nn.functional.softplus(la)
     out = [q, k, v, beta, la]
     if dtype == "bf16":
-        out = [t.to(torch.bfloat16).to(torch.float32) for t in out]
-    state = _to_np(_state(g, (B, H, dk, dv), state_std, device)) if state_std else None
-    return KDAInputs(name, dtype, *(_to_np(t) for t in out), state, None, chunk, prologue=prologue)
+        out = [t.to(torch.bfloat16) for t in out]
+    return out
 
 
 def make_packed(seed: int, lengths, H: int, dk: int, dv: int, dtype: str, chunk: int = 64,
