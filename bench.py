@@ -100,6 +100,19 @@ def summarize(root):
             print(f"| {row['Name'].split('(')[0]} | {row['Calls']} | "
                   f"{float(row['AverageNs']) / 1e3:.1f} us | {float(row['TotalDurationNs']) / 1e6:.3f} ms |")
         print(f"| (other kernels: input generation, copies) | {other[0]} | | {other[1] / 1e6:.3f} ms |")
+    # per-dispatch durations in launch order: the bench runs the plain prefill
+    # (warmup + steps calls) before the fused-prologue prefill, and the
+    # state-only multi-token decodes before those that write per-token states
+    for f in glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True):
+        per = {}
+        for row in sorted(csv.DictReader(open(f)), key=lambda r: int(r["Start_Timestamp"])):
+            if "kda::" in row["Kernel_Name"]:
+                per.setdefault(row["Kernel_Name"].split("(")[0], []).append(
+                    (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
+        print("# dispatch durations in launch order (us)")
+        for k, v in per.items():
+            shown = " ".join(f"{x:.0f}" for x in v[:40]) + (" ..." if len(v) > 40 else "")
+            print(f"- {k}: {shown}")
     acc = {}
     for f in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
         for row in csv.DictReader(open(f)):
