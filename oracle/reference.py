@@ -90,6 +90,50 @@ def prologue(q, k, beta, log_alpha, flags):
     return q, k, beta, log_alpha
 
 
+# ---------------------------------------------------- short convolution --
+# The short causal convolution of the executed sublayer, a small local mixing
+# step on q, k and/or v before the recurrence (Module 04 — KDA II, §3 "The
+# sublayer is bigger than the recurrence"); its rolling state is part of the
+# serving state a rollback must restore (Module 11, §2, row "Serving state").
+# The pages give neither the width nor the form.  Reading: depthwise (one
+# filter per channel), causal, width W, taps ordered oldest input first:
+#     y_t[c] = sum_{j=0}^{W-1} w[c, j] * x_{t-W+1+j}[c]  (+ bias[c]),
+# optionally followed by SiLU (y * sigmoid(y)); inputs before a sequence's
+# first token come from its conv state (the W-1 inputs that preceded it,
+# oldest first), or are zero.
+def short_conv(x, weight, cu_seqlens=None, initial_state=None, bias=None, silu=False):
+    """x [B, T, C]; weight [C, W]; initial_state [N, C, W-1] or None (zeros);
+    bias [C] or None.  Sequences are the B rows, or with ``cu_seqlens``
+    (B == 1) the documents packed along T.  Returns (y [B, T, C] fp64,
+    final_state [N, C, W-1] fp64: the last W-1 inputs of each sequence, taken
+    from its initial state where the sequence is shorter)."""
+    x = np.asarray(x, f64)
+    w = np.asarray(weight, f64)
+    B, T, Cc = x.shape
+    W = w.shape[1]
+    if cu_seqlens is None:
+        seqs = [(b, 0, T) for b in range(B)]
+    else:
+        seqs = [(0, int(cu_seqlens[n]), int(cu_seqlens[n + 1])) for n in range(len(cu_seqlens) - 1)]
+    y = np.zeros_like(x)
+    final = np.zeros((len(seqs), Cc, W - 1), f64)
+    for n, (b, t0, t1) in enumerate(seqs):
+        hist = (np.zeros((W - 1, Cc)) if initial_state is None
+                else np.asarray(initial_state[n], f64).T)           # [W-1, C], oldest first
+        xp = np.concatenate([hist, x[b, t0:t1]], axis=0)             # [W-1+L, C]
+        L = t1 - t0
+        acc = np.zeros((L, Cc))
+        for j in range(W):
+            acc += w[:, j] * xp[j:j + L]
+        if bias is not None:
+            acc += np.asarray(bias, f64)
+        if silu:
+            acc = acc * sigmoid(acc)
+        y[b, t0:t1] = acc
+        final[n] = xp[L:L + W - 1].T
+    return y, final
+
+
 # ------------------------------------------------------- one token ------
 def step(S, q, k, v, beta, log_alpha):
     """One token of the recurrence, batched over any leading axes.
