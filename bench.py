@@ -17,6 +17,8 @@ Prints ONE JSON line:
                sigmoid write gate and q/k L2 norm fused into the kernels)
   decode_multi 4 tokens per sequence per launch (multi-token decode), with
                and without the per-token states written for rollback
+  short_conv   the width-4 causal convolution over a q-shaped prefill input
+               and over one decode token per sequence (state rolled in place)
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -409,6 +411,53 @@ def main():
                          "kernel": "decode_kernel (m = 4)"}}
     del tsb, om, mt
 
+    # Short causal convolution (width 4) over a q-shaped input of the prefill
+    # workload, [B, T, H * d] bf16 -> bf16, and over one decode token per
+    # sequence with the rolling state updated in place.
+    print("[bench] short convolution", file=sys.stderr, flush=True)
+    CW = 4
+    cx = P["q"].reshape(Bp, T, H * d)
+    cw = torch.randn((H * d, CW), generator=_gen(7, dev), device=dev) / 2
+    cy = torch.empty_like(cx)
+    cfin = torch.empty((Bp, H * d, CW - 1), dtype=torch.float32, device=dev)
+    conv = {}
+    for _ in range(2):
+        kda.short_conv(cx, cw, final_state=cfin, y=cy)
+    a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a_.record()
+    for _ in range(10):
+        kda.short_conv(cx, cw, final_state=cfin, y=cy)
+    b_.record()
+    torch.cuda.synchronize()
+    ms = a_.elapsed_time(b_) / 10
+    nbytes = 2 * cx.numel() * 2 + cw.numel() * 4 + cfin.numel() * 4
+    conv["prefill"] = {"value": Bp * T / (ms * 1e-3), "unit": "tokens/s", "avg_ms": ms,
+                       "shape": f"[{Bp}, {T}, {H * d}] bf16 -> bf16, W={CW}",
+                       "roofline": {"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                                    "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                    "frac_of_achievable": None, "algorithmic_bytes": nbytes,
+                                    "kernel": "short_conv_kernel<bf16,bf16,4> + conv_state_kernel"}}
+    del cx, cy, cfin
+    dx = D["q"][0].reshape(Bd, 1, 32 * 128)
+    dst = torch.zeros((Bd, 32 * 128, CW - 1), dtype=torch.float32, device=dev)
+    dy = torch.empty_like(dx)
+    for _ in range(2):
+        kda.short_conv(dx, cw, initial_state=dst, update_state=True, y=dy)
+    a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a_.record()
+    for _ in range(64):
+        kda.short_conv(dx, cw, initial_state=dst, update_state=True, y=dy)
+    b_.record()
+    torch.cuda.synchronize()
+    ms = a_.elapsed_time(b_) / 64
+    nbytes = 2 * dst.numel() * 4 + 2 * dx.numel() * 2 + cw.numel() * 4
+    conv["decode"] = {"value": Bd / (ms * 1e-3), "unit": "seq-steps/s", "avg_ms": ms,
+                      "shape": f"[{Bd}, 1, {32 * 128}] bf16, state [{Bd}, {32 * 128}, {CW - 1}] in place",
+                      "roofline": {"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                                   "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                   "algorithmic_bytes": nbytes}}
+    del dx, dst, dy, cw
+
     rng = range(args.warmup, n_ev)
     pre_ms = [ev.ms(pev[3 * i], pev[3 * i + 2]) for i in rng]
     intra_ms = [ev.ms(pev[3 * i], pev[3 * i + 1]) for i in rng]
@@ -475,6 +524,8 @@ def main():
     for v_ in multi.values():
         v_["roofline"]["frac_of_achievable"] = v_["roofline"]["achieved"] / copy_gbs
     out["decode_multi"] = dict(tokens_per_launch=M_TOK, **multi)
+    conv["prefill"]["roofline"]["frac_of_achievable"] = conv["prefill"]["roofline"]["achieved"] / copy_gbs
+    out["short_conv"] = conv
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline_prefill(P)

@@ -11,6 +11,7 @@ raise.
                    cu_seqlens=None, chunk_size=64)
     o = decode_step(q, k, v, beta, log_alpha, state)     # state updated in place
     o, S, per_token = decode(q, k, v, beta, log_alpha, state)   # m tokens per sequence
+    y, conv_state = short_conv(x, weight, conv_state)            # rolling causal conv
 
 ``prologue`` (prefill and decode) fuses the stages that precede the
 recurrence: PROLOGUE_GATE_SOFTPLUS (log_alpha holds x, log alpha =
@@ -30,8 +31,8 @@ import os
 
 import torch
 
-__all__ = ["prefill", "decode_step", "decode", "workspace_bytes", "max_chunks", "lib", "KDAError",
-           "PrefillArgs", "DecodeArgs", "KDA_F32", "KDA_BF16", "PROLOGUE_GATE_SOFTPLUS",
+__all__ = ["prefill", "decode_step", "decode", "short_conv", "workspace_bytes", "max_chunks", "lib",
+           "KDAError", "PrefillArgs", "DecodeArgs", "ConvArgs", "KDA_F32", "KDA_BF16", "PROLOGUE_GATE_SOFTPLUS",
            "PROLOGUE_BETA_SIGMOID", "PROLOGUE_QK_L2NORM", "PROLOGUE_ALL"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -80,6 +81,18 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class ConvArgs(ctypes.Structure):
+    """Mirror of ``kda_conv_args`` (include/kda.h)."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("C", ctypes.c_int32), ("W", ctypes.c_int32),
+        ("num_seqs", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("activation", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+        ("cu_seqlens", ctypes.c_void_p), ("initial_state", ctypes.c_void_p),
+        ("final_state", ctypes.c_void_p), ("y", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -103,6 +116,8 @@ def lib():
         L.kda_decode_step.restype = I32
         L.kda_decode.argtypes = [ctypes.POINTER(DecodeArgs), P]
         L.kda_decode.restype = I32
+        L.kda_short_conv.argtypes = [ctypes.POINTER(ConvArgs), P]
+        L.kda_short_conv.restype = I32
         L.kda_status_string.argtypes = [I32]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_abi_version.restype = I32
@@ -310,3 +325,43 @@ def decode(q, k, v, beta, log_alpha, state, out_dtype=torch.float32, update_stat
     if st != 0:
         raise KDAError(st, "kda_decode")
     return o, final_state, ts
+
+
+def short_conv(x, weight, initial_state=None, bias=None, cu_seqlens=None, silu=False,
+               out_dtype=None, final_state=None, update_state=False, y=None):
+    """Short causal depthwise convolution with a rolling state.
+
+    x [B,T,C] (float32 or bfloat16, C a multiple of 8); weight fp32 [C,W]
+    (taps oldest input first, W <= 8); bias fp32 [C] or None; initial_state
+    fp32 [N,C,W-1] or None (zeros).  ``cu_seqlens`` (int32 [N+1], B == 1)
+    packs N documents along T.  With ``update_state`` the final state is
+    written back into ``initial_state`` (decode); else into ``final_state``
+    (allocated when None).  Returns (y [B,T,C], final_state)."""
+    dev = _check_dev(x, weight, initial_state, bias, cu_seqlens, final_state, y)
+    if x.dim() != 3:
+        raise ValueError("x must be [B,T,C]")
+    B, T, C = x.shape
+    if weight.dtype != torch.float32 or weight.dim() != 2 or weight.shape[0] != C:
+        raise ValueError(f"weight must be float32 [{C},W]")
+    W = weight.shape[1]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if initial_state is not None and (initial_state.dtype != torch.float32
+                                      or tuple(initial_state.shape) != (N, C, W - 1)):
+        raise ValueError(f"initial_state must be float32 [{N},{C},{W - 1}]")
+    if update_state:
+        if initial_state is None:
+            raise ValueError("update_state needs an initial_state to update")
+        final_state = initial_state
+    elif final_state is None:
+        final_state = torch.empty((N, C, W - 1), dtype=torch.float32, device=dev)
+    if y is None:
+        y = torch.empty((B, T, C), dtype=out_dtype or x.dtype, device=dev)
+    a = ConvArgs()
+    a.B, a.T, a.C, a.W, a.num_seqs = B, T, C, W, N
+    a.in_dtype, a.out_dtype, a.activation = _dt(x.dtype), _dt(y.dtype), 1 if silu else 0
+    a.x, a.weight, a.bias, a.cu_seqlens = _ptr(x), _ptr(weight), _ptr(bias), _ptr(cu_seqlens)
+    a.initial_state, a.final_state, a.y = _ptr(initial_state), _ptr(final_state), _ptr(y)
+    st = lib().kda_short_conv(ctypes.byref(a), _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_short_conv")
+    return y, final_state

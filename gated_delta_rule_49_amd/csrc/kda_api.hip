@@ -161,4 +161,31 @@ kda_status kda_decode(const kda_decode_args *a, void *hip_stream) {
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+kda_status kda_short_conv(const kda_conv_args *a, void *hip_stream) {
+    if (!a) return KDA_ERR_NULL_ARG;
+    if (a->B < 1 || a->T < 0 || a->C < 1 || a->W < 1 || a->num_seqs < 0) return KDA_ERR_BAD_SHAPE;
+    if (a->W > 8 || a->C % 8 != 0) return KDA_ERR_UNSUPPORTED;
+    if (!dtype_ok(a->in_dtype) || !dtype_ok(a->out_dtype)) return KDA_ERR_UNSUPPORTED;
+    if (a->activation != KDA_CONV_NONE && a->activation != KDA_CONV_SILU) return KDA_ERR_UNSUPPORTED;
+    if (a->cu_seqlens) {
+        if (a->B != 1 || a->num_seqs < 1) return KDA_ERR_BAD_SHAPE;
+    } else if (a->num_seqs != a->B) {
+        return KDA_ERR_BAD_SHAPE;
+    }
+    if (static_cast<int64_t>(a->B) * a->T * a->C > (static_cast<int64_t>(1) << 31) - 1) return KDA_ERR_UNSUPPORTED;
+    const bool any_tokens = static_cast<int64_t>(a->B) * a->T > 0;
+    if (!a->weight || (any_tokens && (!a->x || !a->y))) return KDA_ERR_NULL_ARG;
+    // rows and states are moved as 16-byte vectors
+    for (const void *ptr : {a->x, static_cast<const void *>(a->y), static_cast<const void *>(a->initial_state),
+                            static_cast<const void *>(a->final_state)})
+        if (reinterpret_cast<uintptr_t>(ptr) % 16) return KDA_ERR_UNSUPPORTED;
+    ConvParams p{};
+    p.x = a->x; p.weight = a->weight; p.bias = a->bias; p.cu_seqlens = a->cu_seqlens;
+    p.initial_state = a->initial_state; p.final_state = a->final_state; p.y = a->y;
+    p.B = a->B; p.T = a->T; p.C = a->C; p.W = a->W; p.N = a->num_seqs;
+    p.silu = a->activation == KDA_CONV_SILU;
+    hipError_t e = launch_short_conv(p, a->in_dtype, a->out_dtype, static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // extern "C"

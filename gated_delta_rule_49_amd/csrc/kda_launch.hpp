@@ -27,6 +27,20 @@ hipError_t launch_prefill_f32(const PrefillParams &p, int in_dtype, int out_dtyp
 // mid_event (nullable) is recorded between the intra-chunk and the scan kernel
 hipError_t launch_prefill_mfma(const PrefillParams &p, void *blocks, int out_dtype, hipStream_t s,
                                hipEvent_t mid_event);
+// short causal convolution (validated arguments)
+struct ConvParams {
+    const void *x;              // [B, T, C]
+    const float *weight;        // [C, W]
+    const float *bias;          // nullable [C]
+    const int32_t *cu_seqlens;  // nullable [N + 1] (B == 1)
+    const float *initial_state; // nullable [N, C, W - 1]
+    float *final_state;         // nullable [N, C, W - 1], may alias initial_state
+    void *y;                    // [B, T, C]
+    int32_t B, T, C, W, N;
+    int32_t silu;
+};
+hipError_t launch_short_conv(const ConvParams &p, int in_dtype, int out_dtype, hipStream_t s);
+
 // m tokens per sequence; state_out and token_states nullable, state_out may
 // alias state_in
 hipError_t launch_decode(int B, int H, int m, int dk, int dv, int in_dtype, int out_dtype, uint32_t prologue,

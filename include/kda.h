@@ -26,8 +26,11 @@
  *                        every token for rollback (Module 11, §2 "The full
  *                        correctness matrix", row "Serving state").
  *
- * Both families can fuse the stages that run just before the recurrence
- * (KDA_PROLOGUE_* flags below).
+ *   kda_short_conv       the short causal convolution that precedes the
+ *                        recurrence in the sublayer, with its rolling state.
+ *
+ * Both recurrence families can fuse the stages that run just before the
+ * recurrence (KDA_PROLOGUE_* flags below).
  *
  * Conventions common to all entry points
  *   - Pointers marked DEVICE are device memory owned by the caller; the
@@ -222,6 +225,57 @@ typedef struct kda_decode_args {
 } kda_decode_args;
 
 kda_status kda_decode(const kda_decode_args *a, void *hip_stream);
+
+/*
+ * Short causal convolution with a rolling state: the small local mixing step
+ * the executed sublayer applies to q, k and/or v before the recurrence
+ * (Module 04 — KDA II, §3 "The sublayer is bigger than the recurrence").
+ * Its state, the last W - 1 inputs of each sequence, is serving state that a
+ * rollback restores (Module 11, §2, row "Serving state").  The pages give
+ * neither its width nor its form; this is a depthwise causal filter:
+ *
+ *     y_t[c] = sum_{j=0}^{W-1} weight[c][j] * x_{t-W+1+j}[c]  (+ bias[c]),
+ *     then y * sigmoid(y) if activation == KDA_CONV_SILU,
+ *
+ * taps ordered oldest input first; inputs before a sequence's first token
+ * come from its initial state (zeros when NULL).  Prefill passes whole
+ * sequences; decode passes B rows of m tokens with the state updated in
+ * place (final_state == initial_state).
+ *
+ *   x             DEVICE [B, T, C]  in_dtype (C = channels, e.g. H * d)
+ *   weight        DEVICE fp32 [C, W]
+ *   bias          DEVICE fp32 [C], NULL = none
+ *   cu_seqlens    DEVICE int32 [num_seqs + 1], NULL = the B rows are the
+ *                 sequences; else B == 1 and documents are packed along T
+ *                 (offsets are not validated: malformed offsets give
+ *                 unspecified values, never an out-of-range access)
+ *   initial_state DEVICE fp32 [num_seqs, C, W - 1], oldest input first,
+ *                 NULL = zeros
+ *   final_state   DEVICE fp32 [num_seqs, C, W - 1], NULL = not written: the
+ *                 last W - 1 inputs of each sequence (from its initial state
+ *                 where the sequence is shorter).  May alias initial_state.
+ *   y             DEVICE [B, T, C]  out_dtype
+ * Supported: 1 <= W <= 8; C a positive multiple of 8; B * T * C < 2^31;
+ * x, y and the states 16-byte aligned.
+ */
+#define KDA_CONV_NONE 0
+#define KDA_CONV_SILU 1
+typedef struct kda_conv_args {
+    int32_t B, T, C, W;
+    int32_t num_seqs;
+    int32_t in_dtype;              /* kda_dtype */
+    int32_t out_dtype;             /* kda_dtype */
+    int32_t activation;            /* KDA_CONV_NONE or KDA_CONV_SILU */
+    const void *x;
+    const float *weight;
+    const float *bias;
+    const int32_t *cu_seqlens;
+    const float *initial_state;
+    float *final_state;
+    void *y;
+} kda_conv_args;
+
+kda_status kda_short_conv(const kda_conv_args *a, void *hip_stream);
 
 /* Static description of a status code (never NULL). */
 const char *kda_status_string(int32_t status);

@@ -43,7 +43,8 @@ def test_abi_version_and_status_strings(L):
 
 
 @pytest.mark.parametrize("cname,cls", [("kda_prefill_args", kda.PrefillArgs),
-                                       ("kda_decode_args", kda.DecodeArgs)])
+                                       ("kda_decode_args", kda.DecodeArgs),
+                                       ("kda_conv_args", kda.ConvArgs)])
 def test_struct_layout_matches_header(tmp_path, cname, cls):
     """ctypes mirror == the C compiler's layout of the argument structs."""
     fields = [f for f, _ in cls._fields_]
@@ -149,6 +150,27 @@ def test_multi_token_decode_host_validation(L, over, status):
 def test_multi_token_decode_empty_batch_and_null_args(L):
     assert L.kda_decode(ctypes.byref(decode_args(B=0, q=None)), None) == 0
     assert L.kda_decode(None, None) == 1
+
+
+def conv_args(**over):
+    a = kda.ConvArgs()
+    a.B, a.T, a.C, a.W, a.num_seqs, a.in_dtype, a.out_dtype = 2, 16, 64, 4, 2, 1, 1
+    for f in ("x", "weight", "y"):
+        setattr(a, f, FAKE)
+    for key, val in over.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(x=None), 1), (dict(weight=None), 1), (dict(y=None), 1),
+    (dict(B=0), 2), (dict(C=0), 2), (dict(W=0), 2), (dict(num_seqs=3), 2),
+    (dict(cu_seqlens=FAKE), 2),
+    (dict(W=9), 3), (dict(C=60), 3), (dict(in_dtype=5), 3), (dict(activation=2), 3),
+    (dict(x=FAKE + 4), 3), (dict(final_state=FAKE + 8), 3),
+])
+def test_short_conv_host_validation(L, over, status):
+    assert L.kda_short_conv(ctypes.byref(conv_args(**over)), None) == status
 
 
 def test_decode_empty_batch_is_noop(L):
