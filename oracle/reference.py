@@ -195,6 +195,54 @@ def prefill(q, k, v, beta, log_alpha, cu_seqlens=None, initial_state=None, snap_
     return o, final, snaps
 
 
+# ------------------------------------------------------------ backward --
+# Gradients of the recurrence.  The pages call the affine composition the
+# argument for parallel training (course index, module list, the Module 04
+# entry) but derive no backward pass; this is reverse-mode differentiation of
+# the five operations of one token, applied from the last token to the first:
+#   read   o = S_t^T q           dS_t += q do^T          dq = S_t do
+#   write  S_t = S' + b k e^T    dS' = dS_t, u = dS_t^T k, de = b u,
+#                                db = u.e, dk += b dS_t e
+#   error  e = v - p             dv = de, dp = -de
+#   predict p = S'^T k           dS' += k dp^T, dk += S' dp
+#   decay  S' = Diag(a) S        dS_{t-1} = Diag(a) dS', d(log a) = a * rowsum(dS' * S)
+def recurrent_backward(q, k, v, beta, log_alpha, d_o, S0=None, dS_T=None):
+    """One sequence: q, k, log_alpha [T, H, dk]; v, d_o [T, H, dv]; beta [T, H];
+    S0, dS_T [H, dk, dv] or None (zeros).  Returns the gradients
+    (dq, dk, dv, dbeta, dlog_alpha, dS0) of the scalar loss whose gradients
+    with respect to o and S_T are d_o and dS_T."""
+    q, k, v, beta, log_alpha, d_o = (np.asarray(a, dtype=f64) for a in (q, k, v, beta, log_alpha, d_o))
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    S = np.zeros((H, dk, dv), f64) if S0 is None else np.array(S0, dtype=f64)
+    states = [S]                                   # S_0 .. S_T
+    for t in range(T):
+        S, _ = step(S, q[t], k[t], v[t], beta[t], log_alpha[t])
+        states.append(S)
+    dS = np.zeros((H, dk, dv), f64) if dS_T is None else np.array(dS_T, dtype=f64)
+    g = {n: np.zeros_like(a) for n, a in (("q", q), ("k", k), ("v", v), ("b", beta), ("g", log_alpha))}
+    for t in range(T - 1, -1, -1):
+        a = np.exp(log_alpha[t])                              # [H, dk]
+        Sp = a[..., None] * states[t]                         # S'
+        p = np.einsum("hkv,hk->hv", Sp, k[t])
+        e = v[t] - p
+        St = states[t + 1]
+        dS = dS + q[t][..., None] * d_o[t][:, None, :]         # read
+        g["q"][t] = np.einsum("hkv,hv->hk", St, d_o[t])
+        u = np.einsum("hkv,hk->hv", dS, k[t])                   # write
+        de = beta[t][:, None] * u
+        g["b"][t] = np.sum(u * e, axis=-1)
+        dk_t = beta[t][:, None] * np.einsum("hkv,hv->hk", dS, e)
+        g["v"][t] = de                                          # error
+        dp = -de
+        dSp = dS + k[t][..., None] * dp[:, None, :]             # predict
+        dk_t = dk_t + np.einsum("hkv,hv->hk", Sp, dp)
+        g["k"][t] = dk_t
+        g["g"][t] = a * np.sum(dSp * states[t], axis=-1)        # decay
+        dS = a[..., None] * dSp
+    return g["q"], g["k"], g["v"], g["b"], g["g"], dS
+
+
 # -------------------------------------------- dense affine form ---------
 def transition(k, beta, log_alpha, v):
     """Explicit dense affine step for one head and token:
