@@ -12,6 +12,7 @@ raise.
     o = decode_step(q, k, v, beta, log_alpha, state)     # state updated in place
     o, S, per_token = decode(q, k, v, beta, log_alpha, state)   # m tokens per sequence
     y, conv_state = short_conv(x, weight, conv_state)            # rolling causal conv
+    dq, dk, dv, dbeta, dlog_alpha, dS0 = backward(q, k, v, beta, log_alpha, d_o)
 
 ``prologue`` (prefill and decode) fuses the stages that precede the
 recurrence: PROLOGUE_GATE_SOFTPLUS (log_alpha holds x, log alpha =
@@ -31,8 +32,8 @@ import os
 
 import torch
 
-__all__ = ["prefill", "decode_step", "decode", "short_conv", "workspace_bytes", "max_chunks", "lib",
-           "KDAError", "PrefillArgs", "DecodeArgs", "ConvArgs", "KDA_F32", "KDA_BF16", "PROLOGUE_GATE_SOFTPLUS",
+__all__ = ["prefill", "decode_step", "decode", "short_conv", "backward", "workspace_bytes", "max_chunks",
+           "lib", "KDAError", "PrefillArgs", "DecodeArgs", "ConvArgs", "BackwardArgs", "KDA_F32", "KDA_BF16", "PROLOGUE_GATE_SOFTPLUS",
            "PROLOGUE_BETA_SIGMOID", "PROLOGUE_QK_L2NORM", "PROLOGUE_ALL"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -93,6 +94,21 @@ class ConvArgs(ctypes.Structure):
     ]
 
 
+class BackwardArgs(ctypes.Structure):
+    """Mirror of ``kda_backward_args`` (include/kda.h)."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+        ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("beta", ctypes.c_void_p), ("log_alpha", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
+        ("checkpoints", ctypes.c_void_p), ("d_o", ctypes.c_void_p), ("d_final_state", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("dbeta", ctypes.c_void_p), ("dlog_alpha", ctypes.c_void_p), ("d_initial_state", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 _lib = None
 
 
@@ -118,6 +134,11 @@ def lib():
         L.kda_decode.restype = I32
         L.kda_short_conv.argtypes = [ctypes.POINTER(ConvArgs), P]
         L.kda_short_conv.restype = I32
+        BP = ctypes.POINTER(BackwardArgs)
+        L.kda_backward_workspace_bytes.argtypes = [BP]
+        L.kda_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.kda_backward.argtypes = [BP, P]
+        L.kda_backward.restype = I32
         L.kda_status_string.argtypes = [I32]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_abi_version.restype = I32
@@ -365,3 +386,45 @@ def short_conv(x, weight, initial_state=None, bias=None, cu_seqlens=None, silu=F
     if st != 0:
         raise KDAError(st, "kda_short_conv")
     return y, final_state
+
+
+def backward(q, k, v, beta, log_alpha, d_o, initial_state=None, d_final_state=None, cu_seqlens=None,
+             checkpoints=None):
+    """Gradients of the recurrence: (dq, dk, dv, dbeta, dlog_alpha,
+    d_initial_state), all float32, from d_o [B,T,H,d_v] fp32 (and
+    d_final_state fp32 [N,H,d_k,d_v] or None).  The states are recomputed
+    from ``checkpoints`` (the state entering every 16-token chunk); when None
+    they are produced here by a chunked prefill with chunk size 16."""
+    dev = _check_dev(q, k, v, beta, log_alpha, d_o, initial_state, d_final_state, cu_seqlens, checkpoints)
+    if not (q.dtype == k.dtype == v.dtype == beta.dtype == log_alpha.dtype):
+        raise TypeError("q, k, v, beta, log_alpha must share one dtype")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if d_o.dtype != torch.float32 or tuple(d_o.shape) != (B, T, H, dv):
+        raise ValueError(f"d_o must be float32 [{B},{T},{H},{dv}]")
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if checkpoints is None:
+        _, _, checkpoints = prefill(q, k, v, beta, log_alpha, initial_state=initial_state,
+                                    output_final_state=False, cu_seqlens=cu_seqlens, chunk_size=16,
+                                    chunk_states=True)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dq=torch.empty((B, T, H, dk), **f32), dk=torch.empty((B, T, H, dk), **f32),
+               dv=torch.empty((B, T, H, dv), **f32), dbeta=torch.empty((B, T, H), **f32),
+               dlog_alpha=torch.empty((B, T, H, dk), **f32), d_initial_state=torch.empty((N, H, dk, dv), **f32))
+    a = BackwardArgs()
+    a.B, a.T, a.H, a.d_k, a.d_v, a.num_seqs, a.in_dtype = B, T, H, dk, dv, N, _dt(q.dtype)
+    a.q, a.k, a.v, a.beta, a.log_alpha = (_ptr(x) for x in (q, k, v, beta, log_alpha))
+    a.cu_seqlens, a.checkpoints, a.d_o, a.d_final_state = (_ptr(cu_seqlens), _ptr(checkpoints), _ptr(d_o),
+                                                           _ptr(d_final_state))
+    for name, t in out.items():
+        setattr(a, name, _ptr(t))
+    L = lib()
+    need = int(L.kda_backward_workspace_bytes(ctypes.byref(a)))
+    if need == 0:
+        raise KDAError(L.kda_backward(ctypes.byref(a), None), "kda_backward")
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    a.workspace, a.workspace_bytes = _ptr(ws), need
+    st = L.kda_backward(ctypes.byref(a), _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_backward")
+    return out["dq"], out["dk"], out["dv"], out["dbeta"], out["dlog_alpha"], out["d_initial_state"]

@@ -188,4 +188,68 @@ kda_status kda_short_conv(const kda_conv_args *a, void *hip_stream) {
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+namespace {
+// backward: the checks that do not need the workspace
+kda_status check_backward(const kda_backward_args *a, bool need_ptrs) {
+    if (!a) return KDA_ERR_NULL_ARG;
+    if (a->B < 1 || a->T < 0 || a->H < 1 || a->num_seqs < 0) return KDA_ERR_BAD_SHAPE;
+    if (!dim_ok(a->d_k) || !dim_ok(a->d_v)) return (a->d_k < 1 || a->d_v < 1) ? KDA_ERR_BAD_SHAPE : KDA_ERR_UNSUPPORTED;
+    if (!dtype_ok(a->in_dtype) || a->reserved != 0) return KDA_ERR_UNSUPPORTED;
+    if (a->cu_seqlens) {
+        if (a->B != 1 || a->num_seqs < 1) return KDA_ERR_BAD_SHAPE;
+    } else if (a->num_seqs != a->B) {
+        return KDA_ERR_BAD_SHAPE;
+    }
+    const int64_t tokens = static_cast<int64_t>(a->B) * a->T;
+    if (tokens * a->H * (a->d_k > a->d_v ? a->d_k : a->d_v) > (static_cast<int64_t>(1) << 31) - 1)
+        return KDA_ERR_UNSUPPORTED;
+    if (need_ptrs && tokens > 0 &&
+        (!a->q || !a->k || !a->v || !a->beta || !a->log_alpha || !a->checkpoints || !a->d_o || !a->dq ||
+         !a->dk || !a->dv || !a->dbeta || !a->dlog_alpha))
+        return KDA_ERR_NULL_ARG;
+    return KDA_OK;
+}
+constexpr int kCkpt = 16;  // checkpoint spacing of the backward
+int64_t backward_chunks(const kda_backward_args *a) {
+    const int64_t per_row = (static_cast<int64_t>(a->T) + kCkpt - 1) / kCkpt;
+    return a->cu_seqlens ? per_row + a->num_seqs : per_row * a->B;
+}
+}  // namespace
+
+size_t kda_backward_workspace_bytes(const kda_backward_args *a) {
+    if (check_backward(a, false) != KDA_OK) return 0;
+    return table_bytes(a->num_seqs, backward_chunks(a));
+}
+
+kda_status kda_backward(const kda_backward_args *a, void *hip_stream) {
+    kda_status st = check_backward(a, true);
+    if (st != KDA_OK) return st;
+    if (!a->workspace) return KDA_ERR_NULL_ARG;
+    if (reinterpret_cast<uintptr_t>(a->workspace) % kAlign) return KDA_ERR_BAD_SHAPE;
+    if (a->workspace_bytes < kda_backward_workspace_bytes(a)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (a->num_seqs == 0) return KDA_OK;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    char *ws = static_cast<char *>(a->workspace);
+    // the chunk table of 16-token chunks (validates cu_seqlens on the device)
+    PrefillParams tp{};
+    tp.cu_seqlens = a->cu_seqlens;
+    tp.status = reinterpret_cast<int32_t *>(ws);
+    tp.chunk_off = reinterpret_cast<int32_t *>(ws + kAlign);
+    tp.chunk_info = reinterpret_cast<const int4 *>(ws + kAlign + chunk_off_bytes(a->num_seqs));
+    tp.B = a->B; tp.T = a->T; tp.H = a->H; tp.dk = a->d_k; tp.dv = a->d_v;
+    tp.N = a->num_seqs; tp.C = kCkpt;
+    tp.n_chunks_bound = static_cast<int32_t>(backward_chunks(a));
+    hipError_t e = launch_chunk_table(tp, s);
+    if (e != hipSuccess) return KDA_ERR_HIP;
+    BackwardParams p{};
+    p.q = a->q; p.k = a->k; p.v = a->v; p.beta = a->beta; p.log_alpha = a->log_alpha;
+    p.d_o = a->d_o; p.d_final = a->d_final_state; p.checkpoints = a->checkpoints;
+    p.gq = a->dq; p.gk = a->dk; p.gv = a->dv; p.gbeta = a->dbeta; p.gg = a->dlog_alpha;
+    p.d_initial = a->d_initial_state;
+    p.cu_seqlens = a->cu_seqlens; p.chunk_off = tp.chunk_off; p.status = tp.status;
+    p.B = a->B; p.T = a->T; p.H = a->H; p.dk = a->d_k; p.dv = a->d_v; p.N = a->num_seqs;
+    e = launch_backward(p, a->in_dtype, s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // extern "C"

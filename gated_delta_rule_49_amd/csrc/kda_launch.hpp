@@ -41,6 +41,21 @@ struct ConvParams {
 };
 hipError_t launch_short_conv(const ConvParams &p, int in_dtype, int out_dtype, hipStream_t s);
 
+// backward pass (validated arguments)
+struct BackwardParams {
+    const void *q, *k, *v, *beta, *log_alpha;  // [B, T, H, d] / [B, T, H]
+    const float *d_o;                          // [B, T, H, dv]
+    const float *d_final;                      // nullable [N, H, dk, dv]
+    const float *checkpoints;                  // [chunks of 16, H, dk, dv]
+    float *gq, *gk, *gv, *gbeta, *gg;          // fp32 gradients of q, k, v, beta, log alpha
+    float *d_initial;                          // nullable [N, H, dk, dv]
+    const int32_t *cu_seqlens;                 // nullable
+    const int32_t *chunk_off;                  // device [N + 1], 16-token chunks (workspace)
+    const int32_t *status;                     // device, workspace word: 0 = inputs valid
+    int32_t B, T, H, dk, dv, N;
+};
+hipError_t launch_backward(const BackwardParams &p, int in_dtype, hipStream_t s);
+
 // m tokens per sequence; state_out and token_states nullable, state_out may
 // alias state_in
 hipError_t launch_decode(int B, int H, int m, int dk, int dv, int in_dtype, int out_dtype, uint32_t prologue,

@@ -44,7 +44,8 @@ def test_abi_version_and_status_strings(L):
 
 @pytest.mark.parametrize("cname,cls", [("kda_prefill_args", kda.PrefillArgs),
                                        ("kda_decode_args", kda.DecodeArgs),
-                                       ("kda_conv_args", kda.ConvArgs)])
+                                       ("kda_conv_args", kda.ConvArgs),
+                                       ("kda_backward_args", kda.BackwardArgs)])
 def test_struct_layout_matches_header(tmp_path, cname, cls):
     """ctypes mirror == the C compiler's layout of the argument structs."""
     fields = [f for f, _ in cls._fields_]
@@ -171,6 +172,33 @@ def conv_args(**over):
 ])
 def test_short_conv_host_validation(L, over, status):
     assert L.kda_short_conv(ctypes.byref(conv_args(**over)), None) == status
+
+
+def backward_args(**over):
+    a = kda.BackwardArgs()
+    a.B, a.T, a.H, a.d_k, a.d_v, a.num_seqs, a.in_dtype = 1, 64, 2, 128, 128, 1, 1
+    for f in ("q", "k", "v", "beta", "log_alpha", "checkpoints", "d_o", "dq", "dk", "dv", "dbeta",
+              "dlog_alpha", "workspace"):
+        setattr(a, f, FAKE)
+    for key, val in over.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(checkpoints=None), 1), (dict(d_o=None), 1), (dict(dlog_alpha=None), 1), (dict(workspace=None), 1),
+    (dict(H=0), 2), (dict(num_seqs=2), 2), (dict(d_v=0), 2),
+    (dict(d_k=96), 3), (dict(in_dtype=3), 3), (dict(reserved=1), 3),
+    (dict(workspace_bytes=1), 4),
+])
+def test_backward_host_validation(L, over, status):
+    assert L.kda_backward(ctypes.byref(backward_args(**over)), None) == status
+
+
+def test_backward_workspace_query(L):
+    a = backward_args()
+    assert L.kda_backward_workspace_bytes(ctypes.byref(a)) > 0
+    assert L.kda_backward_workspace_bytes(None) == 0
 
 
 def test_decode_empty_batch_is_noop(L):
