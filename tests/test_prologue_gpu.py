@@ -122,3 +122,52 @@ def test_decode_each_stage(flags, dtype):
     e = dict(o=err(o, o_ref), S=err(S1, S_ref))
     report(f"decode prologue flags={flags} {dtype}", **e)
     assert max(e.values()) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_multi_token_decode_with_prologue(dtype):
+    """4 tokens per sequence in one launch from pre-activations."""
+    x = synth.make_preact(70, 5, 4, 3, 128, 128, dtype, state_std=0.02)
+    dt = tdtype(dtype)
+    args = [torch.from_numpy(a).cuda().to(dt) for a in (x.q, x.k, x.v, x.beta, x.log_alpha)]
+    S = torch.from_numpy(x.initial_state).cuda()
+    o, fin, ts = kda.decode(*args, S, prologue=kda.PROLOGUE_ALL, token_states=True)
+    o_ref, S_ref, cs = native.prefill(x.q, x.k, x.v, x.beta, x.log_alpha, initial_state=x.initial_state,
+                                      chunk=1, want_chunk_states=True, prologue_flags=7)
+    after = np.concatenate([cs.reshape(5, 4, 3, 128, 128)[:, 1:], S_ref[:, None]], axis=1)
+    e = dict(o=err(o, o_ref), S=err(fin, S_ref), tokens=err(ts, after))
+    report(f"multi-token decode + prologue {dtype}", **e)
+    assert max(e.values()) <= TOL[dtype]
+
+
+def test_sublayer_conv_then_fused_prefill():
+    """The stages composed as the sublayer runs them: a width-4 causal
+    convolution of q, k and v (with states), then the prefill with every
+    prologue stage fused, against the oracle's convolution and recurrence."""
+    B, T, H, d, W = 1, 200, 4, 128, 4
+    x = synth.make_preact(71, B, T, H, d, d, "bf16", chunk=64, state_std=0.02)
+    rng = np.random.default_rng(72)
+    ws = [(rng.standard_normal((H * d, W)) / 2).astype(np.float32) for _ in range(3)]
+    cs = [rng.standard_normal((1, H * d, W - 1)).astype(np.float32) for _ in range(3)]
+    conv_gpu, conv_ref = [], []
+    for a, w, s0 in zip((x.q, x.k, x.v), ws, cs):
+        y, _ = kda.short_conv(torch.from_numpy(a.reshape(B, T, H * d)).cuda().to(torch.bfloat16),
+                              torch.from_numpy(w).cuda(), initial_state=torch.from_numpy(s0).cuda())
+        conv_gpu.append(y.reshape(B, T, H, d))
+        yr, _ = R.short_conv(a.reshape(B, T, H * d), w, initial_state=s0)
+        conv_ref.append(yr.reshape(B, T, H, d))
+    yq, yk, yv = conv_gpu
+    for g, r in zip(conv_gpu, conv_ref):  # bf16 outputs: within their own rounding
+        gv = g.float().cpu().numpy()
+        assert np.all(np.abs(gv - r) <= 2.0 ** -8 * np.abs(r) + 1e-6 * np.sqrt(np.mean(r ** 2)))
+    b, la = (torch.from_numpy(a).cuda().to(torch.bfloat16) for a in (x.beta, x.log_alpha))
+    init = torch.from_numpy(x.initial_state).cuda()
+    o, S = kda.prefill(yq, yk, yv, b, la, initial_state=init, prologue=kda.PROLOGUE_ALL)
+    # oracle on the GPU's bf16 convolution outputs (rounding at the bf16
+    # boundary is shared), from the same pre-activations
+    gq, gk, gv = (t.float().cpu().numpy() for t in conv_gpu)
+    o_ref, S_ref, _ = native.prefill(gq, gk, gv, x.beta, x.log_alpha, initial_state=x.initial_state,
+                                     prologue_flags=7)
+    e = dict(o=err(o, o_ref), S=err(S, S_ref))
+    report("sublayer conv -> fused prefill", **e)
+    assert max(e.values()) <= TOL["bf16"]
