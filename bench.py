@@ -90,6 +90,26 @@ def measured_traffic(key):
     return c["fetch_kib"] * 1024 * rec["fetch_scale"] + c["write_kib"] * 1024 * rec["write_scale"]
 
 
+def measured_counter(kernel, counter):
+    """Per-dispatch value of a rocprofv3 counter for `kernel` recorded in
+    profiles/traffic.json ("counters"), or None if missing or taken on
+    different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sources_sha") != kernel_sources_sha():
+        return None
+    return rec.get("counters", {}).get(kernel, {}).get(counter)
+
+
+# Vector-ALU issue peak of MI355X: 256 CUs x 4 SIMDs, one wave64 VALU
+# instruction per SIMD every 4 cycles (16 lanes), at 2.4 GHz, counted in
+# lane-operations (64 per wave instruction).
+VALU_PEAK_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+
 def summarize(root):
     """Per-kernel means of rocprofv3 --output-format csv results under root."""
     for f in glob.glob(os.path.join(root, "**", "*kernel_stats.csv"), recursive=True):
@@ -119,7 +139,11 @@ def summarize(root):
             print(f"- {k}: {shown}")
     acc = {}
     for f in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
-        for row in csv.DictReader(open(f)):
+        rows = list(csv.DictReader(open(f)))
+        key = "Dispatch_Id" if rows and "Dispatch_Id" in rows[0] else None
+        if key:
+            rows.sort(key=lambda r: int(r[key]))
+        for row in rows:
             name = row["Kernel_Name"]
             if "kda::" not in name and "copyBuffer" not in name:
                 continue
@@ -129,6 +153,10 @@ def summarize(root):
         print("| kernel | counter | dispatches | mean |\n|---|---|---|---|")
         for (k, c), v in sorted(acc.items()):
             print(f"| {k} | {c} | {len(v)} | {sum(v) / len(v):.6g} |")
+        print("# counter values per dispatch in launch order (kda kernels, first 12)")
+        for (k, c), v in sorted(acc.items()):
+            if "kda::" in k:
+                print(f"- {k} {c}: " + " ".join(f"{x:.6g}" for x in v[:12]))
 
 
 def copy_calibration():
@@ -236,6 +264,20 @@ def cpu_baseline_decode(D):
     dt = time.perf_counter() - t
     return dict(value=B / dt, unit="seq-steps/s", cores=native.max_threads(), kind="oracle",
                 sample=f"one step of all {B} sequences x {D['q'].shape[2]} heads ({dt:.2f} s)")
+
+
+def intra_valu(intra_ms):
+    """The intra-chunk kernel's own roofline: it is bound by vector-ALU issue.
+    VALU wave-instructions per call (rocprofv3 SQ_INSTS_VALU, recorded in
+    profiles/traffic.json) x 64 lanes / the live kernel time, against the
+    issue peak; null when the record does not match the sources."""
+    n = measured_counter("intra_kernel<64,128>", "SQ_INSTS_VALU")
+    if n is None:
+        return None
+    achieved = n * 64 / (intra_ms * 1e-3) / 1e12
+    return {"bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TLANEOPS, "unit": "T lane-op/s",
+            "frac": achieved / VALU_PEAK_TLANEOPS, "valu_wave_insts": n,
+            "peak_basis": "256 CU x 4 SIMD x 16 lanes x 2.4 GHz (one wave64 instruction per 4 cycles)"}
 
 
 def _decode_into(kda, mt, state, om, tsb):
@@ -535,7 +577,8 @@ def main():
                      "algorithmic_bytes": pbytes, "avg_ms": pre,
                      "kernels_ms": {"intra_kernel": intra, "scan_kernel": scan},
                      "useful_mfma_tflops": useful_tf,
-                     "useful_mfma_frac": useful_tf / BF16_PEAK_TFLOPS},
+                     "useful_mfma_frac": useful_tf / BF16_PEAK_TFLOPS,
+                     "intra_valu": intra_valu(intra)},
         "decode": {"value": Bd / (dec * 1e-3), "unit": "seq-steps/s", "avg_ms": dec,
                    "timing": "64 consecutive steps of the decode trajectory, one HIP event pair",
                    "avg_ms_right_after_prefill": dec_in_step,
