@@ -20,7 +20,7 @@ Prints ONE JSON line:
   short_conv   the width-4 causal convolution over a q-shaped prefill input
                and over one decode token per sequence (state rolled in place)
   backward     gradients over the T=4096, H=16 prefill shape: the prefill that
-               writes 16-token checkpoints plus the backward kernel
+               writes the chunk checkpoints plus the chunked backward
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -503,36 +503,38 @@ def main():
     del dx, dst, dy, cw
 
     # Backward over the prefill workload's shape (B=1, T=4096, H=16, d=128,
-    # bf16): the chunked prefill writing 16-token checkpoints, then the
-    # backward kernel; d_o ~ N(0, 1) fp32.
+    # bf16): the chunked prefill writing the chunk checkpoints (chunk 64),
+    # then the chunked backward (prep, reverse state-gradient scan, per-chunk
+    # gradients); d_o ~ N(0, 1) fp32.
     print("[bench] backward", file=sys.stderr, flush=True)
     BX = synth.workload(2, device=dev)
     bt = lambda a: torch.from_numpy(a).to(dev, torch.bfloat16)  # noqa: E731
     bq, bk, bv, bb, bla = (bt(a) for a in (BX.q, BX.k, BX.v, BX.beta, BX.log_alpha))
     bdo = torch.randn(bv.shape, generator=_gen(9, dev), device=dev)
     for _ in range(2):
-        _, _, ck = kda.prefill(bq, bk, bv, bb, bla, output_final_state=False, chunk_size=16, chunk_states=True)
-        kda.backward(bq, bk, bv, bb, bla, bdo, checkpoints=ck)
+        _, _, ck = kda.prefill(bq, bk, bv, bb, bla, output_final_state=False, chunk_size=64, chunk_states=True)
+        kda.backward(bq, bk, bv, bb, bla, bdo, checkpoints=ck, chunk_size=64)
     e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
     e0.record()
-    _, _, ck = kda.prefill(bq, bk, bv, bb, bla, output_final_state=False, chunk_size=16, chunk_states=True)
+    _, _, ck = kda.prefill(bq, bk, bv, bb, bla, output_final_state=False, chunk_size=64, chunk_states=True)
     e1.record()
-    kda.backward(bq, bk, bv, bb, bla, bdo, checkpoints=ck)
+    kda.backward(bq, bk, bv, bb, bla, bdo, checkpoints=ck, chunk_size=64)
     e2.record()
     torch.cuda.synchronize()
     fwd_ms, bwd_ms = e0.elapsed_time(e1), e1.elapsed_time(e2)
     bT, bH = BX.T, BX.H
-    # algorithmic bytes of the backward kernel per token-head: q, k, v, log
-    # alpha (bf16) + beta + d_o (fp32) read, dq, dk, dv, dlog alpha (fp32) and
-    # dbeta written, plus the 16-token checkpoints read once (d^2 * 4 / 16)
-    bwd_unit = 4 * 128 * 2 + 2 + 128 * 4 + 4 * 128 * 4 + 4 + 128 * 128 * 4 // 16
+    # algorithmic bytes of the backward per token-head: q, k, v, log alpha
+    # (bf16) + beta + d_o (fp32) read, dq, dk, dv, dlog alpha (fp32) and dbeta
+    # written, plus the chunk checkpoints read once (d^2 * 4 / 64)
+    bwd_unit = 4 * 128 * 2 + 2 + 128 * 4 + 4 * 128 * 4 + 4 + 128 * 128 * 4 // 64
     bwd_bytes = bT * bH * bwd_unit
     backward = {"value": bT / ((fwd_ms + bwd_ms) * 1e-3), "unit": "tokens/s",
                 "workload": f"prefill shape B=1 T={bT} H={bH} d=128 bf16",
-                "checkpoint_prefill_ms": fwd_ms, "backward_kernel_ms": bwd_ms,
-                "roofline": {"bound": "latency", "achieved": bwd_bytes / (bwd_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                "checkpoint_prefill_ms": fwd_ms, "backward_ms": bwd_ms,
+                "roofline": {"bound": "hbm", "achieved": bwd_bytes / (bwd_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": bwd_bytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                             "algorithmic_bytes": bwd_bytes, "kernel": "backward_kernel<128, bf16>"}}
+                             "algorithmic_bytes": bwd_bytes,
+                             "kernel": "cb_prep_kernel + cb_scan_kernel + cb_grad_kernel (d=128, bf16)"}}
     del bq, bk, bv, bb, bla, bdo, ck, BX
 
     rng = range(args.warmup, n_ev)

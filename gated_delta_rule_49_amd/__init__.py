@@ -99,7 +99,7 @@ class BackwardArgs(ctypes.Structure):
     _fields_ = [
         ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
         ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
-        ("in_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32), ("chunk_size", ctypes.c_int32),
         ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
         ("beta", ctypes.c_void_p), ("log_alpha", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
         ("checkpoints", ctypes.c_void_p), ("d_o", ctypes.c_void_p), ("d_final_state", ctypes.c_void_p),
@@ -389,12 +389,13 @@ def short_conv(x, weight, initial_state=None, bias=None, cu_seqlens=None, silu=F
 
 
 def backward(q, k, v, beta, log_alpha, d_o, initial_state=None, d_final_state=None, cu_seqlens=None,
-             checkpoints=None):
+             checkpoints=None, chunk_size=None):
     """Gradients of the recurrence: (dq, dk, dv, dbeta, dlog_alpha,
     d_initial_state), all float32, from d_o [B,T,H,d_v] fp32 (and
-    d_final_state fp32 [N,H,d_k,d_v] or None).  The states are recomputed
-    from ``checkpoints`` (the state entering every 16-token chunk); when None
-    they are produced here by a chunked prefill with chunk size 16."""
+    d_final_state fp32 [N,H,d_k,d_v] or None).  ``checkpoints`` are the
+    states entering every chunk of ``chunk_size`` tokens (default 64 for
+    bf16 inputs, 16 for fp32); when None they are produced here by a chunked
+    prefill with that chunk size."""
     dev = _check_dev(q, k, v, beta, log_alpha, d_o, initial_state, d_final_state, cu_seqlens, checkpoints)
     if not (q.dtype == k.dtype == v.dtype == beta.dtype == log_alpha.dtype):
         raise TypeError("q, k, v, beta, log_alpha must share one dtype")
@@ -403,9 +404,11 @@ def backward(q, k, v, beta, log_alpha, d_o, initial_state=None, d_final_state=No
     if d_o.dtype != torch.float32 or tuple(d_o.shape) != (B, T, H, dv):
         raise ValueError(f"d_o must be float32 [{B},{T},{H},{dv}]")
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if chunk_size is None:
+        chunk_size = 64 if q.dtype == torch.bfloat16 else 16
     if checkpoints is None:
         _, _, checkpoints = prefill(q, k, v, beta, log_alpha, initial_state=initial_state,
-                                    output_final_state=False, cu_seqlens=cu_seqlens, chunk_size=16,
+                                    output_final_state=False, cu_seqlens=cu_seqlens, chunk_size=chunk_size,
                                     chunk_states=True)
     f32 = dict(dtype=torch.float32, device=dev)
     out = dict(dq=torch.empty((B, T, H, dk), **f32), dk=torch.empty((B, T, H, dk), **f32),
@@ -413,6 +416,7 @@ def backward(q, k, v, beta, log_alpha, d_o, initial_state=None, d_final_state=No
                dlog_alpha=torch.empty((B, T, H, dk), **f32), d_initial_state=torch.empty((N, H, dk, dv), **f32))
     a = BackwardArgs()
     a.B, a.T, a.H, a.d_k, a.d_v, a.num_seqs, a.in_dtype = B, T, H, dk, dv, N, _dt(q.dtype)
+    a.chunk_size = chunk_size
     a.q, a.k, a.v, a.beta, a.log_alpha = (_ptr(x) for x in (q, k, v, beta, log_alpha))
     a.cu_seqlens, a.checkpoints, a.d_o, a.d_final_state = (_ptr(cu_seqlens), _ptr(checkpoints), _ptr(d_o),
                                                            _ptr(d_final_state))

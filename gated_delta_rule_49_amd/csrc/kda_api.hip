@@ -194,7 +194,11 @@ kda_status check_backward(const kda_backward_args *a, bool need_ptrs) {
     if (!a) return KDA_ERR_NULL_ARG;
     if (a->B < 1 || a->T < 0 || a->H < 1 || a->num_seqs < 0) return KDA_ERR_BAD_SHAPE;
     if (!dim_ok(a->d_k) || !dim_ok(a->d_v)) return (a->d_k < 1 || a->d_v < 1) ? KDA_ERR_BAD_SHAPE : KDA_ERR_UNSUPPORTED;
-    if (!dtype_ok(a->in_dtype) || a->reserved != 0) return KDA_ERR_UNSUPPORTED;
+    if (!dtype_ok(a->in_dtype)) return KDA_ERR_UNSUPPORTED;
+    if (a->in_dtype == KDA_BF16 ? !chunk_ok(a->chunk_size) : a->chunk_size != 16) {
+        if (a->chunk_size < 1) return KDA_ERR_BAD_SHAPE;
+        return KDA_ERR_UNSUPPORTED;
+    }
     if (a->cu_seqlens) {
         if (a->B != 1 || a->num_seqs < 1) return KDA_ERR_BAD_SHAPE;
     } else if (a->num_seqs != a->B) {
@@ -209,16 +213,21 @@ kda_status check_backward(const kda_backward_args *a, bool need_ptrs) {
         return KDA_ERR_NULL_ARG;
     return KDA_OK;
 }
-constexpr int kCkpt = 16;  // checkpoint spacing of the backward
 int64_t backward_chunks(const kda_backward_args *a) {
-    const int64_t per_row = (static_cast<int64_t>(a->T) + kCkpt - 1) / kCkpt;
+    const int64_t per_row = (static_cast<int64_t>(a->T) + a->chunk_size - 1) / a->chunk_size;
     return a->cu_seqlens ? per_row + a->num_seqs : per_row * a->B;
+}
+// bf16: chunk table, the per-(chunk, head) blocks, the dS entering every chunk
+size_t backward_blocks_bytes(const kda_backward_args *a) {
+    if (a->in_dtype != KDA_BF16) return 0;
+    const size_t items = static_cast<size_t>(backward_chunks(a)) * a->H;
+    return align_up(items * cb_block_bytes(a->d_k)) + align_up(items * a->d_k * a->d_v * sizeof(float));
 }
 }  // namespace
 
 size_t kda_backward_workspace_bytes(const kda_backward_args *a) {
     if (check_backward(a, false) != KDA_OK) return 0;
-    return table_bytes(a->num_seqs, backward_chunks(a));
+    return table_bytes(a->num_seqs, backward_chunks(a)) + backward_blocks_bytes(a);
 }
 
 kda_status kda_backward(const kda_backward_args *a, void *hip_stream) {
@@ -237,10 +246,28 @@ kda_status kda_backward(const kda_backward_args *a, void *hip_stream) {
     tp.chunk_off = reinterpret_cast<int32_t *>(ws + kAlign);
     tp.chunk_info = reinterpret_cast<const int4 *>(ws + kAlign + chunk_off_bytes(a->num_seqs));
     tp.B = a->B; tp.T = a->T; tp.H = a->H; tp.dk = a->d_k; tp.dv = a->d_v;
-    tp.N = a->num_seqs; tp.C = kCkpt;
+    tp.N = a->num_seqs; tp.C = a->chunk_size;
     tp.n_chunks_bound = static_cast<int32_t>(backward_chunks(a));
     hipError_t e = launch_chunk_table(tp, s);
     if (e != hipSuccess) return KDA_ERR_HIP;
+    if (a->in_dtype == KDA_BF16) {
+        char *wb = ws + table_bytes(a->num_seqs, backward_chunks(a));
+        const size_t items = static_cast<size_t>(backward_chunks(a)) * a->H;
+        CbParams c{};
+        c.q = a->q; c.k = a->k; c.v = a->v; c.beta = a->beta; c.log_alpha = a->log_alpha;
+        c.d_o = a->d_o; c.d_final = a->d_final_state; c.checkpoints = a->checkpoints;
+        c.blocks = reinterpret_cast<float *>(wb);
+        c.dS_right = reinterpret_cast<float *>(wb + align_up(items * cb_block_bytes(a->d_k)));
+        c.gq = a->dq; c.gk = a->dk; c.gv = a->dv; c.gbeta = a->dbeta; c.gg = a->dlog_alpha;
+        c.d_initial = a->d_initial_state;
+        c.chunk_off = tp.chunk_off; c.chunk_info = tp.chunk_info; c.status = tp.status;
+        c.N = a->num_seqs; c.H = a->H; c.dk = a->d_k; c.dv = a->d_v;
+        // the chunk count is only known on the device: the per-chunk kernels
+        // are launched over the bound and items beyond the table's total
+        // return at once (their chunk_info is never read)
+        e = launch_backward_chunked(c, static_cast<int>(items), s);
+        return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
     BackwardParams p{};
     p.q = a->q; p.k = a->k; p.v = a->v; p.beta = a->beta; p.log_alpha = a->log_alpha;
     p.d_o = a->d_o; p.d_final = a->d_final_state; p.checkpoints = a->checkpoints;

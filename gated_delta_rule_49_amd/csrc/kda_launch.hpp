@@ -56,6 +56,25 @@ struct BackwardParams {
 };
 hipError_t launch_backward(const BackwardParams &p, int in_dtype, hipStream_t s);
 
+// chunked backward (bf16 inputs): per-(chunk, head) blocks and the dS
+// entering every chunk from the right live in the workspace
+struct CbParams {
+    const void *q, *k, *v, *beta, *log_alpha;  // bf16 [B, T, H, d] / [B, T, H]
+    const float *d_o;                          // [B, T, H, dv]
+    const float *d_final;                      // nullable [N, H, dk, dv]
+    const float *checkpoints;                  // [chunks, H, dk, dv] state entering each chunk
+    float *blocks;                             // [chunks, H] prep blocks (workspace)
+    float *dS_right;                           // [chunks, H, dk, dv] (workspace)
+    float *gq, *gk, *gv, *gbeta, *gg;          // fp32 gradients
+    float *d_initial;                          // nullable [N, H, dk, dv]
+    const int32_t *chunk_off;                  // [N + 1]
+    const int4 *chunk_info;                    // [chunks]
+    const int32_t *status;
+    int32_t N, H, dk, dv;
+};
+size_t cb_block_bytes(int dk);
+hipError_t launch_backward_chunked(const CbParams &p, int n_items, hipStream_t s);
+
 // m tokens per sequence; state_out and token_states nullable, state_out may
 // alias state_in
 hipError_t launch_decode(int B, int H, int m, int dk, int dv, int in_dtype, int out_dtype, uint32_t prologue,

@@ -28,8 +28,8 @@
  *
  *   kda_short_conv       the short causal convolution that precedes the
  *                        recurrence in the sublayer, with its rolling state.
- *   kda_backward         gradients of the recurrence (reverse mode, states
- *                        recomputed from 16-token checkpoints).
+ *   kda_backward         gradients of the recurrence (reverse mode through the
+ *                        chunked form, from the prefill's chunk checkpoints).
  *
  * Both recurrence families can fuse the stages that run just before the
  * recurrence (KDA_PROLOGUE_* flags below).
@@ -284,15 +284,21 @@ kda_status kda_short_conv(const kda_conv_args *a, void *hip_stream);
  * from the gradients of o and of the final state.  The pages call the affine
  * composition the argument for parallel training (course index, module
  * list, the Module 04 entry) but derive no backward; this is reverse-mode
- * differentiation of the token operations, last token first, in fp32.  The
- * states it needs are recomputed from checkpoints: the state entering every
- * 16-token chunk, exactly what kda_prefill_chunked writes to chunk_states
- * when called with chunk_size 16 on the same inputs and initial state.
+ * differentiation, in fp32, of the chunked form (bf16 inputs: every chunk's
+ * gradients from its structured matrices, the chunks coupled by a reverse
+ * scan of the state gradient) or of the token operations (fp32 inputs, last
+ * token first, states recomputed token by token).  Both start from
+ * checkpoints: the state entering every chunk of chunk_size tokens, exactly
+ * what kda_prefill_chunked writes to chunk_states when called with that
+ * chunk_size on the same inputs and initial state.
+ *
+ *   chunk_size   the checkpoint spacing: 16, 32 or 64 for bf16 inputs (64
+ *                recommended), 16 for fp32 inputs.
  *
  *   q, k, v, beta, log_alpha, cu_seqlens, B, T, H, d_k, d_v, num_seqs,
  *   in_dtype     as for kda_prefill_chunked (no prologue: the gradients are
  *                with respect to the recurrence's own inputs)
- *   checkpoints  DEVICE fp32 [sum_n ceil(len_n / 16), H, d_k, d_v]
+ *   checkpoints  DEVICE fp32 [sum_n ceil(len_n / chunk_size), H, d_k, d_v]
  *   d_o          DEVICE fp32 [B, T, H, d_v]
  *   d_final_state DEVICE fp32 [num_seqs, H, d_k, d_v], NULL = zeros
  *   dq, dk, dlog_alpha  DEVICE fp32 [B, T, H, d_k]    (written)
@@ -300,15 +306,16 @@ kda_status kda_short_conv(const kda_conv_args *a, void *hip_stream);
  *   dbeta        DEVICE fp32 [B, T, H]                 (written)
  *   d_initial_state DEVICE fp32 [num_seqs, H, d_k, d_v], NULL = not written
  *   workspace    DEVICE, >= kda_backward_workspace_bytes(args), 256-aligned
- * dq, dk, dlog_alpha and dbeta are sums over the state's column tiles taken
- * with fp32 atomics: their rounding may differ from run to run.
+ * With fp32 inputs dq, dk, dlog_alpha and dbeta are sums over the state's
+ * column tiles taken with fp32 atomics: their rounding may differ from run to
+ * run; the bf16 path is deterministic.
  * Supported: d_k, d_v in {16, 32, 64, 128}; in_dtype f32 or bf16.
  */
 typedef struct kda_backward_args {
     int32_t B, T, H, d_k, d_v;
     int32_t num_seqs;
     int32_t in_dtype;              /* kda_dtype */
-    int32_t reserved;              /* must be 0 */
+    int32_t chunk_size;            /* checkpoint spacing */
     const void *q, *k, *v, *beta, *log_alpha;
     const int32_t *cu_seqlens;
     const float *checkpoints;

@@ -176,7 +176,7 @@ def test_short_conv_host_validation(L, over, status):
 
 def backward_args(**over):
     a = kda.BackwardArgs()
-    a.B, a.T, a.H, a.d_k, a.d_v, a.num_seqs, a.in_dtype = 1, 64, 2, 128, 128, 1, 1
+    a.B, a.T, a.H, a.d_k, a.d_v, a.num_seqs, a.in_dtype, a.chunk_size = 1, 64, 2, 128, 128, 1, 1, 64
     for f in ("q", "k", "v", "beta", "log_alpha", "checkpoints", "d_o", "dq", "dk", "dv", "dbeta",
               "dlog_alpha", "workspace"):
         setattr(a, f, FAKE)
@@ -188,7 +188,8 @@ def backward_args(**over):
 @pytest.mark.parametrize("over,status", [
     (dict(checkpoints=None), 1), (dict(d_o=None), 1), (dict(dlog_alpha=None), 1), (dict(workspace=None), 1),
     (dict(H=0), 2), (dict(num_seqs=2), 2), (dict(d_v=0), 2),
-    (dict(d_k=96), 3), (dict(in_dtype=3), 3), (dict(reserved=1), 3),
+    (dict(d_k=96), 3), (dict(in_dtype=3), 3), (dict(chunk_size=48), 3), (dict(chunk_size=0), 2),
+    (dict(in_dtype=0, chunk_size=64), 3),
     (dict(workspace_bytes=1), 4),
 ])
 def test_backward_host_validation(L, over, status):

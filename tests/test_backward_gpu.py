@@ -36,13 +36,14 @@ def oracle_grads(x, d_o, d_fin):
     return out
 
 
-def check(x, name, with_final=True, tol=None):
+def check(x, name, with_final=True, tol=None, chunk_size=None):
     rng = np.random.default_rng(len(name) + x.T)
     d_o = rng.standard_normal((x.B, x.T, x.H, x.d_v)).astype(np.float32)
     d_fin = rng.standard_normal((x.num_seqs, x.H, x.d_k, x.d_v)).astype(np.float32) if with_final else None
     q, k, v, b, la, init, cu = dev_tensors(x)
     got = kda.backward(q, k, v, b, la, torch.from_numpy(d_o).cuda(), initial_state=init,
-                       d_final_state=None if d_fin is None else torch.from_numpy(d_fin).cuda(), cu_seqlens=cu)
+                       d_final_state=None if d_fin is None else torch.from_numpy(d_fin).cuda(), cu_seqlens=cu,
+                       chunk_size=chunk_size)
     ref = oracle_grads(x, d_o, d_fin)
     e = {n: err(g, ref[n]) for n, g in zip(NAMES, got)}
     report(f"backward {name} T={x.T} H={x.H} d={x.d_k}x{x.d_v} {x.dtype}", **e)
@@ -105,3 +106,26 @@ def test_bf16_prefill_shape_heads_sampled():
             worst[n] = max(worst.get(n, 0.0), err(sl, ref))
     report("backward T=1024 H=16 d=128 bf16 heads 0,15", **worst)
     assert max(worst.values()) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_bf16_chunk_sizes_ragged(chunk):
+    """The chunked backward at every chunk size, ragged tail, random state."""
+    x = synth.make_uniform(440 + chunk, 2, 150, 2, 128, 128, "bf16", chunk=chunk, state_std=0.02)
+    check(x, f"bf16 chunked C={chunk}", chunk_size=chunk)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (16, 32), (32, 128)])
+def test_bf16_head_sizes(dk, dv):
+    x = synth.make_uniform(450 + dk + dv, 1, 100, 2, dk, dv, "bf16", chunk=64, state_std=0.05)
+    check(x, "bf16 chunked sizes")
+
+
+def test_bf16_slow_decay():
+    x = synth.slow_decay(460, 1, 300, 2, 128, 128, "bf16", chunk=64)
+    check(x, "bf16 chunked slow decay")
+
+
+def test_bf16_extreme_gates():
+    x = synth.make_long(461, 512, 2, 128, 128, "bf16")
+    check(x, "bf16 chunked extreme gates")
