@@ -236,10 +236,13 @@ kda_status kda_backward(const kda_backward_args *a, void *hip_stream) {
     if (!a->workspace) return KDA_ERR_NULL_ARG;
     if (reinterpret_cast<uintptr_t>(a->workspace) % kAlign) return KDA_ERR_BAD_SHAPE;
     if (a->workspace_bytes < kda_backward_workspace_bytes(a)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (a->in_dtype == KDA_BF16 &&
+        (reinterpret_cast<uintptr_t>(a->d_o) % 16 || reinterpret_cast<uintptr_t>(a->checkpoints) % 16))
+        return KDA_ERR_UNSUPPORTED;  // the chunked kernels read them as float4
     if (a->num_seqs == 0) return KDA_OK;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     char *ws = static_cast<char *>(a->workspace);
-    // the chunk table of 16-token chunks (validates cu_seqlens on the device)
+    // the chunk table of chunk_size-token chunks (validates cu_seqlens on the device)
     PrefillParams tp{};
     tp.cu_seqlens = a->cu_seqlens;
     tp.status = reinterpret_cast<int32_t *>(ws);

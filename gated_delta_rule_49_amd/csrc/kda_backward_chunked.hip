@@ -26,14 +26,15 @@ constexpr int CB_C = 64;  // maximum chunk length
 template <int DK>
 struct CbLay {
     static constexpr size_t G = 0;                       // [C][DK]  cumulative log decay
-    static constexpr size_t KT = G + CB_C * DK;          // [DK][C]  (k e^G)^T
+    static constexpr size_t KT = G + CB_C * DK;          // [C][DK]  k e^G
     static constexpr size_t QT = KT + CB_C * DK;         // [C][DK]  q e^G
-    static constexpr size_t KB = QT + CB_C * DK;         // [DK][C]  (k e^{G_L - G})^T
+    static constexpr size_t KB = QT + CB_C * DK;         // [C][DK]  k e^{G_L - G}
     static constexpr size_t W = KB + CB_C * DK;          // [C][DK]  T K~
     static constexpr size_t GH = W + CB_C * DK;          // [C][C]   k_r . k_i e^{..}, i < r
     static constexpr size_t P = GH + CB_C * CB_C;        // [C][C]   q_r . k_i e^{..}, i <= r
-    static constexpr size_t M = P + CB_C * CB_C;         // [C][C]   (I + A)^-1
-    static constexpr size_t MT = M + CB_C * CB_C;        // [C][C]   its transpose
+    static constexpr size_t PT = P + CB_C * CB_C;        // [C][C]   P^T
+    static constexpr size_t M = PT + CB_C * CB_C;        // [C][C]   (I + A)^-1
+    static constexpr size_t MT = M + CB_C * CB_C;        // [C][C]   M^T
     static constexpr size_t GAM = MT + CB_C * CB_C;      // [DK]     e^{G_L}
     static constexpr size_t BETA = GAM + DK;             // [C]
     static constexpr size_t FLOATS = (BETA + CB_C + 63) / 64 * 64;
@@ -91,14 +92,10 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
     // elementwise factors and the decay of the whole chunk
     for (int e = tid; e < CB_C * DK; e += 256) {
         const int r = e / DK, c = e % DK;
-        const float G = sG[r][c];
+        const float G = sG[r][c], E = __expf(G);
         blk[Y::G + e] = G;
-        blk[Y::QT + e] = sq[r][c] * __expf(G);
-    }
-    for (int e = tid; e < CB_C * DK; e += 256) {  // transposed: [channel][row]
-        const int c = e / CB_C, r = e % CB_C;
-        const float G = sG[r][c];
-        blk[Y::KT + e] = sk[r][c] * __expf(G);
+        blk[Y::KT + e] = sk[r][c] * E;
+        blk[Y::QT + e] = sq[r][c] * E;
         blk[Y::KB + e] = sk[r][c] * __expf(sG[CB_C - 1][c] - G);
     }
     for (int c = tid; c < DK; c += 256) blk[Y::GAM + c] = __expf(sG[CB_C - 1][c]);
@@ -134,6 +131,7 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
                 const bool in = r < L && i <= r;
                 blk[Y::GH + r * CB_C + i] = (in && i < r) ? gh[a][b2] : 0.f;
                 blk[Y::P + r * CB_C + i] = in ? pp[a][b2] : 0.f;
+                blk[Y::PT + i * CB_C + r] = in ? pp[a][b2] : 0.f;
                 sA[r][i] = (in && i < r) ? gh[a][b2] * sb[r] : 0.f;
             }
     }
@@ -144,22 +142,37 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
             sA[r][i] = 0.f;
             blk[Y::GH + e] = 0.f;
             blk[Y::P + e] = 0.f;
+            blk[Y::PT + i * CB_C + r] = 0.f;
         }
     }
     __syncthreads();
-    // M = (I + A)^-1 by forward substitution, row by row, in place over A:
-    // M[r, j] = [r == j] - sum_{j <= i < r} A[r, i] M[i, j]
-    for (int r = 0; r < CB_C; ++r) {
-        float val = 0.f;
-        if (tid < CB_C) {
-            const int j = tid;
-            val = (j == r) ? 1.f : 0.f;
-            for (int i = j; i < r; ++i) val -= sA[r][i] * sA[i][j];
+    // M = (I + A)^-1 by forward substitution,
+    //     M[r][j] = [r == j] - sum_{i < r} A[r][i] M[i][j]
+    // (M is lower triangular, so the terms i < j are zero by themselves).
+    // One wave: lane j keeps column j of M in registers and reads the rows
+    // of A as broadcasts; no barrier inside the recurrence.
+    if (tid < CB_C) {
+        float mc[CB_C];
+#pragma unroll
+        for (int r = 0; r < CB_C; ++r) {
+            float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+            for (int i = 0; i + 1 < r; i += 2) {
+                s0 += sA[r][i] * mc[i];
+                s1 += sA[r][i + 1] * mc[i + 1];
+            }
+            if (r & 1) s0 += sA[r][r - 1] * mc[r - 1];
+            mc[r] = (r == tid ? 1.f : 0.f) - (s0 + s1);
         }
-        __syncthreads();
-        if (tid < CB_C) sA[r][tid] = (tid <= r) ? val : 0.f;
-        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < CB_C; ++r) sA[r][tid] = mc[r];
     }
+    // K~ in place of k (k itself is no longer needed)
+    for (int e = tid; e < CB_C * DK; e += 256) {
+        const int r = e / DK, c = e % DK;
+        sk[r][c] *= __expf(sG[r][c]);
+    }
+    __syncthreads();
     for (int e = tid; e < CB_C * CB_C; e += 256) {
         blk[Y::M + e] = sA[e / CB_C][e % CB_C];
         blk[Y::MT + e] = sA[e % CB_C][e / CB_C];
@@ -168,7 +181,7 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
     for (int e = tid; e < CB_C * DK; e += 256) {
         const int r = e / DK, c = e % DK;
         float acc = 0.f;
-        for (int i = 0; i <= r; ++i) acc += sA[r][i] * sb[i] * sk[i][c] * __expf(sG[i][c]);
+        for (int i = 0; i <= r; ++i) acc += sA[r][i] * sb[i] * sk[i][c];
         blk[Y::W + e] = acc;
     }
 }
@@ -182,7 +195,7 @@ constexpr int CB_SCAN_BV = 8;
 template <int DK>
 struct CbScanLds {
     static constexpr int C = CB_C, BV = CB_SCAN_BV;
-    static constexpr int QT = 0, W = QT + C * DK, KB = W + C * DK, P = KB + C * DK;   // [C][DK] x2, [DK][C], [C][C]
+    static constexpr int QT = 0, W = QT + C * DK, KB = W + C * DK, P = KB + C * DK;   // [C][DK] x3, [C][C]
     static constexpr int DS = P + C * C;          // [DK][BV]
     static constexpr int DO = DS + DK * BV;       // [C][BV]
     static constexpr int YY = DO + C * BV;        // [C][BV]
@@ -243,7 +256,7 @@ __global__ void __launch_bounds__(256) cb_scan_kernel(CbParams p) {
             float acc = 0.f;
             for (int i = r; i < C; ++i) acc += sP[i * C + r] * sdO[i * BV + j];
 #pragma unroll 8
-            for (int c = 0; c < DK; ++c) acc += sK[c * C + r] * sdS[c * BV + j];
+            for (int c = 0; c < DK; ++c) acc += sK[r * DK + c] * sdS[c * BV + j];
             sY[e] = acc;
         }
         __syncthreads();
@@ -275,224 +288,291 @@ __global__ void __launch_bounds__(256) cb_scan_kernel(CbParams p) {
 }
 
 // ------------------------------------------------------------------ grad --
-// All gradients of one (chunk, head), CB_GRAD_NT threads.  The value
-// dimension is walked in 16-column tiles.  Thread t keeps in registers the
-// accumulators of dQ~, dK~ and dK^ for the elements e = t + NT m of the
-// C x DK arrays (all in channel t mod DK) and of dP and dT for the elements
-// of the C x C arrays (all in column t mod C), so the tile values of that
-// channel or column are read from LDS once per tile.  The tiles are stored
-// column by column with padded strides, and K~, K^ and M are staged both
-// ways round where needed, so that the lanes of a wave, which take
-// consecutive rows or channels, read consecutive words or one broadcast
-// word.  After the walk the same LDS regions hold dT / dA, Z, dP, the
-// staged decays and inputs, and dG.
+// All gradients of one (chunk, head): 512 threads (8 waves) on the fp32
+// matrix cores (v_mfma_f32_16x16x4f32: fp32 products, fp32 sums).  A 16 x 16
+// block product over 16 contraction indices is four such steps; in step s
+// lane l (g = l / 16, n = l % 16) supplies A[n][4g + s] and B[4g + s][n],
+// and D[4g + u][n] (u = 0..3) is the lane's u-th accumulator.  Operands are
+// stored with the contraction index contiguous, so a lane reads the values
+// of its four steps as one float4.
+//
+// The value dimension is walked in 16-column tiles.  Per tile, with R the
+// wave's 16-row block (wave mod 4):
+//   waves 0-3:  X = V - K~ S,            then Delta = M Diag(beta) X
+//   waves 4-7:  dDelta = P^T dO + K^ dS', then dX = Diag(beta) M^T dDelta  (= dv)
+//   all waves:  dQ~ += dO S^T, dK~ -= dX S^T, dK^ += Delta dS'^T  (C x DK, half
+//               the key blocks each), dP += dO Delta^T, dT += dDelta X^T
+//               (C x C, blocks on or below the diagonal)
+// The left operands of the first two steps (K~, K^, M Diag(beta), P^T,
+// Diag(beta) M^T) are fixed for the chunk and stay in registers for the
+// whole walk; the triangular ones skip their zero blocks.  After the walk
+// the LDS holds dT -> dA, Z, dP, M, M^T, the staged decays and inputs, and
+// dG.  No atomics reach global memory: each chunk-head writes its own
+// tokens' gradients.
 constexpr int CB_GRAD_NT = 512;
 template <int DK>
 struct CbGradLds {
     static constexpr int C = CB_C, BV = 16;
-    static constexpr int LC = C + 4, LK = DK + 4;            // padded column strides of the tiles
-    static constexpr int TILE = 2 * BV * LK + 5 * BV * LC;   // S, dS' | dO, X, Delta, dDelta, dX
-    static constexpr int MAT = 2 * C * C + C;                // dT -> dA, Z, dbeta
-    static constexpr int U = TILE > MAT ? TILE : MAT;
-    static constexpr int R1 = 0;                             // K~^T | K^^T  -> G | k, q (bf16)
-    static constexpr int R2 = R1 + 2 * C * DK;               // tiles        -> dT/dA | Z/dG hi | dbeta
-    static constexpr int R3 = R2 + U;                        // M | M^T | P  -> dG lo | M^T | dP
-    static constexpr int AG = R3 + 3 * C * C;                // dgamma [DK]
-    static constexpr int SB = AG + DK;                       // beta [C]
-    static constexpr int CS = SB + C;                        // sum_r dK^ K^ [DK]
-    static constexpr int FLOATS = CS + DK;
+    static constexpr int LB = BV + 4;  // row stride of the [row][j] tiles
+    static constexpr int LC = C + 4;   // column stride of the [j][row] tiles of C rows
+    static constexpr int LK = DK + 4;  // column stride of the [j][row] tiles of DK rows
+    static constexpr int LA = C + 1;   // row stride of dT / dA and dP
+    // the walk: S, dS' as [DK][LB] and [BV][LK]; dO, X, Delta, dDelta, dX as
+    // [C][LB]; dO, X, dDelta also as [BV][LC]
+    static constexpr int SR = 0, RR = SR + DK * LB, SC = RR + DK * LB, RC = SC + BV * LK;
+    static constexpr int OR = RC + BV * LK, XR = OR + C * LB, DR = XR + C * LB, ER = DR + C * LB;
+    static constexpr int FR = ER + C * LB, OC = FR + C * LB, XC = OC + BV * LC, EC = XC + BV * LC;
+    static constexpr int WALK = EC + BV * LC;
+    // after the walk
+    static constexpr int LM = C + 4;            // row stride of M, M^T and Z
+    static constexpr int GC = 0;                // G [C][DK], then k and q (bf16) [C][DK] each
+    static constexpr int TA = GC + 2 * C * DK;  // dT -> dGh [C][LA]
+    static constexpr int ZZ = TA + C * LA;      // Z [C][LM]  -> dG rows [C/2, C)
+    static constexpr int DB = ZZ + C * LM;      // dbeta [C]
+    static constexpr int MM = DB + C;           // M [C][LM]  -> dG rows [0, C/2)
+    static constexpr int MTT = MM + C * LM;     // M^T [C][LM]
+    static constexpr int DP = MTT + C * LM;     // dP [C][LA]
+    static_assert(C / 2 * DK <= C * LM, "dG halves fit the M and Z slots");
+    static constexpr int POST = DP + C * LA;
+    static constexpr int BASE = WALK > POST ? WALK : POST;
+    static constexpr int AG = BASE;             // dgamma [DK]
+    static constexpr int SB = AG + DK;          // beta [C]
+    static constexpr int PD = SB + C;           // diagonal of dP [C]
+    static constexpr int FLOATS = PD + C;
 };
+
+__device__ __forceinline__ f32x4 mfma4(float a0, float a1, float a2, float a3, const float4 &b, f32x4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, b.z, acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a3, b.w, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma4(const float4 &a, const float4 &b, f32x4 acc) {
+    return mfma4(a.x, a.y, a.z, a.w, b, acc);
+}
+__device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ float wave_max_f(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+    return x;
+}
+// Diagonal blocks of the pair sums are split around the midpoint of their
+// own decay while the largest decay over the block (in nats, over the
+// wave's 16 channels) stays below this; beyond it they are summed pair by
+// pair.  e^32 keeps the split factors far from fp32 overflow.
+constexpr float kCbSpanMax = 64.f;
 
 template <int DK, typename TI>
 __global__ void __launch_bounds__(CB_GRAD_NT) cb_grad_kernel(CbParams p) {
     if (*p.status != 0) return;
     using Y = CbLay<DK>;
     using Q = CbGradLds<DK>;
-    constexpr int NT = CB_GRAD_NT, BV = Q::BV, C = CB_C, LC = Q::LC, LK = Q::LK;
-    constexpr int NE = C * DK / NT, NC = C * C / NT;
-    constexpr int RG = NT / C, JPT = BV / RG;  // column groups and columns per thread of the row passes
-    static_assert(NT % DK == 0 && NT % C == 0 && BV % RG == 0 && C == 64, "thread mapping");
+    constexpr int NT = CB_GRAD_NT, BV = Q::BV, C = CB_C, LB = Q::LB, LC = Q::LC, LK = Q::LK, LA = Q::LA, LM = Q::LM;
+    constexpr int NKB = DK / 16;        // 16-wide blocks of the key dimension
+    constexpr int NCW = (NKB + 1) / 2;  // key blocks per wave in the C x DK products
+    static_assert(NT == 512 && C == 64 && BV == 16, "wave roles: 8 waves, 4 row blocks of 16, 16 columns");
     const int H = p.H, dv = p.dv;
     const int x = blockIdx.x / H, h = blockIdx.x % H;
     if (x >= p.chunk_off[p.N]) return;  // the grid covers a bound on the chunk count
     const int4 ci = p.chunk_info[x];
     const int64_t t0 = static_cast<int64_t>(static_cast<uint32_t>(ci.x)) | (static_cast<int64_t>(ci.y) << 32);
     const int L = ci.z;
-    const int tid = threadIdx.x;
-    const int lr = tid % C, jg = tid / C;  // row and column group of the row passes
-    const int ec = tid % DK;               // channel of the C x DK accumulators
+    const int tid = threadIdx.x, lane = tid % 64, wv = tid / 64;
+    const int g = lane / 16, n = lane % 16;
+    const int R = wv % 4, half = wv / 4;
     const float *blk = p.blocks + (static_cast<size_t>(x) * H + h) * Y::FLOATS;
     const float *S = p.checkpoints + (static_cast<int64_t>(x) * H + h) * DK * dv;
     const float *dSr = p.dS_right + (static_cast<int64_t>(x) * H + h) * DK * dv;
     const TI *v = static_cast<const TI *>(p.v);
 
     extern __shared__ float lds[];
-    float *sKt = lds + Q::R1, *sKb = sKt + C * DK;  // [DK][C]
-    float *tS = lds + Q::R2, *tR = tS + BV * LK;    // [BV][LK]
-    float *tO = tR + BV * LK, *tX = tO + BV * LC, *tD = tX + BV * LC, *tE = tD + BV * LC, *tF = tE + BV * LC;
-    float *sM = lds + Q::R3, *sMT = sM + C * C, *sP = sMT + C * C;  // [C][C]
-    float *aG = lds + Q::AG, *sB = lds + Q::SB, *sCS = lds + Q::CS;
+    float *tSr = lds + Q::SR, *tRr = lds + Q::RR, *tSc = lds + Q::SC, *tRc = lds + Q::RC;
+    float *tOr = lds + Q::OR, *tXr = lds + Q::XR, *tDr = lds + Q::DR, *tEr = lds + Q::ER, *tFr = lds + Q::FR;
+    float *tOc = lds + Q::OC, *tXc = lds + Q::XC, *tEc = lds + Q::EC;
+    float *aG = lds + Q::AG, *sB = lds + Q::SB, *sPD = lds + Q::PD;
 
-    for (int e = tid; e < C * DK / 4; e += NT) {
-        reinterpret_cast<float4 *>(sKt)[e] = reinterpret_cast<const float4 *>(blk + Y::KT)[e];
-        reinterpret_cast<float4 *>(sKb)[e] = reinterpret_cast<const float4 *>(blk + Y::KB)[e];
+    // the fixed left operands, row R*16 + n, contraction indices 16 kb + 4g + s:
+    //   waves 0-3: fa = -K~, fb = M Diag(beta);  waves 4-7: fa = K^, fb = P^T, fc = Diag(beta) M^T
+    float fa[4 * NKB], fb[16], fc[16];
+    {
+        const int row = R * 16 + n;
+        const float *ka = blk + (half ? Y::KB : Y::KT) + row * DK;
+        const float sg = half ? 1.f : -1.f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            const float4 t = ld4(ka + kb * 16 + 4 * g);
+            fa[4 * kb] = sg * t.x; fa[4 * kb + 1] = sg * t.y; fa[4 * kb + 2] = sg * t.z; fa[4 * kb + 3] = sg * t.w;
+        }
+        const float *mb = blk + (half ? Y::PT : Y::M) + row * C;
+        const float *mc = blk + Y::MT + row * C;
+        const float br = blk[Y::BETA + row];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const float4 t = ld4(mb + kb * 16 + 4 * g);
+            const float4 bc = half ? make_float4(1.f, 1.f, 1.f, 1.f) : ld4(blk + Y::BETA + kb * 16 + 4 * g);
+            fb[4 * kb] = t.x * bc.x; fb[4 * kb + 1] = t.y * bc.y; fb[4 * kb + 2] = t.z * bc.z; fb[4 * kb + 3] = t.w * bc.w;
+            const float4 u = ld4(mc + kb * 16 + 4 * g);
+            fc[4 * kb] = br * u.x; fc[4 * kb + 1] = br * u.y; fc[4 * kb + 2] = br * u.z; fc[4 * kb + 3] = br * u.w;
+        }
     }
-    for (int e = tid; e < C * C / 4; e += NT) {
-        reinterpret_cast<float4 *>(sM)[e] = reinterpret_cast<const float4 *>(blk + Y::M)[e];
-        reinterpret_cast<float4 *>(sMT)[e] = reinterpret_cast<const float4 *>(blk + Y::MT)[e];
-        reinterpret_cast<float4 *>(sP)[e] = reinterpret_cast<const float4 *>(blk + Y::P)[e];
-    }
-    for (int e = tid; e < C; e += NT) sB[e] = blk[Y::BETA + e];
-    for (int e = tid; e < DK; e += NT) aG[e] = sCS[e] = 0.f;
+    for (int e = tid; e < DK; e += NT) aG[e] = 0.f;
 
-    float rQ[NE], rK[NE], rB[NE], rP[NC], rT[NC];
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 aQ[NCW], aK[NCW], aB[NCW], aP[2], aT[2];
 #pragma unroll
-    for (int m = 0; m < NE; ++m) rQ[m] = rK[m] = rB[m] = 0.f;
-#pragma unroll
-    for (int m = 0; m < NC; ++m) rP[m] = rT[m] = 0.f;
+    for (int t = 0; t < NCW; ++t) aQ[t] = aK[t] = aB[t] = z4;
+    aP[0] = aP[1] = aT[0] = aT[1] = z4;
 
     for (int j0 = 0; j0 < dv; j0 += BV) {
-        __syncthreads();
-        for (int e = tid; e < DK * BV; e += NT) {
-            const int c = e / BV, j = e % BV;
-            tS[j * LK + c] = S[static_cast<int64_t>(c) * dv + j0 + j];
-            tR[j * LK + c] = dSr[static_cast<int64_t>(c) * dv + j0 + j];
+        __syncthreads();  // the previous tile's readers are done
+        for (int e = tid; e < DK * BV / 4; e += NT) {
+            const int c = e / (BV / 4), jq = 4 * (e % (BV / 4));
+            const float4 sv = ld4(S + static_cast<int64_t>(c) * dv + j0 + jq);
+            const float4 rv = ld4(dSr + static_cast<int64_t>(c) * dv + j0 + jq);
+            *reinterpret_cast<float4 *>(tSr + c * LB + jq) = sv;
+            *reinterpret_cast<float4 *>(tRr + c * LB + jq) = rv;
+            tSc[jq * LK + c] = sv.x; tSc[(jq + 1) * LK + c] = sv.y; tSc[(jq + 2) * LK + c] = sv.z; tSc[(jq + 3) * LK + c] = sv.w;
+            tRc[jq * LK + c] = rv.x; tRc[(jq + 1) * LK + c] = rv.y; tRc[(jq + 2) * LK + c] = rv.z; tRc[(jq + 3) * LK + c] = rv.w;
         }
-        for (int e = tid; e < C * BV; e += NT) {
-            const int r = e / BV, j = e % BV;
-            const int64_t row = (t0 + r) * H + h;
-            tO[j * LC + r] = r < L ? p.d_o[row * dv + j0 + j] : 0.f;
-            tF[j * LC + r] = r < L ? io<TI>::ld(v, row * dv + j0 + j) : 0.f;  // V, for X
+        for (int e = tid; e < C * BV / 4; e += NT) {
+            const int r = e / (BV / 4), jq = 4 * (e % (BV / 4));
+            float4 ov = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (r < L) ov = ld4(p.d_o + ((t0 + r) * H + h) * dv + j0 + jq);
+            *reinterpret_cast<float4 *>(tOr + r * LB + jq) = ov;
+            tOc[jq * LC + r] = ov.x; tOc[(jq + 1) * LC + r] = ov.y; tOc[(jq + 2) * LC + r] = ov.z; tOc[(jq + 3) * LC + r] = ov.w;
         }
         __syncthreads();
-        {   // X = V - K~ S
-            float a[JPT];
+        if (half == 0) {  // X = V - K~ S
+            f32x4 acc;
 #pragma unroll
-            for (int u = 0; u < JPT; ++u) a[u] = tF[(jg + RG * u) * LC + lr];
-#pragma unroll 8
-            for (int c = 0; c < DK; ++c) {
-                const float kt = sKt[c * C + lr];
-#pragma unroll
-                for (int u = 0; u < JPT; ++u) a[u] -= kt * tS[(jg + RG * u) * LK + c];
+            for (int u = 0; u < 4; ++u) {
+                const int r = R * 16 + 4 * g + u;
+                acc[u] = r < L ? io<TI>::ld(v, ((t0 + r) * H + h) * dv + j0 + n) : 0.f;
             }
 #pragma unroll
-            for (int u = 0; u < JPT; ++u) tX[(jg + RG * u) * LC + lr] = lr < L ? a[u] : 0.f;
+            for (int kb = 0; kb < NKB; ++kb)
+                acc = mfma4(fa[4 * kb], fa[4 * kb + 1], fa[4 * kb + 2], fa[4 * kb + 3], ld4(tSc + n * LK + kb * 16 + 4 * g), acc);
+            *reinterpret_cast<float4 *>(tXc + n * LC + R * 16 + 4 * g) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) tXr[(R * 16 + 4 * g + u) * LB + n] = acc[u];
+        } else {  // dDelta = P^T dO + K^ dS'
+            f32x4 acc = z4;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                if (kb >= R)
+                    acc = mfma4(fb[4 * kb], fb[4 * kb + 1], fb[4 * kb + 2], fb[4 * kb + 3], ld4(tOc + n * LC + kb * 16 + 4 * g), acc);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+                acc = mfma4(fa[4 * kb], fa[4 * kb + 1], fa[4 * kb + 2], fa[4 * kb + 3], ld4(tRc + n * LK + kb * 16 + 4 * g), acc);
+            *reinterpret_cast<float4 *>(tEc + n * LC + R * 16 + 4 * g) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) tEr[(R * 16 + 4 * g + u) * LB + n] = acc[u];
         }
         __syncthreads();
-        {   // Delta = M Diag(beta) X,  dDelta = P^T dO + K^ dS'  (the zero triangles of M, P add nothing)
-            float d[JPT], dd[JPT];
+        if (half == 0) {  // Delta = M Diag(beta) X
+            f32x4 acc = z4;
 #pragma unroll
-            for (int u = 0; u < JPT; ++u) d[u] = dd[u] = 0.f;
-#pragma unroll 8
-            for (int i = 0; i < C; ++i) {
-                const float t = sMT[i * C + lr] * sB[i], pv = sP[i * C + lr];
+            for (int kb = 0; kb < 4; ++kb)
+                if (kb <= R)
+                    acc = mfma4(fb[4 * kb], fb[4 * kb + 1], fb[4 * kb + 2], fb[4 * kb + 3], ld4(tXc + n * LC + kb * 16 + 4 * g), acc);
 #pragma unroll
-                for (int u = 0; u < JPT; ++u) {
-                    d[u] += t * tX[(jg + RG * u) * LC + i];
-                    dd[u] += pv * tO[(jg + RG * u) * LC + i];
+            for (int u = 0; u < 4; ++u) tDr[(R * 16 + 4 * g + u) * LB + n] = acc[u];
+        } else {  // dX = Diag(beta) M^T dDelta
+            f32x4 acc = z4;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                if (kb >= R)
+                    acc = mfma4(fc[4 * kb], fc[4 * kb + 1], fc[4 * kb + 2], fc[4 * kb + 3], ld4(tEc + n * LC + kb * 16 + 4 * g), acc);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int r = R * 16 + 4 * g + u;
+                tFr[r * LB + n] = acc[u];
+                if (r < L) p.gv[((t0 + r) * H + h) * dv + j0 + n] = acc[u];
+            }
+        }
+        __syncthreads();
+        {   // the products over this tile's 16 columns
+            const float4 aO = ld4(tOr + (R * 16 + n) * LB + 4 * g);
+            const float4 aF = ld4(tFr + (R * 16 + n) * LB + 4 * g);
+            const float4 aD = ld4(tDr + (R * 16 + n) * LB + 4 * g);
+            const float4 aE = ld4(tEr + (R * 16 + n) * LB + 4 * g);
+#pragma unroll
+            for (int t = 0; t < NCW; ++t) {
+                const int cb = half + 2 * t;
+                if (cb < NKB) {
+                    const float4 bS = ld4(tSr + (cb * 16 + n) * LB + 4 * g);
+                    const float4 bR = ld4(tRr + (cb * 16 + n) * LB + 4 * g);
+                    aQ[t] = mfma4(aO, bS, aQ[t]);
+                    aK[t] = mfma4(aF, bS, aK[t]);
+                    aB[t] = mfma4(aD, bR, aB[t]);
                 }
             }
-#pragma unroll 8
-            for (int c = 0; c < DK; ++c) {
-                const float kb = sKb[c * C + lr];
 #pragma unroll
-                for (int u = 0; u < JPT; ++u) dd[u] += kb * tR[(jg + RG * u) * LK + c];
-            }
-#pragma unroll
-            for (int u = 0; u < JPT; ++u) {
-                tD[(jg + RG * u) * LC + lr] = d[u];
-                tE[(jg + RG * u) * LC + lr] = dd[u];
-            }
-        }
-        __syncthreads();
-        {   // dX = Diag(beta) M^T dDelta  (= dv)
-            float f[JPT];
-#pragma unroll
-            for (int u = 0; u < JPT; ++u) f[u] = 0.f;
-#pragma unroll 8
-            for (int i = 0; i < C; ++i) {
-                const float mv = sM[i * C + lr];
-#pragma unroll
-                for (int u = 0; u < JPT; ++u) f[u] += mv * tE[(jg + RG * u) * LC + i];
-            }
-            const float b = sB[lr];
-#pragma unroll
-            for (int u = 0; u < JPT; ++u) tF[(jg + RG * u) * LC + lr] = f[u] * b;
-        }
-        __syncthreads();
-        for (int e = tid; e < C * BV; e += NT) {
-            const int r = e / BV, j = e % BV;
-            if (r < L) p.gv[((t0 + r) * H + h) * dv + j0 + j] = tF[j * LC + r];
-        }
-        // dQ~ = dO S^T, dK~ = -dX S^T, dK^ = Delta dS'^T (channel ec);
-        // dP = dO Delta^T, dT = dDelta X^T (column lr)
-#pragma unroll 1
-        for (int j = 0; j < BV; ++j) {
-            const float sv = tS[j * LK + ec], rv = tR[j * LK + ec];
-            const float *oj = tO + j * LC, *fj = tF + j * LC, *dj = tD + j * LC, *ej = tE + j * LC;
-#pragma unroll
-            for (int m = 0; m < NE; ++m) {
-                const int r = (tid + NT * m) / DK;
-                rQ[m] += oj[r] * sv;
-                rK[m] -= fj[r] * sv;
-                rB[m] += dj[r] * rv;
-            }
-            const float dvv = dj[lr], xv = tX[j * LC + lr];
-#pragma unroll
-            for (int m = 0; m < NC; ++m) {
-                const int r = (tid + NT * m) / C;
-                rP[m] += oj[r] * dvv;
-                rT[m] += ej[r] * xv;
+            for (int t = 0; t < 2; ++t) {
+                const int ib = half + 2 * t;
+                if (ib <= R) {
+                    aP[t] = mfma4(aO, ld4(tDr + (ib * 16 + n) * LB + 4 * g), aP[t]);
+                    aT[t] = mfma4(aE, ld4(tXr + (ib * 16 + n) * LB + 4 * g), aT[t]);
+                }
             }
         }
         for (int c = tid; c < DK; c += NT) {
             float g_ = 0.f;
 #pragma unroll
-            for (int j = 0; j < BV; ++j) g_ += tR[j * LK + c] * tS[j * LK + c];
+            for (int j = 0; j < BV; ++j) g_ += tRr[c * LB + j] * tSr[c * LB + j];
             aG[c] += g_;
         }
     }
+    __syncthreads();  // the tiles are dead
+    float *sGc = lds + Q::GC;
+    uint16_t *sk16 = reinterpret_cast<uint16_t *>(sGc + C * DK), *sq16 = sk16 + C * DK;
+    float *sT = lds + Q::TA, *Z = lds + Q::ZZ, *sDB = lds + Q::DB, *sM = lds + Q::MM, *sMT = lds + Q::MTT;
+    float *sdP = lds + Q::DP;
+    // dT on and below the diagonal, dP strictly below it with its diagonal
+    // apart; the rest is zero
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int ib = half + 2 * t;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int o = (R * 16 + 4 * g + u) * LA + ib * 16 + n;
+            const bool low = ib < R || (ib == R && n <= 4 * g + u), diag = ib == R && n == 4 * g + u;
+            sdP[o] = low && !diag ? aP[t][u] : 0.f;
+            sT[o] = low ? aT[t][u] : 0.f;
+            if (diag) sPD[R * 16 + n] = aP[t][u];
+        }
+    }
+    for (int e = tid; e < C * C / 4; e += NT) {
+        const int r = e / (C / 4), a4 = 4 * (e % (C / 4));
+        *reinterpret_cast<float4 *>(sM + r * LM + a4) = ld4(blk + Y::M + r * C + a4);
+        *reinterpret_cast<float4 *>(sMT + r * LM + a4) = ld4(blk + Y::MT + r * C + a4);
+    }
+    for (int e = tid; e < C; e += NT) sB[e] = blk[Y::BETA + e];
     __syncthreads();
-    // T = M Diag(beta): dbeta_i = sum_r M_ri dT_ri, dM = dT Diag(beta);
+    // T = M Diag(beta): dM = dT Diag(beta), dbeta_i = (M^T dT)_ii;
     // M = (I + A)^-1: dA = -(M^T dM M^T) on the strict lower triangle;
     // A = Diag(beta) Gh: dbeta_r += sum_i dA_ri Gh_ri, dGh = Diag(beta) dA.
-    float *sT = lds + Q::R2, *Z = sT + C * C, *sDB = Z + C * C;
-    float *sdP = sP;  // P is dead
+    // Z = M^T dT Diag(beta): blocks (R, ib <= R), M^T upper: a from block R on
 #pragma unroll
-    for (int m = 0; m < NC; ++m) {
-        sT[tid + NT * m] = rT[m];
-        sdP[tid + NT * m] = rP[m];
-    }
-    __syncthreads();
-    for (int e = tid; e < C * C; e += NT) {
-        const int r = e / C, i = e % C;   // Z = M^T dM
-        float acc = 0.f;
-        for (int a = r; a < C; ++a) acc += sM[a * C + r] * sT[a * C + i];
-        Z[e] = acc * sB[i];
-    }
-    for (int i = tid; i < C; i += NT) {
-        float acc = 0.f;
-        for (int r = i; r < C; ++r) acc += sM[r * C + i] * sT[r * C + i];
-        sDB[i] = acc;
-    }
-    __syncthreads();
-    // one row of dA per wave: dA_ri = -sum_a Z_ra M_ia, its row sum against Gh
-    // goes to dbeta_r, and dGh replaces dT in place (dT is dead)
-    float *sDA = sT;
-    for (int e = tid; e < C * C; e += NT) {
-        const int r = e / C, i = e % C;
-        float acc = 0.f;
-        if (i < r)
-            for (int a = 0; a <= i; ++a) acc -= Z[r * C + a] * sMT[a * C + i];
-        float g = acc * blk[Y::GH + e];
+    for (int t = 0; t < 2; ++t) {
+        const int ib = half + 2 * t;
+        if (ib > R) break;
+        f32x4 acc = z4;
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) g += __shfl_xor(g, o);
-        if (i == 0) sDB[r] += g;
-        sDA[e] = acc * sB[r];
+        for (int kb = 0; kb < 4; ++kb) {
+            if (kb < R) continue;
+            const float *bt = sT + (kb * 16 + 4 * g) * LA + ib * 16 + n;
+            acc = mfma4(ld4(sMT + (R * 16 + n) * LM + kb * 16 + 4 * g),
+                        make_float4(bt[0], bt[LA], bt[2 * LA], bt[3 * LA]), acc);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = R * 16 + 4 * g + u, i = ib * 16 + n;
+            Z[r * LM + i] = acc[u] * sB[i];
+            if (i == r) sDB[r] = acc[u];
+        }
     }
-    // stage the decays and the raw q, k (bf16) for the pair sums over R1
-    float *sGc = lds + Q::R1;
-    uint16_t *sk16 = reinterpret_cast<uint16_t *>(sGc + C * DK), *sq16 = sk16 + C * DK;
+    // stage the decays and the raw q, k (bf16) for the pair sums
     for (int e = tid; e < C * DK; e += NT) {
         const int r = e / DK, c = e % DK;
         const int64_t off = ((t0 + r) * H + h) * DK + c;
@@ -501,58 +581,164 @@ __global__ void __launch_bounds__(CB_GRAD_NT) cb_grad_kernel(CbParams p) {
         sq16[e] = r < L ? static_cast<const uint16_t *>(p.q)[off] : 0;
     }
     __syncthreads();
+    // dA = -Z M^T, blocks (R, ib <= R), M lower: a up to block ib; strict
+    // lower triangle only.  dGh = Diag(beta) dA replaces dT.
+    float *sDA = sT;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int ib = half + 2 * t;
+        if (ib > R) break;
+        f32x4 acc = z4;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            if (kb > ib) break;
+            acc = mfma4(ld4(Z + (R * 16 + n) * LM + kb * 16 + 4 * g), ld4(sM + (ib * 16 + n) * LM + kb * 16 + 4 * g), acc);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = R * 16 + 4 * g + u, i = ib * 16 + n;
+            const float dA = i < r ? -acc[u] : 0.f;
+            float gs = dA * blk[Y::GH + r * C + i];
+#pragma unroll
+            for (int o = 8; o > 0; o >>= 1) gs += __shfl_xor(gs, o);  // over the 16 columns
+            if (n == 0) atomicAdd(&sDB[r], gs);
+            sDA[r * LA + i] = dA * sB[r];
+        }
+    }
+    __syncthreads();
     if (tid < L) p.gbeta[(t0 + tid) * H + h] = sDB[tid];
     // pair sums over the decay factors, per (row r, channel c):
-    //   rowA = sum_{i<r} dGh_ri k_i e^{G_r-G_i}    rowP = sum_{i<=r} dP_ri k_i e^{G_r-G_i}
-    //   colA = sum_{i>r} dGh_ir k_i e^{G_i-G_r}    colP = sum_{i>=r} dP_ir q_i e^{G_i-G_r}
-    //   dk = rowA + colA + colP + dK~ e^G + dK^ e^{G_L-G},  dq = rowP + dQ~ e^G,
-    //   dG = k rowA + q rowP - k (colA + colP) + dK~ K~ + dQ~ Q~ - dK^ K^
-    // dG rows [0, C/2) go to M's slot, rows [C/2, C) to Z's slot (both dead)
+    //   rowA = sum_{i<r} dGh_ri k_i e^{G_r-G_i}    rowP = sum_{i<r} dP_ri k_i e^{G_r-G_i}
+    //   colA = sum_{i>r} dGh_ir k_i e^{G_i-G_r}    colP = sum_{i>r} dP_ir q_i e^{G_i-G_r}
+    //   dk = rowA + colA + colP + dP_rr q + dK~ e^G + dK^ e^{G_L-G},
+    //   dq = rowP + dP_rr k + dQ~ e^G,
+    //   dg_t = sum_{r>=t} dG_r + sum_{r<t} dK^_r K^_r + dgamma gamma,
+    //   dG = k rowA + q rowP - k (colA + colP) + dK~ K~ + dQ~ Q~.
+    // (G_L - G_r depends on g_t for r < t <= L: summing dK^ K^ forwards
+    // avoids adding it at the chunk's end and taking it back row by row,
+    // which cancels to fp32 noise when the chunk decays strongly; the
+    // diagonal pairs of P leave dG for the same reason.)
+    // For the lane's accumulator elements (R*16 + 4g + u, cb*16 + n), on the
+    // matrix cores.  The decay factor of a pair is split around a reference
+    // row: for rows against earlier blocks the row before block R,
+    // e^{G_r-G_i} = e^{G_r-G_m} e^{G_m-G_i}; for columns against later blocks
+    // the last row of block R, e^{G_i-G_r} = e^{G_i-G_e} e^{G_e-G_r}; all four
+    // factors are <= 1.  Within block R the split is around the midpoint of
+    // the block's decay (factors within e^(+-span/2)), or, where some channel
+    // of the wave decays by more than kCbSpanMax over the block, pair by pair.
+    // dG rows [0, C/2) go to M's slot, rows [C/2, C) to Z's slot (both dead);
+    // dK^ K^ stays in registers until the staged inputs are dead.
     auto dGat = [&](int r, int c) -> float & {
         return r < C / 2 ? sM[r * DK + c] : Z[(r - C / 2) * DK + c];
     };
-    float csum = 0.f;  // this thread's share of sum_r dK^ K^ (channel ec)
+    float vKK[NCW][4];
 #pragma unroll
-    for (int m = 0; m < NE; ++m) {
-        const int e = tid + NT * m, r = e / DK, c = e % DK;
-        const float Gr = sGc[e];
-        float rowA = 0.f, rowP = 0.f, colA = 0.f, colP = 0.f;
-        for (int i = 0; i < L; ++i) {
-            const float ki = bf16_to_f32(sk16[i * DK + c]);
-            const float Gi = sGc[i * DK + c];
-            if (i <= r) {
-                const float f = __expf(Gr - Gi) * ki;
-                rowA += sDA[r * C + i] * f;
-                rowP += sdP[r * C + i] * f;
+    for (int t = 0; t < NCW; ++t) {
+        const int cb = half + 2 * t;
+        if (cb >= NKB) break;
+        const int c = cb * 16 + n;
+        const float Gm = R > 0 ? sGc[(R * 16 - 1) * DK + c] : 0.f;
+        const float Ge = sGc[(R * 16 + 15) * DK + c];
+        const float Gmid = 0.5f * (Gm + Ge);
+        const bool exact = wave_max_f(Gm - Ge) > kCbSpanMax;
+        f32x4 rA = z4, rP = z4, cA = z4, cP = z4, dRA = z4, dRP = z4, dCA = z4, dCP = z4;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            if (b == R && exact) continue;
+            const float ref = b < R ? Gm : b > R ? Ge : Gmid;
+            float bk[4], bq[4], brow[4], a0[4], a1[4], a2[4], a3[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int i = b * 16 + 4 * g + s;
+                const float Gi = sGc[i * DK + c];
+                const float ki = bf16_to_f32(sk16[i * DK + c]);
+                const float ec = __expf(Gi - ref);            // columns: e^{G_i - ref}
+                brow[s] = b <= R ? ki * __expf(ref - Gi) : 0.f;  // rows: e^{ref - G_i}
+                bk[s] = ki * ec;
+                bq[s] = bf16_to_f32(sq16[i * DK + c]) * ec;
+                a0[s] = sDA[(R * 16 + n) * LA + i];   // dGh[r][i]
+                a1[s] = sdP[(R * 16 + n) * LA + i];   // dP[r][i]
+                a2[s] = sDA[i * LA + R * 16 + n];     // dGh[i][r]
+                a3[s] = sdP[i * LA + R * 16 + n];     // dP[i][r]
             }
-            if (i >= r) {
-                const float f = __expf(Gi - Gr);
-                colA += sDA[i * C + r] * ki * f;
-                colP += sdP[i * C + r] * bf16_to_f32(sq16[i * DK + c]) * f;
+            const float4 Br = make_float4(brow[0], brow[1], brow[2], brow[3]);
+            const float4 Bk = make_float4(bk[0], bk[1], bk[2], bk[3]);
+            const float4 Bq = make_float4(bq[0], bq[1], bq[2], bq[3]);
+            if (b < R) {
+                rA = mfma4(a0[0], a0[1], a0[2], a0[3], Br, rA);
+                rP = mfma4(a1[0], a1[1], a1[2], a1[3], Br, rP);
+            } else if (b > R) {
+                cA = mfma4(a2[0], a2[1], a2[2], a2[3], Bk, cA);
+                cP = mfma4(a3[0], a3[1], a3[2], a3[3], Bq, cP);
+            } else {
+                dRA = mfma4(a0[0], a0[1], a0[2], a0[3], Br, dRA);
+                dRP = mfma4(a1[0], a1[1], a1[2], a1[3], Br, dRP);
+                dCA = mfma4(a2[0], a2[1], a2[2], a2[3], Bk, dCA);
+                dCP = mfma4(a3[0], a3[1], a3[2], a3[3], Bq, dCP);
             }
         }
-        const float kr = bf16_to_f32(sk16[e]), qr = bf16_to_f32(sq16[e]);
-        const float E = __expf(Gr), eL = __expf(sGc[(C - 1) * DK + c] - Gr);
-        const float dk_ = rowA + colA + colP + rK[m] * E + rB[m] * eL;
-        const float dq_ = rowP + rQ[m] * E;
-        const float Kb = kr * eL;  // K^ and K~ as the prep kernel forms them
-        dGat(r, c) = kr * rowA + qr * rowP - kr * (colA + colP) + rK[m] * (kr * E) +
-                     rQ[m] * blk[Y::QT + e] - rB[m] * Kb;
-        if (r < L) {
-            p.gq[((t0 + r) * H + h) * DK + c] = dq_;
-            p.gk[((t0 + r) * H + h) * DK + c] = dk_;
+        const float GL = sGc[(C - 1) * DK + c];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = R * 16 + 4 * g + u;
+            const float Gr = sGc[r * DK + c];
+            float rowA = rA[u] * __expf(Gr - Gm), rowP = rP[u] * __expf(Gr - Gm);
+            float colA = cA[u] * __expf(Ge - Gr), colP = cP[u] * __expf(Ge - Gr);
+            if (!exact) {
+                const float fr = __expf(Gr - Gmid), fc = __expf(Gmid - Gr);
+                rowA += dRA[u] * fr;
+                rowP += dRP[u] * fr;
+                colA += dCA[u] * fc;
+                colP += dCP[u] * fc;
+            } else {
+                for (int i = R * 16; i < R * 16 + 16; ++i) {
+                    const float ki = bf16_to_f32(sk16[i * DK + c]);
+                    const float Gi = sGc[i * DK + c];
+                    if (i <= r) {
+                        const float f = __expf(Gr - Gi) * ki;
+                        rowA += sDA[r * LA + i] * f;
+                        rowP += sdP[r * LA + i] * f;
+                    }
+                    if (i >= r) {
+                        const float f = __expf(Gi - Gr);
+                        colA += sDA[i * LA + r] * ki * f;
+                        colP += sdP[i * LA + r] * bf16_to_f32(sq16[i * DK + c]) * f;
+                    }
+                }
+            }
+            const float kr = bf16_to_f32(sk16[r * DK + c]), qr = bf16_to_f32(sq16[r * DK + c]);
+            const float E = __expf(Gr), eL = __expf(GL - Gr), pd = sPD[r];
+            const float rq = aQ[t][u], rk = -aK[t][u], rb = aB[t][u];
+            dGat(r, c) = kr * rowA + qr * rowP - kr * (colA + colP) + rk * (kr * E) + rq * blk[Y::QT + r * DK + c];
+            vKK[t][u] = rb * (kr * eL);  // K^ and K~ as the prep kernel forms them
+            if (r < L) {
+                p.gq[((t0 + r) * H + h) * DK + c] = rowP + pd * kr + rq * E;
+                p.gk[((t0 + r) * H + h) * DK + c] = rowA + colA + colP + pd * qr + rk * E + rb * eL;
+            }
         }
-        csum += rB[m] * Kb;
     }
-    atomicAdd(&sCS[ec], csum);
+    __syncthreads();  // the staged decays and inputs are dead
+    float *sKK = lds + Q::GC;
+#pragma unroll
+    for (int t = 0; t < NCW; ++t) {
+        const int cb = half + 2 * t;
+        if (cb >= NKB) break;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sKK[(R * 16 + 4 * g + u) * DK + cb * 16 + n] = vKK[t][u];
+    }
     __syncthreads();
-    // G_{C-1} (= G of the chunk's last token) also takes sum_r dK^ K^ and
-    // dgamma gamma; dg = reverse cumsum of dG over the chunk
+    // dg: reverse cumsum of dG (in place), then the forward exclusive sum of
+    // dK^ K^ and dgamma gamma on every token
     for (int c = tid; c < DK; c += NT) {
-        float run = sCS[c] + aG[c] * blk[Y::GAM + c];
+        float run = 0.f;
         for (int r = C - 1; r >= 0; --r) {
             run += dGat(r, c);
-            if (r < L) p.gg[((t0 + r) * H + h) * DK + c] = run;
+            dGat(r, c) = run;
+        }
+        float pre = aG[c] * blk[Y::GAM + c];
+        for (int r = 0; r < L; ++r) {
+            p.gg[((t0 + r) * H + h) * DK + c] = dGat(r, c) + pre;
+            pre += sKK[r * DK + c];
         }
     }
 }

@@ -309,7 +309,9 @@ kda_status kda_short_conv(const kda_conv_args *a, void *hip_stream);
  * With fp32 inputs dq, dk, dlog_alpha and dbeta are sums over the state's
  * column tiles taken with fp32 atomics: their rounding may differ from run to
  * run; the bf16 path is deterministic.
- * Supported: d_k, d_v in {16, 32, 64, 128}; in_dtype f32 or bf16.
+ * Supported: d_k, d_v in {16, 32, 64, 128}; in_dtype f32 or bf16; with bf16
+ * inputs checkpoints and d_o must be 16-byte aligned (KDA_ERR_UNSUPPORTED
+ * otherwise).
  */
 typedef struct kda_backward_args {
     int32_t B, T, H, d_k, d_v;

@@ -191,6 +191,7 @@ def backward_args(**over):
     (dict(d_k=96), 3), (dict(in_dtype=3), 3), (dict(chunk_size=48), 3), (dict(chunk_size=0), 2),
     (dict(in_dtype=0, chunk_size=64), 3),
     (dict(workspace_bytes=1), 4),
+    (dict(workspace_bytes=1 << 40, d_o=FAKE + 4), 3), (dict(workspace_bytes=1 << 40, checkpoints=FAKE + 8), 3),
 ])
 def test_backward_host_validation(L, over, status):
     assert L.kda_backward(ctypes.byref(backward_args(**over)), None) == status

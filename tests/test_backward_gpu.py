@@ -129,3 +129,14 @@ def test_bf16_slow_decay():
 def test_bf16_extreme_gates():
     x = synth.make_long(461, 512, 2, 128, 128, "bf16")
     check(x, "bf16 chunked extreme gates")
+
+
+@pytest.mark.parametrize("gate_mean", [2.5, 4.0, 10.0])
+def test_bf16_strong_decay(gate_mean):
+    """log alpha ~ -softplus(N(gate_mean, 1)) on every token: a 16-token block
+    decays by ~40, ~64 and ~160 nats, so the pair sums of the diagonal blocks
+    take the split around the block's midpoint, a mix, and the pair-by-pair
+    sum."""
+    x = synth.make_uniform(470 + int(gate_mean), 1, 200, 2, 128, 128, "bf16", chunk=64, state_std=0.3,
+                           gate_mean=gate_mean)
+    check(x, f"bf16 chunked strong decay {gate_mean}")
