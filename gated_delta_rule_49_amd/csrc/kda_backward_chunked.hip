@@ -10,7 +10,8 @@
 // pages derive no backward (course index, module list, the Module 04 entry
 // calls the affine composition the argument for parallel training).
 //
-// Three kernels, all fp32 on the vector ALUs:
+// Three kernels, all in fp32 (prep on the vector ALUs, scan and grad on the
+// fp32 matrix cores):
 //   prep  (chunk, head):  G, K~, Q~, K^, g, Gh = k k^T e^{..}, P, M, W -> a block
 //   scan  (sequence, head, 16-column tile): dS' of every chunk, last first
 //   grad  (chunk, head):  every gradient of the chunk's tokens from its
@@ -189,101 +190,190 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
 // ------------------------------------------------------------------ scan --
 // dS entering chunk c from the right (dS'), for every chunk, last first:
 //     dS = Diag(g) dS' + Q~^T dO - W^T (P^T dO + K^ dS')
-// One workgroup per (sequence, head, 8-column tile), 256 threads; the
-// chunk's Q~, W, K^ and P are staged in LDS.
-constexpr int CB_SCAN_BV = 8;
+// One workgroup per (sequence, head, 16-column tile), 4 waves, on the fp32
+// matrix cores (v_mfma_f32_16x16x4f32).  A 16 x 16 block product over 16
+// contraction indices is four steps; in step s lane l (g = l / 16,
+// n = l % 16) supplies A[n][4g + s] and B[4g + s][n] and holds
+// D[4g + u][n], u = 0..3.  Wave w computes token block w of
+// Y = P^T dO + K^ dS' and owns key blocks w, w + 4 of dS, which stay in
+// accumulators for the whole walk.  dO, dS' and -Y pass between the waves
+// through LDS, stored with the contraction index contiguous (one float4
+// per lane and step group).  The chunk's operands from the prep block are
+// loaded into registers one chunk ahead: P^T and K^ right after the Y
+// products use them, Q~, W and the decay right after the dS products.
+constexpr int CB_SCAN_BV = 16;
+
 template <int DK>
-struct CbScanLds {
-    static constexpr int C = CB_C, BV = CB_SCAN_BV;
-    static constexpr int QT = 0, W = QT + C * DK, KB = W + C * DK, P = KB + C * DK;   // [C][DK] x3, [C][C]
-    static constexpr int DS = P + C * C;          // [DK][BV]
-    static constexpr int DO = DS + DK * BV;       // [C][BV]
-    static constexpr int YY = DO + C * BV;        // [C][BV]
-    static constexpr int GM = YY + C * BV;        // [DK]
-    static constexpr int FLOATS = GM + DK;
+struct CbScanOps {
+    static constexpr int NKB = DK / 16;           // key blocks
+    static constexpr int KPW = (NKB + 3) / 4;     // key blocks per wave
+    f32x4 pt[4];          // P^T[16w + n][16ib + 4g ..], token blocks ib >= w
+    f32x4 kb[NKB];        // K^[16w + n][16cb + 4g ..]
+    f32x4 qt[KPW][4];     // Q~[16rb + 4g + s][16kb + n], s = 0..3
+    f32x4 wt[KPW][4];     // W [16rb + 4g + s][16kb + n]
+    f32x4 gm[KPW];        // e^{G_L}[16kb + 4g ..]
+    float dov[4];         // dO of this thread's four (token, column) pairs
+
+    __device__ __forceinline__ void load_y(const float *blk, int w, int g, int n) {
+        using Y = CbLay<DK>;
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib)
+            if (ib >= w) pt[ib] = *reinterpret_cast<const f32x4 *>(blk + Y::PT + (16 * w + n) * CB_C + 16 * ib + 4 * g);
+#pragma unroll
+        for (int cb = 0; cb < NKB; ++cb)
+            kb[cb] = *reinterpret_cast<const f32x4 *>(blk + Y::KB + (16 * w + n) * DK + 16 * cb + 4 * g);
+    }
+    __device__ __forceinline__ void load_s(const float *blk, int w, int g, int n) {
+        using Y = CbLay<DK>;
+#pragma unroll
+        for (int i = 0; i < KPW; ++i) {
+            const int kbk = w + 4 * i;
+            if (kbk >= NKB) continue;
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int off = (16 * rb + 4 * g + s) * DK + 16 * kbk + n;
+                    qt[i][rb][s] = blk[Y::QT + off];
+                    wt[i][rb][s] = blk[Y::W + off];
+                }
+            gm[i] = *reinterpret_cast<const f32x4 *>(blk + Y::GAM + 16 * kbk + 4 * g);
+        }
+    }
+    __device__ __forceinline__ void load_do(const float *d_o, int64_t t0, int L, int H, int h, int dv, int j0,
+                                            int tid) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int e = tid + 256 * m, r = e / 16, j = e % 16;
+            dov[m] = r < L ? d_o[((t0 + r) * H + h) * dv + j0 + j] : 0.f;
+        }
+    }
 };
+
+// 16 x 16 x 16 block product: a = A[n][4g .. 4g + 3], b = B[4g .. 4g + 3][n]
+__device__ __forceinline__ f32x4 mm16x16(const f32x4 &a, const f32x4 &b, f32x4 acc) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+    return acc;
+}
 
 template <int DK>
 __global__ void __launch_bounds__(256) cb_scan_kernel(CbParams p) {
     if (*p.status != 0) return;
     using Y = CbLay<DK>;
-    using Q = CbScanLds<DK>;
-    constexpr int BV = CB_SCAN_BV, C = CB_C, NT = 256;
+    using Ops = CbScanOps<DK>;
+    constexpr int BV = CB_SCAN_BV, C = CB_C, NKB = Ops::NKB, KPW = Ops::KPW;
+    constexpr int LC = C + 4, LK = DK + 4;   // padded strides of the [column][row] tiles
     const int H = p.H, dv = p.dv;
     const int nvt = dv / BV;
-    const int vt = blockIdx.x % nvt, h = (blockIdx.x / nvt) % H, n = blockIdx.x / (nvt * H);
+    const int vt = blockIdx.x % nvt, h = (blockIdx.x / nvt) % H, n_seq = blockIdx.x / (nvt * H);
     const int j0 = vt * BV;
     const int tid = threadIdx.x;
-    const int64_t cbase = p.chunk_off[n];
-    const int nch = p.chunk_off[n + 1] - p.chunk_off[n];
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, n = lane & 15;
+    const int64_t cbase = p.chunk_off[n_seq];
+    const int nch = p.chunk_off[n_seq + 1] - p.chunk_off[n_seq];
 
-    extern __shared__ float lds[];
-    float *sQ = lds + Q::QT, *sW = lds + Q::W, *sK = lds + Q::KB, *sP = lds + Q::P;
-    float *sdS = lds + Q::DS, *sdO = lds + Q::DO, *sY = lds + Q::YY, *sG = lds + Q::GM;
-    const int64_t sbase = (static_cast<int64_t>(n) * H + h) * DK * dv;
-    for (int e = tid; e < DK * BV; e += NT) {
-        const int c = e / BV, j = e % BV;
-        sdS[e] = p.d_final ? p.d_final[sbase + static_cast<int64_t>(c) * dv + j0 + j] : 0.f;
+    __shared__ __attribute__((aligned(16))) float doT[BV][LC];    // dO^T
+    __shared__ __attribute__((aligned(16))) float dsT[BV][LK];    // dS'^T
+    __shared__ __attribute__((aligned(16))) float ynT[BV][LC];    // -Y^T
+
+    // the wave's key blocks of dS (accumulator layout)
+    const int64_t sbase = (static_cast<int64_t>(n_seq) * H + h) * DK * dv;
+    f32x4 ds[KPW];
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) {
+        const int kbk = w + 4 * i;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            ds[i][u] = (kbk < NKB && p.d_final) ? p.d_final[sbase + static_cast<int64_t>(16 * kbk + 4 * g + u) * dv + j0 + n]
+                                                : 0.f;
+    }
+    if (nch <= 0) {
+        if (p.d_initial)
+#pragma unroll
+            for (int i = 0; i < KPW; ++i) {
+                const int kbk = w + 4 * i;
+                if (kbk >= NKB) continue;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    p.d_initial[sbase + static_cast<int64_t>(16 * kbk + 4 * g + u) * dv + j0 + n] = ds[i][u];
+            }
+        return;
+    }
+    auto blk_of = [&](int ch) { return p.blocks + (static_cast<size_t>(cbase + ch) * H + h) * Y::FLOATS; };
+    auto coords = [&](int ch, int64_t &t0, int &L) {
+        const int4 ci = p.chunk_info[cbase + ch];
+        t0 = static_cast<int64_t>(static_cast<uint32_t>(ci.x)) | (static_cast<int64_t>(ci.y) << 32);
+        L = ci.z;
+    };
+    Ops op;
+    {
+        int64_t t0; int L;
+        coords(nch - 1, t0, L);
+        op.load_y(blk_of(nch - 1), w, g, n);
+        op.load_s(blk_of(nch - 1), w, g, n);
+        op.load_do(p.d_o, t0, L, H, h, dv, j0, tid);
     }
     for (int ch = nch - 1; ch >= 0; --ch) {
         const int64_t x = cbase + ch;
-        const int4 ci = p.chunk_info[x];
-        const int64_t t0 = static_cast<int64_t>(static_cast<uint32_t>(ci.x)) | (static_cast<int64_t>(ci.y) << 32);
-        const int L = ci.z;
-        const float *blk = p.blocks + (static_cast<size_t>(x) * H + h) * Y::FLOATS;
-        __syncthreads();  // sdS complete; the previous chunk's readers are done
+        const int nx = ch > 0 ? ch - 1 : 0;   // the chunk whose operands are loaded next
+        lds_barrier();  // the previous chunk's readers of doT, dsT are done
+        // dO and dS' -> LDS; dS' is also recorded for the gradient kernel
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int e = tid + 256 * m;
+            doT[e % 16][e / 16] = op.dov[m];
+        }
         float *rec = p.dS_right + (x * H + h) * static_cast<int64_t>(DK) * dv;
-        for (int e = tid; e < DK * BV; e += NT) {
-            const int c = e / BV, j = e % BV;
-            rec[static_cast<int64_t>(c) * dv + j0 + j] = sdS[e];
-        }
-        for (int e = tid; e < C * DK / 4; e += NT) {
-            reinterpret_cast<float4 *>(sQ)[e] = reinterpret_cast<const float4 *>(blk + Y::QT)[e];
-            reinterpret_cast<float4 *>(sW)[e] = reinterpret_cast<const float4 *>(blk + Y::W)[e];
-            reinterpret_cast<float4 *>(sK)[e] = reinterpret_cast<const float4 *>(blk + Y::KB)[e];
-        }
-        for (int e = tid; e < C * C / 4; e += NT)
-            reinterpret_cast<float4 *>(sP)[e] = reinterpret_cast<const float4 *>(blk + Y::P)[e];
-        for (int e = tid; e < DK; e += NT) sG[e] = blk[Y::GAM + e];
-        for (int e = tid; e < C * BV; e += NT) {
-            const int r = e / BV, j = e % BV;
-            sdO[e] = r < L ? p.d_o[((t0 + r) * H + h) * dv + j0 + j] : 0.f;
-        }
-        __syncthreads();
-        // Y = P^T dO + K^ dS'   (C x BV, 2 per thread)
-        for (int e = tid; e < C * BV; e += NT) {
-            const int r = e / BV, j = e % BV;
-            float acc = 0.f;
-            for (int i = r; i < C; ++i) acc += sP[i * C + r] * sdO[i * BV + j];
-#pragma unroll 8
-            for (int c = 0; c < DK; ++c) acc += sK[r * DK + c] * sdS[c * BV + j];
-            sY[e] = acc;
-        }
-        __syncthreads();
-        // dS <- Diag(g) dS' + Q~^T dO - W^T Y   (DK x BV)
-        float nv[(DK * BV + NT - 1) / NT];
 #pragma unroll
-        for (int m = 0; m < (DK * BV + NT - 1) / NT; ++m) {
-            const int e = tid + NT * m;
-            if (e >= DK * BV) continue;
-            const int c = e / BV, j = e % BV;
-            float acc = sG[c] * sdS[e];
-#pragma unroll 8
-            for (int r = 0; r < C; ++r) acc += sQ[r * DK + c] * sdO[r * BV + j] - sW[r * DK + c] * sY[r * BV + j];
-            nv[m] = acc;
-        }
-        __syncthreads();
+        for (int i = 0; i < KPW; ++i) {
+            const int kbk = w + 4 * i;
+            if (kbk >= NKB) continue;
+            *reinterpret_cast<f32x4 *>(&dsT[n][16 * kbk + 4 * g]) = ds[i];
 #pragma unroll
-        for (int m = 0; m < (DK * BV + NT - 1) / NT; ++m) {
-            const int e = tid + NT * m;
-            if (e < DK * BV) sdS[e] = nv[m];
+            for (int u = 0; u < 4; ++u) rec[static_cast<int64_t>(16 * kbk + 4 * g + u) * dv + j0 + n] = ds[i][u];
         }
+        {
+            int64_t t0; int L;
+            coords(nx, t0, L);
+            op.load_do(p.d_o, t0, L, H, h, dv, j0, tid);
+        }
+        lds_barrier();
+        // Y block w = P^T dO + K^ dS'  (token rows 16w ..)
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib)
+            if (ib >= w) y = mm16x16(op.pt[ib], *reinterpret_cast<const f32x4 *>(&doT[n][16 * ib + 4 * g]), y);
+#pragma unroll
+        for (int cb = 0; cb < NKB; ++cb)
+            y = mm16x16(op.kb[cb], *reinterpret_cast<const f32x4 *>(&dsT[n][16 * cb + 4 * g]), y);
+        *reinterpret_cast<f32x4 *>(&ynT[n][16 * w + 4 * g]) = -y;
+        op.load_y(blk_of(nx), w, g, n);
+        lds_barrier();
+        // dS = Diag(g) dS' + Q~^T dO + W^T (-Y)  (the wave's key blocks)
+#pragma unroll
+        for (int i = 0; i < KPW; ++i) {
+            const int kbk = w + 4 * i;
+            if (kbk >= NKB) continue;
+            f32x4 acc = op.gm[i] * ds[i];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                acc = mm16x16(op.qt[i][rb], *reinterpret_cast<const f32x4 *>(&doT[n][16 * rb + 4 * g]), acc);
+                acc = mm16x16(op.wt[i][rb], *reinterpret_cast<const f32x4 *>(&ynT[n][16 * rb + 4 * g]), acc);
+            }
+            ds[i] = acc;
+        }
+        op.load_s(blk_of(nx), w, g, n);
     }
-    __syncthreads();
     if (p.d_initial)
-        for (int e = tid; e < DK * BV; e += NT) {
-            const int c = e / BV, j = e % BV;
-            p.d_initial[sbase + static_cast<int64_t>(c) * dv + j0 + j] = sdS[e];
+#pragma unroll
+        for (int i = 0; i < KPW; ++i) {
+            const int kbk = w + 4 * i;
+            if (kbk >= NKB) continue;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                p.d_initial[sbase + static_cast<int64_t>(16 * kbk + 4 * g + u) * dv + j0 + n] = ds[i][u];
         }
 }
 
@@ -749,16 +839,10 @@ hipError_t run_cb(const CbParams &p, int n_items, hipStream_t s) {
     hipLaunchKernelGGL((cb_prep_kernel<DK, TI>), dim3(n_items), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    {
-        const size_t lds = CbScanLds<DK>::FLOATS * sizeof(float);
-        auto kern = cb_scan_kernel<DK>;
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                static_cast<int>(lds));
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(p.N) * p.H * (p.dv / CB_SCAN_BV)), dim3(256), lds, s, p);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
+    hipLaunchKernelGGL((cb_scan_kernel<DK>), dim3(static_cast<unsigned>(p.N) * p.H * (p.dv / CB_SCAN_BV)), dim3(256),
+                       0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     const size_t lds = CbGradLds<DK>::FLOATS * sizeof(float);
     auto kern = cb_grad_kernel<DK, TI>;
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
