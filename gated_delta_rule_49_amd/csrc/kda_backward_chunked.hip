@@ -22,6 +22,9 @@
 namespace kda {
 
 constexpr int CB_C = 64;  // maximum chunk length
+// a diagonal 16-token block of the prep's Gram products is factorised around
+// its midpoint while it decays by at most this many nats in every channel
+constexpr float kCbDiagSpan = 80.f;
 
 // per-(chunk, head) block of the prep kernel, fp32, row-major
 template <int DK>
@@ -101,45 +104,95 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
     }
     for (int c = tid; c < DK; c += 256) blk[Y::GAM + c] = __expf(sG[CB_C - 1][c]);
     if (tid < CB_C) blk[Y::BETA + tid] = sb[tid];
-    // Gh and P on the lower triangle, 4 x 4 pair blocks per thread
-    constexpr int NB = CB_C / 4;
-    for (int bi = tid; bi < NB * (NB + 1) / 2; bi += 256) {
-        int R = 0;
-        while ((R + 1) * (R + 2) / 2 <= bi) ++R;
-        const int I = bi - R * (R + 1) / 2;  // I <= R
-        float gh[4][4] = {}, pp[4][4] = {};
-        for (int c = 0; c < DK; ++c) {
-            float kr[4], qr[4], gr[4], ki[4], gi[4];
+    // Gh and P in 16 x 16 blocks (R, I <= R) on the fp32 matrix cores: in
+    // step s lane l (g = l / 16, n = l % 16) supplies row r = 16R + n and
+    // column i = 16I + n of channel c = 16cb + 4g + s, and holds the pairs
+    // (16R + 4g + u, 16I + n).  The decay e^{G_r - G_i} is split around a
+    // reference: off the diagonal the row m = 16R - 1 between the blocks
+    // (both factors <= 1, so an underflow only drops a term below fp32's
+    // range); on a diagonal block the per-channel midpoint of the block's
+    // own decay (both factors within e^{+-span/2}), or, when the block decays
+    // by more than kCbDiagSpan in some channel, pair by pair on the vector
+    // ALUs.  Wave w takes diagonal block w and the off-diagonal pairs w and
+    // w + 4 of (1,0) (2,0) (2,1) (3,0) (3,1) (3,2).
+    {
+        const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int g = lane >> 4, n = lane & 15;
+        auto emit = [&](int R, int I, const f32x4 &gh, const f32x4 &pp) {
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                kr[a] = sk[4 * R + a][c]; qr[a] = sq[4 * R + a][c]; gr[a] = sG[4 * R + a][c];
-                ki[a] = sk[4 * I + a][c]; gi[a] = sG[4 * I + a][c];
-            }
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int b2 = 0; b2 < 4; ++b2) {
-                    const float e = __expf(fminf(gr[a] - gi[b2], 0.f));
-                    gh[a][b2] += kr[a] * ki[b2] * e;
-                    pp[a][b2] += qr[a] * ki[b2] * e;
-                }
-        }
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b2 = 0; b2 < 4; ++b2) {
-                const int r = 4 * R + a, i = 4 * I + b2;
+            for (int u = 0; u < 4; ++u) {
+                const int r = 16 * R + 4 * g + u, i = 16 * I + n;
                 const bool in = r < L && i <= r;
-                blk[Y::GH + r * CB_C + i] = (in && i < r) ? gh[a][b2] : 0.f;
-                blk[Y::P + r * CB_C + i] = in ? pp[a][b2] : 0.f;
-                blk[Y::PT + i * CB_C + r] = in ? pp[a][b2] : 0.f;
-                sA[r][i] = (in && i < r) ? gh[a][b2] * sb[r] : 0.f;
+                const float ghv = (in && i < r) ? gh[u] : 0.f, pv = in ? pp[u] : 0.f;
+                blk[Y::GH + r * CB_C + i] = ghv;
+                blk[Y::P + r * CB_C + i] = pv;
+                blk[Y::PT + i * CB_C + r] = pv;
+                sA[r][i] = ghv * sb[r];
             }
+        };
+        for (int t = 0; t < 3; ++t) {
+            int R, I;
+            if (t == 0) {
+                R = I = wv;
+            } else {
+                const int q = wv + 4 * (t - 1);
+                if (q >= 6) break;
+                R = q < 1 ? 1 : q < 3 ? 2 : 3;
+                I = q - R * (R - 1) / 2;
+            }
+            const int r = 16 * R + n, i = 16 * I + n;
+            f32x4 gh = {0.f, 0.f, 0.f, 0.f}, pp = gh;
+            if (R != I) {
+                const int m = 16 * R - 1;
+                for (int c0 = 0; c0 < DK; c0 += 16)
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2) {
+                        const int c = c0 + 4 * g + s2;
+                        const float fr = __expf(sG[r][c] - sG[m][c]), fc = __expf(sG[m][c] - sG[i][c]);
+                        const float bk = sk[i][c] * fc;
+                        gh = __builtin_amdgcn_mfma_f32_16x16x4f32(sk[r][c] * fr, bk, gh, 0, 0, 0);
+                        pp = __builtin_amdgcn_mfma_f32_16x16x4f32(sq[r][c] * fr, bk, pp, 0, 0, 0);
+                    }
+                emit(R, I, gh, pp);
+                continue;
+            }
+            // diagonal block: the steepest channel decides the method
+            float span = 0.f;
+            for (int c = lane; c < DK; c += 64)
+                span = fmaxf(span, (R > 0 ? sG[16 * R - 1][c] : 0.f) - sG[16 * R + 15][c]);
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) span = fmaxf(span, __shfl_xor(span, o));
+            if (span <= kCbDiagSpan) {
+                for (int c0 = 0; c0 < DK; c0 += 16)
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2) {
+                        const int c = c0 + 4 * g + s2;
+                        const float mid = 0.5f * ((R > 0 ? sG[16 * R - 1][c] : 0.f) + sG[16 * R + 15][c]);
+                        const float fr = __expf(sG[r][c] - mid), fc = __expf(mid - sG[r][c]);
+                        const float bk = sk[r][c] * fc;   // columns are the same 16 tokens
+                        gh = __builtin_amdgcn_mfma_f32_16x16x4f32(sk[r][c] * fr, bk, gh, 0, 0, 0);
+                        pp = __builtin_amdgcn_mfma_f32_16x16x4f32(sq[r][c] * fr, bk, pp, 0, 0, 0);
+                    }
+            } else {
+                // lane holds the pairs (16R + 4g + u, 16R + n) of the accumulator layout
+                for (int c = 0; c < DK; ++c) {
+                    const float gi = sG[i][c], ki = sk[i][c];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int ru = 16 * R + 4 * g + u;
+                        const float f = ki * __expf(fminf(sG[ru][c] - gi, 0.f));
+                        gh[u] += sk[ru][c] * f;
+                        pp[u] += sq[ru][c] * f;
+                    }
+                }
+            }
+            emit(R, I, gh, pp);
+        }
     }
-    // upper-triangle pairs of A are zero
+    // blocks above the diagonal are zero
     for (int e = tid; e < CB_C * CB_C; e += 256) {
         const int r = e / CB_C, i = e % CB_C;
-        if (i / 4 > r / 4) {
+        if (i / 16 > r / 16) {
             sA[r][i] = 0.f;
             blk[Y::GH + e] = 0.f;
             blk[Y::P + e] = 0.f;
@@ -178,12 +231,29 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
         blk[Y::M + e] = sA[e / CB_C][e % CB_C];
         blk[Y::MT + e] = sA[e % CB_C][e / CB_C];
     }
-    // W = T K~ = M Diag(beta) K~
-    for (int e = tid; e < CB_C * DK; e += 256) {
-        const int r = e / DK, c = e % DK;
-        float acc = 0.f;
-        for (int i = 0; i <= r; ++i) acc += sA[r][i] * sb[i] * sk[i][c];
-        blk[Y::W + e] = acc;
+    // W = T K~ = M Diag(beta) K~ on the fp32 matrix cores: 16 x 16 output
+    // blocks (token block rb, key block cb) dealt round-robin to the four
+    // waves, the contraction over the token blocks ib <= rb (M is lower
+    // triangular).  In step s lane l (g = l / 16, n = l % 16) supplies
+    // A[n][4g + s] = M[16rb + n][i] beta_i and B[4g + s][n] = K~[i][16cb + n]
+    // with i = 16ib + 4g + s, and holds W[16rb + 4g + u][16cb + n].
+    {
+        constexpr int NKB = DK / 16;
+        const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int g = lane >> 4, n = lane & 15;
+        for (int b = wv; b < 4 * NKB; b += 4) {
+            const int rb = b / NKB, cb = b % NKB;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int ib = 0; ib <= rb; ++ib)
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) {
+                    const int i = 16 * ib + 4 * g + s2;
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[16 * rb + n][i] * sb[i], sk[i][16 * cb + n], acc, 0,
+                                                               0, 0);
+                }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) blk[Y::W + (16 * rb + 4 * g + u) * DK + 16 * cb + n] = acc[u];
+        }
     }
 }
 
