@@ -12,7 +12,7 @@ Prints ONE JSON line:
                back to back (HIP events around the 64 calls); the figure for
                the decode step inside each timed step is reported beside it
   roofline     prefill: algorithmic HBM bytes / average call duration vs 8 TB/s,
-               and vs what a plain 512 MiB device copy reaches in the same run
+               and vs what torch's plain 512 MiB device copy reaches in the same run
   prologue     the same prefill from raw pre-activations (softplus decay gate,
                sigmoid write gate and q/k L2 norm fused into the kernels)
   decode_multi 4 tokens per sequence per launch (multi-token decode), with
@@ -27,11 +27,13 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload long|prefill|packed] [--no-cpu-baseline]
        python bench.py --summarize DIR    per-kernel means of a rocprofv3 CSV run
        python bench.py --copy-calibration one 1 GiB device copy (counter scale)
+       python bench.py --steps S --warmup W --record-traffic FETCH WRITE SQ CAL_FETCH CAL_WRITE
+                        profiles/traffic.json from rocprofv3 --pmc result folders
 
 `roofline.traffic` is filled from profiles/traffic.json (HBM bytes per call
 measured with rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by the same counters
-on a plain 1 GiB copy) when the kernel sources still hash to the recorded
-value, else null.
+on a plain 1 GiB copy) while the sources of that call's kernels still hash to
+the recorded value, else null.
 """
 from __future__ import annotations
 
@@ -66,48 +68,131 @@ def chunk_flops_per_token_head(C=64, d=128):
     return 10 * C * d + 6 * d * d
 
 
-def kernel_sources_sha() -> str:
-    """sha256 over the HIP sources of libkda (what the counters were taken on)."""
+# Kernel sources behind each measured call: a recorded counter stays valid
+# only while its group's sources (and the shared device headers) are unchanged.
+SOURCE_GROUPS = {
+    "prefill": ["kda_prefill_mfma.hip", "kda_prefill_table.hip"],
+    "decode": ["kda_decode.hip"],
+    "short_conv": ["kda_conv.hip"],
+    "backward": ["kda_backward_chunked.hip", "kda_prefill_table.hip"],
+}
+SHARED_HEADERS = ["kda_common.hpp", "kda_prefill_common.hpp", "kda_launch.hpp"]
+# call key in profiles/traffic.json -> source group
+CALL_GROUPS = {"prefill_long": "prefill", "decode": "decode", "short_conv_prefill": "short_conv",
+               "short_conv_decode": "short_conv", "backward_T4096_H16": "backward"}
+
+
+def kernel_sources_sha(group: str) -> str:
+    """sha256 over the HIP sources of one kernel group (what its counters were
+    taken on)."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "gated_delta_rule_49_amd", "csrc")
-    for f in sorted(glob.glob(os.path.join(d, "*.hip")) + glob.glob(os.path.join(d, "*.hpp"))):
-        h.update(os.path.basename(f).encode())
-        h.update(open(f, "rb").read())
+    for f in sorted(SOURCE_GROUPS[group]) + SHARED_HEADERS:
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()
+
+
+def _traffic_record():
+    try:
+        return json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+    except (OSError, ValueError):
+        return None
 
 
 def measured_traffic(key):
     """HBM bytes per call for `key` from profiles/traffic.json, or None if the
     record is missing or was taken on different kernel sources."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    try:
-        rec = json.load(open(path))
-    except (OSError, ValueError):
+    rec = _traffic_record()
+    group = CALL_GROUPS.get(key)
+    if rec is None or group is None or key not in rec.get("calls", {}):
         return None
-    if rec.get("kernel_sources_sha") != kernel_sources_sha() or key not in rec.get("calls", {}):
+    if rec.get("sources_sha", {}).get(group) != kernel_sources_sha(group):
         return None
     c = rec["calls"][key]
     return c["fetch_kib"] * 1024 * rec["fetch_scale"] + c["write_kib"] * 1024 * rec["write_scale"]
 
 
-def measured_counter(kernel, counter):
+def measured_counter(kernel, counter, group="prefill"):
     """Per-dispatch value of a rocprofv3 counter for `kernel` recorded in
     profiles/traffic.json ("counters"), or None if missing or taken on
     different kernel sources."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    try:
-        rec = json.load(open(path))
-    except (OSError, ValueError):
-        return None
-    if rec.get("kernel_sources_sha") != kernel_sources_sha():
+    rec = _traffic_record()
+    if rec is None or rec.get("sources_sha", {}).get(group) != kernel_sources_sha(group):
         return None
     return rec.get("counters", {}).get(kernel, {}).get(counter)
 
 
-# Vector-ALU issue peak of MI355X: 256 CUs x 4 SIMDs, one wave64 VALU
-# instruction per SIMD every 4 cycles (16 lanes), at 2.4 GHz, counted in
-# lane-operations (64 per wave instruction).
-VALU_PEAK_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+def _counter_runs(dirs):
+    """{(kernel, counter): [per-dispatch values in launch order]} over the
+    rocprofv3 --pmc result folders `dirs`; kernel names without spaces, the
+    namespace or the argument list."""
+    acc = {}
+    for root in dirs:
+        for f in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
+            rows = list(csv.DictReader(open(f)))
+            if rows and "Dispatch_Id" in rows[0]:
+                rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+            for row in rows:
+                name = row["Kernel_Name"].split("(")[0].replace("void ", "").replace("kda::", "")
+                acc.setdefault((name.replace(" ", ""), row["Counter_Name"]), []).append(float(row["Counter_Value"]))
+    return acc
+
+
+# bytes a plain copy of 1 GiB (`--copy-calibration`) reads and writes
+COPY_CAL_KIB = float(1 << 20)
+
+
+def record_traffic(fetch_dir, write_dir, sq_dir, cal_fetch_dir, cal_write_dir, calls):
+    """Write profiles/traffic.json from rocprofv3 --pmc runs: FETCH_SIZE,
+    WRITE_SIZE and SQ instruction counters of `bench.py --steps S --warmup W
+    --no-cpu-baseline`, and FETCH_SIZE, WRITE_SIZE of `bench.py
+    --copy-calibration` (which fix the counters' scale).  `calls` = W + S
+    plain prefill calls, which come first in launch order (the fused-prologue
+    calls and the backward's checkpoint prefill follow and are left out)."""
+    acc = _counter_runs([fetch_dir, write_dir, sq_dir])
+    cal = _counter_runs([cal_fetch_dir, cal_write_dir])
+
+    def mean(table, kernel, counter, first=None):
+        v = table.get((kernel, counter))
+        if not v:
+            raise SystemExit(f"no {counter} dispatches of {kernel} in the counter runs")
+        v = v[:first] if first else v
+        return sum(v) / len(v)
+
+    fetch_scale = COPY_CAL_KIB / mean(cal, "__amd_rocclr_copyBuffer", "FETCH_SIZE")
+    write_scale = COPY_CAL_KIB / mean(cal, "__amd_rocclr_copyBuffer", "WRITE_SIZE")
+    groups = {
+        "prefill_long": [("intra_kernel<64,128>", calls), ("scan_kernel<64,128,float>", calls),
+                         ("chunk_table_kernel", calls)],
+        "decode": [("decode_kernel<128,128,unsignedshort,float,false>", None)],
+        "short_conv_prefill": [("short_conv_kernel<unsignedshort,unsignedshort,4,16>", None),
+                               ("conv_state_kernel<unsignedshort,4>", None)],
+        "short_conv_decode": [("conv_rows_kernel<unsignedshort,unsignedshort,4>", None)],
+        "backward_T4096_H16": [("cb_prep_kernel<128,unsignedshort>", None), ("cb_scan_kernel<128>", None),
+                               ("cb_grad_kernel<128,unsignedshort>", None)],
+    }
+    out_calls = {}
+    for key, ks in groups.items():
+        per = {k: [mean(acc, k, "FETCH_SIZE", n), mean(acc, k, "WRITE_SIZE", n)] for k, n in ks}
+        out_calls[key] = {"fetch_kib": sum(v[0] for v in per.values()),
+                          "write_kib": sum(v[1] for v in per.values()), "kernels": per}
+    counters = {}
+    for k in ("intra_kernel<64,128>", "scan_kernel<64,128,float>"):
+        counters[k] = {c: mean(acc, k, c, calls) for (kk, c) in acc if kk == k and c.startswith("SQ_")}
+    rec = {"what": "HBM bytes per call = FETCH_SIZE KiB * 1024 * fetch_scale + WRITE_SIZE KiB * 1024 * "
+                   "write_scale, means over dispatches of rocprofv3 --pmc runs of bench.py; the scales make "
+                   "the counters read 1 GiB each way on a plain 1 GiB device copy. counters: per-dispatch SQ "
+                   "counters of the plain prefill calls. A call is valid while its kernel group's sources "
+                   "hash to sources_sha (bench.py SOURCE_GROUPS).",
+           "sources_sha": {g: kernel_sources_sha(g) for g in SOURCE_GROUPS},
+           "fetch_scale": fetch_scale, "write_scale": write_scale,
+           "calls": out_calls, "counters": counters}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps({"fetch_scale": fetch_scale, "write_scale": write_scale,
+                      **{k: (v["fetch_kib"] * fetch_scale + v["write_kib"] * write_scale) * 1024 / 1e9
+                         for k, v in out_calls.items()}}))
 
 
 def summarize(root):
@@ -307,9 +392,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--record-traffic", nargs=5,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "SQ_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
+                    help="write profiles/traffic.json from rocprofv3 --pmc runs of "
+                         "`bench.py --steps S --warmup W --no-cpu-baseline` and `bench.py --copy-calibration` "
+                         "(give the same --steps/--warmup)")
     args = ap.parse_args()
     if args.summarize:
         summarize(args.summarize)
+        return
+    if args.record_traffic:
+        record_traffic(*args.record_traffic, calls=args.warmup + args.steps)
         return
     if args.copy_calibration:
         copy_calibration()
@@ -388,8 +481,10 @@ def main():
     torch.cuda.synchronize()
     dec_loop = dec_a.elapsed_time(dec_b) / 64
 
-    # Achievable HBM bandwidth on this machine right now: a plain 512 MiB device
+    # A reference rate for this box right now: torch's plain 512 MiB device
     # copy (read + write, the traffic of one decode step), best of 3 x 10.
+    # It is not the ceiling: copies with non-temporal accesses and small
+    # per-workgroup tiles move ~6.2-6.8 TB/s on MI355X.
     csrc = torch.empty(1 << 27, dtype=torch.float32, device=dev).fill_(1.0)
     cdst = torch.empty_like(csrc)
     copy_gbs = 0.0
@@ -451,7 +546,7 @@ def main():
         multi["with_token_states" if with_states else "state_only"] = {
             "value": Bd * M_TOK / (ms * 1e-3), "unit": "seq-token-steps/s", "avg_ms": ms,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "frac_of_achievable": None, "algorithmic_bytes": nbytes,
+                         "frac": gbs / HBM_PEAK_GBS, "frac_of_torch_copy": None, "algorithmic_bytes": nbytes,
                          "kernel": "decode_kernel (m = 4)"}}
     del tsb, om, mt
 
@@ -479,8 +574,9 @@ def main():
                        "shape": f"[{Bp}, {T}, {H * d}] bf16 -> bf16, W={CW}",
                        "roofline": {"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                                     "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                    "frac_of_achievable": None, "algorithmic_bytes": nbytes,
-                                    "kernel": "short_conv_kernel<bf16,bf16,4> + conv_state_kernel"}}
+                                    "frac_of_torch_copy": None, "algorithmic_bytes": nbytes,
+                                    "kernel": "short_conv_kernel<bf16,bf16,4> + conv_state_kernel",
+                                    "traffic": measured_traffic("short_conv_prefill")}}
     del cx, cy, cfin
     dx = D["q"][0].reshape(Bd, 1, 32 * 128)
     dst = torch.zeros((Bd, 32 * 128, CW - 1), dtype=torch.float32, device=dev)
@@ -534,7 +630,8 @@ def main():
                 "roofline": {"bound": "hbm", "achieved": bwd_bytes / (bwd_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": bwd_bytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                              "algorithmic_bytes": bwd_bytes,
-                             "kernel": "cb_prep_kernel + cb_scan_kernel + cb_grad_kernel (d=128, bf16)"}}
+                             "kernel": "cb_prep_kernel + cb_scan_kernel + cb_grad_kernel (d=128, bf16)",
+                             "traffic": measured_traffic("backward_T4096_H16")}}
     del bq, bk, bv, bb, bla, bdo, ck, BX
 
     rng = range(args.warmup, n_ev)
@@ -574,7 +671,7 @@ def main():
                    "decode_workload": "decode_B256_H32_d128", "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": p_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": p_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(f"prefill_{args.workload}"),
-                     "achievable_copy_gbs": copy_gbs, "frac_of_achievable": p_gbs / copy_gbs,
+                     "torch_copy_gbs": copy_gbs, "frac_of_torch_copy": p_gbs / copy_gbs,
                      "kernel": "kda_prefill_chunked (chunk table + intra_kernel + scan_kernel)",
                      "algorithmic_bytes": pbytes, "avg_ms": pre,
                      "kernels_ms": {"intra_kernel": intra, "scan_kernel": scan},
@@ -586,7 +683,7 @@ def main():
                    "avg_ms_right_after_prefill": dec_in_step,
                    "roofline": {"bound": "hbm", "achieved": d_gbs, "peak": HBM_PEAK_GBS,
                                 "unit": "GB/s", "frac": d_gbs / HBM_PEAK_GBS,
-                                "achievable_copy_gbs": copy_gbs, "frac_of_achievable": d_gbs / copy_gbs,
+                                "torch_copy_gbs": copy_gbs, "frac_of_torch_copy": d_gbs / copy_gbs,
                                 "traffic": measured_traffic("decode"),
                                 "kernel": "decode_kernel (m = 1)", "algorithmic_bytes": dbytes}},
         "prefill_ms": pre,
@@ -602,9 +699,9 @@ def main():
                                         "frac": pro_bytes / (pro * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                         "algorithmic_bytes": pro_bytes}}
     for v_ in multi.values():
-        v_["roofline"]["frac_of_achievable"] = v_["roofline"]["achieved"] / copy_gbs
+        v_["roofline"]["frac_of_torch_copy"] = v_["roofline"]["achieved"] / copy_gbs
     out["decode_multi"] = dict(tokens_per_launch=M_TOK, **multi)
-    conv["prefill"]["roofline"]["frac_of_achievable"] = conv["prefill"]["roofline"]["achieved"] / copy_gbs
+    conv["prefill"]["roofline"]["frac_of_torch_copy"] = conv["prefill"]["roofline"]["achieved"] / copy_gbs
     out["short_conv"] = conv
     out["backward"] = backward
     if not args.no_cpu_baseline:

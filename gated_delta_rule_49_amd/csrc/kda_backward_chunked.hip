@@ -336,7 +336,13 @@ __global__ void __launch_bounds__(256) cb_scan_kernel(CbParams p) {
     constexpr int LC = C + 4, LK = DK + 4;   // padded strides of the [column][row] tiles
     const int H = p.H, dv = p.dv;
     const int nvt = dv / BV;
-    const int vt = blockIdx.x % nvt, h = (blockIdx.x / nvt) % H, n_seq = blockIdx.x / (nvt * H);
+    // XCD-aware order: the nvt column tiles of one (sequence, head) share
+    // blockIdx % 8, hence one XCD and its L2, where the chunk blocks they all
+    // read are shared
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int vt = slot % nvt, pair = xcd + 8 * (slot / nvt);
+    if (pair >= p.N * H) return;
+    const int h = pair % H, n_seq = pair / H;
     const int j0 = vt * BV;
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -909,8 +915,8 @@ hipError_t run_cb(const CbParams &p, int n_items, hipStream_t s) {
     hipLaunchKernelGGL((cb_prep_kernel<DK, TI>), dim3(n_items), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((cb_scan_kernel<DK>), dim3(static_cast<unsigned>(p.N) * p.H * (p.dv / CB_SCAN_BV)), dim3(256),
-                       0, s, p);
+    const unsigned pairs8 = static_cast<unsigned>((p.N * p.H + 7) / 8);
+    hipLaunchKernelGGL((cb_scan_kernel<DK>), dim3(pairs8 * 8 * (p.dv / CB_SCAN_BV)), dim3(256), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t lds = CbGradLds<DK>::FLOATS * sizeof(float);
