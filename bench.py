@@ -195,6 +195,12 @@ def record_traffic(fetch_dir, write_dir, sq_dir, cal_fetch_dir, cal_write_dir, c
                          for k, v in out_calls.items()}}))
 
 
+# Vector-ALU issue peak of MI355X: 256 CUs x 4 SIMDs, one wave64 VALU
+# instruction per SIMD every 4 cycles (16 lanes), at 2.4 GHz, counted in
+# lane-operations (64 per wave instruction).
+VALU_PEAK_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+
 def summarize(root):
     """Per-kernel means of rocprofv3 --output-format csv results under root."""
     for f in glob.glob(os.path.join(root, "**", "*kernel_stats.csv"), recursive=True):
