@@ -27,7 +27,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload long|prefill|packed] [--no-cpu-baseline]
        python bench.py --summarize DIR    per-kernel means of a rocprofv3 CSV run
        python bench.py --copy-calibration one 1 GiB device copy (counter scale)
-       python bench.py --steps S --warmup W --record-traffic FETCH WRITE SQ CAL_FETCH CAL_WRITE
+       python bench.py --steps S --warmup W --record-traffic FETCH WRITE SQ CAL_FETCH CAL_WRITE MFMA
                         profiles/traffic.json from rocprofv3 --pmc result folders
 
 `roofline.traffic` is filled from profiles/traffic.json (HBM bytes per call
@@ -143,14 +143,16 @@ def _counter_runs(dirs):
 COPY_CAL_KIB = float(1 << 20)
 
 
-def record_traffic(fetch_dir, write_dir, sq_dir, cal_fetch_dir, cal_write_dir, calls):
+def record_traffic(fetch_dir, write_dir, sq_dir, cal_fetch_dir, cal_write_dir, mfma_dir, calls):
     """Write profiles/traffic.json from rocprofv3 --pmc runs: FETCH_SIZE,
     WRITE_SIZE and SQ instruction counters of `bench.py --steps S --warmup W
     --no-cpu-baseline`, and FETCH_SIZE, WRITE_SIZE of `bench.py
-    --copy-calibration` (which fix the counters' scale).  `calls` = W + S
+    --copy-calibration` (which fix the counters' scale), and the matrix-core
+    counters (SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_*,
+    GRBM_GUI_ACTIVE) of the bench in `mfma_dir`.  `calls` = W + S
     plain prefill calls, which come first in launch order (the fused-prologue
     calls and the backward's checkpoint prefill follow and are left out)."""
-    acc = _counter_runs([fetch_dir, write_dir, sq_dir])
+    acc = _counter_runs([fetch_dir, write_dir, sq_dir, mfma_dir])
     cal = _counter_runs([cal_fetch_dir, cal_write_dir])
 
     def mean(table, kernel, counter, first=None):
@@ -179,7 +181,8 @@ def record_traffic(fetch_dir, write_dir, sq_dir, cal_fetch_dir, cal_write_dir, c
                           "write_kib": sum(v[1] for v in per.values()), "kernels": per}
     counters = {}
     for k in ("intra_kernel<64,128>", "scan_kernel<64,128,float>"):
-        counters[k] = {c: mean(acc, k, c, calls) for (kk, c) in acc if kk == k and c.startswith("SQ_")}
+        counters[k] = {c: mean(acc, k, c, calls) for (kk, c) in acc
+                       if kk == k and (c.startswith("SQ_") or c == "GRBM_GUI_ACTIVE")}
     rec = {"what": "HBM bytes per call = FETCH_SIZE KiB * 1024 * fetch_scale + WRITE_SIZE KiB * 1024 * "
                    "write_scale, means over dispatches of rocprofv3 --pmc runs of bench.py; the scales make "
                    "the counters read 1 GiB each way on a plain 1 GiB device copy. counters: per-dispatch SQ "
@@ -371,6 +374,26 @@ def intra_valu(intra_ms):
             "peak_basis": "256 CU x 4 SIMD x 16 lanes x 2.4 GHz (one wave64 instruction per 4 cycles)"}
 
 
+def mfma_busy(kernel_ms):
+    """rocprofv3 matrix-core utilisation of the prefill kernels: busy cycles
+    of the MFMA units summed over the 1024 SIMDs (SQ_VALU_MFMA_BUSY_CYCLES)
+    over 1024 x the active cycles of one XCD (GRBM_GUI_ACTIVE summed over the
+    8 XCDs / 8), and the MFMA flops issued (SQ_INSTS_VALU_MFMA_MOPS_* x 512)
+    per live kernel time; null when the record does not match the sources."""
+    out = {}
+    for name, key in (("intra_kernel", "intra_kernel<64,128>"), ("scan_kernel", "scan_kernel<64,128,float>")):
+        busy = measured_counter(key, "SQ_VALU_MFMA_BUSY_CYCLES")
+        active = measured_counter(key, "GRBM_GUI_ACTIVE")
+        if busy is None or active is None:
+            return None
+        mops = sum(measured_counter(key, f"SQ_INSTS_VALU_MFMA_MOPS_{t}") or 0.0 for t in ("BF16", "F32"))
+        out[name] = {"busy_frac": busy / (active / 8 * 1024),
+                     "issued_tflops": mops * 512 / (kernel_ms[name] * 1e-3) / 1e12}
+    out["source"] = ("rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+                     "SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE, plain prefill calls")
+    return out
+
+
 def _decode_into(kda, mt, state, om, tsb):
     """kda.decode writing the per-token states into a preallocated buffer
     (the binding allocates them otherwise)."""
@@ -398,8 +421,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--record-traffic", nargs=5,
-                    metavar=("FETCH_DIR", "WRITE_DIR", "SQ_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
+    ap.add_argument("--record-traffic", nargs=6,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "SQ_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR", "MFMA_DIR"),
                     help="write profiles/traffic.json from rocprofv3 --pmc runs of "
                          "`bench.py --steps S --warmup W --no-cpu-baseline` and `bench.py --copy-calibration` "
                          "(give the same --steps/--warmup)")
@@ -683,7 +706,10 @@ def main():
                      "kernels_ms": {"intra_kernel": intra, "scan_kernel": scan},
                      "useful_mfma_tflops": useful_tf,
                      "useful_mfma_frac": useful_tf / BF16_PEAK_TFLOPS,
-                     "intra_valu": intra_valu(intra)},
+                     # counters recorded on the long workload's calls
+                     "intra_valu": intra_valu(intra) if args.workload == "long" else None,
+                     "mfma_busy": (mfma_busy({"intra_kernel": intra, "scan_kernel": scan})
+                                   if args.workload == "long" else None)},
         "decode": {"value": Bd / (dec * 1e-3), "unit": "seq-steps/s", "avg_ms": dec,
                    "timing": "64 consecutive steps of the decode trajectory, one HIP event pair",
                    "avg_ms_right_after_prefill": dec_in_step,
