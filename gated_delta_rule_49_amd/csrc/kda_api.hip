@@ -54,10 +54,18 @@ bool use_mfma(const kda_prefill_args *a) {
     return a->in_dtype == KDA_BF16 && mfma_supported(a->d_k, a->d_v, a->chunk_size);
 }
 
+// the fp32 matrix-core path: fp32 inputs, and bf16 inputs whose head sizes
+// the bf16 matrix-core path does not take (chunk 32 or 64, no prologue)
+bool use_f32mm(const kda_prefill_args *a) {
+    return !use_mfma(a) && f32mm_supported(a->d_k, a->d_v, a->chunk_size, a->prologue);
+}
+
 size_t workspace_for(const kda_prefill_args *a) {
     size_t bytes = table_bytes(a->num_seqs, max_chunks(a));
     if (use_mfma(a))
         bytes += static_cast<size_t>(max_chunks(a)) * a->H * mfma_block_bytes(a->chunk_size, a->d_k);
+    else if (use_f32mm(a))
+        bytes += static_cast<size_t>(max_chunks(a)) * a->H * cb_block_bytes(a->d_k);
     return bytes;
 }
 
@@ -123,6 +131,9 @@ kda_status kda_prefill_chunked(const kda_prefill_args *a, void *hip_stream) {
         if (use_mfma(a))
             e = launch_prefill_mfma(p, ws + table_bytes(p.N, p.n_chunks_bound), a->out_dtype, s,
                                     ev ? ev[1] : nullptr);
+        else if (use_f32mm(a))
+            e = launch_prefill_f32mm(p, reinterpret_cast<float *>(ws + table_bytes(p.N, p.n_chunks_bound)),
+                                     a->in_dtype, a->out_dtype, s, ev ? ev[1] : nullptr);
         else {
             e = launch_prefill_f32(p, a->in_dtype, a->out_dtype, s);
             if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);

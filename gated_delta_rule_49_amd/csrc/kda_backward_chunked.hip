@@ -17,32 +17,12 @@
 //   grad  (chunk, head):  every gradient of the chunk's tokens from its
 //         entering state (the forward checkpoint), dS', dO and the block.
 // No atomics: each chunk-head writes its own tokens' gradients.
+#include <type_traits>
+
+#include "kda_chunk_block.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
-
-constexpr int CB_C = 64;  // maximum chunk length
-// a diagonal 16-token block of the prep's Gram products is factorised around
-// its midpoint while it decays by at most this many nats in every channel
-constexpr float kCbDiagSpan = 80.f;
-
-// per-(chunk, head) block of the prep kernel, fp32, row-major
-template <int DK>
-struct CbLay {
-    static constexpr size_t G = 0;                       // [C][DK]  cumulative log decay
-    static constexpr size_t KT = G + CB_C * DK;          // [C][DK]  k e^G
-    static constexpr size_t QT = KT + CB_C * DK;         // [C][DK]  q e^G
-    static constexpr size_t KB = QT + CB_C * DK;         // [C][DK]  k e^{G_L - G}
-    static constexpr size_t W = KB + CB_C * DK;          // [C][DK]  T K~
-    static constexpr size_t GH = W + CB_C * DK;          // [C][C]   k_r . k_i e^{..}, i < r
-    static constexpr size_t P = GH + CB_C * CB_C;        // [C][C]   q_r . k_i e^{..}, i <= r
-    static constexpr size_t PT = P + CB_C * CB_C;        // [C][C]   P^T
-    static constexpr size_t M = PT + CB_C * CB_C;        // [C][C]   (I + A)^-1
-    static constexpr size_t MT = M + CB_C * CB_C;        // [C][C]   M^T
-    static constexpr size_t GAM = MT + CB_C * CB_C;      // [DK]     e^{G_L}
-    static constexpr size_t BETA = GAM + DK;             // [C]
-    static constexpr size_t FLOATS = (BETA + CB_C + 63) / 64 * 64;
-};
 
 size_t cb_block_bytes(int dk) {
     switch (dk) {
@@ -54,7 +34,9 @@ size_t cb_block_bytes(int dk) {
 }
 
 // ------------------------------------------------------------------ prep --
-template <int DK, typename TI>
+// FWD: only what the forward needs (K~, Q~, K^, g, beta, P, M): no G, Gh,
+// P^T, M^T or W.
+template <int DK, typename TI, bool FWD>
 __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
     if (*p.status != 0) return;
     using Y = CbLay<DK>;
@@ -71,7 +53,16 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
     const TI *la = static_cast<const TI *>(p.log_alpha);
     const TI *beta = static_cast<const TI *>(p.beta);
 
-    __shared__ float sq[CB_C][DK + 1], sk[CB_C][DK + 1], sG[CB_C][DK + 1];
+    // fp32 inputs (the 1e-5 contract): the cumulative decay stays in fp64,
+    // exponents are differences taken in fp64 and exponentials are the
+    // correctly rounded expf (a cumulative log-decay of ~50 held in fp32 puts
+    // ~4e-6 relative error on a decay factor); bf16 inputs: fp32 and the
+    // hardware exp
+    constexpr bool kExact = sizeof(TI) == 4;
+    using GT = typename std::conditional<kExact, double, float>::type;
+    auto ex = [](GT x) { return kExact ? expf(static_cast<float>(x)) : __expf(static_cast<float>(x)); };
+    __shared__ float sq[CB_C][DK + 1], sk[CB_C][DK + 1];
+    __shared__ GT sG[CB_C][DK + 1];
     __shared__ float sA[CB_C][CB_C + 1];
     __shared__ float sb[CB_C];
 
@@ -89,20 +80,21 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
         double acc = 0.0;
         for (int r = 0; r < CB_C; ++r) {
             acc += static_cast<double>(sG[r][tid]);
-            sG[r][tid] = static_cast<float>(acc);
+            sG[r][tid] = static_cast<GT>(acc);
         }
     }
     __syncthreads();
     // elementwise factors and the decay of the whole chunk
     for (int e = tid; e < CB_C * DK; e += 256) {
         const int r = e / DK, c = e % DK;
-        const float G = sG[r][c], E = __expf(G);
-        blk[Y::G + e] = G;
+        const GT G = sG[r][c];
+        const float E = ex(G);
+        if (!FWD) blk[Y::G + e] = static_cast<float>(G);
         blk[Y::KT + e] = sk[r][c] * E;
         blk[Y::QT + e] = sq[r][c] * E;
-        blk[Y::KB + e] = sk[r][c] * __expf(sG[CB_C - 1][c] - G);
+        blk[Y::KB + e] = sk[r][c] * ex(sG[CB_C - 1][c] - G);
     }
-    for (int c = tid; c < DK; c += 256) blk[Y::GAM + c] = __expf(sG[CB_C - 1][c]);
+    for (int c = tid; c < DK; c += 256) blk[Y::GAM + c] = ex(sG[CB_C - 1][c]);
     if (tid < CB_C) blk[Y::BETA + tid] = sb[tid];
     // Gh and P in 16 x 16 blocks (R, I <= R) on the fp32 matrix cores: in
     // step s lane l (g = l / 16, n = l % 16) supplies row r = 16R + n and
@@ -124,9 +116,11 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
                 const int r = 16 * R + 4 * g + u, i = 16 * I + n;
                 const bool in = r < L && i <= r;
                 const float ghv = (in && i < r) ? gh[u] : 0.f, pv = in ? pp[u] : 0.f;
-                blk[Y::GH + r * CB_C + i] = ghv;
                 blk[Y::P + r * CB_C + i] = pv;
-                blk[Y::PT + i * CB_C + r] = pv;
+                if (!FWD) {
+                    blk[Y::GH + r * CB_C + i] = ghv;
+                    blk[Y::PT + i * CB_C + r] = pv;
+                }
                 sA[r][i] = ghv * sb[r];
             }
         };
@@ -148,7 +142,7 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
 #pragma unroll
                     for (int s2 = 0; s2 < 4; ++s2) {
                         const int c = c0 + 4 * g + s2;
-                        const float fr = __expf(sG[r][c] - sG[m][c]), fc = __expf(sG[m][c] - sG[i][c]);
+                        const float fr = ex(sG[r][c] - sG[m][c]), fc = ex(sG[m][c] - sG[i][c]);
                         const float bk = sk[i][c] * fc;
                         gh = __builtin_amdgcn_mfma_f32_16x16x4f32(sk[r][c] * fr, bk, gh, 0, 0, 0);
                         pp = __builtin_amdgcn_mfma_f32_16x16x4f32(sq[r][c] * fr, bk, pp, 0, 0, 0);
@@ -159,7 +153,7 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
             // diagonal block: the steepest channel decides the method
             float span = 0.f;
             for (int c = lane; c < DK; c += 64)
-                span = fmaxf(span, (R > 0 ? sG[16 * R - 1][c] : 0.f) - sG[16 * R + 15][c]);
+                span = fmaxf(span, static_cast<float>((R > 0 ? sG[16 * R - 1][c] : GT(0)) - sG[16 * R + 15][c]));
 #pragma unroll
             for (int o = 32; o >= 1; o >>= 1) span = fmaxf(span, __shfl_xor(span, o));
             if (span <= kCbDiagSpan) {
@@ -167,8 +161,8 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
 #pragma unroll
                     for (int s2 = 0; s2 < 4; ++s2) {
                         const int c = c0 + 4 * g + s2;
-                        const float mid = 0.5f * ((R > 0 ? sG[16 * R - 1][c] : 0.f) + sG[16 * R + 15][c]);
-                        const float fr = __expf(sG[r][c] - mid), fc = __expf(mid - sG[r][c]);
+                        const GT mid = GT(0.5) * ((R > 0 ? sG[16 * R - 1][c] : GT(0)) + sG[16 * R + 15][c]);
+                        const float fr = ex(sG[r][c] - mid), fc = ex(mid - sG[r][c]);
                         const float bk = sk[r][c] * fc;   // columns are the same 16 tokens
                         gh = __builtin_amdgcn_mfma_f32_16x16x4f32(sk[r][c] * fr, bk, gh, 0, 0, 0);
                         pp = __builtin_amdgcn_mfma_f32_16x16x4f32(sq[r][c] * fr, bk, pp, 0, 0, 0);
@@ -176,11 +170,13 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
             } else {
                 // lane holds the pairs (16R + 4g + u, 16R + n) of the accumulator layout
                 for (int c = 0; c < DK; ++c) {
-                    const float gi = sG[i][c], ki = sk[i][c];
+                    const GT gi = sG[i][c];
+                    const float ki = sk[i][c];
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const int ru = 16 * R + 4 * g + u;
-                        const float f = ki * __expf(fminf(sG[ru][c] - gi, 0.f));
+                        const GT d = sG[ru][c] - gi;
+                        const float f = ki * ex(d < GT(0) ? d : GT(0));
                         gh[u] += sk[ru][c] * f;
                         pp[u] += sq[ru][c] * f;
                     }
@@ -194,9 +190,11 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
         const int r = e / CB_C, i = e % CB_C;
         if (i / 16 > r / 16) {
             sA[r][i] = 0.f;
-            blk[Y::GH + e] = 0.f;
             blk[Y::P + e] = 0.f;
-            blk[Y::PT + i * CB_C + r] = 0.f;
+            if (!FWD) {
+                blk[Y::GH + e] = 0.f;
+                blk[Y::PT + i * CB_C + r] = 0.f;
+            }
         }
     }
     __syncthreads();
@@ -221,10 +219,15 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
 #pragma unroll
         for (int r = 0; r < CB_C; ++r) sA[r][tid] = mc[r];
     }
+    if (FWD) {
+        __syncthreads();
+        for (int e = tid; e < CB_C * CB_C; e += 256) blk[Y::M + e] = sA[e / CB_C][e % CB_C];
+        return;
+    }
     // K~ in place of k (k itself is no longer needed)
     for (int e = tid; e < CB_C * DK; e += 256) {
         const int r = e / DK, c = e % DK;
-        sk[r][c] *= __expf(sG[r][c]);
+        sk[r][c] *= ex(sG[r][c]);
     }
     __syncthreads();
     for (int e = tid; e < CB_C * CB_C; e += 256) {
@@ -912,7 +915,7 @@ __global__ void __launch_bounds__(CB_GRAD_NT) cb_grad_kernel(CbParams p) {
 namespace {
 template <int DK, typename TI>
 hipError_t run_cb(const CbParams &p, int n_items, hipStream_t s) {
-    hipLaunchKernelGGL((cb_prep_kernel<DK, TI>), dim3(n_items), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((cb_prep_kernel<DK, TI, false>), dim3(n_items), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned pairs8 = static_cast<unsigned>((p.N * p.H + 7) / 8);
@@ -928,6 +931,26 @@ hipError_t run_cb(const CbParams &p, int n_items, hipStream_t s) {
     return hipGetLastError();
 }
 }  // namespace
+
+hipError_t launch_chunk_prep_fwd(const CbParams &p, int n_items, int in_dtype, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(n_items)), block(256);
+    if (in_dtype == 0) {
+        switch (p.dk) {
+            case 16: hipLaunchKernelGGL((cb_prep_kernel<16, float, true>), grid, block, 0, s, p); break;
+            case 32: hipLaunchKernelGGL((cb_prep_kernel<32, float, true>), grid, block, 0, s, p); break;
+            case 64: hipLaunchKernelGGL((cb_prep_kernel<64, float, true>), grid, block, 0, s, p); break;
+            default: hipLaunchKernelGGL((cb_prep_kernel<128, float, true>), grid, block, 0, s, p); break;
+        }
+    } else {
+        switch (p.dk) {
+            case 16: hipLaunchKernelGGL((cb_prep_kernel<16, bf16_t, true>), grid, block, 0, s, p); break;
+            case 32: hipLaunchKernelGGL((cb_prep_kernel<32, bf16_t, true>), grid, block, 0, s, p); break;
+            case 64: hipLaunchKernelGGL((cb_prep_kernel<64, bf16_t, true>), grid, block, 0, s, p); break;
+            default: hipLaunchKernelGGL((cb_prep_kernel<128, bf16_t, true>), grid, block, 0, s, p); break;
+        }
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_backward_chunked(const CbParams &p, int n_items, hipStream_t s) {
     switch (p.dk) {

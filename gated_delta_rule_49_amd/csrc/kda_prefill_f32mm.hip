@@ -1,0 +1,206 @@
+// Chunked KDA prefill in fp32 on the fp32 matrix cores (v_mfma_f32_16x16x4_f32:
+// fp32 products and fp32 sums), for fp32 inputs (the 1e-5 contract) and for
+// head sizes the bf16 matrix-core path does not take.
+//
+// Module 04 — KDA II: Chunked Parallelism & the Full Sublayer, §1 "The
+// recurrence has affine form": each chunk's transition is formed from the
+// chunk alone, in structured form, and the chunks are then applied in order.
+// For a chunk of L tokens with incoming state S (K~ = k e^G, Q~ = q e^G,
+// K^ = k e^{G_L - G}, g = e^{G_L}, M = (I + Diag(beta) Gh)^-1):
+//     X = V - K~ S,   Delta = M Diag(beta) X,   O = Q~ S + P Delta,
+//     S' = Diag(g) S + K^^T Delta.
+// Two kernels: the chunk prep kernel (forward mode; one workgroup per
+// (chunk, head), shared with the chunked backward) writes K~, Q~, K^, g,
+// beta, P and M per (chunk, head); the scan below walks each sequence's
+// chunks in order, one workgroup per (sequence, head, 16-column tile of S).
+#include "kda_chunk_block.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+namespace {
+
+// 16 x 16 x 16 block product on fp32 matrix cores: in step s lane l
+// (g = l / 16, n = l % 16) supplies A[n][4g + s] = a[s] and B[4g + s][n] = b[s];
+// the lane holds D[4g + u][n] in acc[u].
+__device__ __forceinline__ f32x4 mmf32(const f32x4 &a, const f32x4 &b, f32x4 acc) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+    return acc;
+}
+
+// Wave w computes token block w of X, Delta and O and owns key blocks
+// w, w + 4 of the state (accumulator layout, for the whole sequence).  S, X
+// and Delta pass between the waves through LDS transposed ([column][row]),
+// so a lane's four contraction values are one 16-byte read.
+template <int DK, typename TI, typename TO>
+__global__ void __launch_bounds__(256) f32mm_scan_kernel(PrefillParams p, const float *__restrict__ blocks) {
+    if (*p.status != 0) return;
+    using Y = CbLay<DK>;
+    constexpr int C = CB_C, NKB = DK / 16, KPW = (NKB + 3) / 4;
+    constexpr int LC = C + 4, LK = DK + 4;  // padded strides of the [column][row] tiles
+    const int H = p.H, dv = p.dv;
+    const int nvt = dv / 16;
+    // XCD-aware order: the column tiles of one (sequence, head) share
+    // blockIdx % 8, hence one XCD and its L2, where their chunk blocks are
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int vt = slot % nvt, pair = xcd + 8 * (slot / nvt);
+    if (pair >= p.N * H) return;
+    const int h = pair % H, n_seq = pair / H;
+    const int j0 = 16 * vt;
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, n = lane & 15;
+    const SeqRange sr = seq_range(p, n_seq);
+    const int64_t cbase = p.chunk_off[n_seq];
+    const int nch = p.chunk_off[n_seq + 1] - p.chunk_off[n_seq];
+    const TI *v = static_cast<const TI *>(p.v);
+    TO *o = static_cast<TO *>(p.o);
+
+    __shared__ __attribute__((aligned(16))) float sT[16][LK];   // S^T
+    __shared__ __attribute__((aligned(16))) float xT[16][LC];   // X^T
+    __shared__ __attribute__((aligned(16))) float dT[16][LC];   // Delta^T
+
+    const int64_t soff = (static_cast<int64_t>(n_seq) * H + h) * DK * dv;
+    f32x4 st[KPW];
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) {
+        const int kb = w + 4 * i;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            st[i][u] = (kb < NKB && p.initial_state)
+                           ? p.initial_state[soff + static_cast<int64_t>(16 * kb + 4 * g + u) * dv + j0 + n]
+                           : 0.f;
+        if (kb < NKB) *reinterpret_cast<f32x4 *>(&sT[n][16 * kb + 4 * g]) = st[i];
+    }
+    __syncthreads();
+
+    for (int ch = 0; ch < nch; ++ch) {
+        const int64_t x = cbase + ch;
+        const int64_t t0 = sr.start + static_cast<int64_t>(ch) * p.C;
+        const int L = min(p.C, sr.len - ch * p.C);
+        const float *blk = blocks + (static_cast<size_t>(x) * H + h) * Y::FLOATS;
+        if (p.chunk_states) {
+            float *cs = p.chunk_states + (x * H + h) * static_cast<int64_t>(DK) * dv;
+#pragma unroll
+            for (int i = 0; i < KPW; ++i) {
+                const int kb = w + 4 * i;
+                if (kb >= NKB) continue;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) cs[static_cast<int64_t>(16 * kb + 4 * g + u) * dv + j0 + n] = st[i][u];
+            }
+        }
+        // (1) token block w: X = V - K~ S and (q e^G) S
+        const int r0 = 16 * w;
+        f32x4 xa = {0.f, 0.f, 0.f, 0.f}, oa = xa;
+#pragma unroll
+        for (int cb = 0; cb < NKB; ++cb) {
+            const f32x4 sb = *reinterpret_cast<const f32x4 *>(&sT[n][16 * cb + 4 * g]);
+            xa = mmf32(*reinterpret_cast<const f32x4 *>(blk + Y::KT + (r0 + n) * DK + 16 * cb + 4 * g), sb, xa);
+            oa = mmf32(*reinterpret_cast<const f32x4 *>(blk + Y::QT + (r0 + n) * DK + 16 * cb + 4 * g), sb, oa);
+        }
+        f32x4 xv;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = r0 + 4 * g + u;
+            const float vv = r < L ? io<TI>::ld(v, ((t0 + r) * H + h) * dv + j0 + n) : 0.f;
+            xv[u] = vv - xa[u];
+        }
+        *reinterpret_cast<f32x4 *>(&xT[n][r0 + 4 * g]) = xv;
+        __syncthreads();
+        // (2) token block w: Delta = M Diag(beta) X (M lower triangular)
+        f32x4 da = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ib = 0; ib < C / 16; ++ib) {
+            if (ib > w) continue;
+            const f32x4 m4 = *reinterpret_cast<const f32x4 *>(blk + Y::M + (r0 + n) * C + 16 * ib + 4 * g);
+            const f32x4 b4 = *reinterpret_cast<const f32x4 *>(blk + Y::BETA + 16 * ib + 4 * g);
+            da = mmf32(m4 * b4, *reinterpret_cast<const f32x4 *>(&xT[n][16 * ib + 4 * g]), da);
+        }
+        *reinterpret_cast<f32x4 *>(&dT[n][r0 + 4 * g]) = da;
+        __syncthreads();
+        // (3) token block w: O = (q e^G) S + P Delta (P lower triangular)
+#pragma unroll
+        for (int ib = 0; ib < C / 16; ++ib) {
+            if (ib > w) continue;
+            oa = mmf32(*reinterpret_cast<const f32x4 *>(blk + Y::P + (r0 + n) * C + 16 * ib + 4 * g),
+                       *reinterpret_cast<const f32x4 *>(&dT[n][16 * ib + 4 * g]), oa);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = r0 + 4 * g + u;
+            if (r < L) io<TO>::st(o, ((t0 + r) * H + h) * dv + j0 + n, oa[u]);
+        }
+        // (4) key blocks w, w + 4: S = Diag(g) S + K^^T Delta; the new state
+        //     replaces S^T in LDS (every wave's reads of it were in step 1)
+#pragma unroll
+        for (int i = 0; i < KPW; ++i) {
+            const int kb = w + 4 * i;
+            if (kb >= NKB) continue;
+            f32x4 acc = *reinterpret_cast<const f32x4 *>(blk + Y::GAM + 16 * kb + 4 * g) * st[i];
+#pragma unroll
+            for (int rb = 0; rb < C / 16; ++rb) {
+                f32x4 a4;
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) a4[s2] = blk[Y::KB + (16 * rb + 4 * g + s2) * DK + 16 * kb + n];
+                acc = mmf32(a4, *reinterpret_cast<const f32x4 *>(&dT[n][16 * rb + 4 * g]), acc);
+            }
+            st[i] = acc;
+            *reinterpret_cast<f32x4 *>(&sT[n][16 * kb + 4 * g]) = acc;
+        }
+        __syncthreads();
+    }
+    if (p.final_state)
+#pragma unroll
+        for (int i = 0; i < KPW; ++i) {
+            const int kb = w + 4 * i;
+            if (kb >= NKB) continue;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                p.final_state[soff + static_cast<int64_t>(16 * kb + 4 * g + u) * dv + j0 + n] = st[i][u];
+        }
+}
+
+template <int DK, typename TI>
+hipError_t run_scan(const PrefillParams &p, const float *blocks, int out_dtype, hipStream_t s) {
+    const unsigned pairs8 = static_cast<unsigned>((p.N * p.H + 7) / 8);
+    const dim3 grid(pairs8 * 8 * (p.dv / 16)), block(256);
+    if (out_dtype == 0)
+        hipLaunchKernelGGL((f32mm_scan_kernel<DK, TI, float>), grid, block, 0, s, p, blocks);
+    else
+        hipLaunchKernelGGL((f32mm_scan_kernel<DK, TI, bf16_t>), grid, block, 0, s, p, blocks);
+    return hipGetLastError();
+}
+
+template <typename TI>
+hipError_t run_scan_dk(const PrefillParams &p, const float *blocks, int out_dtype, hipStream_t s) {
+    switch (p.dk) {
+        case 16: return run_scan<16, TI>(p, blocks, out_dtype, s);
+        case 32: return run_scan<32, TI>(p, blocks, out_dtype, s);
+        case 64: return run_scan<64, TI>(p, blocks, out_dtype, s);
+        default: return run_scan<128, TI>(p, blocks, out_dtype, s);
+    }
+}
+
+}  // namespace
+
+bool f32mm_supported(int dk, int dv, int C, uint32_t prologue) {
+    const bool dim = [](int d) { return d == 16 || d == 32 || d == 64 || d == 128; }(dk);
+    return dim && dv % 16 == 0 && dv >= 16 && dv <= 128 && (C == 32 || C == 64) && prologue == 0;
+}
+
+hipError_t launch_prefill_f32mm(const PrefillParams &p, float *blocks, int in_dtype, int out_dtype, hipStream_t s,
+                                hipEvent_t mid) {
+    CbParams c{};
+    c.q = p.q; c.k = p.k; c.v = p.v; c.beta = p.beta; c.log_alpha = p.log_alpha;
+    c.blocks = blocks;
+    c.chunk_off = p.chunk_off;
+    c.chunk_info = p.chunk_info;
+    c.status = p.status;
+    c.N = p.N; c.H = p.H; c.dk = p.dk; c.dv = p.dv;
+    hipError_t e = launch_chunk_prep_fwd(c, p.n_chunks_bound * p.H, in_dtype, s);
+    if (e == hipSuccess && mid) e = hipEventRecord(mid, s);
+    if (e != hipSuccess) return e;
+    return in_dtype == 0 ? run_scan_dk<float>(p, blocks, out_dtype, s) : run_scan_dk<bf16_t>(p, blocks, out_dtype, s);
+}
+
+}  // namespace kda

@@ -127,15 +127,20 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *   workspace   DEVICE, >= kda_prefill_workspace_bytes(args), 256-byte aligned.
  *   timing_events  HOST, nullable: pointer to 3 hipEvent_t created by the
  *               caller; recorded on hip_stream before the first kernel
- *               (the chunk table), between the intra-chunk and the scan kernel
- *               (after the single kernel on the fp32 path) and after the
- *               last kernel.  A profiling hook; costs nothing when NULL.
+ *               (the chunk table), between the per-chunk kernel and the scan
+ *               kernel (after the single kernel on the fp32 vector-ALU path)
+ *               and after the last kernel.  A profiling hook; costs nothing
+ *               when NULL.
  *   prologue    KDA_PROLOGUE_* bits, 0 = q, k, beta, log_alpha used as given.
  *
  * Supported: d_k, d_v in {16, 32, 64, 128}; chunk_size in {16, 32, 64};
- * in_dtype f32 (computed entirely in fp32) or bf16 (matrix-core path with
- * fp32 state and accumulation, for d_k == d_v in {64, 128}; other sizes use
- * the fp32 path); out_dtype f32 or bf16.
+ * in_dtype f32 or bf16; out_dtype f32 or bf16.  Paths (all with fp32 state
+ * and accumulation): bf16 inputs with d_k == d_v in {64, 128} run on bf16
+ * matrix cores; every other case with chunk_size 32 or 64 and no prologue
+ * (fp32 inputs for the 1e-5 contract, other bf16 head sizes) runs on the
+ * fp32 matrix cores, with a workspace of about 240 KB (d_k = 128) per
+ * (chunk, head); the rest (chunk_size 16, or a prologue with such inputs)
+ * runs in fp32 on the vector ALUs.
  */
 typedef struct kda_prefill_args {
     int32_t B, T, H, d_k, d_v;

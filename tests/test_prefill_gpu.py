@@ -68,6 +68,35 @@ def test_bf16_small_heads_use_fp32_path(dk, dv):
     check(x, name="bf16 small heads")
 
 
+@pytest.mark.parametrize("dk,dv,chunk", [(16, 32, 32), (32, 32, 64), (128, 64, 64), (64, 16, 32)])
+def test_bf16_small_or_unequal_heads_on_fp32_matrix_cores(dk, dv, chunk):
+    """bf16 inputs with head sizes the bf16 matrix-core path does not take,
+    at chunk 32 / 64: the chunk prep plus the fp32 matrix-core scan."""
+    x = synth.make_uniform(310 + dk + dv, 2, 150, 2, dk, dv, "bf16", chunk=chunk, state_std=0.2)
+    check(x, name="bf16 heads on fp32 matrix cores")
+
+
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_fp32_packed_with_empty_and_tiny_documents(chunk):
+    x = synth.make_packed(28, [70, 0, 1, 64, 129, 5], 3, 128, 128, "f32", chunk=chunk)
+    check(x, name="f32 packed")
+
+
+def test_fp32_bf16_output_and_extreme_gates():
+    """fp32 inputs with 10 % extreme-gate tokens (log alpha in [-20, -10],
+    beta in {1e-4, 1 - 1e-4}) and a bf16 output (checked elementwise against
+    the contract plus bf16's own rounding)."""
+    x = synth.make_long(29, 300, 2, 128, 128, "f32", chunk=64)
+    q, k, v, b, la, init, _ = dev_tensors(x)
+    o, S = kda.prefill(q, k, v, b, la, initial_state=init, chunk_size=64, out_dtype=torch.bfloat16)
+    o_ref, S_ref, _ = native.prefill(x.q, x.k, x.v, x.beta, x.log_alpha, None, x.initial_state)
+    d = np.abs(o.float().cpu().numpy() - o_ref)
+    rms = np.sqrt(np.mean(o_ref ** 2))
+    report("f32 extreme gates, bf16 output", o_max=float(d.max() / rms), S=err(S, S_ref))
+    assert np.all(d <= 1e-5 * rms + 2.0 ** -8 * np.abs(o_ref))
+    assert err(S, S_ref) <= 1e-5
+
+
 def test_empty_sequences_keep_state():
     x = synth.make_packed(9, [0, 5, 0], 1, 16, 16, "f32", chunk=16)
     o, S = check(x, name="empty docs")
