@@ -21,6 +21,7 @@ Prints ONE JSON line:
                and over one decode token per sequence (state rolled in place)
   backward     gradients over the T=4096, H=16 prefill shape: the prefill that
                writes the chunk checkpoints plus the chunked backward
+  prefill_fp32 the same shape with fp32 inputs (1e-5 contract), chunk 64
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -53,6 +54,7 @@ sys.path.insert(0, ROOT)
 METRIC = "KDA prefill tokens/s + decode seq-steps/s @H=32,d=128; % MFMA / HBM peak"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3   # dense fp32 matrix cores
 # Algorithmic bytes per (token, head): q, k, v, log_alpha in bf16 (4 x 256 B),
 # beta (2 B), o in fp32 (512 B).
 PREFILL_BYTES_PER_TOKEN_HEAD = 4 * 128 * 2 + 2 + 128 * 4
@@ -74,7 +76,7 @@ SOURCE_GROUPS = {
     "prefill": ["kda_prefill_mfma.hip", "kda_prefill_table.hip"],
     "decode": ["kda_decode.hip"],
     "short_conv": ["kda_conv.hip"],
-    "backward": ["kda_backward_chunked.hip", "kda_prefill_table.hip"],
+    "backward": ["kda_backward_chunked.hip", "kda_prefill_table.hip", "kda_chunk_block.hpp"],
 }
 SHARED_HEADERS = ["kda_common.hpp", "kda_prefill_common.hpp", "kda_launch.hpp"]
 # call key in profiles/traffic.json -> source group
@@ -665,7 +667,33 @@ def main():
                              "algorithmic_bytes": bwd_bytes,
                              "kernel": "cb_prep_kernel + cb_scan_kernel + cb_grad_kernel (d=128, bf16)",
                              "traffic": measured_traffic("backward_T4096_H16")}}
-    del bq, bk, bv, bb, bla, bdo, ck, BX
+    del bq, bk, bv, bb, bla, bdo, ck
+
+    # fp32 inputs (the 1e-5 contract) over the same shape, chunk 64: the
+    # chunk prep and the scan on fp32 matrix cores.  Bound: fp32 MFMA.
+    print("[bench] fp32 prefill", file=sys.stderr, flush=True)
+    ft = lambda a: torch.from_numpy(a).to(dev, torch.float32)  # noqa: E731
+    fq, fk, fv, fb, fla = (ft(a) for a in (BX.q, BX.k, BX.v, BX.beta, BX.log_alpha))
+    fo = torch.empty_like(fv)
+    ffin = torch.empty((1, bH, 128, 128), dtype=torch.float32, device=dev)
+    for _ in range(2):
+        kda.prefill(fq, fk, fv, fb, fla, chunk_size=64, o=fo, final_state=ffin)
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record()
+    for _ in range(5):
+        kda.prefill(fq, fk, fv, fb, fla, chunk_size=64, o=fo, final_state=ffin)
+    f1.record()
+    torch.cuda.synchronize()
+    f_ms = f0.elapsed_time(f1) / 5
+    f_tf = bT * bH * chunk_flops_per_token_head(64, 128) / (f_ms * 1e-3) / 1e12
+    prefill_f32 = {"value": bT / (f_ms * 1e-3), "unit": "tokens/s", "avg_ms": f_ms,
+                   "workload": f"prefill shape B=1 T={bT} H={bH} d=128, fp32 inputs, chunk 64",
+                   "roofline": {"bound": "mfma", "achieved": f_tf, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                "frac": f_tf / FP32_PEAK_TFLOPS,
+                                "basis": "useful chunked-form flops (10 C d + 6 d^2 per token-head) against "
+                                         "the fp32 matrix-core peak",
+                                "kernel": "cb_prep_kernel (forward mode) + f32mm_scan_kernel"}}
+    del fq, fk, fv, fb, fla, fo, ffin, BX
 
     rng = range(args.warmup, n_ev)
     pre_ms = [ev.ms(pev[3 * i], pev[3 * i + 2]) for i in rng]
@@ -740,6 +768,7 @@ def main():
     conv["prefill"]["roofline"]["frac_of_torch_copy"] = conv["prefill"]["roofline"]["achieved"] / copy_gbs
     out["short_conv"] = conv
     out["backward"] = backward
+    out["prefill_fp32"] = prefill_f32
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline_prefill(P)
