@@ -55,9 +55,13 @@ bool use_mfma(const kda_prefill_args *a) {
 }
 
 // the fp32 matrix-core path: fp32 inputs, and bf16 inputs whose head sizes
-// the bf16 matrix-core path does not take (chunk 32 or 64, no prologue)
+// the bf16 matrix-core path does not take (no prologue).  Its per-(chunk,
+// head) blocks have 64 rows whatever the chunk size, so chunk 16 takes this
+// path only while they stay within 4 GiB.
 bool use_f32mm(const kda_prefill_args *a) {
-    return !use_mfma(a) && f32mm_supported(a->d_k, a->d_v, a->chunk_size, a->prologue);
+    if (use_mfma(a) || !f32mm_supported(a->d_k, a->d_v, a->chunk_size, a->prologue)) return false;
+    const double blocks = static_cast<double>(max_chunks(a)) * a->H * cb_block_bytes(a->d_k);
+    return a->chunk_size > 16 || blocks <= 4.0 * (1u << 30);
 }
 
 size_t workspace_for(const kda_prefill_args *a) {

@@ -77,8 +77,8 @@ hipError_t launch_backward_chunked(const CbParams &p, int n_items, hipStream_t s
 // the chunk prep kernel in forward mode (K~, Q~, K^, g, beta, P, M per block);
 // in_dtype 0 = fp32, 1 = bf16
 hipError_t launch_chunk_prep_fwd(const CbParams &p, int n_items, int in_dtype, hipStream_t s);
-// fp32 matrix-core prefill: chunk prep, then the forward scan (chunk 32 or
-// 64, no prologue); blocks = n_chunks_bound x H prep blocks
+// fp32 matrix-core prefill: chunk prep, then the forward scan (no
+// prologue); blocks = n_chunks_bound x H prep blocks
 bool f32mm_supported(int dk, int dv, int C, uint32_t prologue);
 hipError_t launch_prefill_f32mm(const PrefillParams &p, float *blocks, int in_dtype, int out_dtype, hipStream_t s,
                                 hipEvent_t mid);

@@ -89,11 +89,16 @@ __global__ void __launch_bounds__(256) f32mm_scan_kernel(PrefillParams p, const 
                 for (int u = 0; u < 4; ++u) cs[static_cast<int64_t>(16 * kb + 4 * g + u) * dv + j0 + n] = st[i][u];
             }
         }
-        // (1) token block w: X = V - K~ S and (q e^G) S
+        // Token blocks at or beyond L hold only zeros (the prep zeroes those
+        // rows): their waves skip steps 1-3 and no product reads them.
         const int r0 = 16 * w;
+        const bool live = r0 < L;
+        const int nb = (L + 15) / 16;   // live token blocks (uniform)
+        // (1) token block w: X = V - K~ S and (q e^G) S
         f32x4 xa = {0.f, 0.f, 0.f, 0.f}, oa = xa;
 #pragma unroll
         for (int cb = 0; cb < NKB; ++cb) {
+            if (!live) break;
             const f32x4 sb = *reinterpret_cast<const f32x4 *>(&sT[n][16 * cb + 4 * g]);
             xa = mmf32(*reinterpret_cast<const f32x4 *>(blk + Y::KT + (r0 + n) * DK + 16 * cb + 4 * g), sb, xa);
             oa = mmf32(*reinterpret_cast<const f32x4 *>(blk + Y::QT + (r0 + n) * DK + 16 * cb + 4 * g), sb, oa);
@@ -105,23 +110,23 @@ __global__ void __launch_bounds__(256) f32mm_scan_kernel(PrefillParams p, const 
             const float vv = r < L ? io<TI>::ld(v, ((t0 + r) * H + h) * dv + j0 + n) : 0.f;
             xv[u] = vv - xa[u];
         }
-        *reinterpret_cast<f32x4 *>(&xT[n][r0 + 4 * g]) = xv;
+        if (live) *reinterpret_cast<f32x4 *>(&xT[n][r0 + 4 * g]) = xv;
         __syncthreads();
         // (2) token block w: Delta = M Diag(beta) X (M lower triangular)
         f32x4 da = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ib = 0; ib < C / 16; ++ib) {
-            if (ib > w) continue;
+            if (ib > w || !live) continue;
             const f32x4 m4 = *reinterpret_cast<const f32x4 *>(blk + Y::M + (r0 + n) * C + 16 * ib + 4 * g);
             const f32x4 b4 = *reinterpret_cast<const f32x4 *>(blk + Y::BETA + 16 * ib + 4 * g);
             da = mmf32(m4 * b4, *reinterpret_cast<const f32x4 *>(&xT[n][16 * ib + 4 * g]), da);
         }
-        *reinterpret_cast<f32x4 *>(&dT[n][r0 + 4 * g]) = da;
+        if (live) *reinterpret_cast<f32x4 *>(&dT[n][r0 + 4 * g]) = da;
         __syncthreads();
         // (3) token block w: O = (q e^G) S + P Delta (P lower triangular)
 #pragma unroll
         for (int ib = 0; ib < C / 16; ++ib) {
-            if (ib > w) continue;
+            if (ib > w || !live) continue;
             oa = mmf32(*reinterpret_cast<const f32x4 *>(blk + Y::P + (r0 + n) * C + 16 * ib + 4 * g),
                        *reinterpret_cast<const f32x4 *>(&dT[n][16 * ib + 4 * g]), oa);
         }
@@ -139,6 +144,7 @@ __global__ void __launch_bounds__(256) f32mm_scan_kernel(PrefillParams p, const 
             f32x4 acc = *reinterpret_cast<const f32x4 *>(blk + Y::GAM + 16 * kb + 4 * g) * st[i];
 #pragma unroll
             for (int rb = 0; rb < C / 16; ++rb) {
+                if (rb >= nb) break;
                 f32x4 a4;
 #pragma unroll
                 for (int s2 = 0; s2 < 4; ++s2) a4[s2] = blk[Y::KB + (16 * rb + 4 * g + s2) * DK + 16 * kb + n];
@@ -185,7 +191,7 @@ hipError_t run_scan_dk(const PrefillParams &p, const float *blocks, int out_dtyp
 
 bool f32mm_supported(int dk, int dv, int C, uint32_t prologue) {
     const bool dim = [](int d) { return d == 16 || d == 32 || d == 64 || d == 128; }(dk);
-    return dim && dv % 16 == 0 && dv >= 16 && dv <= 128 && (C == 32 || C == 64) && prologue == 0;
+    return dim && dv % 16 == 0 && dv >= 16 && dv <= 128 && (C == 16 || C == 32 || C == 64) && prologue == 0;
 }
 
 hipError_t launch_prefill_f32mm(const PrefillParams &p, float *blocks, int in_dtype, int out_dtype, hipStream_t s,
