@@ -55,7 +55,7 @@ bool use_mfma(const kda_prefill_args *a) {
 }
 
 // the fp32 matrix-core path: fp32 inputs, and bf16 inputs whose head sizes
-// the bf16 matrix-core path does not take (no prologue).  Its per-(chunk,
+// the bf16 matrix-core path does not take.  Its per-(chunk,
 // head) blocks have 64 rows whatever the chunk size, so chunk 16 takes this
 // path only while they stay within 4 GiB.
 bool use_f32mm(const kda_prefill_args *a) {

@@ -66,16 +66,46 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
     __shared__ float sA[CB_C][CB_C + 1];
     __shared__ float sb[CB_C];
 
+    // Prologue (forward only; the arguments hold pre-activations): log alpha
+    // = -softplus(x), beta = sigmoid(x), q and k divided by their L2 norms
+    // over d_k; in fp32, with the correctly rounded functions for fp32 inputs.
+    const uint32_t pro = FWD ? p.prologue : 0u;
     for (int e = tid; e < CB_C * DK; e += 256) {
         const int r = e / DK, c = e % DK;
         const int64_t off = ((t0 + r) * H + h) * DK + c;
         const bool live = r < L;
         sq[r][c] = live ? io<TI>::ld(q, off) : 0.f;
         sk[r][c] = live ? io<TI>::ld(k, off) : 0.f;
-        sG[r][c] = live ? io<TI>::ld(la, off) : 0.f;
+        float x = live ? io<TI>::ld(la, off) : 0.f;
+        if (pro & kProGate)
+            x = !live ? 0.f : kExact ? -(fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)))) : -softplus_f32(x);
+        sG[r][c] = x;
     }
-    if (tid < CB_C) sb[tid] = tid < L ? io<TI>::ld(beta, (t0 + tid) * H + h) : 0.f;
+    if (tid < CB_C) {
+        float b = tid < L ? io<TI>::ld(beta, (t0 + tid) * H + h) : 0.f;
+        if ((pro & kProBeta) && tid < L) b = kExact ? 1.f / (1.f + expf(-b)) : sigmoid_f32(b);
+        sb[tid] = b;
+    }
     __syncthreads();
+    if (pro & kProQKNorm) {  // rows of q and k to unit L2 norm (eps as in the other kernels)
+        __shared__ float s_inv[2][CB_C];
+        if (tid < 2 * CB_C) {
+            const int r = tid % CB_C;
+            float sum = 0.f;
+            for (int c = 0; c < DK; ++c) {
+                const float x = tid < CB_C ? sq[r][c] : sk[r][c];
+                sum += x * x;
+            }
+            s_inv[tid / CB_C][r] = 1.f / sqrtf(sum + kQKNormEps);
+        }
+        __syncthreads();
+        for (int e = tid; e < CB_C * DK; e += 256) {
+            const int r = e / DK, c = e % DK;
+            sq[r][c] *= s_inv[0][r];
+            sk[r][c] *= s_inv[1][r];
+        }
+        __syncthreads();
+    }
     if (tid < DK) {  // cumulative decay, accumulated in fp64
         double acc = 0.0;
         for (int r = 0; r < CB_C; ++r) {

@@ -71,14 +71,15 @@ struct CbParams {
     const int4 *chunk_info;                    // [chunks]
     const int32_t *status;
     int32_t N, H, dk, dv;
+    uint32_t prologue;                         // kPro* bits (forward prep only)
 };
 size_t cb_block_bytes(int dk);
 hipError_t launch_backward_chunked(const CbParams &p, int n_items, hipStream_t s);
 // the chunk prep kernel in forward mode (K~, Q~, K^, g, beta, P, M per block);
 // in_dtype 0 = fp32, 1 = bf16
 hipError_t launch_chunk_prep_fwd(const CbParams &p, int n_items, int in_dtype, hipStream_t s);
-// fp32 matrix-core prefill: chunk prep, then the forward scan (no
-// prologue); blocks = n_chunks_bound x H prep blocks
+// fp32 matrix-core prefill: chunk prep (with the prologue, if any), then
+// the forward scan; blocks = n_chunks_bound x H prep blocks
 bool f32mm_supported(int dk, int dv, int C, uint32_t prologue);
 hipError_t launch_prefill_f32mm(const PrefillParams &p, float *blocks, int in_dtype, int out_dtype, hipStream_t s,
                                 hipEvent_t mid);

@@ -10,8 +10,8 @@
 //     X = V - K~ S,   Delta = M Diag(beta) X,   O = Q~ S + P Delta,
 //     S' = Diag(g) S + K^^T Delta.
 // Two kernels: the chunk prep kernel (forward mode; one workgroup per
-// (chunk, head), shared with the chunked backward) writes K~, Q~, K^, g,
-// beta, P and M per (chunk, head); the scan below walks each sequence's
+// (chunk, head), shared with the chunked backward; it also applies the
+// fused prologue) writes K~, Q~, K^, g, beta, P and M per (chunk, head); the scan below walks each sequence's
 // chunks in order, one workgroup per (sequence, head, 16-column tile of S).
 #include "kda_chunk_block.hpp"
 #include "kda_launch.hpp"
@@ -191,7 +191,7 @@ hipError_t run_scan_dk(const PrefillParams &p, const float *blocks, int out_dtyp
 
 bool f32mm_supported(int dk, int dv, int C, uint32_t prologue) {
     const bool dim = [](int d) { return d == 16 || d == 32 || d == 64 || d == 128; }(dk);
-    return dim && dv % 16 == 0 && dv >= 16 && dv <= 128 && (C == 16 || C == 32 || C == 64) && prologue == 0;
+    return dim && dv % 16 == 0 && dv >= 16 && dv <= 128 && (C == 16 || C == 32 || C == 64);
 }
 
 hipError_t launch_prefill_f32mm(const PrefillParams &p, float *blocks, int in_dtype, int out_dtype, hipStream_t s,
@@ -203,6 +203,7 @@ hipError_t launch_prefill_f32mm(const PrefillParams &p, float *blocks, int in_dt
     c.chunk_info = p.chunk_info;
     c.status = p.status;
     c.N = p.N; c.H = p.H; c.dk = p.dk; c.dv = p.dv;
+    c.prologue = p.prologue;
     hipError_t e = launch_chunk_prep_fwd(c, p.n_chunks_bound * p.H, in_dtype, s);
     if (e == hipSuccess && mid) e = hipEventRecord(mid, s);
     if (e != hipSuccess) return e;

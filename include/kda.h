@@ -136,12 +136,11 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  * Supported: d_k, d_v in {16, 32, 64, 128}; chunk_size in {16, 32, 64};
  * in_dtype f32 or bf16; out_dtype f32 or bf16.  Paths (all with fp32 state
  * and accumulation): bf16 inputs with d_k == d_v in {64, 128} run on bf16
- * matrix cores; every other case without a prologue (fp32 inputs for the
- * 1e-5 contract, other bf16 head sizes) runs on the fp32 matrix cores, with
- * a workspace of about 240 KB (d_k = 128) per (chunk, head) whatever the
- * chunk size (chunk_size 16 only while that stays within 4 GiB); the rest
- * (a prologue with such inputs, or larger chunk-16 calls) runs in fp32 on
- * the vector ALUs.
+ * matrix cores; every other case (fp32 inputs for the 1e-5 contract, other
+ * bf16 head sizes) runs on the fp32 matrix cores, with a workspace of about
+ * 240 KB (d_k = 128) per (chunk, head) whatever the chunk size
+ * (chunk_size 16 only while that stays within 4 GiB); larger chunk-16 calls
+ * run in fp32 on the vector ALUs.
  */
 typedef struct kda_prefill_args {
     int32_t B, T, H, d_k, d_v;
