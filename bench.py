@@ -173,7 +173,7 @@ def record_traffic(fetch_dir, write_dir, sq_dir, cal_fetch_dir, cal_write_dir, m
         "short_conv_prefill": [("short_conv_kernel<unsignedshort,unsignedshort,4,16>", None),
                                ("conv_state_kernel<unsignedshort,4>", None)],
         "short_conv_decode": [("conv_rows_kernel<unsignedshort,unsignedshort,4>", None)],
-        "backward_T4096_H16": [("cb_prep_kernel<128,unsignedshort>", None), ("cb_scan_kernel<128>", None),
+        "backward_T4096_H16": [("cb_prep_kernel<128,unsignedshort,false>", None), ("cb_scan_kernel<128>", None),
                                ("cb_grad_kernel<128,unsignedshort>", None)],
     }
     out_calls = {}
