@@ -29,6 +29,57 @@ __device__ __forceinline__ f32x4 mmf32(const f32x4 &a, const f32x4 &b, f32x4 acc
     return acc;
 }
 
+}  // namespace
+
+// One wave's operands of one chunk (token block w, key blocks w, w + 4),
+// loaded into registers a chunk ahead: each part is reloaded for the next
+// chunk right after the current chunk's products have used it.
+template <int DK, typename TI>
+struct F32ScanOps {
+    using Y = CbLay<DK>;
+    static constexpr int NKB = DK / 16, KPW = (NKB + 3) / 4;
+    f32x4 kt[NKB], qt[NKB];   // K~, Q~ [16w + n][16cb + 4g ..]           (step 1)
+    float vv[4];              // V [16w + 4g + u][j0 + n]                 (step 1)
+    f32x4 mb[4], pb[4];       // M Diag(beta), P [16w + n][16ib + 4g ..]  (steps 2, 3)
+    f32x4 ka[KPW][4];         // K^ [16rb + 4g + s][16kb + n], kb = w + 4i (step 4)
+    f32x4 gm[KPW];            // e^{G_L} [16kb + 4g ..]                   (step 4)
+
+    __device__ __forceinline__ void load1(const float *blk, const TI *v, int64_t t0, int L, int H, int h, int dv,
+                                          int j0, int w, int g, int n) {
+#pragma unroll
+        for (int cb = 0; cb < NKB; ++cb) {
+            kt[cb] = *reinterpret_cast<const f32x4 *>(blk + Y::KT + (16 * w + n) * DK + 16 * cb + 4 * g);
+            qt[cb] = *reinterpret_cast<const f32x4 *>(blk + Y::QT + (16 * w + n) * DK + 16 * cb + 4 * g);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = 16 * w + 4 * g + u;
+            vv[u] = r < L ? io<TI>::ld(v, ((t0 + r) * H + h) * dv + j0 + n) : 0.f;
+        }
+    }
+    __device__ __forceinline__ void load23(const float *blk, int w, int g, int n) {
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib) {
+            if (ib > w) continue;
+            const f32x4 m4 = *reinterpret_cast<const f32x4 *>(blk + Y::M + (16 * w + n) * CB_C + 16 * ib + 4 * g);
+            mb[ib] = m4 * *reinterpret_cast<const f32x4 *>(blk + Y::BETA + 16 * ib + 4 * g);
+            pb[ib] = *reinterpret_cast<const f32x4 *>(blk + Y::P + (16 * w + n) * CB_C + 16 * ib + 4 * g);
+        }
+    }
+    __device__ __forceinline__ void load4(const float *blk, int w, int g, int n) {
+#pragma unroll
+        for (int i = 0; i < KPW; ++i) {
+            const int kb = w + 4 * i;
+            if (kb >= NKB) continue;
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) ka[i][rb][s2] = blk[Y::KB + (16 * rb + 4 * g + s2) * DK + 16 * kb + n];
+            gm[i] = *reinterpret_cast<const f32x4 *>(blk + Y::GAM + 16 * kb + 4 * g);
+        }
+    }
+};
+
 // Wave w computes token block w of X, Delta and O and owns key blocks
 // w, w + 4 of the state (accumulator layout, for the whole sequence).  S, X
 // and Delta pass between the waves through LDS transposed ([column][row]),
@@ -37,7 +88,8 @@ template <int DK, typename TI, typename TO>
 __global__ void __launch_bounds__(256) f32mm_scan_kernel(PrefillParams p, const float *__restrict__ blocks) {
     if (*p.status != 0) return;
     using Y = CbLay<DK>;
-    constexpr int C = CB_C, NKB = DK / 16, KPW = (NKB + 3) / 4;
+    using Ops = F32ScanOps<DK, TI>;
+    constexpr int C = CB_C, NKB = Ops::NKB, KPW = Ops::KPW;
     constexpr int LC = C + 4, LK = DK + 4;  // padded strides of the [column][row] tiles
     const int H = p.H, dv = p.dv;
     const int nvt = dv / 16;
@@ -72,13 +124,22 @@ __global__ void __launch_bounds__(256) f32mm_scan_kernel(PrefillParams p, const 
                            : 0.f;
         if (kb < NKB) *reinterpret_cast<f32x4 *>(&sT[n][16 * kb + 4 * g]) = st[i];
     }
+    auto blk_of = [&](int ch) { return blocks + (static_cast<size_t>(cbase + ch) * H + h) * Y::FLOATS; };
+    auto len_of = [&](int ch) { return min(p.C, sr.len - ch * p.C); };
+    auto t0_of = [&](int ch) { return sr.start + static_cast<int64_t>(ch) * p.C; };
+    Ops op;
+    if (nch > 0) {
+        op.load1(blk_of(0), v, t0_of(0), len_of(0), H, h, dv, j0, w, g, n);
+        op.load23(blk_of(0), w, g, n);
+        op.load4(blk_of(0), w, g, n);
+    }
     __syncthreads();
 
     for (int ch = 0; ch < nch; ++ch) {
         const int64_t x = cbase + ch;
-        const int64_t t0 = sr.start + static_cast<int64_t>(ch) * p.C;
-        const int L = min(p.C, sr.len - ch * p.C);
-        const float *blk = blocks + (static_cast<size_t>(x) * H + h) * Y::FLOATS;
+        const int64_t t0 = t0_of(ch);
+        const int L = len_of(ch);
+        const int nx = ch + 1 < nch ? ch + 1 : ch;   // the chunk whose operands are loaded next
         if (p.chunk_states) {
             float *cs = p.chunk_states + (x * H + h) * static_cast<int64_t>(DK) * dv;
 #pragma unroll
@@ -100,26 +161,21 @@ __global__ void __launch_bounds__(256) f32mm_scan_kernel(PrefillParams p, const 
         for (int cb = 0; cb < NKB; ++cb) {
             if (!live) break;
             const f32x4 sb = *reinterpret_cast<const f32x4 *>(&sT[n][16 * cb + 4 * g]);
-            xa = mmf32(*reinterpret_cast<const f32x4 *>(blk + Y::KT + (r0 + n) * DK + 16 * cb + 4 * g), sb, xa);
-            oa = mmf32(*reinterpret_cast<const f32x4 *>(blk + Y::QT + (r0 + n) * DK + 16 * cb + 4 * g), sb, oa);
+            xa = mmf32(op.kt[cb], sb, xa);
+            oa = mmf32(op.qt[cb], sb, oa);
         }
         f32x4 xv;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int r = r0 + 4 * g + u;
-            const float vv = r < L ? io<TI>::ld(v, ((t0 + r) * H + h) * dv + j0 + n) : 0.f;
-            xv[u] = vv - xa[u];
-        }
+        for (int u = 0; u < 4; ++u) xv[u] = op.vv[u] - xa[u];
         if (live) *reinterpret_cast<f32x4 *>(&xT[n][r0 + 4 * g]) = xv;
+        op.load1(blk_of(nx), v, t0_of(nx), len_of(nx), H, h, dv, j0, w, g, n);
         __syncthreads();
         // (2) token block w: Delta = M Diag(beta) X (M lower triangular)
         f32x4 da = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ib = 0; ib < C / 16; ++ib) {
             if (ib > w || !live) continue;
-            const f32x4 m4 = *reinterpret_cast<const f32x4 *>(blk + Y::M + (r0 + n) * C + 16 * ib + 4 * g);
-            const f32x4 b4 = *reinterpret_cast<const f32x4 *>(blk + Y::BETA + 16 * ib + 4 * g);
-            da = mmf32(m4 * b4, *reinterpret_cast<const f32x4 *>(&xT[n][16 * ib + 4 * g]), da);
+            da = mmf32(op.mb[ib], *reinterpret_cast<const f32x4 *>(&xT[n][16 * ib + 4 * g]), da);
         }
         if (live) *reinterpret_cast<f32x4 *>(&dT[n][r0 + 4 * g]) = da;
         __syncthreads();
@@ -127,9 +183,9 @@ __global__ void __launch_bounds__(256) f32mm_scan_kernel(PrefillParams p, const 
 #pragma unroll
         for (int ib = 0; ib < C / 16; ++ib) {
             if (ib > w || !live) continue;
-            oa = mmf32(*reinterpret_cast<const f32x4 *>(blk + Y::P + (r0 + n) * C + 16 * ib + 4 * g),
-                       *reinterpret_cast<const f32x4 *>(&dT[n][16 * ib + 4 * g]), oa);
+            oa = mmf32(op.pb[ib], *reinterpret_cast<const f32x4 *>(&dT[n][16 * ib + 4 * g]), oa);
         }
+        op.load23(blk_of(nx), w, g, n);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int r = r0 + 4 * g + u;
@@ -141,18 +197,16 @@ __global__ void __launch_bounds__(256) f32mm_scan_kernel(PrefillParams p, const 
         for (int i = 0; i < KPW; ++i) {
             const int kb = w + 4 * i;
             if (kb >= NKB) continue;
-            f32x4 acc = *reinterpret_cast<const f32x4 *>(blk + Y::GAM + 16 * kb + 4 * g) * st[i];
+            f32x4 acc = op.gm[i] * st[i];
 #pragma unroll
             for (int rb = 0; rb < C / 16; ++rb) {
                 if (rb >= nb) break;
-                f32x4 a4;
-#pragma unroll
-                for (int s2 = 0; s2 < 4; ++s2) a4[s2] = blk[Y::KB + (16 * rb + 4 * g + s2) * DK + 16 * kb + n];
-                acc = mmf32(a4, *reinterpret_cast<const f32x4 *>(&dT[n][16 * rb + 4 * g]), acc);
+                acc = mmf32(op.ka[i][rb], *reinterpret_cast<const f32x4 *>(&dT[n][16 * rb + 4 * g]), acc);
             }
             st[i] = acc;
             *reinterpret_cast<f32x4 *>(&sT[n][16 * kb + 4 * g]) = acc;
         }
+        op.load4(blk_of(nx), w, g, n);
         __syncthreads();
     }
     if (p.final_state)
@@ -165,6 +219,8 @@ __global__ void __launch_bounds__(256) f32mm_scan_kernel(PrefillParams p, const 
                 p.final_state[soff + static_cast<int64_t>(16 * kb + 4 * g + u) * dv + j0 + n] = st[i][u];
         }
 }
+
+namespace {
 
 template <int DK, typename TI>
 hipError_t run_scan(const PrefillParams &p, const float *blocks, int out_dtype, hipStream_t s) {
