@@ -70,16 +70,55 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
     // = -softplus(x), beta = sigmoid(x), q and k divided by their L2 norms
     // over d_k; in fp32, with the correctly rounded functions for fp32 inputs.
     const uint32_t pro = FWD ? p.prologue : 0u;
-    for (int e = tid; e < CB_C * DK; e += 256) {
-        const int r = e / DK, c = e % DK;
-        const int64_t off = ((t0 + r) * H + h) * DK + c;
-        const bool live = r < L;
-        sq[r][c] = live ? io<TI>::ld(q, off) : 0.f;
-        sk[r][c] = live ? io<TI>::ld(k, off) : 0.f;
-        float x = live ? io<TI>::ld(la, off) : 0.f;
+    auto stage = [&](int r, int c, float qv, float kv, float x, bool live) {
+        sq[r][c] = qv;
+        sk[r][c] = kv;
         if (pro & kProGate)
             x = !live ? 0.f : kExact ? -(fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)))) : -softplus_f32(x);
         sG[r][c] = x;
+    };
+    // 16-byte loads (8 bf16 or 4 fp32 per request) when the three arrays
+    // allow it, all of a thread's requests issued before any is used
+    constexpr int VEC = 16 / sizeof(TI);
+    constexpr int NVL = CB_C * DK / VEC / 256;  // requests per thread and array
+    const bool vec = ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                       reinterpret_cast<uintptr_t>(la)) & 15) == 0;
+    bool staged = false;
+    if constexpr (NVL >= 1) {
+        if (vec) {
+            typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+            u32x4 rq[NVL], rk[NVL], ra[NVL];
+#pragma unroll
+            for (int u = 0; u < NVL; ++u) {
+                const int e = (tid + 256 * u) * VEC, r = e / DK, c0 = e % DK;
+                const int64_t off = ((t0 + min(r, L - 1)) * H + h) * DK + c0;   // rows >= L: zeroed below
+                rq[u] = *reinterpret_cast<const u32x4 *>(q + off);
+                rk[u] = *reinterpret_cast<const u32x4 *>(k + off);
+                ra[u] = *reinterpret_cast<const u32x4 *>(la + off);
+            }
+#pragma unroll
+            for (int u = 0; u < NVL; ++u) {
+                const int e = (tid + 256 * u) * VEC, r = e / DK, c0 = e % DK;
+                const bool live = r < L;
+                const TI *qe = reinterpret_cast<const TI *>(&rq[u]);
+                const TI *ke = reinterpret_cast<const TI *>(&rk[u]);
+                const TI *ae = reinterpret_cast<const TI *>(&ra[u]);
+#pragma unroll
+                for (int j = 0; j < VEC; ++j)
+                    stage(r, c0 + j, live ? io<TI>::ld(qe, j) : 0.f, live ? io<TI>::ld(ke, j) : 0.f,
+                          live ? io<TI>::ld(ae, j) : 0.f, live);
+            }
+            staged = true;
+        }
+    }
+    if (!staged) {
+        for (int e = tid; e < CB_C * DK; e += 256) {
+            const int r = e / DK, c = e % DK;
+            const int64_t off = ((t0 + r) * H + h) * DK + c;
+            const bool live = r < L;
+            stage(r, c, live ? io<TI>::ld(q, off) : 0.f, live ? io<TI>::ld(k, off) : 0.f,
+                  live ? io<TI>::ld(la, off) : 0.f, live);
+        }
     }
     if (tid < CB_C) {
         float b = tid < L ? io<TI>::ld(beta, (t0 + tid) * H + h) : 0.f;
@@ -114,15 +153,24 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
         }
     }
     __syncthreads();
-    // elementwise factors and the decay of the whole chunk
-    for (int e = tid; e < CB_C * DK; e += 256) {
-        const int r = e / DK, c = e % DK;
-        const GT G = sG[r][c];
-        const float E = ex(G);
-        if (!FWD) blk[Y::G + e] = static_cast<float>(G);
-        blk[Y::KT + e] = sk[r][c] * E;
-        blk[Y::QT + e] = sq[r][c] * E;
-        blk[Y::KB + e] = sk[r][c] * ex(sG[CB_C - 1][c] - G);
+    // elementwise factors and the decay of the whole chunk, four
+    // consecutive channels per thread (16-byte stores)
+    for (int e4 = tid; e4 < CB_C * DK / 4; e4 += 256) {
+        const int e = 4 * e4, r = e / DK, c0 = e % DK;
+        f32x4 gv, kt, qt, kb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const GT G = sG[r][c0 + j];
+            const float E = ex(G);
+            gv[j] = static_cast<float>(G);
+            kt[j] = sk[r][c0 + j] * E;
+            qt[j] = sq[r][c0 + j] * E;
+            kb[j] = sk[r][c0 + j] * ex(sG[CB_C - 1][c0 + j] - G);
+        }
+        if (!FWD) *reinterpret_cast<f32x4 *>(blk + Y::G + e) = gv;
+        *reinterpret_cast<f32x4 *>(blk + Y::KT + e) = kt;
+        *reinterpret_cast<f32x4 *>(blk + Y::QT + e) = qt;
+        *reinterpret_cast<f32x4 *>(blk + Y::KB + e) = kb;
     }
     for (int c = tid; c < DK; c += 256) blk[Y::GAM + c] = ex(sG[CB_C - 1][c]);
     if (tid < CB_C) blk[Y::BETA + tid] = sb[tid];
