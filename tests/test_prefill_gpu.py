@@ -97,6 +97,21 @@ def test_fp32_bf16_output_and_extreme_gates():
     assert err(S, S_ref) <= 1e-5
 
 
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_fp32_long_sequence_on_fp32_matrix_cores(chunk):
+    """T=16384, H=4, d=128 fp32: 1024 or 256 chunks carried in sequence on
+    the fp32 matrix-core path, every output and the final state within
+    1e-5."""
+    x = synth.make_uniform(34, 1, 16384, 4, 128, 128, "f32", chunk=chunk, state_std=0.1)
+    q, k, v, b, la, init, _ = dev_tensors(x)
+    assert kda.workspace_bytes(q, k, v, b, la, chunk_size=chunk) > (1 << 26)   # chunk blocks: this path
+    o, S = kda.prefill(q, k, v, b, la, initial_state=init, chunk_size=chunk)
+    o_ref, S_ref, _ = native.prefill(x.q, x.k, x.v, x.beta, x.log_alpha, None, x.initial_state)
+    e = dict(o=err(o, o_ref), S=err(S, S_ref))
+    report(f"f32 long T=16384 H=4 d=128 C={chunk} (fp32 matrix cores)", **e)
+    assert max(e.values()) <= TOL["f32"]
+
+
 def test_fp32_chunk16_beyond_the_block_budget_uses_the_vector_path():
     """A chunk-16 fp32 call whose 64-row chunk blocks would exceed 4 GiB
     (T=32768, H=16: 32768 blocks of 240 KB) runs on the vector-ALU kernel:
