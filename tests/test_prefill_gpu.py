@@ -112,19 +112,20 @@ def test_fp32_long_sequence_on_fp32_matrix_cores(chunk):
     assert max(e.values()) <= TOL["f32"]
 
 
-def test_fp32_chunk16_beyond_the_block_budget_uses_the_vector_path():
+@pytest.mark.parametrize("T,H,d", [(32768, 16, 128), (16384, 48, 16)])
+def test_fp32_chunk16_beyond_the_block_budget_uses_the_vector_path(T, H, d):
     """A chunk-16 fp32 call whose 64-row chunk blocks would exceed 4 GiB
-    (T=32768, H=16: 32768 blocks of 240 KB) runs on the vector-ALU kernel:
-    the workspace query shows no blocks, and the result meets the contract
-    on every head."""
-    x = synth.make_uniform(33, 1, 32768, 16, 128, 128, "f32", chunk=16, state_std=0.1)
+    (T/16 x H blocks of 240 KB at d = 128, 103 KB at d = 16) runs on the
+    vector-ALU kernel: the workspace query shows no blocks, and the result
+    meets the contract on every head."""
+    x = synth.make_uniform(33, 1, T, H, d, d, "f32", chunk=16, state_std=0.1)
     q, k, v, b, la, init, _ = dev_tensors(x)
     assert kda.workspace_bytes(q, k, v, b, la, chunk_size=16) < (1 << 20)   # chunk table only
     assert kda.workspace_bytes(q, k, v, b, la, chunk_size=64) > (1 << 30)   # 64-token blocks
     o, S = kda.prefill(q, k, v, b, la, initial_state=init, chunk_size=16)
     o_ref, S_ref, _ = native.prefill(x.q, x.k, x.v, x.beta, x.log_alpha, None, x.initial_state)
     e = dict(o=err(o, o_ref), S=err(S, S_ref))
-    report("f32 chunk 16, T=32768 H=16 d=128 (vector-ALU path)", **e)
+    report(f"f32 chunk 16, T={T} H={H} d={d} (vector-ALU path)", **e)
     assert max(e.values()) <= TOL["f32"]
 
 
