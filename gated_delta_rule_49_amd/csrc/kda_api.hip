@@ -108,6 +108,10 @@ kda_status kda_prefill_chunked(const kda_prefill_args *a, void *hip_stream) {
     if (!a->workspace) return KDA_ERR_NULL_ARG;
     if (reinterpret_cast<uintptr_t>(a->workspace) % kAlign) return KDA_ERR_BAD_SHAPE;
     if (a->workspace_bytes < workspace_for(a)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    // the bf16 matrix-core path reads q, k, v and the gate as 128-bit vectors
+    if (use_mfma(a))
+        for (const void *ptr : {a->q, a->k, a->v, a->log_alpha})
+            if (reinterpret_cast<uintptr_t>(ptr) % 16) return KDA_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
 
     char *ws = static_cast<char *>(a->workspace);
@@ -170,6 +174,10 @@ kda_status kda_decode(const kda_decode_args *a, void *hip_stream) {
     if (a->B == 0) return KDA_OK;
     if (!a->q || !a->k || !a->v || !a->beta || !a->log_alpha || !a->initial_state || !a->o)
         return KDA_ERR_NULL_ARG;
+    // the kernel moves state rows as 128-bit vectors
+    for (const float *ptr : {a->initial_state, static_cast<const float *>(a->final_state),
+                             static_cast<const float *>(a->token_states)})
+        if (reinterpret_cast<uintptr_t>(ptr) % 16) return KDA_ERR_UNSUPPORTED;
     hipError_t e = launch_decode(a->B, a->H, a->n_tokens, a->d_k, a->d_v, a->in_dtype, a->out_dtype, a->prologue,
                                  a->q, a->k, a->v, a->beta, a->log_alpha, a->initial_state, a->final_state,
                                  a->token_states, a->o, static_cast<hipStream_t>(hip_stream));

@@ -136,7 +136,9 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  * Supported: d_k, d_v in {16, 32, 64, 128}; chunk_size in {16, 32, 64};
  * in_dtype f32 or bf16; out_dtype f32 or bf16.  Paths (all with fp32 state
  * and accumulation): bf16 inputs with d_k == d_v in {64, 128} run on bf16
- * matrix cores; every other case (fp32 inputs for the 1e-5 contract, other
+ * matrix cores, reading q, k, v and log_alpha as 128-bit vectors (each
+ * must be 16-byte aligned there, else KDA_ERR_UNSUPPORTED); every other
+ * case (fp32 inputs for the 1e-5 contract, other
  * bf16 head sizes) runs on the fp32 matrix cores, with a workspace of about
  * 240 KB (d_k = 128) per (chunk, head) whatever the chunk size
  * (chunk_size 16 only while that stays within 4 GiB); larger chunk-16 calls
@@ -216,7 +218,9 @@ kda_status kda_decode_step(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
  *   o                DEVICE [B, m, H, d_v]  out_dtype; o[b, j] uses the
  *                    state after token j.
  *   prologue         KDA_PROLOGUE_* bits.
- * Supported: d_k, d_v in {16, 32, 64, 128}; 1 <= m; B * m * H < 2^31.
+ * Supported: d_k, d_v in {16, 32, 64, 128}; 1 <= m; B * m * H < 2^31; the
+ * three state pointers 16-byte aligned (the kernel moves state rows as
+ * 128-bit vectors), else KDA_ERR_UNSUPPORTED.
  */
 typedef struct kda_decode_args {
     int32_t B, H, d_k, d_v;

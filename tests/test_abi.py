@@ -83,6 +83,8 @@ def base_args(**over):
     (dict(d_k=96), 3), (dict(d_v=256), 3), (dict(chunk_size=48), 3), (dict(in_dtype=7), 3),
     (dict(out_dtype=2), 3), (dict(prologue=8), 3), (dict(prologue=0x80000000), 3),
     (dict(workspace_bytes=0), 4),
+    # the bf16 matrix-core path reads q, k, v, log_alpha as 128-bit vectors
+    (dict(workspace_bytes=1 << 40, q=FAKE + 2), 3), (dict(workspace_bytes=1 << 40, log_alpha=FAKE + 8), 3),
 ])
 def test_prefill_host_validation(L, over, status):
     a = base_args(**over)
@@ -143,6 +145,8 @@ def decode_args(**over):
     (dict(H=0), 2), (dict(n_tokens=0), 2), (dict(B=-1), 2),
     (dict(d_k=96), 3), (dict(in_dtype=4), 3), (dict(prologue=16), 3),
     (dict(B=1 << 20, n_tokens=1 << 10, H=4), 3),
+    # state rows move as 128-bit vectors
+    (dict(initial_state=FAKE + 4), 3), (dict(final_state=FAKE + 8), 3), (dict(token_states=FAKE + 12), 3),
 ])
 def test_multi_token_decode_host_validation(L, over, status):
     assert L.kda_decode(ctypes.byref(decode_args(**over)), None) == status
