@@ -22,13 +22,19 @@
 // MI355X for B=256, H=32, d=128 (1.09 GB per step): 512 threads per state
 // with non-temporal accesses 187 us per step; 256 threads 208 us (213 us
 // with ordinary accesses); 1024 threads 221 us; splitting a state by columns
-// over 4 workgroups of 256 threads 196 us.
+// over 4 workgroups of 256 threads 196 us; the persistent single-token
+// kernel below (each workgroup prefetching its next state) 182 us.
 #include "kda_launch.hpp"
 
 namespace kda {
 
 // threads per workgroup (at most)
 constexpr int kDecodeThreads = 512;
+// workgroups of the persistent single-token launch.  Measured for B=256,
+// H=32, d=128 (148 VGPRs: one 512-thread workgroup resident per CU):
+// 256 -> 187.7 us per step, 512 -> 182.6, 768 -> 185.9, 1024 -> 182.2,
+// 2048 -> 186.1; one workgroup per state 187.7.
+constexpr int kDecodeGrid = 512;
 
 template <int DK, int DV>
 struct DecodeShape {
@@ -215,6 +221,159 @@ __global__ void __launch_bounds__((DecodeShape<DK, DV>::NT)) decode_kernel(Decod
     }
 }
 
+
+// Single-token launch, persistent: workgroup w updates the states w, w + G,
+// w + 2G, ... (G = gridDim.x) and requests the next state and its token
+// vectors before it updates the current one, so that one state's transfer
+// from HBM overlaps the previous state's update and write-back.  The token
+// vectors are staged in one of two LDS buffers by state parity and every
+// wave forms kappa and the norms itself: two LDS-only barriers per state.
+template <typename TI>
+struct DecodeTok {  // one thread's share of a token's vectors (raw, converted at use)
+    TI a, k, q, v, b;
+};
+
+template <int DK, int DV, typename TI>
+__device__ __forceinline__ void decode1_request(const DecodeParams &p, int bh, int tid,
+                                                f32x4 (&sv)[DecodeShape<DK, DV>::RPT], DecodeTok<TI> &in) {
+    using Sh = DecodeShape<DK, DV>;
+    const int c4 = tid % Sh::TPR, rg = tid / Sh::TPR;
+    // uniform base, 32-bit per-lane offsets (shared by all states of the walk)
+    const float *src = p.state_in + static_cast<int64_t>(bh) * DK * DV;
+    const uint32_t lo = static_cast<uint32_t>(rg * DV + 4 * c4);
+#pragma unroll
+    for (int i = 0; i < Sh::RPT; ++i)
+        sv[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(src + (lo + static_cast<uint32_t>(Sh::RG * i * DV))));
+    if (tid < DK) {
+        const int64_t off = static_cast<int64_t>(bh) * DK + tid;
+        in.a = static_cast<const TI *>(p.log_alpha)[off];
+        in.k = static_cast<const TI *>(p.k)[off];
+        in.q = static_cast<const TI *>(p.q)[off];
+    }
+    if (tid < DV) in.v = static_cast<const TI *>(p.v)[static_cast<int64_t>(bh) * DV + tid];
+    if (tid == 0) in.b = static_cast<const TI *>(p.beta)[bh];
+}
+
+template <int DK, int DV, typename TI, typename TO, int PAR>
+__device__ __forceinline__ void decode1_update(const DecodeParams &p, int bh, int tid,
+                                               f32x4 (&sv)[DecodeShape<DK, DV>::RPT], const DecodeTok<TI> &in,
+                                               float (&s_a)[2][DK], float (&s_k)[2][DK], float (&s_q)[2][DK],
+                                               float (&s_v)[2][DV], float (&s_b)[2],
+                                               float (&s_red)[2][DecodeShape<DK, DV>::NW][DV]) {
+    using Sh = DecodeShape<DK, DV>;
+    const int c4 = tid % Sh::TPR, rg = tid / Sh::TPR, wave = tid / 64, lane = tid % 64;
+    if (tid < DK) {
+        const float x = io<TI>::ld(&in.a, 0);
+        s_a[PAR][tid] = (p.prologue & kProGate) ? sigmoid_f32(-x) : __expf(x);
+        s_k[PAR][tid] = io<TI>::ld(&in.k, 0);
+        s_q[PAR][tid] = io<TI>::ld(&in.q, 0);
+    }
+    if (tid < DV) s_v[PAR][tid] = io<TI>::ld(&in.v, 0);
+    if (tid == 0) {
+        float bt = io<TI>::ld(&in.b, 0);
+        if (p.prologue & kProBeta) bt = sigmoid_f32(bt);
+        s_b[PAR] = bt;
+    }
+    lds_barrier();
+    // kappa = k.q and, with the norm, 1/|k| and 1/|q|, formed by every wave
+    float kq = 0.f, k2 = 0.f, q2 = 0.f;
+    for (int i = lane; i < DK; i += 64) {
+        const float kk = s_k[PAR][i], qq = s_q[PAR][i];
+        kq += kk * qq;
+        k2 += kk * kk;
+        q2 += qq * qq;
+    }
+#pragma unroll
+    for (int msk = 32; msk >= 1; msk >>= 1) {
+        kq += __shfl_xor(kq, msk);
+        k2 += __shfl_xor(k2, msk);
+        q2 += __shfl_xor(q2, msk);
+    }
+    float nk = 1.f, nq = 1.f;
+    if (p.prologue & kProQKNorm) {
+        nk = 1.f / __builtin_sqrtf(k2 + kQKNormEps);
+        nq = 1.f / __builtin_sqrtf(q2 + kQKNormEps);
+    }
+    const float kappa = kq * nk * nq;
+    // partial p = S^T (a k), r = S^T (a q) over this thread's rows
+    f32x4 pr = {0.f, 0.f, 0.f, 0.f}, rr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < Sh::RPT; ++i) {
+        const int row = rg + Sh::RG * i;
+        const float a = s_a[PAR][row];
+        pr += sv[i] * (a * s_k[PAR][row]);
+        rr += sv[i] * (a * s_q[PAR][row]);
+    }
+#pragma unroll
+    for (int msk = Sh::TPR; msk < 64 && msk < Sh::NT; msk <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pr[j] += __shfl_xor(pr[j], msk);
+            rr[j] += __shfl_xor(rr[j], msk);
+        }
+    }
+    if (lane < Sh::TPR) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            s_red[0][wave][4 * c4 + j] = pr[j];
+            s_red[1][wave][4 * c4 + j] = rr[j];
+        }
+    }
+    lds_barrier();
+    f32x4 pt = {0.f, 0.f, 0.f, 0.f}, rt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < Sh::NW; ++w) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pt[j] += s_red[0][w][4 * c4 + j];
+            rt[j] += s_red[1][w][4 * c4 + j];
+        }
+    }
+    const float bt = s_b[PAR];
+    f32x4 delta;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) delta[j] = bt * (s_v[PAR][4 * c4 + j] - pt[j] * nk);
+    if (rg == 0) {
+        TO *o = static_cast<TO *>(p.o);
+        const int64_t ooff = static_cast<int64_t>(bh) * DV + 4 * c4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) io<TO>::st(o, ooff + j, rt[j] * nq + kappa * delta[j]);
+    }
+    float *dst = p.state_out + static_cast<int64_t>(bh) * DK * DV;
+    const uint32_t lo = static_cast<uint32_t>(rg * DV + 4 * c4);
+#pragma unroll
+    for (int i = 0; i < Sh::RPT; ++i) {
+        const int row = rg + Sh::RG * i;
+        const float a = s_a[PAR][row], kk = s_k[PAR][row] * nk;
+        __builtin_nontemporal_store(a * sv[i] + kk * delta,
+                                    reinterpret_cast<f32x4 *>(dst + (lo + static_cast<uint32_t>(Sh::RG * i * DV))));
+    }
+}
+
+template <int DK, int DV, typename TI, typename TO>
+__global__ void __launch_bounds__((DecodeShape<DK, DV>::NT)) decode1_kernel(DecodeParams p, int BH) {
+    using Sh = DecodeShape<DK, DV>;
+    __shared__ float s_a[2][DK], s_k[2][DK], s_q[2][DK], s_v[2][DV], s_b[2];
+    __shared__ float s_red[2][Sh::NW][DV];
+    const int tid = threadIdx.x, G = gridDim.x;
+    f32x4 svA[Sh::RPT], svB[Sh::RPT];
+    DecodeTok<TI> inA{}, inB{};
+    int bh = blockIdx.x;   // uniform: every wave takes the same branches
+    if (bh >= BH) return;
+    decode1_request<DK, DV, TI>(p, bh, tid, svA, inA);
+    for (;;) {
+        const int bh1 = bh + G;
+        if (bh1 < BH) decode1_request<DK, DV, TI>(p, bh1, tid, svB, inB);
+        decode1_update<DK, DV, TI, TO, 0>(p, bh, tid, svA, inA, s_a, s_k, s_q, s_v, s_b, s_red);
+        if (bh1 >= BH) break;
+        const int bh2 = bh1 + G;
+        if (bh2 < BH) decode1_request<DK, DV, TI>(p, bh2, tid, svA, inA);
+        decode1_update<DK, DV, TI, TO, 1>(p, bh1, tid, svB, inB, s_a, s_k, s_q, s_v, s_b, s_red);
+        if (bh2 >= BH) break;
+        bh = bh2;
+    }
+}
+
 }  // namespace kda
 
 namespace kda {
@@ -224,7 +383,11 @@ template <int DK, int DV, typename TI, typename TO>
 hipError_t run_decode(const DecodeParams &p, int B, hipStream_t s) {
     using Sh = DecodeShape<DK, DV>;
     const dim3 grid(static_cast<unsigned>(B) * p.H), block(Sh::NT);
-    if (p.m == 1 && !p.token_states)
+    if (p.m == 1 && !p.token_states && p.state_out) {
+        const int BH = B * p.H;
+        const int G = BH < kDecodeGrid ? BH : kDecodeGrid;
+        hipLaunchKernelGGL((decode1_kernel<DK, DV, TI, TO>), dim3(G), block, 0, s, p, BH);
+    } else if (p.m == 1 && !p.token_states)
         hipLaunchKernelGGL((decode_kernel<DK, DV, TI, TO, false>), grid, block, 0, s, p);
     else
         hipLaunchKernelGGL((decode_kernel<DK, DV, TI, TO, true>), grid, block, 0, s, p);

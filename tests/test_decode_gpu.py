@@ -47,6 +47,16 @@ def test_decode_small(dk, dv, dtype):
     report(f"decode B=3 H=2 d={dk}x{dv} {dtype}", o=eo, S=es)
 
 
+@pytest.mark.parametrize("B,H,dk,dv,dtype", [(100, 16, 128, 128, "bf16"), (275, 4, 64, 32, "f32")])
+def test_decode_persistent_walk_with_uneven_share(B, H, dk, dv, dtype):
+    # B*H states over the persistent single-token grid (512 workgroups): with
+    # 1600 and 1100 states some workgroups update one state more than others,
+    # so both halves of the prefetch walk end a workgroup's share
+    x = synth.decode_workload(B=B, H=H, dk=dk, dv=dv, steps=3, seed=47 + B, dtype=dtype, state_std=0.02)
+    eo, es = run_case(x)
+    report(f"decode B={B} H={H} d={dk}x{dv} {dtype}", o=eo, S=es)
+
+
 def test_decode_bf16_output():
     x = synth.decode_workload(B=4, H=3, steps=1, seed=41, state_std=0.3)
     S = torch.from_numpy(x.initial_state).cuda()
