@@ -169,7 +169,7 @@ def record_traffic(fetch_dir, write_dir, sq_dir, cal_fetch_dir, cal_write_dir, m
     groups = {
         "prefill_long": [("intra_kernel<64,128>", calls), ("scan_kernel<64,128,float>", calls),
                          ("chunk_table_kernel", calls)],
-        "decode": [("decode_kernel<128,128,unsignedshort,float,false>", None)],
+        "decode": [("decode1_kernel<128,128,unsignedshort,float>", None)],
         "short_conv_prefill": [("short_conv_kernel<unsignedshort,unsignedshort,4,16>", None),
                                ("conv_state_kernel<unsignedshort,4>", None)],
         "short_conv_decode": [("conv_rows_kernel<unsignedshort,unsignedshort,4>", None)],
@@ -749,7 +749,7 @@ def main():
                                 "unit": "GB/s", "frac": d_gbs / HBM_PEAK_GBS,
                                 "torch_copy_gbs": copy_gbs, "frac_of_torch_copy": d_gbs / copy_gbs,
                                 "traffic": measured_traffic("decode"),
-                                "kernel": "decode_kernel (m = 1)", "algorithmic_bytes": dbytes}},
+                                "kernel": "decode1_kernel (m = 1, persistent)", "algorithmic_bytes": dbytes}},
         "prefill_ms": pre,
     }
     if pro is not None:
