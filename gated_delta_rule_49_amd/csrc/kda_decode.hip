@@ -374,6 +374,203 @@ __global__ void __launch_bounds__((DecodeShape<DK, DV>::NT)) decode1_kernel(Deco
     }
 }
 
+
+// Multi-token launch with the state after every token (speculative
+// verification with rollback), m <= NT / max(DK, DV) tokens (4 at d = 128),
+// persistent like decode1_kernel: the next state and the raw token vectors
+// of its m tokens (one element per thread and vector) are requested before
+// the current state's m tokens are applied.  Per state: one barrier after
+// staging; wave t mod NW forms token t's k.q and norms, published by the
+// barrier of token 0's partials; one barrier per token (partials
+// double-buffered by token parity).  Measured for B=256, m=4, H=32, d=128
+// (145 VGPRs: one workgroup resident per CU): 595 us per launch against
+// 649 us for decode_kernel<..., true>; without the per-token states it is
+// slower (387 against 254 us: with one resident workgroup the m token
+// updates of successive states no longer overlap), so that case stays on
+// decode_kernel.
+template <int DK, int DV>
+struct DecodeMShape {
+    using Sh = DecodeShape<DK, DV>;
+    static constexpr int MT = Sh::NT / (DK > DV ? DK : DV);   // tokens per state at most
+};
+
+template <int DK, int DV, typename TI>
+__device__ __forceinline__ void decodem_request(const DecodeParams &p, int bh, int tid,
+                                                f32x4 (&sv)[DecodeShape<DK, DV>::RPT], DecodeTok<TI> &in) {
+    using Sh = DecodeShape<DK, DV>;
+    const int c4 = tid % Sh::TPR, rg = tid / Sh::TPR;
+    const float *src = p.state_in + static_cast<int64_t>(bh) * DK * DV;
+    const uint32_t lo = static_cast<uint32_t>(rg * DV + 4 * c4);
+#pragma unroll
+    for (int i = 0; i < Sh::RPT; ++i)
+        sv[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(src + (lo + static_cast<uint32_t>(Sh::RG * i * DV))));
+    const int b = bh / p.H, h = bh % p.H;
+    const int64_t tok0 = static_cast<int64_t>(b) * p.m * p.H + h;   // row of [B, m, H] of token 0
+    if (tid < p.m * DK) {
+        const int t = tid / DK, i = tid % DK;
+        const int64_t off = (tok0 + static_cast<int64_t>(t) * p.H) * DK + i;
+        in.a = static_cast<const TI *>(p.log_alpha)[off];
+        in.k = static_cast<const TI *>(p.k)[off];
+        in.q = static_cast<const TI *>(p.q)[off];
+    }
+    if (tid < p.m * DV) {
+        const int t = tid / DV, j = tid % DV;
+        in.v = static_cast<const TI *>(p.v)[(tok0 + static_cast<int64_t>(t) * p.H) * DV + j];
+    }
+    if (tid < p.m) in.b = static_cast<const TI *>(p.beta)[tok0 + static_cast<int64_t>(tid) * p.H];
+}
+
+template <int DK, int DV>
+struct DecodeMShared {
+    using Sh = DecodeShape<DK, DV>;
+    static constexpr int MT = DecodeMShape<DK, DV>::MT;
+    float a[2][MT][DK], k[2][MT][DK], q[2][MT][DK], v[2][MT][DV], b[2][MT];
+    float kappa[MT], nk[MT], nq[MT];
+    float red[2][2][Sh::NW][DV];
+};
+
+template <int DK, int DV, typename TI, typename TO, int PAR>
+__device__ __forceinline__ void decodem_update(const DecodeParams &p, int bh, int tid,
+                                               f32x4 (&sv)[DecodeShape<DK, DV>::RPT], const DecodeTok<TI> &in,
+                                               DecodeMShared<DK, DV> &sm, int &par) {
+    using Sh = DecodeShape<DK, DV>;
+    const int c4 = tid % Sh::TPR, rg = tid / Sh::TPR, wave = tid / 64, lane = tid % 64;
+    const int m = p.m;
+    if (tid < m * DK) {
+        const int t = tid / DK, i = tid % DK;
+        const float x = io<TI>::ld(&in.a, 0);
+        sm.a[PAR][t][i] = (p.prologue & kProGate) ? sigmoid_f32(-x) : __expf(x);
+        sm.k[PAR][t][i] = io<TI>::ld(&in.k, 0);
+        sm.q[PAR][t][i] = io<TI>::ld(&in.q, 0);
+    }
+    if (tid < m * DV) sm.v[PAR][tid / DV][tid % DV] = io<TI>::ld(&in.v, 0);
+    if (tid < m) {
+        float bt = io<TI>::ld(&in.b, 0);
+        if (p.prologue & kProBeta) bt = sigmoid_f32(bt);
+        sm.b[PAR][tid] = bt;
+    }
+    lds_barrier();
+    // token t's kappa = k.q and, with the norm, 1/|k| and 1/|q|, on wave
+    // t mod NW; read after the barrier of token 0's partials
+    for (int t = wave; t < m; t += Sh::NW) {
+        float kq = 0.f, k2 = 0.f, q2 = 0.f;
+        for (int i = lane; i < DK; i += 64) {
+            const float kk = sm.k[PAR][t][i], qq = sm.q[PAR][t][i];
+            kq += kk * qq;
+            k2 += kk * kk;
+            q2 += qq * qq;
+        }
+#pragma unroll
+        for (int msk = 32; msk >= 1; msk >>= 1) {
+            kq += __shfl_xor(kq, msk);
+            k2 += __shfl_xor(k2, msk);
+            q2 += __shfl_xor(q2, msk);
+        }
+        if (lane == 0) {
+            float nk = 1.f, nq = 1.f;
+            if (p.prologue & kProQKNorm) {
+                nk = 1.f / __builtin_sqrtf(k2 + kQKNormEps);
+                nq = 1.f / __builtin_sqrtf(q2 + kQKNormEps);
+            }
+            sm.nk[t] = nk;
+            sm.nq[t] = nq;
+            sm.kappa[t] = kq * nk * nq;
+        }
+    }
+    const int b = bh / p.H, h = bh % p.H;
+    const int64_t tok0 = static_cast<int64_t>(b) * m * p.H + h;
+    const uint32_t lo = static_cast<uint32_t>(rg * DV + 4 * c4);
+    for (int t = 0; t < m; ++t, par ^= 1) {
+        const int64_t tok = tok0 + static_cast<int64_t>(t) * p.H;
+        f32x4 pr = {0.f, 0.f, 0.f, 0.f}, rr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < Sh::RPT; ++i) {
+            const int row = rg + Sh::RG * i;
+            const float a = sm.a[PAR][t][row];
+            pr += sv[i] * (a * sm.k[PAR][t][row]);
+            rr += sv[i] * (a * sm.q[PAR][t][row]);
+        }
+#pragma unroll
+        for (int msk = Sh::TPR; msk < 64 && msk < Sh::NT; msk <<= 1) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pr[j] += __shfl_xor(pr[j], msk);
+                rr[j] += __shfl_xor(rr[j], msk);
+            }
+        }
+        if (lane < Sh::TPR) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sm.red[par][0][wave][4 * c4 + j] = pr[j];
+                sm.red[par][1][wave][4 * c4 + j] = rr[j];
+            }
+        }
+        lds_barrier();
+        f32x4 pt = {0.f, 0.f, 0.f, 0.f}, rt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < Sh::NW; ++w) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pt[j] += sm.red[par][0][w][4 * c4 + j];
+                rt[j] += sm.red[par][1][w][4 * c4 + j];
+            }
+        }
+        const float nk = sm.nk[t], nq = sm.nq[t], bt = sm.b[PAR][t];
+        f32x4 delta;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) delta[j] = bt * (sm.v[PAR][t][4 * c4 + j] - pt[j] * nk);
+        if (rg == 0) {
+            TO *o = static_cast<TO *>(p.o);
+            const float kappa = sm.kappa[t];
+            const int64_t ooff = tok * DV + 4 * c4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) io<TO>::st(o, ooff + j, rt[j] * nq + kappa * delta[j]);
+        }
+#pragma unroll
+        for (int i = 0; i < Sh::RPT; ++i) {
+            const int row = rg + Sh::RG * i;
+            const float a = sm.a[PAR][t][row], kk = sm.k[PAR][t][row] * nk;
+            sv[i] = a * sv[i] + kk * delta;
+        }
+        if (p.token_states) {
+            float *ts = p.token_states + tok * DK * DV;
+#pragma unroll
+            for (int i = 0; i < Sh::RPT; ++i)
+                __builtin_nontemporal_store(sv[i], reinterpret_cast<f32x4 *>(ts + (lo + static_cast<uint32_t>(Sh::RG * i * DV))));
+        }
+    }
+    if (p.state_out) {
+        float *dst = p.state_out + static_cast<int64_t>(bh) * DK * DV;
+#pragma unroll
+        for (int i = 0; i < Sh::RPT; ++i)
+            __builtin_nontemporal_store(sv[i], reinterpret_cast<f32x4 *>(dst + (lo + static_cast<uint32_t>(Sh::RG * i * DV))));
+    }
+}
+
+template <int DK, int DV, typename TI, typename TO>
+__global__ void __launch_bounds__((DecodeShape<DK, DV>::NT)) decodem_kernel(DecodeParams p, int BH) {
+    using Sh = DecodeShape<DK, DV>;
+    __shared__ DecodeMShared<DK, DV> sm;
+    const int tid = threadIdx.x, G = gridDim.x;
+    f32x4 svA[Sh::RPT], svB[Sh::RPT];
+    DecodeTok<TI> inA{}, inB{};
+    int par = 0;
+    int bh = blockIdx.x;   // uniform: every wave takes the same branches
+    if (bh >= BH) return;
+    decodem_request<DK, DV, TI>(p, bh, tid, svA, inA);
+    for (;;) {
+        const int bh1 = bh + G;
+        if (bh1 < BH) decodem_request<DK, DV, TI>(p, bh1, tid, svB, inB);
+        decodem_update<DK, DV, TI, TO, 0>(p, bh, tid, svA, inA, sm, par);
+        if (bh1 >= BH) break;
+        const int bh2 = bh1 + G;
+        if (bh2 < BH) decodem_request<DK, DV, TI>(p, bh2, tid, svA, inA);
+        decodem_update<DK, DV, TI, TO, 1>(p, bh1, tid, svB, inB, sm, par);
+        if (bh2 >= BH) break;
+        bh = bh2;
+    }
+}
+
 }  // namespace kda
 
 namespace kda {
@@ -387,6 +584,10 @@ hipError_t run_decode(const DecodeParams &p, int B, hipStream_t s) {
         const int BH = B * p.H;
         const int G = BH < kDecodeGrid ? BH : kDecodeGrid;
         hipLaunchKernelGGL((decode1_kernel<DK, DV, TI, TO>), dim3(G), block, 0, s, p, BH);
+    } else if (p.token_states && p.m <= DecodeMShape<DK, DV>::MT) {
+        const int BH = B * p.H;
+        const int G = BH < kDecodeGrid ? BH : kDecodeGrid;
+        hipLaunchKernelGGL((decodem_kernel<DK, DV, TI, TO>), dim3(G), block, 0, s, p, BH);
     } else if (p.m == 1 && !p.token_states)
         hipLaunchKernelGGL((decode_kernel<DK, DV, TI, TO, false>), grid, block, 0, s, p);
     else

@@ -49,6 +49,23 @@ def test_multi_token_parity(m, dtype):
     assert torch.equal(ts[:, -1], fin)
 
 
+@pytest.mark.parametrize("B,m,H,dk,dv", [(150, 4, 4, 128, 128), (275, 3, 4, 64, 32), (130, 4, 5, 16, 16)])
+def test_multi_token_states_persistent_walk_with_uneven_share(B, m, H, dk, dv):
+    """With per-token states, m up to 4 (d=128) runs on the persistent grid of
+    512 workgroups; 600, 1100 and 650 states give workgroups shares that end
+    on either half of the prefetch walk."""
+    tok, S0 = draw(75 + B, B, m, H, dk, dv, "bf16")
+    args = [torch.from_numpy(a).cuda().to(torch.bfloat16) for a in tok]
+    S = torch.from_numpy(S0).cuda()
+    o, fin, ts = kda.decode(*args, S, token_states=True)     # in place
+    o_ref, after_ref, fin_ref = oracle(tok, S0)
+    e = dict(o=err(o, o_ref), S=err(fin, fin_ref),
+             tokens=max(err(ts[:, j], after_ref[:, j]) for j in range(m)))
+    report(f"multi-token decode m={m} B={B} H={H} d={dk}x{dv} bf16, token states", **e)
+    assert max(e.values()) <= TOL["bf16"]
+    assert fin is S and torch.equal(ts[:, -1], fin)
+
+
 @pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 128), (128, 16)])
 def test_multi_token_head_sizes(dk, dv):
     tok, S0 = draw(80 + dk + dv, 3, 3, 2, dk, dv, "f32")
