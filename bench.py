@@ -578,7 +578,7 @@ def main():
             "value": Bd * M_TOK / (ms * 1e-3), "unit": "seq-token-steps/s", "avg_ms": ms,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "frac_of_torch_copy": None, "algorithmic_bytes": nbytes,
-                         "kernel": "decode_kernel (m = 4)"}}
+                         "kernel": "decodem_kernel (m = 4, persistent)" if with_states else "decode_kernel (m = 4)"}}
     del tsb, om, mt
 
     # Short causal convolution (width 4) over a q-shaped input of the prefill
