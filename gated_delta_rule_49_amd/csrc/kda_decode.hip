@@ -14,10 +14,15 @@
 // over rows are taken on the inputs and scaled once.
 // The state is HBM-bound: it is read once into registers, the m tokens are
 // applied there, and it is written once (plus once per token when the
-// per-token states are requested).  One workgroup of 512 threads per (b, h);
-// the column space of S is split across lanes in float4 groups (16-byte
-// coalesced rows) and the row space across row groups; the d_k reductions
-// run lane-to-lane inside a wave (__shfl_xor) and across waves through LDS.
+// per-token states are requested).  A workgroup of 512 threads works on one
+// (b, h) state at a time: the column space of S is split across lanes in
+// float4 groups (16-byte coalesced rows) and the row space across row
+// groups; the d_k reductions run lane-to-lane inside a wave (__shfl_xor) and
+// across waves through LDS.  Three kernels share this layout:
+// decode1_kernel (one token, output state: persistent, prefetching each
+// workgroup's next state), decodem_kernel (m tokens with per-token states,
+// m <= NT / max(d_k, d_v): persistent likewise) and decode_kernel (one
+// workgroup per state: the remaining launches).
 // The state is read and written with non-temporal accesses.  Measured on
 // MI355X for B=256, H=32, d=128 (1.09 GB per step): 512 threads per state
 // with non-temporal accesses 187 us per step; 256 threads 208 us (213 us
