@@ -24,8 +24,17 @@ Prints ONE JSON line:
   prefill_fp32 the same shape with fp32 inputs (1e-5 contract), chunk 64
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
 
+  prefill_workloads  the T=4096, H=16 prefill and the packed 8-document
+               prefill (H=32), each timed per call over >= 20 repetitions
+               with a 512 MiB write between them (so their ~100 MB-2 GB
+               working sets are not served from the 256 MB last-level cache)
+  every per-call figure carries median, min, max and mean over its repetitions
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload long|prefill|packed] [--no-cpu-baseline]
+       python bench.py --leg prefill_long|prefill_c2|prefill_c4|decode|backward
+                       [--steps K] [--warmup W]
+                       only that workload's calls (one rocprofv3 trace per workload)
        python bench.py --summarize DIR    per-kernel means of a rocprofv3 CSV run
        python bench.py --copy-calibration one 1 GiB device copy (counter scale)
        python bench.py --steps S --warmup W --record-traffic FETCH WRITE SQ CAL_FETCH CAL_WRITE MFMA
@@ -255,6 +264,42 @@ def summarize(root):
                 print(f"- {k} {c}: " + " ".join(f"{x:.6g}" for x in v[:12]))
 
 
+def stats(xs):
+    """median / min / max / mean of per-call durations (ms)."""
+    ys = sorted(xs)
+    n = len(ys)
+    med = ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+    return {"median": med, "min": ys[0], "max": ys[-1], "mean": sum(ys) / n, "n": n}
+
+
+def host_cpu():
+    """Model name of the host CPU and the number of cores this process may use."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"model": model, "cores_available": len(os.sched_getaffinity(0)),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+class CacheFlush:
+    """Writes a 512 MiB device buffer (twice the 256 MB last-level cache of an
+    MI355X) so that the next call's inputs come from HBM."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.buf.fill_(float(self.n))
+
+
 def copy_calibration():
     import torch
     n = 1 << 28  # floats: 1 GiB
@@ -313,6 +358,53 @@ def prefill_inputs(name, dev):
                 init=init, cu=cu, cu_host=x.cu_seqlens, chunk=x.chunk_size)
 
 
+def prefill_leg(kda, name, dev, reps, warmup, flush):
+    """Per-call timing of one prefill workload: warmup calls, then ``reps``
+    calls each preceded by a cache flush (untimed) and bracketed by HIP events
+    on the stream the library launches on (torch's current stream)."""
+    import torch
+    P = prefill_inputs(name, dev)
+    Bp, T, H, d = P["q"].shape
+    N = Bp if P["cu"] is None else P["cu"].numel() - 1
+    ws = torch.empty(kda.workspace_bytes(P["q"], P["k"], P["v"], P["beta"], P["log_alpha"], P["cu"],
+                                         P["chunk"]), dtype=torch.uint8, device=dev)
+    o = torch.empty((Bp, T, H, d), dtype=torch.float32, device=dev)
+    fin = torch.empty((N, H, d, d), dtype=torch.float32, device=dev)
+    # cu_seqlens validated once on the host; the timed calls do not synchronise
+    kda.prefill(P["q"], P["k"], P["v"], P["beta"], P["log_alpha"], initial_state=P["init"],
+                cu_seqlens=P["cu"], chunk_size=P["chunk"], workspace=ws, o=o, final_state=fin,
+                check_seqlens=True)
+
+    def call():
+        kda.prefill(P["q"], P["k"], P["v"], P["beta"], P["log_alpha"], initial_state=P["init"],
+                    cu_seqlens=P["cu"], chunk_size=P["chunk"], workspace=ws, o=o, final_state=fin,
+                    check_seqlens=False)
+    for _ in range(warmup):
+        call()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a_, b_ in evs:
+        if flush is not None:
+            flush()
+        a_.record()
+        call()
+        b_.record()
+    torch.cuda.synchronize()
+    st = stats([a_.elapsed_time(b_) for a_, b_ in evs])
+    tokens = int(P["cu_host"][-1]) if P["cu_host"] is not None else Bp * T
+    nbytes = tokens * H * PREFILL_BYTES_PER_TOKEN_HEAD + (2 * N * H * d * d * 4 if P["init"] is not None else 0)
+    gbs = nbytes / (st["median"] * 1e-3) / 1e9
+    useful_tf = tokens * H * chunk_flops_per_token_head(P["chunk"], d) / (st["median"] * 1e-3) / 1e12
+    out = {"value": tokens / (st["median"] * 1e-3), "unit": "tokens/s", "workload": P["workload"],
+           "tokens": tokens, "H": H, "num_seqs": N, "ms": st,
+           "cache_flush": "512 MiB device write before every timed call" if flush is not None else None,
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
+                        "useful_mfma_frac": useful_tf / BF16_PEAK_TFLOPS,
+                        "kernel": "kda_prefill_chunked (chunk table + intra_kernel + scan_kernel)"}}
+    del P, ws, o, fin
+    return out
+
+
 def cpu_baseline_prefill(P, target_s=12.0):
     """The fp64 oracle on the first S tokens of every head of the prefill
     workload (S sized for ~target_s of CPU work)."""
@@ -344,9 +436,22 @@ def cpu_baseline_prefill(P, target_s=12.0):
     S2 = int(min(T, max(2048, S * target_s / max(dt, 1e-3))))
     if S2 > S:
         dt, S = run(S2)
+    # the same recurrence on one thread, first S1 tokens of all heads (~4 s)
+    arrs1 = [host(a, 256) for a in (q, k, v, b, la)]
+    t1 = time.perf_counter()
+    native.prefill(*arrs1, nthreads=1)
+    d1 = time.perf_counter() - t1
+    S1 = int(min(T, max(256, 256 * 4.0 / max(d1, 1e-3))))
+    arrs1 = [host(a, S1) for a in (q, k, v, b, la)]
+    t1 = time.perf_counter()
+    native.prefill(*arrs1, nthreads=1)
+    d1 = time.perf_counter() - t1
     return dict(value=S / dt, unit="tokens/s", cores=native.max_threads(), kind="oracle",
                 sample=f"first {S} of {T} tokens, all {H} heads, fp64 token-by-token recurrence "
-                       f"({dt:.1f} s)")
+                       f"({dt:.1f} s)",
+                one_thread={"value": S1 / d1, "unit": "tokens/s", "cores": 1,
+                            "sample": f"first {S1} of {T} tokens, all {H} heads ({d1:.1f} s)"},
+                host_cpu=host_cpu())
 
 
 def cpu_baseline_decode(D):
@@ -414,6 +519,55 @@ def _decode_into(kda, mt, state, om, tsb):
         raise kda.KDAError(st, "kda_decode")
 
 
+def run_leg(kda, args, dev):
+    """One workload's calls only (warmup + steps), for a rocprofv3 trace whose
+    per-kernel averages are per-call figures of that workload."""
+    import torch
+    from synth.kda_inputs import _draw_tokens, _gen, _state
+    if args.leg.startswith("prefill"):
+        name = {"prefill_long": "long", "prefill_c2": "prefill", "prefill_c4": "packed"}[args.leg]
+        r = prefill_leg(kda, name, dev, reps=args.steps, warmup=args.warmup, flush=None)
+        print(json.dumps({"leg": args.leg, "workload": r["workload"], "ms": r["ms"], "value": r["value"],
+                          "unit": r["unit"]}), flush=True)
+        return
+    if args.leg == "decode":
+        gg = _gen(3, dev)
+        dq, dk_, dv_, db, dla = (t.to(torch.bfloat16) for t in _draw_tokens(gg, 64, 256, 32, 128, 128, 0.0,
+                                                                               dev, True))
+        state = _state(gg, (256, 32, 128, 128), 0.02, dev)
+        od = torch.empty((256, 32, 128), dtype=torch.float32, device=dev)
+        evs = []
+        for i in range(args.warmup + args.steps):
+            s_ = i % 64
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record()
+            kda.decode_step(dq[s_], dk_[s_], dv_[s_], db[s_], dla[s_], state, o=od)
+            b_.record()
+            evs.append((a_, b_))
+        torch.cuda.synchronize()
+        st = stats([a_.elapsed_time(b_) for a_, b_ in evs[args.warmup:]])
+        print(json.dumps({"leg": "decode", "workload": "decode_B256_H32_d128", "ms": st,
+                          "value": 256 / (st["median"] * 1e-3), "unit": "seq-steps/s"}), flush=True)
+        return
+    import synth
+    BX = synth.workload(2, device=dev)
+    bt = lambda a: torch.from_numpy(a).to(dev, torch.bfloat16)  # noqa: E731
+    bq, bk, bv, bb, bla = (bt(a) for a in (BX.q, BX.k, BX.v, BX.beta, BX.log_alpha))
+    bdo = torch.randn(bv.shape, generator=_gen(9, dev), device=dev)
+    _, _, ck = kda.prefill(bq, bk, bv, bb, bla, output_final_state=False, chunk_size=64, chunk_states=True)
+    evs = []
+    for i in range(args.warmup + args.steps):
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        kda.backward(bq, bk, bv, bb, bla, bdo, checkpoints=ck, chunk_size=64)
+        b_.record()
+        evs.append((a_, b_))
+    torch.cuda.synchronize()
+    st = stats([a_.elapsed_time(b_) for a_, b_ in evs[args.warmup:]])
+    print(json.dumps({"leg": "backward", "workload": "prefill shape B=1 T=4096 H=16 d=128 bf16", "ms": st,
+                      "value": BX.T / (st["median"] * 1e-3), "unit": "tokens/s"}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -421,6 +575,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long", choices=["long", "prefill", "packed"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill-workloads", action="store_true",
+                    help="skip the per-call timing of the T=4096 and packed prefill workloads")
+    ap.add_argument("--leg", choices=["prefill_long", "prefill_c2", "prefill_c4", "decode", "backward"],
+                    help="run only this workload's calls (warmup + steps), for a per-workload profile")
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--record-traffic", nargs=6,
@@ -449,6 +607,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.leg:
+        run_leg(kda, args, dev)
+        return
     ev = HipEvents()
     print(f"[bench] generating {args.workload} prefill + decode inputs", file=sys.stderr, flush=True)
     P = prefill_inputs(args.workload, dev)
@@ -481,7 +642,7 @@ def main():
     def step(i):
         kda.prefill(P["q"], P["k"], P["v"], P["beta"], P["log_alpha"], initial_state=P["init"],
                     cu_seqlens=P["cu"], chunk_size=P["chunk"], workspace=ws, o=o, final_state=fin,
-                    timing_events=ctypes.cast(ctypes.byref(pev, 3 * i * ctypes.sizeof(ctypes.c_void_p)),
+                    check_seqlens=False, timing_events=ctypes.cast(ctypes.byref(pev, 3 * i * ctypes.sizeof(ctypes.c_void_p)),
                                               ctypes.c_void_p))
         s = i % 64
         dstart[i].record()
@@ -700,8 +861,8 @@ def main():
     intra_ms = [ev.ms(pev[3 * i], pev[3 * i + 1]) for i in rng]
     scan_ms = [ev.ms(pev[3 * i + 1], pev[3 * i + 2]) for i in rng]
     dec_ms = [dstart[i].elapsed_time(dend[i]) for i in rng]
-    mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
-    pre, intra, scan, dec_in_step = mean(pre_ms), mean(intra_ms), mean(scan_ms), mean(dec_ms)
+    pre_st, intra_st, scan_st, dec_st = stats(pre_ms), stats(intra_ms), stats(scan_ms), stats(dec_ms)
+    pre, intra, scan, dec_in_step = pre_st["median"], intra_st["median"], scan_st["median"], dec_st["median"]
     dec = dec_loop
 
     tokens = Bp * T
@@ -716,6 +877,7 @@ def main():
 
     out = {
         "metric": METRIC,
+        "value_basis": "prefill tokens / median per-call time over the timed steps",
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -734,8 +896,10 @@ def main():
                      "frac": p_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(f"prefill_{args.workload}"),
                      "torch_copy_gbs": copy_gbs, "frac_of_torch_copy": p_gbs / copy_gbs,
                      "kernel": "kda_prefill_chunked (chunk table + intra_kernel + scan_kernel)",
-                     "algorithmic_bytes": pbytes, "avg_ms": pre,
+                     "algorithmic_bytes": pbytes, "avg_ms": pre_st["mean"], "median_ms": pre,
+                     "call_ms": pre_st,
                      "kernels_ms": {"intra_kernel": intra, "scan_kernel": scan},
+                     "kernels_ms_stats": {"intra_kernel": intra_st, "scan_kernel": scan_st},
                      "useful_mfma_tflops": useful_tf,
                      "useful_mfma_frac": useful_tf / BF16_PEAK_TFLOPS,
                      # counters recorded on the long workload's calls
@@ -745,6 +909,7 @@ def main():
         "decode": {"value": Bd / (dec * 1e-3), "unit": "seq-steps/s", "avg_ms": dec,
                    "timing": "64 consecutive steps of the decode trajectory, one HIP event pair",
                    "avg_ms_right_after_prefill": dec_in_step,
+                   "right_after_prefill_ms": dec_st,
                    "roofline": {"bound": "hbm", "achieved": d_gbs, "peak": HBM_PEAK_GBS,
                                 "unit": "GB/s", "frac": d_gbs / HBM_PEAK_GBS,
                                 "torch_copy_gbs": copy_gbs, "frac_of_torch_copy": d_gbs / copy_gbs,
@@ -769,6 +934,13 @@ def main():
     out["short_conv"] = conv
     out["backward"] = backward
     out["prefill_fp32"] = prefill_f32
+    if not args.no_prefill_workloads:
+        print("[bench] prefill workloads (T=4096 H=16; packed 8 documents H=32)", file=sys.stderr, flush=True)
+        flush = CacheFlush(dev)
+        out["prefill_workloads"] = {
+            "prefill_T4096_H16": prefill_leg(kda, "prefill", dev, reps=max(20, args.steps), warmup=3, flush=flush),
+            "packed_8docs_H32": prefill_leg(kda, "packed", dev, reps=max(20, args.steps), warmup=3, flush=flush)}
+        del flush
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline_prefill(P)

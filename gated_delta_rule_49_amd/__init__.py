@@ -181,6 +181,29 @@ def _check_dev(*ts):
     return dev
 
 
+def _check_buffer(t, name, shape, dtypes):
+    """A caller-supplied output or scratch buffer must have exactly the shape
+    and one of the dtypes the kernels will write (they write through raw
+    pointers: a smaller or narrower buffer would be overrun)."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be " + " or ".join(str(d) for d in dtypes) + f", got {t.dtype}")
+
+
+def _host_chunk_count(B, T, cu_seqlens, chunk_size):
+    """Number of chunk_size-token chunks over all sequences (one host copy of
+    cu_seqlens when packed)."""
+    if cu_seqlens is None:
+        return B * ((T + chunk_size - 1) // chunk_size)
+    lens = (cu_seqlens[1:] - cu_seqlens[:-1]).cpu().long()
+    if bool((lens < 0).any()):
+        raise KDAError(_STATUS_BAD_SEQLENS, "cu_seqlens")
+    return int(((lens + chunk_size - 1) // chunk_size).sum())
+
+
 def _stream(dev):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
@@ -204,6 +227,7 @@ def _make_args(q, k, v, beta, log_alpha, cu_seqlens, chunk_size, out_dtype, cu_h
 
 def workspace_bytes(q, k, v, beta, log_alpha, cu_seqlens=None, chunk_size=64,
                     out_dtype=torch.float32) -> int:
+    """Bytes of scratch a prefill call with these inputs needs."""
     return int(lib().kda_prefill_workspace_bytes(
         ctypes.byref(_make_args(q, k, v, beta, log_alpha, cu_seqlens, chunk_size, out_dtype))))
 
@@ -214,8 +238,8 @@ def max_chunks(q, k, v, beta, log_alpha, cu_seqlens=None, chunk_size=64) -> int:
 
 
 def prefill(q, k, v, beta, log_alpha, initial_state=None, output_final_state=True,
-            cu_seqlens=None, chunk_size=64, out_dtype=torch.float32, chunk_states=False,
-            workspace=None, final_state=None, o=None, check_seqlens=False, timing_events=None,
+            cu_seqlens=None, chunk_size=64, out_dtype=None, chunk_states=False,
+            workspace=None, final_state=None, o=None, check_seqlens=True, timing_events=None,
             prologue=0):
     """Chunked prefill.
 
@@ -224,12 +248,25 @@ def prefill(q, k, v, beta, log_alpha, initial_state=None, output_final_state=Tru
     documents along T.  ``initial_state`` fp32 [N,H,d_k,d_v] or None (zeros).
     Returns (o, final_state or None) or, with ``chunk_states=True``,
     (o, final_state, chunk_states) where chunk_states[c] is the state entering
-    global chunk c (documents in order).  ``check_seqlens`` additionally
-    validates cu_seqlens on the host (one device-to-host copy) and raises on a
-    device-side rejection (one synchronisation).  ``timing_events`` (a ctypes
-    pointer to three hipEvent_t) is passed through to the library's
-    profiling hook.  ``prologue``: PROLOGUE_* bits (which inputs are
-    pre-activations)."""
+    global chunk c (documents in order).
+
+    ``o`` / ``final_state`` / ``workspace``: optional preallocated buffers
+    ([B,T,H,d_v] float32 or bfloat16 — the output dtype is taken from ``o``
+    when given —, [N,H,d_k,d_v] float32, and at least workspace_bytes()
+    bytes); a buffer of another shape or dtype is rejected before launch.
+    ``out_dtype`` (default float32) is the dtype of an allocated ``o``.
+
+    ``check_seqlens`` (packed input only, default True) validates cu_seqlens
+    on the host (one device-to-host copy) and raises on a device-side
+    rejection (one synchronisation).  With ``check_seqlens=False`` nothing
+    synchronises; malformed cu_seqlens are still caught on the device, where
+    they stop every kernel before it writes, so o and final_state then keep
+    whatever their buffers held (uninitialised memory when allocated here):
+    the results are UNDEFINED and no error is raised.
+
+    ``timing_events`` (a ctypes pointer to three hipEvent_t) is passed
+    through to the library's profiling hook.  ``prologue``: PROLOGUE_* bits
+    (which inputs are pre-activations)."""
     dev = _check_dev(q, k, v, beta, log_alpha, initial_state, cu_seqlens, workspace, final_state, o)
     if not (q.dtype == k.dtype == v.dtype == beta.dtype == log_alpha.dtype):
         raise TypeError("q, k, v, beta, log_alpha must share one dtype")
@@ -245,6 +282,14 @@ def prefill(q, k, v, beta, log_alpha, initial_state=None, output_final_state=Tru
     if initial_state is not None:
         if initial_state.dtype != torch.float32 or tuple(initial_state.shape) != (N, H, dk, dv):
             raise ValueError(f"initial_state must be float32 [{N},{H},{dk},{dv}]")
+    if o is not None:
+        _check_buffer(o, "o", (B, T, H, dv), (torch.float32, torch.bfloat16))
+        if out_dtype is not None and out_dtype != o.dtype:
+            raise TypeError(f"out_dtype {out_dtype} disagrees with o.dtype {o.dtype}")
+        out_dtype = o.dtype
+    elif out_dtype is None:
+        out_dtype = torch.float32
+    _check_buffer(final_state, "final_state", (N, H, dk, dv), (torch.float32,))
     cu_host = None
     if cu_seqlens is not None and check_seqlens:
         cu_host = cu_seqlens.cpu().numpy()
@@ -264,7 +309,7 @@ def prefill(q, k, v, beta, log_alpha, initial_state=None, output_final_state=Tru
     if chunk_states:
         nmax = int(L.kda_prefill_max_chunks(ctypes.byref(a)))
         cs = torch.zeros((nmax, H, dk, dv), dtype=torch.float32, device=dev)
-    status = torch.zeros(1, dtype=torch.int32, device=dev) if check_seqlens else None
+    status = torch.zeros(1, dtype=torch.int32, device=dev) if (check_seqlens and cu_seqlens is not None) else None
     a.o = _ptr(o)
     a.initial_state = _ptr(initial_state)
     a.final_state = _ptr(final_state)
@@ -279,12 +324,7 @@ def prefill(q, k, v, beta, log_alpha, initial_state=None, output_final_state=Tru
     if status is not None and int(status.item()) != 0:
         raise KDAError(int(status.item()), "kda_prefill_chunked (device check)")
     if chunk_states:
-        if cu_seqlens is None:
-            nch = B * ((T + chunk_size - 1) // chunk_size)
-        else:
-            lens = (cu_seqlens[1:] - cu_seqlens[:-1]).cpu()
-            nch = int(((lens + chunk_size - 1) // chunk_size).sum())
-        return o, final_state, cs[:nch]
+        return o, final_state, cs[:_host_chunk_count(B, T, cu_seqlens, chunk_size)]
     return o, final_state
 
 
@@ -300,6 +340,7 @@ def decode_step(q, k, v, beta, log_alpha, state, out_dtype=torch.float32, o=None
         raise ValueError("shape mismatch")
     if state.dtype != torch.float32 or tuple(state.shape) != (B, H, dk, dv):
         raise ValueError(f"state must be float32 [{B},{H},{dk},{dv}]")
+    _check_buffer(o, "o", (B, H, dv), (torch.float32, torch.bfloat16))
     if o is None:
         o = torch.empty((B, H, dv), dtype=out_dtype, device=dev)
     st = lib().kda_decode_step(B, H, dk, dv, _dt(q.dtype), _dt(o.dtype), _ptr(q), _ptr(k), _ptr(v),
@@ -332,6 +373,10 @@ def decode(q, k, v, beta, log_alpha, state, out_dtype=torch.float32, update_stat
     dv = v.shape[-1]
     if state.dtype != torch.float32 or tuple(state.shape) != (B, H, dk, dv):
         raise ValueError(f"state must be float32 [{B},{H},{dk},{dv}]")
+    _check_buffer(o, "o", (B, m, H, dv), (torch.float32, torch.bfloat16))
+    _check_buffer(final_state, "final_state", (B, H, dk, dv), (torch.float32,))
+    if update_state and final_state is not None and final_state.data_ptr() != state.data_ptr():
+        raise ValueError("update_state writes the final state into `state`; do not pass final_state too")
     if o is None:
         o = torch.empty((B, m, H, dv), dtype=out_dtype, device=dev)
     if update_state:
@@ -369,9 +414,16 @@ def short_conv(x, weight, initial_state=None, bias=None, cu_seqlens=None, silu=F
     if initial_state is not None and (initial_state.dtype != torch.float32
                                       or tuple(initial_state.shape) != (N, C, W - 1)):
         raise ValueError(f"initial_state must be float32 [{N},{C},{W - 1}]")
+    _check_buffer(final_state, "final_state", (N, C, W - 1), (torch.float32,))
+    if y is not None:
+        _check_buffer(y, "y", (B, T, C), (torch.float32, torch.bfloat16))
+        if out_dtype is not None and out_dtype != y.dtype:
+            raise TypeError(f"out_dtype {out_dtype} disagrees with y.dtype {y.dtype}")
     if update_state:
         if initial_state is None:
             raise ValueError("update_state needs an initial_state to update")
+        if final_state is not None and final_state.data_ptr() != initial_state.data_ptr():
+            raise ValueError("update_state writes the final state into initial_state; do not pass final_state too")
         final_state = initial_state
     elif final_state is None:
         final_state = torch.empty((N, C, W - 1), dtype=torch.float32, device=dev)
@@ -404,8 +456,17 @@ def backward(q, k, v, beta, log_alpha, d_o, initial_state=None, d_final_state=No
     if d_o.dtype != torch.float32 or tuple(d_o.shape) != (B, T, H, dv):
         raise ValueError(f"d_o must be float32 [{B},{T},{H},{dv}]")
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
     if chunk_size is None:
         chunk_size = 64 if q.dtype == torch.bfloat16 else 16
+    for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
+        _check_buffer(t, name, (N, H, dk, dv), (torch.float32,))
+    if checkpoints is not None:
+        # the kernels address checkpoints through the device chunk table of
+        # chunk_size-token chunks: the buffer must hold exactly that many
+        nch = _host_chunk_count(B, T, cu_seqlens, chunk_size)
+        _check_buffer(checkpoints, "checkpoints", (nch, H, dk, dv), (torch.float32,))
     if checkpoints is None:
         _, _, checkpoints = prefill(q, k, v, beta, log_alpha, initial_state=initial_state,
                                     output_final_state=False, cu_seqlens=cu_seqlens, chunk_size=chunk_size,

@@ -34,11 +34,14 @@
 // chunk).  Split: the Gram factors, T in U, q*e^G, k*e^{G_L-G}, P, Delta and
 // S inside (q*e^G) S.
 //
-// Overflow: Gram blocks are factorised around a reference row m (the row
-// before the 16-row block): e^{G_r-G_i} = e^{G_r-G_m} e^{G_m-G_i}.  Off the
-// diagonal both factors are <= 1.  On a diagonal block the column factor is
-// >= 1 and bounded by the block's own decay; when that exceeds 2^100 in some
-// channel the block is computed exactly, pair by pair, on the vector ALUs.
+// Overflow: off-diagonal Gram blocks are factorised around a reference row m
+// (the row before the 16-row block): e^{G_r-G_i} = e^{G_r-G_m} e^{G_m-G_i},
+// both factors <= 1.  A diagonal block is factorised per channel around the
+// midpoint c of its own decay (c halfway between G at the row before the
+// block and G at its last row): e^{G_r-c} e^{c-G_i}, both within
+// 2^(+-span/2), span = that decay in powers of two.  When the span exceeds
+// 200 in some channel of a wave's channel half, that half of the block is
+// computed exactly, pair by pair, on the vector ALUs.
 #include "kda_launch.hpp"
 
 namespace kda {

@@ -30,3 +30,10 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True)
     assert r.returncode == 2 and "one GPU" in r.stdout
+
+
+def test_per_call_statistics_and_host_description():
+    assert bench.stats([3.0, 1.0, 2.0, 10.0]) == {"median": 2.5, "min": 1.0, "max": 10.0, "mean": 4.0, "n": 4}
+    assert bench.stats([5.0, 1.0, 4.0])["median"] == 4.0
+    h = bench.host_cpu()
+    assert h["cores_available"] >= 1

@@ -13,7 +13,24 @@ from kda_testutil import TOL, err, report, tdtype
 pytestmark = pytest.mark.gpu
 
 
-def run_case(x, check_every=1, pair_sample=None, full_every=None):
+def state_err(S_gpu, S_ref):
+    """err(S) = max|S - S_ref| / RMS(S_ref) over the whole state, in fp64,
+    in blocks of rows so that the temporaries stay small."""
+    x = S_gpu.detach().cpu().numpy().reshape(-1, S_gpu.shape[-1])
+    r = S_ref.reshape(-1, S_ref.shape[-1])
+    d, ss = 0.0, 0.0
+    for i in range(0, x.shape[0], 1 << 16):
+        xs, rs = x[i:i + (1 << 16)], r[i:i + (1 << 16)]
+        d = max(d, float(np.max(np.abs(xs - rs))))
+        ss += float(np.einsum("ij,ij->", rs, rs))
+    rms = np.sqrt(ss / r.size)
+    return d / rms if rms > 0 else (0.0 if d == 0 else float("inf"))
+
+
+def run_case(x):
+    """Every step: the GPU decode step against the oracle's own fp64
+    trajectory (never re-synchronised to the GPU state), outputs and the
+    full state compared after every step."""
     steps, B, H, dk = x.q.shape
     dt = tdtype(x.dtype)
     S = torch.from_numpy(x.initial_state).cuda()
@@ -25,16 +42,11 @@ def run_case(x, check_every=1, pair_sample=None, full_every=None):
         o_ref, S_ref, _ = native.prefill(x.q[s][None], x.k[s][None], x.v[s][None], x.beta[s][None],
                                          x.log_alpha[s][None], cu_seqlens=np.arange(B + 1),
                                          initial_state=S_ref)
-        if s % check_every == 0 or s == steps - 1:
-            eo = err(o, o_ref[0])
-            if pair_sample is not None and not (full_every and (s + 1) % full_every == 0):
-                b, h = pair_sample
-                es = err(S[b, h], S_ref[b, h])
-            else:
-                es = err(S, S_ref)
-            worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
-            assert eo <= TOL[x.dtype], f"step {s}: err(o) = {eo:.3e}"
-            assert es <= TOL[x.dtype], f"step {s}: err(S) = {es:.3e}"
+        eo = err(o, o_ref[0])
+        es = state_err(S, S_ref)
+        worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
+        assert eo <= TOL[x.dtype], f"step {s}: err(o) = {eo:.3e}"
+        assert es <= TOL[x.dtype], f"step {s}: err(S) = {es:.3e}"
     return worst_o, worst_s
 
 
@@ -74,11 +86,8 @@ def test_decode_bf16_output():
 
 def test_decode_workload_b256_h32_64_steps():
     """B=256 sequences, H=32, d=128, 64 steps of fresh bf16 inputs from an
-    N(0, 0.02^2) fp32 state: outputs checked in full after every step; the
-    state checked on a fixed sample of 64 (b, h) pairs after every step and
-    in full every 16 steps."""
+    N(0, 0.02^2) fp32 state: the outputs and the full 512 MiB state checked
+    against the oracle's trajectory after every one of the 64 steps."""
     x = synth.decode_workload()
-    rng = np.random.default_rng(0)
-    sample = (rng.integers(0, 256, 64), rng.integers(0, 32, 64))
-    eo, es = run_case(x, pair_sample=sample, full_every=16)
-    report("decode B=256 H=32 d=128 64 steps", o=eo, S=es)
+    eo, es = run_case(x)
+    report("decode B=256 H=32 d=128 64 steps (full state every step)", o=eo, S=es)
