@@ -171,8 +171,9 @@ int kda_oracle_prefill(int64_t num_seqs, const int64_t *cu_seqlens, int64_t T, i
     const int64_t sz = dk * dv;
     int err = 0;
 #ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
-#pragma omp parallel
+    /* the thread count applies to this call only (no global side effect) */
+    const int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel num_threads(nt)
 #endif
     {
         double *S = (double *)malloc(sizeof(double) * (size_t)(sz + 2 * dv + 2 * dk));
