@@ -32,7 +32,7 @@ import os
 
 import torch
 
-__all__ = ["prefill", "decode_step", "decode", "short_conv", "backward", "workspace_bytes", "max_chunks",
+__all__ = ["prefill", "prefill_noalloc", "NOALLOC_SCRATCH_BYTES", "decode_step", "decode", "short_conv", "backward", "workspace_bytes", "max_chunks",
            "lib", "KDAError", "PrefillArgs", "DecodeArgs", "ConvArgs", "BackwardArgs", "KDA_F32", "KDA_BF16", "PROLOGUE_GATE_SOFTPLUS",
            "PROLOGUE_BETA_SIGMOID", "PROLOGUE_QK_L2NORM", "PROLOGUE_ALL"]
 
@@ -43,6 +43,8 @@ KDA_F32, KDA_BF16 = 0, 1
 PROLOGUE_GATE_SOFTPLUS, PROLOGUE_BETA_SIGMOID, PROLOGUE_QK_L2NORM = 1, 2, 4
 PROLOGUE_ALL = 7
 _STATUS_BAD_SEQLENS = 6
+# fixed per-GPU scratch of kda_prefill_chunked_noalloc (KDA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 class KDAError(RuntimeError):
@@ -128,6 +130,8 @@ def lib():
         L.kda_prefill_max_chunks.restype = ctypes.c_int64
         L.kda_prefill_chunked.argtypes = [AP, P]
         L.kda_prefill_chunked.restype = I32
+        L.kda_prefill_chunked_noalloc.argtypes = [AP, P]
+        L.kda_prefill_chunked_noalloc.restype = I32
         L.kda_decode_step.argtypes = [I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P]
         L.kda_decode_step.restype = I32
         L.kda_decode.argtypes = [ctypes.POINTER(DecodeArgs), P]
@@ -325,6 +329,43 @@ def prefill(q, k, v, beta, log_alpha, initial_state=None, output_final_state=Tru
         raise KDAError(int(status.item()), "kda_prefill_chunked (device check)")
     if chunk_states:
         return o, final_state, cs[:_host_chunk_count(B, T, cu_seqlens, chunk_size)]
+    return o, final_state
+
+
+def prefill_noalloc(q, k, v, beta, log_alpha, o, final_state=None, initial_state=None, cu_seqlens=None,
+                    chunk_size=64, prologue=0):
+    """Chunked prefill through ``kda_prefill_chunked_noalloc``: the library
+    takes its scratch from a fixed per-GPU array (NOALLOC_SCRATCH_BYTES)
+    instead of a workspace, and this wrapper allocates nothing either — the
+    caller passes ``o`` ([B,T,H,d_v] float32 or bfloat16, which sets the
+    output dtype) and, if wanted, ``final_state`` (float32 [N,H,d_k,d_v]).
+    cu_seqlens are validated on the device only (no host copy, no
+    synchronisation): malformed offsets leave o and final_state unwritten.
+    Calls that overlap in time on one GPU race on the shared scratch.
+    Raises KDAError (status 7) when the call needs more scratch than the
+    array holds.  Returns (o, final_state)."""
+    dev = _check_dev(q, k, v, beta, log_alpha, initial_state, cu_seqlens, final_state, o)
+    if not (q.dtype == k.dtype == v.dtype == beta.dtype == log_alpha.dtype):
+        raise TypeError("q, k, v, beta, log_alpha must share one dtype")
+    if q.dim() != 4 or k.shape != q.shape or log_alpha.shape != q.shape:
+        raise ValueError("q, k, log_alpha must be [B,T,H,d_k]")
+    B, T, H, dk = q.shape
+    if v.dim() != 4 or v.shape[:3] != q.shape[:3] or beta.shape != q.shape[:3]:
+        raise ValueError("v must be [B,T,H,d_v] and beta [B,T,H]")
+    dv = v.shape[-1]
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if o is None:
+        raise ValueError("prefill_noalloc needs the output buffer o")
+    _check_buffer(o, "o", (B, T, H, dv), (torch.float32, torch.bfloat16))
+    _check_buffer(initial_state, "initial_state", (N, H, dk, dv), (torch.float32,))
+    _check_buffer(final_state, "final_state", (N, H, dk, dv), (torch.float32,))
+    a = _make_args(q, k, v, beta, log_alpha, cu_seqlens, chunk_size, o.dtype, None, prologue)
+    a.o, a.initial_state, a.final_state = _ptr(o), _ptr(initial_state), _ptr(final_state)
+    st = lib().kda_prefill_chunked_noalloc(ctypes.byref(a), _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_prefill_chunked_noalloc")
     return o, final_state
 
 

@@ -4,6 +4,8 @@
 #include "../../include/kda.h"
 #include "kda_launch.hpp"
 
+#include <mutex>
+
 using namespace kda;
 
 namespace {
@@ -88,6 +90,7 @@ const char *kda_status_string(int32_t s) {
         case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
         case KDA_ERR_HIP: return "HIP launch failed";
         case KDA_ERR_BAD_SEQLENS: return "cu_seqlens malformed";
+        case KDA_ERR_SCRATCH_LIMIT: return "needs more scratch than the allocation-free entry point holds";
         default: return "unknown status";
     }
 }
@@ -102,19 +105,21 @@ size_t kda_prefill_workspace_bytes(const kda_prefill_args *a) {
     return workspace_for(a);
 }
 
-kda_status kda_prefill_chunked(const kda_prefill_args *a, void *hip_stream) {
-    kda_status st = check_prefill(a, true);
-    if (st != KDA_OK) return st;
-    if (!a->workspace) return KDA_ERR_NULL_ARG;
-    if (reinterpret_cast<uintptr_t>(a->workspace) % kAlign) return KDA_ERR_BAD_SHAPE;
-    if (a->workspace_bytes < workspace_for(a)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+}  // extern "C"
+
+namespace {
+
+// The prefill after host validation, with its scratch at ws (ws_bytes long).
+kda_status prefill_on(const kda_prefill_args *a, char *ws, size_t ws_bytes, void *hip_stream) {
+    if (!ws) return KDA_ERR_NULL_ARG;
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign) return KDA_ERR_BAD_SHAPE;
+    if (ws_bytes < workspace_for(a)) return KDA_ERR_WORKSPACE_TOO_SMALL;
     // the bf16 matrix-core path reads q, k, v and the gate as 128-bit vectors
     if (use_mfma(a))
         for (const void *ptr : {a->q, a->k, a->v, a->log_alpha})
             if (reinterpret_cast<uintptr_t>(ptr) % 16) return KDA_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
 
-    char *ws = static_cast<char *>(a->workspace);
     PrefillParams p{};
     p.q = a->q; p.k = a->k; p.v = a->v; p.beta = a->beta; p.log_alpha = a->log_alpha;
     p.o = a->o;
@@ -149,6 +154,63 @@ kda_status kda_prefill_chunked(const kda_prefill_args *a, void *hip_stream) {
     }
     if (e == hipSuccess && ev) e = hipEventRecord(ev[2], s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+// Scratch of the allocation-free prefill: one copy of this array per GPU,
+// allocated when the library's code object is loaded on that GPU and held
+// until the process ends.  In host code its name is only a stand-in for the
+// device symbol, never an address: host code uses the per-device address
+// that scratch_address() looks up.
+static __device__ __align__(256) char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that owns hip_stream (the
+// current device for the null stream), looked up once per device with that
+// device current.
+kda_status scratch_address(void *hip_stream, char **out) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return KDA_ERR_HIP;
+    int dev = cur;
+    if (hip_stream) {
+        hipDevice_t d = -1;
+        if (hipStreamGetDevice(static_cast<hipStream_t>(hip_stream), &d) != hipSuccess) return KDA_ERR_HIP;
+        dev = static_cast<int>(d);
+    }
+    if (dev < 0 || dev >= kMaxDevices) return KDA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return KDA_ERR_HIP;
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (dev != cur && hipSetDevice(cur) != hipSuccess) return KDA_ERR_HIP;
+        if (e != hipSuccess || ptr == nullptr) return KDA_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = static_cast<char *>(g_scratch_ptr[dev]);
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_prefill_chunked(const kda_prefill_args *a, void *hip_stream) {
+    kda_status st = check_prefill(a, true);
+    if (st != KDA_OK) return st;
+    return prefill_on(a, static_cast<char *>(a->workspace), a->workspace_bytes, hip_stream);
+}
+
+kda_status kda_prefill_chunked_noalloc(const kda_prefill_args *a, void *hip_stream) {
+    kda_status st = check_prefill(a, true);
+    if (st != KDA_OK) return st;
+    if (workspace_for(a) > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_SCRATCH_LIMIT;
+    char *ws = nullptr;
+    st = scratch_address(hip_stream, &ws);
+    if (st != KDA_OK) return st;
+    return prefill_on(a, ws, KDA_NOALLOC_SCRATCH_BYTES, hip_stream);
 }
 
 kda_status kda_decode_step(int32_t B, int32_t H, int32_t d_k, int32_t d_v, int32_t in_dtype,

@@ -38,7 +38,8 @@
  *   - Pointers marked DEVICE are device memory owned by the caller; the
  *     library never allocates, frees or synchronises.  Scratch memory for
  *     prefill is a caller-provided workspace sized by
- *     kda_prefill_workspace_bytes().
+ *     kda_prefill_workspace_bytes(), or, for kda_prefill_chunked_noalloc, a
+ *     fixed array the library's code holds on each GPU.
  *   - Tensors are contiguous, row-major, with the layouts given below.
  *   - Every argument is validated on the host before the first launch; on an
  *     error nothing is launched and nothing is written.  After the launches
@@ -47,8 +48,9 @@
  *   - No query scale is applied: callers pre-scale q.
  *   - log_alpha must be <= 0 and all inputs finite; other values are not
  *     checked and propagate (NaN in, NaN out).
- *   - The library holds no mutable global state: concurrent calls on
- *     different streams with disjoint outputs and workspaces are safe.
+ *   - Apart from the fixed scratch of kda_prefill_chunked_noalloc, the
+ *     library holds no mutable global state: concurrent calls on different
+ *     streams with disjoint outputs and workspaces are safe.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -60,7 +62,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum {
     KDA_OK = 0,
@@ -69,7 +71,9 @@ typedef enum {
     KDA_ERR_UNSUPPORTED = 3,        /* valid but not implemented (dtype, d, C)    */
     KDA_ERR_WORKSPACE_TOO_SMALL = 4,
     KDA_ERR_HIP = 5,                /* a HIP launch failed                        */
-    KDA_ERR_BAD_SEQLENS = 6         /* host-visible cu_seqlens are malformed      */
+    KDA_ERR_BAD_SEQLENS = 6,        /* host-visible cu_seqlens are malformed      */
+    KDA_ERR_SCRATCH_LIMIT = 7       /* needs more than the fixed scratch of
+                                       kda_prefill_chunked_noalloc             */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -175,6 +179,31 @@ int64_t kda_prefill_max_chunks(const kda_prefill_args *a);
 /* Chunked prefill over all sequences and heads.  Returns KDA_OK once the
  * kernels are enqueued on hip_stream. */
 kda_status kda_prefill_chunked(const kda_prefill_args *a, void *hip_stream);
+
+/*
+ * Allocation-free variant of kda_prefill_chunked, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same operation, arguments, validation
+ * and results as kda_prefill_chunked, except that the scratch comes from a
+ * fixed device array inside the library instead of a->workspace (which is
+ * ignored, with a->workspace_bytes):
+ *   - the array holds KDA_NOALLOC_SCRATCH_BYTES on every GPU the library runs
+ *     on, from the load of the library's code on that GPU until the process
+ *     ends; its device address is looked up once per GPU, on the first call
+ *     for that GPU (the GPU owning hip_stream, or the current one for NULL);
+ *   - a call whose scratch need (kda_prefill_workspace_bytes) exceeds it
+ *     returns KDA_ERR_SCRATCH_LIMIT before anything is launched;
+ *   - nothing is allocated or freed (no hipMalloc, hipFree or allocating
+ *     library routine);
+ *   - every call on one GPU shares that GPU's array and finds the previous
+ *     call's contents there (each call rewrites all it reads): calls that
+ *     overlap in time on one GPU (on different streams, or from threads
+ *     without ordering) race and give undefined results; calls ordered on
+ *     one stream are safe.
+ * The caller still provides every input and output buffer.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (256u << 20)
+kda_status kda_prefill_chunked_noalloc(const kda_prefill_args *a, void *hip_stream);
 
 /*
  * One decode step for B independent sequences (one token each), fused:

@@ -36,8 +36,8 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.kda_abi_version() == 2
-    for s in range(7):
+    assert L.kda_abi_version() == 3
+    for s in range(8):
         assert L.kda_status_string(s)
     assert L.kda_status_string(99) == b"unknown status"
 
@@ -218,3 +218,14 @@ def test_binding_refuses_cpu_tensors():
         kda.prefill(q, q, q, torch.zeros(1, 4, 1), q)
     with pytest.raises(ValueError, match="GPU"):
         kda.decode_step(q[0], q[0], q[0], torch.zeros(1, 4), q[0], torch.zeros(1, 4, 16, 16))
+
+
+def test_noalloc_prefill_rejects_beyond_its_scratch_on_the_host(L):
+    """The allocation-free prefill refuses a call whose scratch need exceeds
+    its fixed array before any device call (status 7), and applies the same
+    host validation as the workspace entry point."""
+    a = base_args(T=131072, H=32, workspace=None)
+    assert L.kda_prefill_workspace_bytes(ctypes.byref(a)) > kda.NOALLOC_SCRATCH_BYTES
+    assert L.kda_prefill_chunked_noalloc(ctypes.byref(a), None) == 7
+    assert L.kda_prefill_chunked_noalloc(ctypes.byref(base_args(chunk_size=48)), None) == 3
+    assert L.kda_prefill_chunked_noalloc(ctypes.byref(base_args(q=None)), None) == 1
