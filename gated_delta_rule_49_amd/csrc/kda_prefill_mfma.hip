@@ -158,24 +158,36 @@ struct IntraRaw {
         asm volatile("" : "+v"(beta));
     }
 
-    __device__ __forceinline__ void load(const PrefillParams &p, int64_t t0, int L, int h, int tid) {
+    // element offset of this thread's vector u of the (chunk, head) tile
+    __device__ __forceinline__ static int64_t offset(int64_t t0, int L, int h, int H, int tid, int u) {
+        const int e = min(tid + 512 * u, M::NVEC - 1);
+        const int r = min(e / (D / 8), L - 1), c8 = (e % (D / 8)) * 8;
+        return ((t0 + r) * H + h) * D + c8;
+    }
+    // Two load sites, each reached once per item: k and q (issued after the
+    // Gram phase), then v, the gate and beta (issued after the UT solve), so
+    // that no phase stalls on issuing all 64 KB of the next item's inputs.
+    __device__ __forceinline__ void load_kq(const PrefillParams &p, int64_t t0, int L, int h, int tid) {
         const bf16_t *Kg = static_cast<const bf16_t *>(p.k);
-        const bf16_t *Vg = static_cast<const bf16_t *>(p.v);
         const bf16_t *Qg = static_cast<const bf16_t *>(p.q);
-        const bf16_t *Ag = static_cast<const bf16_t *>(p.log_alpha);
-        const bf16_t *Bg = static_cast<const bf16_t *>(p.beta);
-        const int H = p.H;
 #pragma unroll
         for (int u = 0; u < M::NV; ++u) {
-            const int e = min(tid + 512 * u, M::NVEC - 1);
-            const int r = min(e / (D / 8), L - 1), c8 = (e % (D / 8)) * 8;
-            const int64_t off = ((t0 + r) * H + h) * D + c8;
+            const int64_t off = offset(t0, L, h, p.H, tid, u);
             k[u] = *reinterpret_cast<const u32x4 *>(Kg + off);
-            v[u] = *reinterpret_cast<const u32x4 *>(Vg + off);
             q[u] = *reinterpret_cast<const u32x4 *>(Qg + off);
+        }
+    }
+    __device__ __forceinline__ void load_va(const PrefillParams &p, int64_t t0, int L, int h, int tid) {
+        const bf16_t *Vg = static_cast<const bf16_t *>(p.v);
+        const bf16_t *Ag = static_cast<const bf16_t *>(p.log_alpha);
+        const bf16_t *Bg = static_cast<const bf16_t *>(p.beta);
+#pragma unroll
+        for (int u = 0; u < M::NV; ++u) {
+            const int64_t off = offset(t0, L, h, p.H, tid, u);
+            v[u] = *reinterpret_cast<const u32x4 *>(Vg + off);
             a[u] = *reinterpret_cast<const u32x4 *>(Ag + off);
         }
-        beta = Bg[(t0 + min(tid, L - 1)) * H + h];
+        beta = Bg[(t0 + min(tid, L - 1)) * p.H + h];
     }
 };
 
@@ -634,9 +646,9 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
                 }
             }
         }  // live
-        // the next item's raw inputs: loads in flight during the rest of this
+        // the next item's k and q: loads in flight during the rest of this
         // item (issued after the Gram phase, whose registers they would crowd)
-        if (next < nitems) raw.load(p, itn.t0, itn.L, itn.h, tid);
+        if (next < nitems) raw.load_kq(p, itn.t0, itn.L, itn.h, tid);
         if (live) {
             lds_barrier();
 
@@ -740,6 +752,10 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
                 if (f >= NF) break;
                 operand_fragment(f);
             }
+        }  // live
+        // the next item's v, gate and beta
+        if (next < nitems) raw.load_va(p, itn.t0, itn.L, itn.h, tid);
+        if (live) {
             lds_barrier();
 
             // ---- 3b. T = X Diag(beta) as MFMA operands: bf16, and hi/lo (q, A dead)
