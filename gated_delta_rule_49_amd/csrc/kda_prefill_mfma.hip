@@ -84,6 +84,21 @@ __device__ __forceinline__ uint2 pack4(const bf16_t *s) {
     return r;
 }
 
+// Four 16-bit values of a row-major [row][col] LDS tile, transposed across the
+// 16 lanes of each lane group (ds_read_b64_tr_b16): lane i of group g
+// receives X[r0 + 4g + j][c0 + i], j = 0..3, when every lane of the group
+// addresses X[r0 + 4g + i / 4][c0 + 4 (i % 4)] (its 8-byte piece of the four
+// rows).  Two such reads (r0 and r0 + 16) give an MFMA operand with K along
+// the rows in the kperm order.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+__device__ __forceinline__ uint2 lds_read_tr16(const bf16_t *piece) {
+    // piece points into LDS (a __shared__ array): the C-style cast is the
+    // generic-to-local address-space conversion
+    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(piece));
+    return __builtin_bit_cast(uint2, r);
+}
+
 // persistent intra-chunk grid: one workgroup per CU of an MI355X (256 CUs)
 constexpr int kIntraGrid = 256;
 
@@ -99,7 +114,6 @@ template <int C, int D>
 struct IntraLds {
     static constexpr int CP = Lay<C, D>::CP;
     static constexpr int RK = D + 8;       // bf16 row stride of [token][channel]
-    static constexpr int RT = CP + 16;     // bf16 row stride of [channel][token] (octets XOR-swizzled)
     static constexpr int RTF = CP + 8;     // bf16 row stride of the T fragments
     static constexpr int RG = D + 4;       // fp32 row stride of G
     static constexpr int RA = CP + 4;      // fp32 row stride of A and X
@@ -108,29 +122,22 @@ struct IntraLds {
     static constexpr size_t SK = 0;                                   // k   [CP][RK] bf16
     static constexpr size_t SQ = SK + CP * RK * 2;                    // q   [CP][RK] bf16
     static constexpr size_t SA = SQ + CP * RK * 2;                    // A   [CP][RA] f32
-    static constexpr size_t SKT = SA + CP * RA * 4;                   // k^T [D][RT] bf16
-    static constexpr size_t SVT = SKT + D * RT * 2;                   // v^T [D][RT] bf16
-    static constexpr size_t SG = SVT + D * RT * 2;                    // G   [CP][RG] f32 (log2 units)
+    static constexpr size_t SV = SA + CP * RA * 4;                    // v   [CP][RK] bf16
+    static constexpr size_t SG = SV + CP * RK * 2;                    // G   [CP][RG] f32 (log2 units)
     static constexpr size_t ST = SG + CP * RG * 4;                    // X = (I+A)^-1 [CP][RA] f32
     static constexpr size_t SB = ST + CP * RA * 4;                    // beta [CP]
     static constexpr size_t SNK = SB + CP * 4;                        // 1/|k_r| [CP] (1 without the norm)
     static constexpr size_t SNQ = SNK + CP * 4;                       // 1/|q_r| [CP]
     static constexpr size_t SCNT = SNQ + CP * 4;                      // work counter (int)
-    static constexpr size_t END = SCNT + 16;
-    // after the Gram phase q and A are dead: the T fragments reuse [SQ, SKT)
+    static constexpr size_t SKG = SCNT + 16;                          // k e^G [CP][RK] bf16 (for W)
+    static constexpr size_t END = SKG + CP * RK * 2;
+    // after the Gram phase q and A are dead: the T fragments reuse [SQ, SV)
     // when they fit there, else they get their own region
-    static constexpr bool REUSE = 3 * CP * RTF * 2 <= SKT - SQ;
+    static constexpr bool REUSE = 3 * CP * RTF * 2 <= SV - SQ;
     static constexpr size_t TB = REUSE ? SQ : END;                    // T   bf16 [CP][RTF]
     static constexpr size_t TH = TB + CP * RTF * 2;                   // hi
     static constexpr size_t TL = TH + CP * RTF * 2;                   // lo
     static constexpr size_t BYTES = REUSE ? END : TL + CP * RTF * 2;
-    static constexpr int OMASK = CP / 8 - 1;
-    // element offset of (channel, token) in a transposed [channel][token]
-    // array: token octets are XOR-swizzled by the channel octet so that the
-    // staging writes and the fragment reads spread over the banks
-    __device__ static __forceinline__ int tpos(int ch, int tok) {
-        return ch * RT + ((((tok >> 3) ^ (ch >> 3)) & OMASK) << 3) + (tok & 7);
-    }
     // raw inputs prefetched per thread
     static constexpr int NVEC = CP * D / 8;                           // 16-byte vectors per array
     static constexpr int NV = (NVEC + 511) / 512;
@@ -301,8 +308,8 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
     auto SK = reinterpret_cast<bf16_t(*)[M::RK]>(smem + M::SK);
     auto SQ = reinterpret_cast<bf16_t(*)[M::RK]>(smem + M::SQ);
     auto SA = reinterpret_cast<float(*)[M::RA]>(smem + M::SA);
-    bf16_t *SKT = reinterpret_cast<bf16_t *>(smem + M::SKT);
-    bf16_t *SVT = reinterpret_cast<bf16_t *>(smem + M::SVT);
+    auto SV = reinterpret_cast<bf16_t(*)[M::RK]>(smem + M::SV);
+    auto SKG = reinterpret_cast<bf16_t(*)[M::RK]>(smem + M::SKG);
     auto SG = reinterpret_cast<float(*)[M::RG]>(smem + M::SG);
     auto SX = reinterpret_cast<float(*)[M::RA]>(smem + M::ST);
     auto SBETA = reinterpret_cast<float *>(smem + M::SB);
@@ -346,8 +353,8 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
 
         if (live) {
             raw.settle();
-            // ---- 1. stage k, q (natural), k^T, v^T (transposed, swizzled) and
-            //         log alpha (fp32, natural; becomes G in place), zero beyond L;
+            // ---- 1. stage k, q, v (bf16) and log alpha (fp32; becomes G in
+            //         place), all in natural [token][channel] layout, zero beyond L;
             //         then the gate cumsum, one wave per D/8 channels: lane
             //         (channel, token segment) sums its segment and the segment
             //         offsets come from a scan across lanes.
@@ -363,18 +370,12 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
                 const u32x4 av = live ? raw.a[u] : z;
                 *reinterpret_cast<u32x4 *>(&SK[r][c8]) = kv;
                 *reinterpret_cast<u32x4 *>(&SQ[r][c8]) = qv;
+                *reinterpret_cast<u32x4 *>(&SV[r][c8]) = vv;
+                if (C < CP && r >= C) *reinterpret_cast<u32x4 *>(&SKG[r][c8]) = z;
                 // 32-bit word operations on the raw registers (element j of a
                 // vector is the low (j even) or high (j odd) half of word j / 2)
                 const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
-                const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
                 const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
-#pragma unroll
-                for (int j2 = 0; j2 < 4; ++j2) {
-                    SKT[M::tpos(c8 + 2 * j2, r)] = static_cast<bf16_t>(kw[j2] & 0xffffu);
-                    SKT[M::tpos(c8 + 2 * j2 + 1, r)] = static_cast<bf16_t>(kw[j2] >> 16);
-                    SVT[M::tpos(c8 + 2 * j2, r)] = static_cast<bf16_t>(vw[j2] & 0xffffu);
-                    SVT[M::tpos(c8 + 2 * j2 + 1, r)] = static_cast<bf16_t>(vw[j2] >> 16);
-                }
                 f32x4 g0 = {__uint_as_float(aw[0] << 16), __uint_as_float(aw[0] & 0xffff0000u),
                             __uint_as_float(aw[1] << 16), __uint_as_float(aw[1] & 0xffff0000u)};
                 f32x4 g1 = {__uint_as_float(aw[2] << 16), __uint_as_float(aw[2] & 0xffff0000u),
@@ -669,11 +670,22 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
                     const bf16_t *qa = reinterpret_cast<const bf16_t *>(&q0);
                     const bf16_t *qb = reinterpret_cast<const bf16_t *>(&q1);
                     const float nq = SNQ[r];
+                    // the same elements of k e^G (bf16, natural layout) for W
+                    const uint2 k0 = *reinterpret_cast<const uint2 *>(&SK[r][cA]);
+                    const uint2 k1 = *reinterpret_cast<const uint2 *>(&SK[r][cB]);
+                    const bf16_t *ka = reinterpret_cast<const bf16_t *>(&k0);
+                    const bf16_t *kb = reinterpret_cast<const bf16_t *>(&k1);
+                    bf16_t kga[4], kgb[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        split_bf16(bf16_to_f32(qa[j]) * nq * fast_exp2(g0[j]), hi.s[j], lo.s[j]);
-                        split_bf16(bf16_to_f32(qb[j]) * nq * fast_exp2(g1[j]), hi.s[4 + j], lo.s[4 + j]);
+                        const float ea = fast_exp2(g0[j]), eb = fast_exp2(g1[j]);
+                        split_bf16(bf16_to_f32(qa[j]) * nq * ea, hi.s[j], lo.s[j]);
+                        split_bf16(bf16_to_f32(qb[j]) * nq * eb, hi.s[4 + j], lo.s[4 + j]);
+                        kga[j] = f32_to_bf16(bf16_to_f32(ka[j]) * ea);
+                        kgb[j] = f32_to_bf16(bf16_to_f32(kb[j]) * eb);
                     }
+                    *reinterpret_cast<uint2 *>(&SKG[r][cA]) = pack4(kga);
+                    *reinterpret_cast<uint2 *>(&SKG[r][cB]) = pack4(kgb);
                     const size_t fo = (static_cast<size_t>(f) * 64 + lane) * 16;
                     dst_h = Y::QH + fo;
                     dst_l = Y::QL + fo;
@@ -683,8 +695,10 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
                     const int ch = 16 * mt + li;
                     const float gl = SG[C - 1][ch];
                     const int iA = 32 * ks + 4 * g, iB = iA + 16;
-                    const uint2 k0 = *reinterpret_cast<const uint2 *>(&SKT[M::tpos(ch, iA)]);
-                    const uint2 k1 = *reinterpret_cast<const uint2 *>(&SKT[M::tpos(ch, iB)]);
+                    // k at tokens iA..iA+3 and iB..iB+3 of channel ch
+                    const bf16_t *kp = &SK[32 * ks + 4 * g + li / 4][16 * mt + 4 * (li % 4)];
+                    const uint2 k0 = lds_read_tr16(kp);
+                    const uint2 k1 = lds_read_tr16(kp + 16 * M::RK);
                     const bf16_t *ka = reinterpret_cast<const bf16_t *>(&k0);
                     const bf16_t *kb = reinterpret_cast<const bf16_t *>(&k1);
                     const f32x4 nka = *reinterpret_cast<const f32x4 *>(&SNK[iA]);
@@ -758,7 +772,11 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
         if (live) {
             lds_barrier();
 
-            // ---- 3b. T = X Diag(beta) as MFMA operands: bf16, and hi/lo (q, A dead)
+            // ---- 3b. T = X Diag(beta) as MFMA operands: bf16, and hi/lo (q, A
+            //          dead).  Columns (tokens) are stored in the kperm order of
+            //          their 32-token step, so that the 8 values an MFMA lane
+            //          takes are one 16-byte row piece: tokens 4g..4g+3 and
+            //          16+4g..16+4g+3 of the step at positions 8g..8g+7.
             for (int e = tid; e < CP * CP / 4; e += 512) {
                 const int r = e / (CP / 4), i4 = (e % (CP / 4)) * 4;
                 // X is only defined on the lower block triangle of the C x C part
@@ -771,9 +789,10 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
                     tb[j] = f32_to_bf16(t * SNK[i4 + j]);  // W = T Diag(1/|k|) (k e^G)
                     split_bf16(t, th[j], tl[j]);
                 }
-                *reinterpret_cast<uint2 *>(&TB[r][i4]) = pack4(tb);
-                *reinterpret_cast<uint2 *>(&TH[r][i4]) = pack4(th);
-                *reinterpret_cast<uint2 *>(&TL[r][i4]) = pack4(tl);
+                const int pos = (i4 & ~31) + 8 * ((i4 >> 2) & 3) + 4 * ((i4 >> 4) & 1);
+                *reinterpret_cast<uint2 *>(&TB[r][pos]) = pack4(tb);
+                *reinterpret_cast<uint2 *>(&TH[r][pos]) = pack4(th);
+                *reinterpret_cast<uint2 *>(&TL[r][pos]) = pack4(tl);
             }
             lds_barrier();
 
@@ -783,35 +802,34 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
             for (int wi = wave; wi < 2 * Y::NDT; wi += 8) {
                 const bool isW = wi < Y::NDT;
                 const int ct = isW ? wi : wi - Y::NDT;
-                const int ch = 16 * ct + li;
                 f32x4 acc[Y::NMT];
 #pragma unroll
                 for (int tt = 0; tt < Y::NMT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s2 = 0; s2 < Y::KSC; ++s2) {
-                    const int i0 = 32 * s2 + 8 * g;
-                    frag8 opk;  // W: (k e^G)^T, channel row ch, tokens i0..i0+7; U: V^T
-                    if (isW) {
-                        const uint4 kraw = *reinterpret_cast<const uint4 *>(&SKT[M::tpos(ch, i0)]);
-                        const bf16_t *kk = reinterpret_cast<const bf16_t *>(&kraw);
-#pragma unroll
-                        for (int j = 0; j < 8; ++j)
-                            opk.s[j] = f32_to_bf16(bf16_to_f32(kk[j]) * fast_exp2(SG[i0 + j][ch]));
-                    } else {
-                        opk.u = *reinterpret_cast<const uint4 *>(&SVT[M::tpos(ch, i0)]);
+                    // token k-step s2 in the kperm order: tokens iA..iA+3 and
+                    // iA+16..iA+19 of the step for lane group g
+                    const int iA = 32 * s2 + 4 * g;
+                    frag8 opk;  // W: (k e^G)^T, channel row ch; U: V^T, value column ch
+                    {
+                        const bf16_t *src = isW ? &SKG[iA + li / 4][16 * ct + 4 * (li % 4)]
+                                                : &SV[iA + li / 4][16 * ct + 4 * (li % 4)];
+                        const uint2 lo4 = lds_read_tr16(src), hi4 = lds_read_tr16(src + 16 * M::RK);
+                        opk.u = make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
                     }
 #pragma unroll
                     for (int tt = 0; tt < Y::NMT; ++tt) {
                         if (32 * s2 > 16 * tt + 15) continue;
                         const int r = 16 * tt + li;
+                        const int tp = 32 * s2 + 8 * g;   // this lane group's kperm piece
                         if (isW) {
                             frag8 tb;
-                            tb.u = *reinterpret_cast<const uint4 *>(&TB[r][i0]);
+                            tb.u = *reinterpret_cast<const uint4 *>(&TB[r][tp]);
                             acc[tt] = mfma16(opk.v, tb.v, acc[tt]);   // rows: channels, cols: tokens
                         } else {
                             frag8 th, tl;
-                            th.u = *reinterpret_cast<const uint4 *>(&TH[r][i0]);
-                            tl.u = *reinterpret_cast<const uint4 *>(&TL[r][i0]);
+                            th.u = *reinterpret_cast<const uint4 *>(&TH[r][tp]);
+                            tl.u = *reinterpret_cast<const uint4 *>(&TL[r][tp]);
                             acc[tt] = mfma16(th.v, opk.v, acc[tt]);   // rows: tokens, cols: channels
                             acc[tt] = mfma16(tl.v, opk.v, acc[tt]);
                         }
