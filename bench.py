@@ -209,6 +209,38 @@ def record_traffic(fetch_dir, write_dir, sq_dir, cal_fetch_dir, cal_write_dir, m
                          for k, v in out_calls.items()}}))
 
 
+def record_prefill_traffic(fetch_dir, write_dir, sq_dir, mfma_dir, calls):
+    """Refresh the long-prefill entry of profiles/traffic.json (its HBM bytes
+    and the prefill kernels' SQ / matrix-core counters) from rocprofv3 --pmc
+    runs of `bench.py --leg prefill_long --steps S --warmup W` (calls = W + S
+    plain prefill calls), keeping the other entries and the copy calibration
+    already recorded."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    rec = json.load(open(path))
+    acc = _counter_runs([fetch_dir, write_dir, sq_dir, mfma_dir])
+
+    def mean(kernel, counter):
+        v = acc.get((kernel, counter))
+        if not v:
+            raise SystemExit(f"no {counter} dispatches of {kernel} in the counter runs")
+        v = v[:calls]
+        return sum(v) / len(v)
+
+    ks = ["intra_kernel<64,128>", "scan_kernel<64,128,float>", "chunk_table_kernel"]
+    per = {k: [mean(k, "FETCH_SIZE"), mean(k, "WRITE_SIZE")] for k in ks}
+    rec["calls"]["prefill_long"] = {"fetch_kib": sum(v[0] for v in per.values()),
+                                    "write_kib": sum(v[1] for v in per.values()), "kernels": per}
+    rec["counters"] = {k: {c: mean(k, c) for (kk, c) in acc if kk == k and (c.startswith("SQ_") or
+                                                                          c == "GRBM_GUI_ACTIVE")}
+                       for k in ks[:2]}
+    rec["sources_sha"]["prefill"] = kernel_sources_sha("prefill")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    v = rec["calls"]["prefill_long"]
+    print(json.dumps({"prefill_long_gb": (v["fetch_kib"] * rec["fetch_scale"] + v["write_kib"] * rec["write_scale"])
+                      * 1024 / 1e9}))
+
+
 # Vector-ALU issue peak of MI355X: 256 CUs x 4 SIMDs, one wave64 VALU
 # instruction per SIMD every 4 cycles (16 lanes), at 2.4 GHz, counted in
 # lane-operations (64 per wave instruction).
@@ -577,6 +609,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill-workloads", action="store_true",
                     help="skip the per-call timing of the T=4096 and packed prefill workloads")
+    ap.add_argument("--record-prefill-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "SQ_DIR", "MFMA_DIR"),
+                    help="refresh the long-prefill entry of profiles/traffic.json from rocprofv3 --pmc runs of "
+                         "`bench.py --leg prefill_long --steps S --warmup W` (give the same --steps/--warmup)")
     ap.add_argument("--leg", choices=["prefill_long", "prefill_c2", "prefill_c4", "decode", "backward"],
                     help="run only this workload's calls (warmup + steps), for a per-workload profile")
     ap.add_argument("--summarize", metavar="DIR")
@@ -592,6 +627,9 @@ def main():
         return
     if args.record_traffic:
         record_traffic(*args.record_traffic, calls=args.warmup + args.steps)
+        return
+    if args.record_prefill_traffic:
+        record_prefill_traffic(*args.record_prefill_traffic, calls=args.warmup + args.steps)
         return
     if args.copy_calibration:
         copy_calibration()
