@@ -18,11 +18,13 @@
 // (b, h) state at a time: the column space of S is split across lanes in
 // float4 groups (16-byte coalesced rows) and the row space across row
 // groups; the d_k reductions run lane-to-lane inside a wave (__shfl_xor) and
-// across waves through LDS.  Three kernels share this layout:
+// across waves through LDS.  Four kernels share this layout:
 // decode1_kernel (one token, output state: persistent, prefetching each
-// workgroup's next state), decodem_kernel (m tokens with per-token states,
-// m <= NT / max(d_k, d_v): persistent likewise) and decode_kernel (one
-// workgroup per state: the remaining launches).
+// workgroup's next state), decodec_kernel (2 to 4 tokens without per-token
+// states, applied as one small chunk: persistent likewise), decodem_kernel
+// (m tokens with per-token states, m <= NT / max(d_k, d_v): persistent
+// likewise) and decode_kernel (one workgroup per state: the remaining
+// launches).
 // The state is read and written with non-temporal accesses.  Measured on
 // MI355X for B=256, H=32, d=128 (1.09 GB per step): 512 threads per state
 // with non-temporal accesses 187 us per step; 256 threads 208 us (213 us
@@ -576,6 +578,397 @@ __global__ void __launch_bounds__((DecodeShape<DK, DV>::NT)) decodem_kernel(Deco
     }
 }
 
+
+// Multi-token launch as one small chunk, 2 <= m <= 4 tokens, persistent
+// like decode1_kernel.  The chunked form of the recurrence (Module 04 —
+// KDA II, §1 "The recurrence has affine form") restricted to the m tokens
+// gives every token's delta vector from the state S0 they start from:
+//     X_t = v_t - S0^T (khat_t * Gamma_t),   Gamma_t = a_0 * ... * a_t
+//     (I + A) Delta = Diag(beta) X,   A_ti = beta_t sum_c khat_t khat_i a_{i+1}..a_t  (i < t)
+//     o_t = S0^T (qhat_t * Gamma_t) + sum_{i<=t} P_ti Delta_i,
+//           P_ti = sum_c qhat_t khat_i a_{i+1}..a_t  (i <= t)
+// (khat, qhat: k and q with the optional norm; the decay products are
+// taken per channel), and then
+//     S_m = Gamma_{m-1} * S0 + sum_t (khat_t * a_{t+1}..a_{m-1}) Delta_t^T,
+// or, when the state after every token is asked for, token by token
+// S_{t+1} = a_t * S_t + khat_t Delta_t^T.
+// Roles: threads [0, DV) own a column each (they solve for Delta and form
+// the outputs once per column), threads [DV, DV + DK) own a row each (they
+// turn a state's tokens into per-row factors and per-channel terms of the
+// m^2 + m pair sums kk_ti, qk_ti, |k_t|^2, |q_t|^2).  The row work depends
+// on the tokens only, so it is done one state ahead, while the column
+// owners work: per state there is one pass of 2m reductions over the rows
+// of S0, a barrier, the column work beside the next state's row work, a
+// barrier, and the update of the state.  Measured for B=256, H=32, d=128
+// (state only, 512 workgroups, one resident per CU): m = 2 in 188 us and
+// m = 4 in 209 us per launch, against 216 and 251 us token by token on
+// decode_kernel; 256 workgroups gave 193 and 205 us, 1024 gave 191 and
+// 219 us.  With per-token states decodem_kernel stays faster (590 against
+// 682 us at m = 4: the token-by-token sweep writes every state anyway).
+template <int M>
+struct DecodeCJobs {
+    static constexpr int NKK = M * (M - 1) / 2, NQK = M * (M + 1) / 2, N = NKK + NQK + 2 * M;
+    static constexpr int kk(int t, int i) { return t * (t - 1) / 2 + i; }         // i < t
+    static constexpr int qk(int t, int i) { return NKK + t * (t + 1) / 2 + i; }   // i <= t
+    static constexpr int k2(int t) { return NKK + NQK + t; }
+    static constexpr int q2(int t) { return NKK + NQK + M + t; }
+};
+
+template <int DK, int DV>
+struct DecodeCRoles {
+    static constexpr int W0 = DV / 64, W1 = (DV + DK - 1) / 64;   // waves holding row owners
+    static constexpr int NPART = W1 - W0 + 1;                      // partial pair sums per job
+};
+
+template <int DK, int DV, int M>
+struct DecodeCShared {
+    using Sh = DecodeShape<DK, DV>;
+    // first: 16-byte aligned; DK and DV are multiples of 4
+    float red[2][M][Sh::NW][DV];   // wave partials of S0^T Ktil_t (0) and S0^T Qtil_t (1)
+    // by state parity: per-row factors of each token
+    float kt[2][M][DK];    // k_t Gamma_t
+    float qt[2][M][DK];    // q_t Gamma_t
+    float kh[2][M][DK];    // k_t a_{t+1} .. a_{m-1}
+    float a[2][M][DK], k[2][M][DK];
+    float gm[2][DK];       // Gamma_{m-1}
+    float pj[2][DecodeCJobs<M>::N][DecodeCRoles<DK, DV>::NPART];   // partial pair sums
+    float dl[M][DV];       // nk_t Delta_t
+};
+
+// one thread's token values: a row owner's a_t, k_t, q_t of its row, a
+// column owner's v_t and beta_t of its column (raw, converted at use)
+template <int M, typename TI>
+struct DecodeCTok {
+    TI r[3 * M];
+};
+
+// thread (rg, c4) holds the RPT consecutive rows rg * RPT .. rg * RPT + RPT - 1
+// of the state, so that its rows' factors are contiguous in LDS; each load
+// instruction still covers whole 512-byte rows of the state.  bh_col names
+// the state whose v and beta the column owners take, bh_row the state whose
+// a, k, q the row owners take.  Every load is unconditional (indices
+// clamped) so that the wait counts leave the request in flight.
+template <int DK, int DV, int M, typename TI>
+__device__ __forceinline__ void decodec_request(const DecodeParams &p, int bh, int bh_col, int bh_row, int tid,
+                                                f32x4 (&sv)[DecodeShape<DK, DV>::RPT], DecodeCTok<M, TI> &in) {
+    using Sh = DecodeShape<DK, DV>;
+    const int c4 = tid % Sh::TPR, rg = tid / Sh::TPR;
+    const float *src = p.state_in + static_cast<int64_t>(bh) * DK * DV;
+    const uint32_t lo = static_cast<uint32_t>(rg * Sh::RPT * DV + 4 * c4);
+#pragma unroll
+    for (int i = 0; i < Sh::RPT; ++i)
+        sv[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(src + (lo + static_cast<uint32_t>(i * DV))));
+    // rows [B, m, H] of token 0 of the two states
+    const int64_t tc = static_cast<int64_t>(bh_col / p.H) * M * p.H + bh_col % p.H;
+    const int64_t tr = static_cast<int64_t>(bh_row / p.H) * M * p.H + bh_row % p.H;
+    const bool col = tid < DV;
+    const int j = col ? tid : 0;
+    const int c = col ? 0 : (tid - DV < DK ? tid - DV : DK - 1);
+    const TI *v = static_cast<const TI *>(p.v), *be = static_cast<const TI *>(p.beta);
+    const TI *la = static_cast<const TI *>(p.log_alpha), *k = static_cast<const TI *>(p.k), *q = static_cast<const TI *>(p.q);
+#pragma unroll
+    for (int t = 0; t < M; ++t) {
+        const int64_t rc = tc + static_cast<int64_t>(t) * p.H, rr = tr + static_cast<int64_t>(t) * p.H;
+        in.r[t] = col ? v[rc * DV + j] : la[rr * DK + c];
+        in.r[M + t] = col ? be[rc] : k[rr * DK + c];
+        in.r[2 * M + t] = col ? be[rc] : q[rr * DK + c];
+    }
+}
+
+// this thread's RPT consecutive entries of a per-row LDS vector
+template <int RPT>
+__device__ __forceinline__ void lds_rows(const float *src, float (&dst)[RPT]) {
+    if constexpr (RPT % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < RPT; i += 4) {
+            const float4 x = *reinterpret_cast<const float4 *>(src + i);
+            dst[i] = x.x; dst[i + 1] = x.y; dst[i + 2] = x.z; dst[i + 3] = x.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) dst[i] = src[i];
+    }
+}
+
+// x[l] + x[l ^ 32] in every lane: one swap of the wave's halves (VALU, no LDS)
+__device__ __forceinline__ float sum_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// x of the lane named by a DPP control within its row of 16 (quad permutes
+// and row mirrors only, so every lane has a source)
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// the sum over the row groups of a wave (lanes that hold the same columns)
+template <int TPR>
+__device__ __forceinline__ float rowgroup_sum(float x) {
+#pragma unroll
+    for (int msk = TPR; msk < 32; msk <<= 1) x += __shfl_xor(x, msk);
+    return TPR < 64 ? sum_halves(x) : x;
+}
+
+// Sums over the 64 lanes of N values at once (N a power of two, 4 <= N <= 32):
+// a reduce-scatter butterfly.  Each step pairs every lane with a lane whose
+// bit b differs; the lane with bit b clear keeps the lower half of its
+// values, the other the upper half, and each adds its partner's copy of the
+// half it keeps, so the values per lane halve.  Bits 5 and 4 pair lanes
+// with the half and row swaps (v_permlane32_swap, v_permlane16_swap), bits
+// 3, 2, 1 with DPP within rows of 16 (rotate by 8, half-row mirror, quad
+// permute); bits left after the values run out are summed plainly.  Lane l
+// ends with the total of value l >> (6 - log2 N) in x[0].
+// (both halves are summed with the partner and the kept one selected after
+// the sums, so that no array element is chosen by a run-time index)
+template <int CTRL, int N>
+__device__ __forceinline__ void bfly_dpp(float (&x)[N], int n, bool hi) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+        if (i < n / 2) {
+            const float lo = x[i] + dpp_row<CTRL>(x[i]);
+            const float up = x[i + n / 2] + dpp_row<CTRL>(x[i + n / 2]);
+            x[i] = hi ? up : lo;
+        }
+    }
+}
+template <int N>
+__device__ __forceinline__ void wave_reduce_scatter(float (&x)[N], int lane) {
+    static_assert(N >= 4 && N <= 32 && (N & (N - 1)) == 0, "4, 8, 16 or 32 values");
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {      // bit 5
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[i]), __float_as_uint(x[i + N / 2]), false, false);
+        x[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {      // bit 4
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[i]), __float_as_uint(x[i + N / 4]), false, false);
+        x[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    constexpr int n3 = N / 4, n2 = N / 8, n1 = N / 16;   // values entering the bit 3, 2, 1 steps
+    if constexpr (n3 >= 2) bfly_dpp<0x128, N>(x, n3, (lane >> 3) & 1);   // row_ror:8
+    else x[0] += dpp_row<0x128>(x[0]);
+    if constexpr (n2 >= 2) bfly_dpp<0x141, N>(x, n2, (lane >> 2) & 1);   // row_half_mirror
+    else x[0] += dpp_row<0x141>(x[0]);
+    if constexpr (n1 >= 2) bfly_dpp<0x4E, N>(x, n1, (lane >> 1) & 1);    // quad_perm [2, 3, 0, 1]
+    else x[0] += dpp_row<0x4E>(x[0]);
+    x[0] += dpp_row<0xB1>(x[0]);                                        // quad_perm [1, 0, 3, 2]
+}
+
+// the row owners' work for one state's tokens, into buffer P: per-row
+// factors, and per wave the partial pair sums over its row owners' channels
+template <int DK, int DV, typename TI, int M, int P>
+__device__ __forceinline__ void decodec_stage(const DecodeParams &p, int tid, const DecodeCTok<M, TI> &in,
+                                              DecodeCShared<DK, DV, M> &sm) {
+    using R = DecodeCRoles<DK, DV>;
+    using J = DecodeCJobs<M>;
+    const int wave = tid / 64, lane = tid % 64;
+    if (wave < R::W0 || wave > R::W1) return;   // uniform: no row owner in this wave
+    const int c = tid - DV;
+    const bool row = c >= 0 && c < DK;
+    float av[M], kv[M], qv[M];
+#pragma unroll
+    for (int t = 0; t < M; ++t) {
+        // lanes that own no row (column owners in small head shapes hold v
+        // here) take a = 1 and k = q = 0: their terms are exactly zero
+        const float x = io<TI>::ld(&in.r[t], 0);
+        av[t] = !row ? 1.f : (p.prologue & kProGate) ? sigmoid_f32(-x) : __expf(x);
+        kv[t] = row ? io<TI>::ld(&in.r[M + t], 0) : 0.f;
+        qv[t] = row ? io<TI>::ld(&in.r[2 * M + t], 0) : 0.f;
+    }
+    if (row) {
+        float g = 1.f;
+#pragma unroll
+        for (int t = 0; t < M; ++t) {
+            g *= av[t];
+            sm.a[P][t][c] = av[t];
+            sm.k[P][t][c] = kv[t];
+            sm.kt[P][t][c] = kv[t] * g;
+            sm.qt[P][t][c] = qv[t] * g;
+        }
+        sm.gm[P][c] = g;
+        float suf = 1.f;
+#pragma unroll
+        for (int t = M - 1; t >= 0; --t) {
+            sm.kh[P][t][c] = kv[t] * suf;
+            suf *= av[t];
+        }
+    }
+    // this channel's terms of the pair sums (zero outside the row owners),
+    // padded with zeros to a power of two
+    constexpr int NP = J::N <= 4 ? 4 : J::N <= 8 ? 8 : J::N <= 16 ? 16 : 32;
+    float term[NP];
+#pragma unroll
+    for (int jb = J::N; jb < NP; ++jb) term[jb] = 0.f;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        float w = 1.f;
+#pragma unroll
+        for (int t = i; t < M; ++t) {
+            if (t > i) {
+                w *= av[t];
+                term[J::kk(t, i)] = kv[t] * kv[i] * w;
+            }
+            term[J::qk(t, i)] = qv[t] * kv[i] * w;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < M; ++t) {
+        term[J::k2(t)] = kv[t] * kv[t];
+        term[J::q2(t)] = qv[t] * qv[t];
+    }
+    wave_reduce_scatter<NP>(term, lane);
+    constexpr int SH = NP == 4 ? 4 : NP == 8 ? 3 : NP == 16 ? 2 : 1;   // 6 - log2 NP
+    const int jb = lane >> SH;
+    if ((lane & ((1 << SH) - 1)) == 0 && jb < J::N) sm.pj[P][jb][wave - R::W0] = term[0];
+}
+
+template <int DK, int DV, typename TI, typename TO, int M, int PAR>
+__device__ __forceinline__ void decodec_update(const DecodeParams &p, int bh, int tid,
+                                               f32x4 (&sv)[DecodeShape<DK, DV>::RPT], const DecodeCTok<M, TI> &in,
+                                               DecodeCShared<DK, DV, M> &sm) {
+    using Sh = DecodeShape<DK, DV>;
+    using J = DecodeCJobs<M>;
+    using R = DecodeCRoles<DK, DV>;
+    const int c4 = tid % Sh::TPR, rg = tid / Sh::TPR, wave = tid / 64, lane = tid % 64;
+    // partial S0^T Ktil_t and S0^T Qtil_t over this thread's rows
+    const int r0 = rg * Sh::RPT;
+#pragma unroll
+    for (int t = 0; t < M; ++t) {
+        float kr[Sh::RPT], qr[Sh::RPT];
+        lds_rows<Sh::RPT>(&sm.kt[PAR][t][r0], kr);
+        lds_rows<Sh::RPT>(&sm.qt[PAR][t][r0], qr);
+        f32x4 x = sv[0] * kr[0], y = sv[0] * qr[0];
+#pragma unroll
+        for (int i = 1; i < Sh::RPT; ++i) {
+            x += sv[i] * kr[i];
+            y += sv[i] * qr[i];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[j] = rowgroup_sum<Sh::TPR>(x[j]);
+            y[j] = rowgroup_sum<Sh::TPR>(y[j]);
+        }
+        if (lane < Sh::TPR) {
+            *reinterpret_cast<f32x4 *>(&sm.red[0][t][wave][4 * c4]) = x;
+            *reinterpret_cast<f32x4 *>(&sm.red[1][t][wave][4 * c4]) = y;
+        }
+    }
+    lds_barrier();
+    const int64_t tok0 = static_cast<int64_t>(bh / p.H) * M * p.H + bh % p.H;
+    // column owners: Delta by forward substitution and the outputs, once per column
+    if (tid < DV) {
+        const int j = tid;
+        const bool norm = (p.prologue & kProQKNorm) != 0;
+        auto pair = [&](int jb) {
+            float s = sm.pj[PAR][jb][0];
+#pragma unroll
+            for (int u = 1; u < R::NPART; ++u) s += sm.pj[PAR][jb][u];
+            return s;
+        };
+        float nk[M], nq[M], x[M], y[M], dl[M];
+#pragma unroll
+        for (int t = 0; t < M; ++t) {
+            nk[t] = nq[t] = 1.f;
+            if (norm) {
+                nk[t] = 1.f / __builtin_sqrtf(pair(J::k2(t)) + kQKNormEps);
+                nq[t] = 1.f / __builtin_sqrtf(pair(J::q2(t)) + kQKNormEps);
+            }
+            x[t] = sm.red[0][t][0][j];
+            y[t] = sm.red[1][t][0][j];
+#pragma unroll
+            for (int w = 1; w < Sh::NW; ++w) {
+                x[t] += sm.red[0][t][w][j];
+                y[t] += sm.red[1][t][w][j];
+            }
+        }
+        TO *o = static_cast<TO *>(p.o);
+#pragma unroll
+        for (int t = 0; t < M; ++t) {
+            float bt = io<TI>::ld(&in.r[M + t], 0);
+            if (p.prologue & kProBeta) bt = sigmoid_f32(bt);
+            float d = bt * (io<TI>::ld(&in.r[t], 0) - nk[t] * x[t]);
+#pragma unroll
+            for (int i = 0; i < t; ++i) d -= (bt * nk[t] * nk[i] * pair(J::kk(t, i))) * dl[i];
+            dl[t] = d;
+            float ot = nq[t] * y[t];
+#pragma unroll
+            for (int i = 0; i <= t; ++i) ot += (nq[t] * nk[i] * pair(J::qk(t, i))) * dl[i];
+            io<TO>::st(o, (tok0 + static_cast<int64_t>(t) * p.H) * DV + j, ot);
+            sm.dl[t][j] = nk[t] * d;
+        }
+    }
+    // row owners meanwhile: the next state's factors and pair sums
+    decodec_stage<DK, DV, TI, M, PAR ^ 1>(p, tid, in, sm);
+    lds_barrier();
+    f32x4 dl[M];
+#pragma unroll
+    for (int t = 0; t < M; ++t) dl[t] = *reinterpret_cast<const f32x4 *>(&sm.dl[t][4 * c4]);
+    const uint32_t lo = static_cast<uint32_t>(r0 * DV + 4 * c4);
+    if (p.token_states) {   // token by token: S_{t+1} = a_t S_t + k_t (nk_t Delta_t)^T
+#pragma unroll
+        for (int t = 0; t < M; ++t) {
+            float *ts = p.token_states + (tok0 + static_cast<int64_t>(t) * p.H) * DK * DV;
+            float ar[Sh::RPT], kr[Sh::RPT];
+            lds_rows<Sh::RPT>(&sm.a[PAR][t][r0], ar);
+            lds_rows<Sh::RPT>(&sm.k[PAR][t][r0], kr);
+#pragma unroll
+            for (int i = 0; i < Sh::RPT; ++i) {
+                sv[i] = ar[i] * sv[i] + kr[i] * dl[t];
+                __builtin_nontemporal_store(sv[i], reinterpret_cast<f32x4 *>(ts + (lo + static_cast<uint32_t>(i * DV))));
+            }
+        }
+    } else {                // S_m = Gamma_{m-1} S0 + sum_t kh_t (nk_t Delta_t)^T
+        float gr[Sh::RPT];
+        lds_rows<Sh::RPT>(&sm.gm[PAR][r0], gr);
+#pragma unroll
+        for (int i = 0; i < Sh::RPT; ++i) sv[i] *= gr[i];
+#pragma unroll
+        for (int t = 0; t < M; ++t) {
+            float kr[Sh::RPT];
+            lds_rows<Sh::RPT>(&sm.kh[PAR][t][r0], kr);
+#pragma unroll
+            for (int i = 0; i < Sh::RPT; ++i) sv[i] += kr[i] * dl[t];
+        }
+    }
+    if (p.state_out) {
+        float *dst = p.state_out + static_cast<int64_t>(bh) * DK * DV;
+#pragma unroll
+        for (int i = 0; i < Sh::RPT; ++i)
+            __builtin_nontemporal_store(sv[i], reinterpret_cast<f32x4 *>(dst + (lo + static_cast<uint32_t>(i * DV))));
+    }
+}
+
+template <int DK, int DV, typename TI, typename TO, int M>
+__global__ void __launch_bounds__((DecodeShape<DK, DV>::NT)) decodec_kernel(DecodeParams p, int BH) {
+    using Sh = DecodeShape<DK, DV>;
+    static_assert(M >= 2 && DK + DV <= Sh::NT, "a column owner per column and a row owner per row");
+    __shared__ DecodeCShared<DK, DV, M> sm;
+    const int tid = threadIdx.x, G = gridDim.x;
+    f32x4 svA[Sh::RPT], svB[Sh::RPT];
+    DecodeCTok<M, TI> inA{}, inB{};
+    auto clamp = [&](int x) { return x < BH ? x : BH - 1; };
+    int bh = blockIdx.x;   // uniform: every wave takes the same branches
+    if (bh >= BH) return;
+    // the first state's tokens staged before the walk; afterwards every
+    // update stages the tokens of the state after it
+    decodec_request<DK, DV, M, TI>(p, bh, bh, bh, tid, svA, inA);
+    decodec_stage<DK, DV, TI, M, 0>(p, tid, inA, sm);
+    decodec_request<DK, DV, M, TI>(p, bh, bh, clamp(bh + G), tid, svA, inA);
+    lds_barrier();
+    for (;;) {
+        // inA: state bh, v and beta of bh, a, k, q of bh + G
+        const int bh1 = bh + G;
+        decodec_request<DK, DV, M, TI>(p, clamp(bh1), clamp(bh1), clamp(bh1 + G), tid, svB, inB);
+        decodec_update<DK, DV, TI, TO, M, 0>(p, bh, tid, svA, inA, sm);
+        if (bh1 >= BH) break;
+        const int bh2 = bh1 + G;
+        decodec_request<DK, DV, M, TI>(p, clamp(bh2), clamp(bh2), clamp(bh2 + G), tid, svA, inA);
+        decodec_update<DK, DV, TI, TO, M, 1>(p, bh1, tid, svB, inB, sm);
+        if (bh2 >= BH) break;
+        bh = bh2;
+    }
+}
+
 }  // namespace kda
 
 namespace kda {
@@ -589,6 +982,12 @@ hipError_t run_decode(const DecodeParams &p, int B, hipStream_t s) {
         const int BH = B * p.H;
         const int G = BH < kDecodeGrid ? BH : kDecodeGrid;
         hipLaunchKernelGGL((decode1_kernel<DK, DV, TI, TO>), dim3(G), block, 0, s, p, BH);
+    } else if (p.m >= 2 && p.m <= 4 && !p.token_states) {
+        const int BH = B * p.H;
+        const int G = BH < kDecodeGrid ? BH : kDecodeGrid;
+        if (p.m == 2) hipLaunchKernelGGL((decodec_kernel<DK, DV, TI, TO, 2>), dim3(G), block, 0, s, p, BH);
+        else if (p.m == 3) hipLaunchKernelGGL((decodec_kernel<DK, DV, TI, TO, 3>), dim3(G), block, 0, s, p, BH);
+        else hipLaunchKernelGGL((decodec_kernel<DK, DV, TI, TO, 4>), dim3(G), block, 0, s, p, BH);
     } else if (p.token_states && p.m <= DecodeMShape<DK, DV>::MT) {
         const int BH = B * p.H;
         const int G = BH < kDecodeGrid ? BH : kDecodeGrid;

@@ -66,6 +66,27 @@ def test_multi_token_states_persistent_walk_with_uneven_share(B, m, H, dk, dv):
     assert fin is S and torch.equal(ts[:, -1], fin)
 
 
+@pytest.mark.parametrize("m", [2, 3, 4])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("flags", [0, 7])
+def test_multi_token_state_only(m, dtype, flags):
+    """Launches without per-token states (the state updated in place), with
+    and without the fused prologue: every output and the final state against
+    the oracle.  150 x 4 = 600 states give the persistent workgroups an
+    uneven share."""
+    B, H = 150, 4
+    x = synth.make_preact(95 + m + flags, B, m, H, 128, 128, dtype, state_std=0.02, prologue=flags)
+    args = [torch.from_numpy(a).cuda().to(tdtype(dtype)) for a in (x.q, x.k, x.v, x.beta, x.log_alpha)]
+    S = torch.from_numpy(x.initial_state).cuda()
+    o, fin, ts = kda.decode(*args, S, prologue=flags)
+    o_ref, S_ref, _ = native.prefill(x.q, x.k, x.v, x.beta, x.log_alpha, initial_state=x.initial_state,
+                                     prologue_flags=flags)
+    e = dict(o=err(o, o_ref), S=err(S, S_ref))
+    report(f"state-only multi-token decode m={m} {dtype} prologue={flags}", **e)
+    assert max(e.values()) <= TOL[dtype]
+    assert fin is S and ts is None
+
+
 @pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 128), (128, 16)])
 def test_multi_token_head_sizes(dk, dv):
     tok, S0 = draw(80 + dk + dv, 3, 3, 2, dk, dv, "f32")
