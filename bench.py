@@ -89,8 +89,22 @@ SOURCE_GROUPS = {
 }
 SHARED_HEADERS = ["kda_common.hpp", "kda_prefill_common.hpp", "kda_launch.hpp"]
 # call key in profiles/traffic.json -> source group
-CALL_GROUPS = {"prefill_long": "prefill", "decode": "decode", "short_conv_prefill": "short_conv",
-               "short_conv_decode": "short_conv", "backward_T4096_H16": "backward"}
+CALL_GROUPS = {"prefill_long": "prefill", "decode": "decode", "decode_multi_m4": "decode",
+               "short_conv_prefill": "short_conv", "short_conv_decode": "short_conv",
+               "backward_T4096_H16": "backward"}
+# kernels of each call key, as rocprofv3 names them (without namespace, spaces and arguments)
+CALL_KERNELS = {
+    "prefill_long": ["intra_kernel<64,128>", "scan_kernel<64,128,float>", "chunk_table_kernel"],
+    "decode": ["decode1_kernel<128,128,unsignedshort,float>"],
+    "decode_multi_m4": ["decodec_kernel<128,128,unsignedshort,float,4>"],
+    "short_conv_prefill": ["short_conv_kernel<unsignedshort,unsignedshort,4,16>", "conv_state_kernel<unsignedshort,4>"],
+    "short_conv_decode": ["conv_rows_kernel<unsignedshort,unsignedshort,4>"],
+    "backward_T4096_H16": ["cb_prep_kernel<128,unsignedshort,false>", "cb_scan_kernel<128>",
+                           "cb_grad_kernel<128,unsignedshort>"],
+}
+# call keys whose kernels each `--leg` runs
+LEG_CALLS = {"prefill_long": ["prefill_long"], "decode": ["decode"], "decode_multi": ["decode_multi_m4"],
+             "backward": ["backward_T4096_H16"]}
 
 
 def kernel_sources_sha(group: str) -> str:
@@ -175,16 +189,8 @@ def record_traffic(fetch_dir, write_dir, sq_dir, cal_fetch_dir, cal_write_dir, m
 
     fetch_scale = COPY_CAL_KIB / mean(cal, "__amd_rocclr_copyBuffer", "FETCH_SIZE")
     write_scale = COPY_CAL_KIB / mean(cal, "__amd_rocclr_copyBuffer", "WRITE_SIZE")
-    groups = {
-        "prefill_long": [("intra_kernel<64,128>", calls), ("scan_kernel<64,128,float>", calls),
-                         ("chunk_table_kernel", calls)],
-        "decode": [("decode1_kernel<128,128,unsignedshort,float>", None)],
-        "short_conv_prefill": [("short_conv_kernel<unsignedshort,unsignedshort,4,16>", None),
-                               ("conv_state_kernel<unsignedshort,4>", None)],
-        "short_conv_decode": [("conv_rows_kernel<unsignedshort,unsignedshort,4>", None)],
-        "backward_T4096_H16": [("cb_prep_kernel<128,unsignedshort,false>", None), ("cb_scan_kernel<128>", None),
-                               ("cb_grad_kernel<128,unsignedshort>", None)],
-    }
+    groups = {key: [(k, calls if key == "prefill_long" else None) for k in ks]
+              for key, ks in CALL_KERNELS.items()}
     out_calls = {}
     for key, ks in groups.items():
         per = {k: [mean(acc, k, "FETCH_SIZE", n), mean(acc, k, "WRITE_SIZE", n)] for k, n in ks}
@@ -239,6 +245,34 @@ def record_prefill_traffic(fetch_dir, write_dir, sq_dir, mfma_dir, calls):
     v = rec["calls"]["prefill_long"]
     print(json.dumps({"prefill_long_gb": (v["fetch_kib"] * rec["fetch_scale"] + v["write_kib"] * rec["write_scale"])
                       * 1024 / 1e9}))
+
+
+def record_leg_traffic(leg, fetch_dir, write_dir):
+    """Refresh the entries of profiles/traffic.json for the calls that
+    `bench.py --leg LEG` runs, from a FETCH_SIZE and a WRITE_SIZE rocprofv3
+    --pmc run of that leg (every dispatch of the call's kernels averaged),
+    keeping the other entries and the copy calibration already recorded."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    rec = json.load(open(path))
+    acc = _counter_runs([fetch_dir, write_dir])
+
+    def mean(kernel, counter):
+        v = acc.get((kernel, counter))
+        if not v:
+            raise SystemExit(f"no {counter} dispatches of {kernel} in the counter runs")
+        return sum(v) / len(v)
+
+    res = {}
+    for key in LEG_CALLS[leg]:
+        per = {k: [mean(k, "FETCH_SIZE"), mean(k, "WRITE_SIZE")] for k in CALL_KERNELS[key]}
+        rec["calls"][key] = {"fetch_kib": sum(v[0] for v in per.values()),
+                             "write_kib": sum(v[1] for v in per.values()), "kernels": per}
+        rec["sources_sha"][CALL_GROUPS[key]] = kernel_sources_sha(CALL_GROUPS[key])
+        c = rec["calls"][key]
+        res[key + "_gb"] = (c["fetch_kib"] * rec["fetch_scale"] + c["write_kib"] * rec["write_scale"]) * 1024 / 1e9
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(res))
 
 
 # Vector-ALU issue peak of MI355X: 256 CUs x 4 SIMDs, one wave64 VALU
@@ -581,6 +615,25 @@ def run_leg(kda, args, dev):
         print(json.dumps({"leg": "decode", "workload": "decode_B256_H32_d128", "ms": st,
                           "value": 256 / (st["median"] * 1e-3), "unit": "seq-steps/s"}), flush=True)
         return
+    if args.leg == "decode_multi":   # 4 tokens per sequence per launch, no per-token states
+        gg = _gen(3, dev)
+        D = [t.to(torch.bfloat16) for t in _draw_tokens(gg, 64, 256, 32, 128, 128, 0.0, dev, True)]
+        state = _state(gg, (256, 32, 128, 128), 0.02, dev)
+        mt = [x[:4].transpose(0, 1).contiguous() for x in D]
+        om = torch.empty((256, 4, 32, 128), dtype=torch.float32, device=dev)
+        evs = []
+        for i in range(args.warmup + args.steps):
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record()
+            kda.decode(*mt, state, o=om)
+            b_.record()
+            evs.append((a_, b_))
+        torch.cuda.synchronize()
+        st = stats([a_.elapsed_time(b_) for a_, b_ in evs[args.warmup:]])
+        print(json.dumps({"leg": "decode_multi", "workload": "decode_B256_H32_d128, 4 tokens per launch",
+                          "ms": st, "value": 256 * 4 / (st["median"] * 1e-3), "unit": "seq-token-steps/s"}),
+              flush=True)
+        return
     import synth
     BX = synth.workload(2, device=dev)
     bt = lambda a: torch.from_numpy(a).to(dev, torch.bfloat16)  # noqa: E731
@@ -612,7 +665,11 @@ def main():
     ap.add_argument("--record-prefill-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "SQ_DIR", "MFMA_DIR"),
                     help="refresh the long-prefill entry of profiles/traffic.json from rocprofv3 --pmc runs of "
                          "`bench.py --leg prefill_long --steps S --warmup W` (give the same --steps/--warmup)")
-    ap.add_argument("--leg", choices=["prefill_long", "prefill_c2", "prefill_c4", "decode", "backward"],
+    ap.add_argument("--record-leg-traffic", nargs=3, metavar=("LEG", "FETCH_DIR", "WRITE_DIR"),
+                    help="refresh the traffic.json entries of one --leg's calls from a FETCH_SIZE and a "
+                         "WRITE_SIZE rocprofv3 --pmc run of that leg")
+    ap.add_argument("--leg", choices=["prefill_long", "prefill_c2", "prefill_c4", "decode", "decode_multi",
+                                      "backward"],
                     help="run only this workload's calls (warmup + steps), for a per-workload profile")
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -630,6 +687,9 @@ def main():
         return
     if args.record_prefill_traffic:
         record_prefill_traffic(*args.record_prefill_traffic, calls=args.warmup + args.steps)
+        return
+    if args.record_leg_traffic:
+        record_leg_traffic(*args.record_leg_traffic)
         return
     if args.copy_calibration:
         copy_calibration()
@@ -777,7 +837,9 @@ def main():
             "value": Bd * M_TOK / (ms * 1e-3), "unit": "seq-token-steps/s", "avg_ms": ms,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "frac_of_torch_copy": None, "algorithmic_bytes": nbytes,
-                         "kernel": "decodem_kernel (m = 4, persistent)" if with_states else "decode_kernel (m = 4)"}}
+                         "traffic": None if with_states else measured_traffic("decode_multi_m4"),
+                         "kernel": ("decodem_kernel (m = 4, persistent)" if with_states
+                                    else "decodec_kernel (m = 4 as one chunk, persistent)")}}
     del tsb, om, mt
 
     # Short causal convolution (width 4) over a q-shaped input of the prefill
