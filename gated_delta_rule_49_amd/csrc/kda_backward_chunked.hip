@@ -464,6 +464,26 @@ __global__ void __launch_bounds__(256) cb_scan_kernel(CbParams p) {
         t0 = static_cast<int64_t>(static_cast<uint32_t>(ci.x)) | (static_cast<int64_t>(ci.y) << 32);
         L = ci.z;
     };
+    // L2 warm-up (as in the forward scan): while chunk ch is computed, the
+    // column tiles of the head together touch every 128-byte line of the
+    // block regions this scan reads (Q~, K^ and W, which are contiguous, P^T
+    // and e^{G_L}) of chunk ch - kWarmAhead, one line per thread, so the
+    // next chunk's operand loads find them in L2; the loaded word is only
+    // consumed (without instructions) a chunk later.  Threads without a
+    // line repeat the first one, so the load needs no branch.
+    constexpr int kWarmAhead = 2;
+    constexpr int kLinesA = 3 * C * DK * 4 / 128, kLinesB = C * C * 4 / 128, kLinesC = (DK * 4 + 127) / 128;
+    static_assert(Y::KB == Y::QT + C * DK && Y::W == Y::KB + C * DK, "Q~, K^, W contiguous");
+    const int wl = vt + nvt * tid;
+    const int woff = wl < kLinesA ? static_cast<int>(Y::QT) + 32 * wl
+                   : wl < kLinesA + kLinesB ? static_cast<int>(Y::PT) + 32 * (wl - kLinesA)
+                   : wl < kLinesA + kLinesB + kLinesC ? static_cast<int>(Y::GAM) + 32 * (wl - kLinesA - kLinesB)
+                   : static_cast<int>(Y::QT);
+    uint32_t warm = 0;
+    auto warm_up = [&](int ch) {
+        asm volatile("" ::"v"(warm));
+        warm = *reinterpret_cast<const uint32_t *>(blk_of(ch > kWarmAhead ? ch - kWarmAhead : 0) + woff);
+    };
     Ops op;
     {
         int64_t t0; int L;
@@ -475,6 +495,7 @@ __global__ void __launch_bounds__(256) cb_scan_kernel(CbParams p) {
     for (int ch = nch - 1; ch >= 0; --ch) {
         const int64_t x = cbase + ch;
         const int nx = ch > 0 ? ch - 1 : 0;   // the chunk whose operands are loaded next
+        warm_up(ch);
         lds_barrier();  // the previous chunk's readers of doT, dsT are done
         // dO and dS' -> LDS; dS' is also recorded for the gradient kernel
 #pragma unroll
@@ -523,6 +544,7 @@ __global__ void __launch_bounds__(256) cb_scan_kernel(CbParams p) {
         }
         op.load_s(blk_of(nx), w, g, n);
     }
+    asm volatile("" ::"v"(warm));
     if (p.d_initial)
 #pragma unroll
         for (int i = 0; i < KPW; ++i) {
