@@ -648,9 +648,9 @@ struct DecodeCTok {
 // the state whose v and beta the column owners take, bh_row the state whose
 // a, k, q the row owners take.  Every load is unconditional (indices
 // clamped) so that the wait counts leave the request in flight.
-template <int DK, int DV, int M, typename TI>
-__device__ __forceinline__ void decodec_request(const DecodeParams &p, int bh, int bh_col, int bh_row, int tid,
-                                                f32x4 (&sv)[DecodeShape<DK, DV>::RPT], DecodeCTok<M, TI> &in) {
+template <int DK, int DV>
+__device__ __forceinline__ void decodec_request_state(const DecodeParams &p, int bh, int tid,
+                                                      f32x4 (&sv)[DecodeShape<DK, DV>::RPT]) {
     using Sh = DecodeShape<DK, DV>;
     const int c4 = tid % Sh::TPR, rg = tid / Sh::TPR;
     const float *src = p.state_in + static_cast<int64_t>(bh) * DK * DV;
@@ -658,6 +658,10 @@ __device__ __forceinline__ void decodec_request(const DecodeParams &p, int bh, i
 #pragma unroll
     for (int i = 0; i < Sh::RPT; ++i)
         sv[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(src + (lo + static_cast<uint32_t>(i * DV))));
+}
+template <int DK, int DV, int M, typename TI>
+__device__ __forceinline__ void decodec_request_tokens(const DecodeParams &p, int bh_col, int bh_row, int tid,
+                                                       DecodeCTok<M, TI> &in) {
     // rows [B, m, H] of token 0 of the two states
     const int64_t tc = static_cast<int64_t>(bh_col / p.H) * M * p.H + bh_col % p.H;
     const int64_t tr = static_cast<int64_t>(bh_row / p.H) * M * p.H + bh_row % p.H;
@@ -673,6 +677,12 @@ __device__ __forceinline__ void decodec_request(const DecodeParams &p, int bh, i
         in.r[M + t] = col ? be[rc] : k[rr * DK + c];
         in.r[2 * M + t] = col ? be[rc] : q[rr * DK + c];
     }
+}
+template <int DK, int DV, int M, typename TI>
+__device__ __forceinline__ void decodec_request(const DecodeParams &p, int bh, int bh_col, int bh_row, int tid,
+                                                f32x4 (&sv)[DecodeShape<DK, DV>::RPT], DecodeCTok<M, TI> &in) {
+    decodec_request_state<DK, DV>(p, bh, tid, sv);
+    decodec_request_tokens<DK, DV, M, TI>(p, bh_col, bh_row, tid, in);
 }
 
 // this thread's RPT consecutive entries of a per-row LDS vector
@@ -953,7 +963,7 @@ __global__ void __launch_bounds__((DecodeShape<DK, DV>::NT)) decodec_kernel(Deco
     // update stages the tokens of the state after it
     decodec_request<DK, DV, M, TI>(p, bh, bh, bh, tid, svA, inA);
     decodec_stage<DK, DV, TI, M, 0>(p, tid, inA, sm);
-    decodec_request<DK, DV, M, TI>(p, bh, bh, clamp(bh + G), tid, svA, inA);
+    decodec_request_tokens<DK, DV, M, TI>(p, bh, clamp(bh + G), tid, inA);
     lds_barrier();
     for (;;) {
         // inA: state bh, v and beta of bh, a, k, q of bh + G
