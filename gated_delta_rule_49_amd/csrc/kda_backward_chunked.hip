@@ -61,18 +61,39 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
     constexpr bool kExact = sizeof(TI) == 4;
     using GT = typename std::conditional<kExact, double, float>::type;
     auto ex = [](GT x) { return kExact ? expf(static_cast<float>(x)) : __expf(static_cast<float>(x)); };
-    __shared__ float sq[CB_C][DK + 1], sk[CB_C][DK + 1];
+    // q and k staged in LDS: the backward's bf16 inputs as their raw bits
+    // (exact; nothing rescales them), otherwise fp32.  A = Diag(beta) Gh
+    // shares q's storage: it is written once the Gram products have read q.
+    // With bf16 q, k the block's LDS is 66.6 KB, so two workgroups fit per CU.
+    constexpr bool kRaw = sizeof(TI) == 2 && !FWD;
+    using QKT = typename std::conditional<kRaw, bf16_t, float>::type;
+    constexpr int QKS = kRaw ? DK + 2 : DK + 1;   // row stride, in elements
+    constexpr int QBYTES = CB_C * QKS * static_cast<int>(sizeof(QKT)), ABYTES = CB_C * (CB_C + 1) * 4;
+    __shared__ __attribute__((aligned(16))) char sqa[QBYTES > ABYTES ? QBYTES : ABYTES];
+    __shared__ QKT sk[CB_C][QKS];
     __shared__ GT sG[CB_C][DK + 1];
-    __shared__ float sA[CB_C][CB_C + 1];
     __shared__ float sb[CB_C];
+    QKT (*sq)[QKS] = reinterpret_cast<QKT (*)[QKS]>(sqa);
+    float (*sA)[CB_C + 1] = reinterpret_cast<float (*)[CB_C + 1]>(sqa);
+    auto ldq = [&](int r, int c) -> float {
+        if constexpr (kRaw) return bf16_to_f32(sq[r][c]); else return sq[r][c];
+    };
+    auto ldk = [&](int r, int c) -> float {
+        if constexpr (kRaw) return bf16_to_f32(sk[r][c]); else return sk[r][c];
+    };
 
     // Prologue (forward only; the arguments hold pre-activations): log alpha
     // = -softplus(x), beta = sigmoid(x), q and k divided by their L2 norms
     // over d_k; in fp32, with the correctly rounded functions for fp32 inputs.
     const uint32_t pro = FWD ? p.prologue : 0u;
     auto stage = [&](int r, int c, float qv, float kv, float x, bool live) {
-        sq[r][c] = qv;
-        sk[r][c] = kv;
+        if constexpr (kRaw) {
+            sq[r][c] = f32_to_bf16(qv);   // qv, kv came from bf16: exact
+            sk[r][c] = f32_to_bf16(kv);
+        } else {
+            sq[r][c] = qv;
+            sk[r][c] = kv;
+        }
         if (pro & kProGate)
             x = !live ? 0.f : kExact ? -(fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)))) : -softplus_f32(x);
         sG[r][c] = x;
@@ -126,7 +147,7 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
         sb[tid] = b;
     }
     __syncthreads();
-    if (pro & kProQKNorm) {  // rows of q and k to unit L2 norm (eps as in the other kernels)
+    if constexpr (!kRaw) if (pro & kProQKNorm) {  // rows of q and k to unit L2 norm (eps as in the other kernels)
         __shared__ float s_inv[2][CB_C];
         if (tid < 2 * CB_C) {
             const int r = tid % CB_C;
@@ -163,9 +184,9 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
             const GT G = sG[r][c0 + j];
             const float E = ex(G);
             gv[j] = static_cast<float>(G);
-            kt[j] = sk[r][c0 + j] * E;
-            qt[j] = sq[r][c0 + j] * E;
-            kb[j] = sk[r][c0 + j] * ex(sG[CB_C - 1][c0 + j] - G);
+            kt[j] = ldk(r, c0 + j) * E;
+            qt[j] = ldq(r, c0 + j) * E;
+            kb[j] = ldk(r, c0 + j) * ex(sG[CB_C - 1][c0 + j] - G);
         }
         if (!FWD) *reinterpret_cast<f32x4 *>(blk + Y::G + e) = gv;
         *reinterpret_cast<f32x4 *>(blk + Y::KT + e) = kt;
@@ -188,7 +209,12 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
     {
         const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int g = lane >> 4, n = lane & 15;
-        auto emit = [&](int R, int I, const f32x4 &gh, const f32x4 &pp) {
+        // A's values stay in registers until every wave is done with q
+        f32x4 av[3];
+        int aR[3], aI[3];
+        auto emit = [&](int t, int R, int I, const f32x4 &gh, const f32x4 &pp) {
+            aR[t] = R;
+            aI[t] = I;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int r = 16 * R + 4 * g + u, i = 16 * I + n;
@@ -199,9 +225,11 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
                     blk[Y::GH + r * CB_C + i] = ghv;
                     blk[Y::PT + i * CB_C + r] = pv;
                 }
-                sA[r][i] = ghv * sb[r];
+                av[t][u] = ghv * sb[r];
             }
         };
+#pragma unroll
+        for (int t = 0; t < 3; ++t) aR[t] = -1;
         for (int t = 0; t < 3; ++t) {
             int R, I;
             if (t == 0) {
@@ -221,11 +249,11 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
                     for (int s2 = 0; s2 < 4; ++s2) {
                         const int c = c0 + 4 * g + s2;
                         const float fr = ex(sG[r][c] - sG[m][c]), fc = ex(sG[m][c] - sG[i][c]);
-                        const float bk = sk[i][c] * fc;
-                        gh = __builtin_amdgcn_mfma_f32_16x16x4f32(sk[r][c] * fr, bk, gh, 0, 0, 0);
-                        pp = __builtin_amdgcn_mfma_f32_16x16x4f32(sq[r][c] * fr, bk, pp, 0, 0, 0);
+                        const float bk = ldk(i, c) * fc;
+                        gh = __builtin_amdgcn_mfma_f32_16x16x4f32(ldk(r, c) * fr, bk, gh, 0, 0, 0);
+                        pp = __builtin_amdgcn_mfma_f32_16x16x4f32(ldq(r, c) * fr, bk, pp, 0, 0, 0);
                     }
-                emit(R, I, gh, pp);
+                emit(t, R, I, gh, pp);
                 continue;
             }
             // diagonal block: the steepest channel decides the method
@@ -241,26 +269,33 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
                         const int c = c0 + 4 * g + s2;
                         const GT mid = GT(0.5) * ((R > 0 ? sG[16 * R - 1][c] : GT(0)) + sG[16 * R + 15][c]);
                         const float fr = ex(sG[r][c] - mid), fc = ex(mid - sG[r][c]);
-                        const float bk = sk[r][c] * fc;   // columns are the same 16 tokens
-                        gh = __builtin_amdgcn_mfma_f32_16x16x4f32(sk[r][c] * fr, bk, gh, 0, 0, 0);
-                        pp = __builtin_amdgcn_mfma_f32_16x16x4f32(sq[r][c] * fr, bk, pp, 0, 0, 0);
+                        const float bk = ldk(r, c) * fc;   // columns are the same 16 tokens
+                        gh = __builtin_amdgcn_mfma_f32_16x16x4f32(ldk(r, c) * fr, bk, gh, 0, 0, 0);
+                        pp = __builtin_amdgcn_mfma_f32_16x16x4f32(ldq(r, c) * fr, bk, pp, 0, 0, 0);
                     }
             } else {
                 // lane holds the pairs (16R + 4g + u, 16R + n) of the accumulator layout
                 for (int c = 0; c < DK; ++c) {
                     const GT gi = sG[i][c];
-                    const float ki = sk[i][c];
+                    const float ki = ldk(i, c);
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const int ru = 16 * R + 4 * g + u;
                         const GT d = sG[ru][c] - gi;
                         const float f = ki * ex(d < GT(0) ? d : GT(0));
-                        gh[u] += sk[ru][c] * f;
-                        pp[u] += sq[ru][c] * f;
+                        gh[u] += ldk(ru, c) * f;
+                        pp[u] += ldq(ru, c) * f;
                     }
                 }
             }
-            emit(R, I, gh, pp);
+            emit(t, R, I, gh, pp);
+        }
+        __syncthreads();   // q is dead: A takes its storage
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            if (aR[t] < 0) continue;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sA[16 * aR[t] + 4 * g + u][16 * aI[t] + n] = av[t][u];
         }
     }
     // blocks above the diagonal are zero
@@ -302,11 +337,6 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
         for (int e = tid; e < CB_C * CB_C; e += 256) blk[Y::M + e] = sA[e / CB_C][e % CB_C];
         return;
     }
-    // K~ in place of k (k itself is no longer needed)
-    for (int e = tid; e < CB_C * DK; e += 256) {
-        const int r = e / DK, c = e % DK;
-        sk[r][c] *= ex(sG[r][c]);
-    }
     __syncthreads();
     for (int e = tid; e < CB_C * CB_C; e += 256) {
         blk[Y::M + e] = sA[e / CB_C][e % CB_C];
@@ -329,8 +359,9 @@ __global__ void __launch_bounds__(256) cb_prep_kernel(CbParams p) {
 #pragma unroll
                 for (int s2 = 0; s2 < 4; ++s2) {
                     const int i = 16 * ib + 4 * g + s2;
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[16 * rb + n][i] * sb[i], sk[i][16 * cb + n], acc, 0,
-                                                               0, 0);
+                    const int c = 16 * cb + n;   // K~ = k e^G formed here
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[16 * rb + n][i] * sb[i],
+                                                               ldk(i, c) * ex(sG[i][c]), acc, 0, 0, 0);
                 }
 #pragma unroll
             for (int u = 0; u < 4; ++u) blk[Y::W + (16 * rb + 4 * g + u) * DK + 16 * cb + n] = acc[u];
