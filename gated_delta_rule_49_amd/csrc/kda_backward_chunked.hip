@@ -723,32 +723,51 @@ __global__ void __launch_bounds__(CB_GRAD_NT) cb_grad_kernel(CbParams p) {
     for (int t = 0; t < NCW; ++t) aQ[t] = aK[t] = aB[t] = z4;
     aP[0] = aP[1] = aT[0] = aT[1] = z4;
 
+    // A tile's S, dS' and dO vectors (thread e: row e / (BV/4), columns
+    // 4 (e % (BV/4)) ..) and the V values of waves 0-3 are loaded into
+    // registers one tile ahead, unconditionally (rows clamped, surplus values
+    // unused); the walk's barriers are LDS-only, so these loads and the dv
+    // stores stay in flight across them.
+    static_assert(DK * BV / 4 <= NT && C * BV / 4 <= NT, "one vector per thread and tile");
+    const int er = tid / (BV / 4), ejq = 4 * (tid % (BV / 4));
+    const bool has_s = tid < DK * BV / 4, has_o = tid < C * BV / 4;
+    float4 nsv, nrv, nov;
+    float nvv[4];
+    auto load_tile = [&](int j0) {
+        const int c = has_s ? er : 0;
+        nsv = ld4(S + static_cast<int64_t>(c) * dv + j0 + ejq);
+        nrv = ld4(dSr + static_cast<int64_t>(c) * dv + j0 + ejq);
+        nov = ld4(p.d_o + ((t0 + min(er, L - 1)) * H + h) * dv + j0 + ejq);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            nvv[u] = io<TI>::ld(v, ((t0 + min(R * 16 + 4 * g + u, L - 1)) * H + h) * dv + j0 + n);
+    };
+    load_tile(0);
     for (int j0 = 0; j0 < dv; j0 += BV) {
-        __syncthreads();  // the previous tile's readers are done
-        for (int e = tid; e < DK * BV / 4; e += NT) {
-            const int c = e / (BV / 4), jq = 4 * (e % (BV / 4));
-            const float4 sv = ld4(S + static_cast<int64_t>(c) * dv + j0 + jq);
-            const float4 rv = ld4(dSr + static_cast<int64_t>(c) * dv + j0 + jq);
+        lds_barrier();  // the previous tile's readers are done
+        if (has_s) {
+            const int c = er, jq = ejq;
+            const float4 sv = nsv, rv = nrv;
             *reinterpret_cast<float4 *>(tSr + c * LB + jq) = sv;
             *reinterpret_cast<float4 *>(tRr + c * LB + jq) = rv;
             tSc[jq * LK + c] = sv.x; tSc[(jq + 1) * LK + c] = sv.y; tSc[(jq + 2) * LK + c] = sv.z; tSc[(jq + 3) * LK + c] = sv.w;
             tRc[jq * LK + c] = rv.x; tRc[(jq + 1) * LK + c] = rv.y; tRc[(jq + 2) * LK + c] = rv.z; tRc[(jq + 3) * LK + c] = rv.w;
         }
-        for (int e = tid; e < C * BV / 4; e += NT) {
-            const int r = e / (BV / 4), jq = 4 * (e % (BV / 4));
-            float4 ov = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (r < L) ov = ld4(p.d_o + ((t0 + r) * H + h) * dv + j0 + jq);
+        if (has_o) {
+            const int r = er, jq = ejq;
+            const float4 ov = r < L ? nov : make_float4(0.f, 0.f, 0.f, 0.f);
             *reinterpret_cast<float4 *>(tOr + r * LB + jq) = ov;
             tOc[jq * LC + r] = ov.x; tOc[(jq + 1) * LC + r] = ov.y; tOc[(jq + 2) * LC + r] = ov.z; tOc[(jq + 3) * LC + r] = ov.w;
         }
-        __syncthreads();
+        float vv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) vv[u] = R * 16 + 4 * g + u < L ? nvv[u] : 0.f;
+        load_tile(j0 + BV < dv ? j0 + BV : j0);
+        lds_barrier();
         if (half == 0) {  // X = V - K~ S
             f32x4 acc;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int r = R * 16 + 4 * g + u;
-                acc[u] = r < L ? io<TI>::ld(v, ((t0 + r) * H + h) * dv + j0 + n) : 0.f;
-            }
+            for (int u = 0; u < 4; ++u) acc[u] = vv[u];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
                 acc = mfma4(fa[4 * kb], fa[4 * kb + 1], fa[4 * kb + 2], fa[4 * kb + 3], ld4(tSc + n * LK + kb * 16 + 4 * g), acc);
@@ -768,7 +787,7 @@ __global__ void __launch_bounds__(CB_GRAD_NT) cb_grad_kernel(CbParams p) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) tEr[(R * 16 + 4 * g + u) * LB + n] = acc[u];
         }
-        __syncthreads();
+        lds_barrier();
         if (half == 0) {  // Delta = M Diag(beta) X
             f32x4 acc = z4;
 #pragma unroll
@@ -790,7 +809,7 @@ __global__ void __launch_bounds__(CB_GRAD_NT) cb_grad_kernel(CbParams p) {
                 if (r < L) p.gv[((t0 + r) * H + h) * dv + j0 + n] = acc[u];
             }
         }
-        __syncthreads();
+        lds_barrier();
         {   // the products over this tile's 16 columns
             const float4 aO = ld4(tOr + (R * 16 + n) * LB + 4 * g);
             const float4 aF = ld4(tFr + (R * 16 + n) * LB + 4 * g);
@@ -823,7 +842,26 @@ __global__ void __launch_bounds__(CB_GRAD_NT) cb_grad_kernel(CbParams p) {
             aG[c] += g_;
         }
     }
-    __syncthreads();  // the tiles are dead
+    // G, k and q of the chunk for the pair sums, requested now (the walk's
+    // fixed operands are dead) as 16-byte vectors, staged in LDS once Z is
+    // formed, so the transfers overlap the dT / M staging and the Z products
+    constexpr int NG4 = (C * DK / 4 + NT - 1) / NT, NQ8 = (C * DK / 8 + NT - 1) / NT;
+    typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+    const bool kq_vec = ((reinterpret_cast<uintptr_t>(p.k) | reinterpret_cast<uintptr_t>(p.q)) & 15) == 0;
+    float4 gpre[NG4];
+    u32x4 kpre[NQ8], qpre[NQ8];
+#pragma unroll
+    for (int i = 0; i < NG4; ++i) gpre[i] = ld4(blk + Y::G + 4 * min(tid + NT * i, C * DK / 4 - 1));
+    if (kq_vec) {
+#pragma unroll
+        for (int i = 0; i < NQ8; ++i) {
+            const int e = 8 * min(tid + NT * i, C * DK / 8 - 1), r = e / DK, c0 = e % DK;
+            const int64_t off = ((t0 + min(r, L - 1)) * H + h) * DK + c0;
+            kpre[i] = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p.k) + off);
+            qpre[i] = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p.q) + off);
+        }
+    }
+    lds_barrier();  // the tiles are dead
     float *sGc = lds + Q::GC;
     uint16_t *sk16 = reinterpret_cast<uint16_t *>(sGc + C * DK), *sq16 = sk16 + C * DK;
     float *sT = lds + Q::TA, *Z = lds + Q::ZZ, *sDB = lds + Q::DB, *sM = lds + Q::MM, *sMT = lds + Q::MTT;
@@ -848,7 +886,7 @@ __global__ void __launch_bounds__(CB_GRAD_NT) cb_grad_kernel(CbParams p) {
         *reinterpret_cast<float4 *>(sMT + r * LM + a4) = ld4(blk + Y::MT + r * C + a4);
     }
     for (int e = tid; e < C; e += NT) sB[e] = blk[Y::BETA + e];
-    __syncthreads();
+    lds_barrier();
     // T = M Diag(beta): dM = dT Diag(beta), dbeta_i = (M^T dT)_ii;
     // M = (I + A)^-1: dA = -(M^T dM M^T) on the strict lower triangle;
     // A = Diag(beta) Gh: dbeta_r += sum_i dA_ri Gh_ri, dGh = Diag(beta) dA.
@@ -873,14 +911,27 @@ __global__ void __launch_bounds__(CB_GRAD_NT) cb_grad_kernel(CbParams p) {
         }
     }
     // stage the decays and the raw q, k (bf16) for the pair sums
-    for (int e = tid; e < C * DK; e += NT) {
-        const int r = e / DK, c = e % DK;
-        const int64_t off = ((t0 + r) * H + h) * DK + c;
-        sGc[e] = blk[Y::G + e];
-        sk16[e] = r < L ? static_cast<const uint16_t *>(p.k)[off] : 0;
-        sq16[e] = r < L ? static_cast<const uint16_t *>(p.q)[off] : 0;
+#pragma unroll
+    for (int i = 0; i < NG4; ++i)
+        if (tid + NT * i < C * DK / 4) *reinterpret_cast<float4 *>(sGc + 4 * (tid + NT * i)) = gpre[i];
+    if (kq_vec) {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < NQ8; ++i) {
+            if (tid + NT * i >= C * DK / 8) continue;
+            const int e = 8 * (tid + NT * i), r = e / DK;
+            *reinterpret_cast<u32x4 *>(sk16 + e) = r < L ? kpre[i] : zero;
+            *reinterpret_cast<u32x4 *>(sq16 + e) = r < L ? qpre[i] : zero;
+        }
+    } else {
+        for (int e = tid; e < C * DK; e += NT) {
+            const int r = e / DK, c = e % DK;
+            const int64_t off = ((t0 + r) * H + h) * DK + c;
+            sk16[e] = r < L ? static_cast<const uint16_t *>(p.k)[off] : 0;
+            sq16[e] = r < L ? static_cast<const uint16_t *>(p.q)[off] : 0;
+        }
     }
-    __syncthreads();
+    lds_barrier();
     // dA = -Z M^T, blocks (R, ib <= R), M lower: a up to block ib; strict
     // lower triangle only.  dGh = Diag(beta) dA replaces dT.
     float *sDA = sT;
@@ -905,7 +956,7 @@ __global__ void __launch_bounds__(CB_GRAD_NT) cb_grad_kernel(CbParams p) {
             sDA[r * LA + i] = dA * sB[r];
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < L) p.gbeta[(t0 + tid) * H + h] = sDB[tid];
     // pair sums over the decay factors, per (row r, channel c):
     //   rowA = sum_{i<r} dGh_ri k_i e^{G_r-G_i}    rowP = sum_{i<r} dP_ri k_i e^{G_r-G_i}
@@ -1017,7 +1068,7 @@ __global__ void __launch_bounds__(CB_GRAD_NT) cb_grad_kernel(CbParams p) {
             }
         }
     }
-    __syncthreads();  // the staged decays and inputs are dead
+    lds_barrier();  // the staged decays and inputs are dead
     float *sKK = lds + Q::GC;
 #pragma unroll
     for (int t = 0; t < NCW; ++t) {
@@ -1026,7 +1077,7 @@ __global__ void __launch_bounds__(CB_GRAD_NT) cb_grad_kernel(CbParams p) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) sKK[(R * 16 + 4 * g + u) * DK + cb * 16 + n] = vKK[t][u];
     }
-    __syncthreads();
+    lds_barrier();
     // dg: reverse cumsum of dG (in place), then the forward exclusive sum of
     // dK^ K^ and dgamma gamma on every token
     for (int c = tid; c < DK; c += NT) {

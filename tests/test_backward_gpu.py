@@ -140,3 +140,30 @@ def test_bf16_strong_decay(gate_mean):
     x = synth.make_uniform(470 + int(gate_mean), 1, 200, 2, 128, 128, "bf16", chunk=64, state_std=0.3,
                            gate_mean=gate_mean)
     check(x, f"bf16 chunked strong decay {gate_mean}")
+
+
+def test_bf16_unaligned_inputs_match_aligned():
+    """q, k, v, beta and log alpha passed to the backward as views that start
+    one element into their allocation (2-byte aligned, not 16-byte aligned):
+    the chunk prep and gradient kernels take their scalar staging paths and
+    must give the same gradients, bit for bit, as with aligned tensors."""
+    x = synth.make_uniform(480, 1, 130, 2, 128, 128, "bf16", chunk=64, state_std=0.05)
+    q, k, v, b, la, init, cu = dev_tensors(x)
+    d_o = torch.from_numpy(np.random.default_rng(7).standard_normal((x.B, x.T, x.H, x.d_v)).astype(np.float32)).cuda()
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        view = buf[1:].view(t.shape)
+        view.copy_(t)
+        assert view.data_ptr() % 16 != 0
+        return view
+
+    # the chunk-entry states from the prefill on the aligned inputs (the
+    # prefill's matrix-core path takes 16-byte aligned inputs only)
+    _, _, ck = kda.prefill(q, k, v, b, la, initial_state=init, output_final_state=False, chunk_size=64,
+                           chunk_states=True)
+    ref = kda.backward(q, k, v, b, la, d_o, initial_state=init, checkpoints=ck, chunk_size=64)
+    got = kda.backward(*(shifted(t) for t in (q, k, v, b, la)), d_o, initial_state=init, checkpoints=ck,
+                       chunk_size=64)
+    for n, a, c in zip(NAMES, ref, got):
+        assert torch.equal(a, c), n
