@@ -691,6 +691,27 @@ __global__ void __launch_bounds__(CB_GRAD_NT) cb_grad_kernel(CbParams p) {
     float *tOc = lds + Q::OC, *tXc = lds + Q::XC, *tEc = lds + Q::EC;
     float *aG = lds + Q::AG, *sB = lds + Q::SB, *sPD = lds + Q::PD;
 
+    // A tile's S, dS' and dO vectors (thread e: row e / (BV/4), columns
+    // 4 (e % (BV/4)) ..) and the V values of waves 0-3 are loaded into
+    // registers one tile ahead, unconditionally (rows clamped, surplus values
+    // unused); the walk's barriers are LDS-only, so these loads and the dv
+    // stores stay in flight across them.
+    static_assert(DK * BV / 4 <= NT && C * BV / 4 <= NT, "one vector per thread and tile");
+    const int er = tid / (BV / 4), ejq = 4 * (tid % (BV / 4));
+    const bool has_s = tid < DK * BV / 4, has_o = tid < C * BV / 4;
+    float4 nsv, nrv, nov;
+    float nvv[4];
+    auto load_tile = [&](int j0) {
+        const int c = has_s ? er : 0;
+        nsv = ld4(S + static_cast<int64_t>(c) * dv + j0 + ejq);
+        nrv = ld4(dSr + static_cast<int64_t>(c) * dv + j0 + ejq);
+        nov = ld4(p.d_o + ((t0 + min(er, L - 1)) * H + h) * dv + j0 + ejq);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            nvv[u] = io<TI>::ld(v, ((t0 + min(R * 16 + 4 * g + u, L - 1)) * H + h) * dv + j0 + n);
+    };
+    load_tile(0);   // in flight with the fixed operands' loads below
+
     // the fixed left operands, row R*16 + n, contraction indices 16 kb + 4g + s:
     //   waves 0-3: fa = -K~, fb = M Diag(beta);  waves 4-7: fa = K^, fb = P^T, fc = Diag(beta) M^T
     float fa[4 * NKB], fb[16], fc[16];
@@ -723,26 +744,6 @@ __global__ void __launch_bounds__(CB_GRAD_NT) cb_grad_kernel(CbParams p) {
     for (int t = 0; t < NCW; ++t) aQ[t] = aK[t] = aB[t] = z4;
     aP[0] = aP[1] = aT[0] = aT[1] = z4;
 
-    // A tile's S, dS' and dO vectors (thread e: row e / (BV/4), columns
-    // 4 (e % (BV/4)) ..) and the V values of waves 0-3 are loaded into
-    // registers one tile ahead, unconditionally (rows clamped, surplus values
-    // unused); the walk's barriers are LDS-only, so these loads and the dv
-    // stores stay in flight across them.
-    static_assert(DK * BV / 4 <= NT && C * BV / 4 <= NT, "one vector per thread and tile");
-    const int er = tid / (BV / 4), ejq = 4 * (tid % (BV / 4));
-    const bool has_s = tid < DK * BV / 4, has_o = tid < C * BV / 4;
-    float4 nsv, nrv, nov;
-    float nvv[4];
-    auto load_tile = [&](int j0) {
-        const int c = has_s ? er : 0;
-        nsv = ld4(S + static_cast<int64_t>(c) * dv + j0 + ejq);
-        nrv = ld4(dSr + static_cast<int64_t>(c) * dv + j0 + ejq);
-        nov = ld4(p.d_o + ((t0 + min(er, L - 1)) * H + h) * dv + j0 + ejq);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            nvv[u] = io<TI>::ld(v, ((t0 + min(R * 16 + 4 * g + u, L - 1)) * H + h) * dv + j0 + n);
-    };
-    load_tile(0);
     for (int j0 = 0; j0 < dv; j0 += BV) {
         lds_barrier();  // the previous tile's readers are done
         if (has_s) {
@@ -1078,17 +1079,40 @@ __global__ void __launch_bounds__(CB_GRAD_NT) cb_grad_kernel(CbParams p) {
         for (int u = 0; u < 4; ++u) sKK[(R * 16 + 4 * g + u) * DK + cb * 16 + n] = vKK[t][u];
     }
     lds_barrier();
-    // dg: reverse cumsum of dG (in place), then the forward exclusive sum of
-    // dK^ K^ and dgamma gamma on every token
-    for (int c = tid; c < DK; c += NT) {
-        float run = 0.f;
-        for (int r = C - 1; r >= 0; --r) {
-            run += dGat(r, c);
-            dGat(r, c) = run;
+    // dg: per channel the reverse cumulative sum of dG plus the forward
+    // exclusive sum of dK^ K^ and dgamma gamma, on every token.  A channel's
+    // rows are split into NSEG segments over all the threads: the segment
+    // sums meet in LDS (the dead k, q staging), then each thread runs its
+    // own rows.  (Rows >= L contribute zeros to both sums.)
+    {
+        constexpr int NSEG = NT / DK, RPS = C / NSEG;   // segments per channel, rows per segment
+        static_assert(NSEG * DK == NT && RPS * NSEG == C && 2 * NT <= C * DK, "segments tile the chunk");
+        float *segG = lds + Q::GC + C * DK, *segK = segG + NT;
+        const int c = tid % DK, sgi = tid / DK, r0 = sgi * RPS;
+        float sgs = 0.f, sks = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPS; ++i) {
+            sgs += dGat(r0 + i, c);
+            sks += sKK[(r0 + i) * DK + c];
         }
-        float pre = aG[c] * blk[Y::GAM + c];
-        for (int r = 0; r < L; ++r) {
-            p.gg[((t0 + r) * H + h) * DK + c] = dGat(r, c) + pre;
+        segG[sgi * DK + c] = sgs;
+        segK[sgi * DK + c] = sks;
+        lds_barrier();
+        float run = 0.f, pre = aG[c] * blk[Y::GAM + c];
+        for (int u = 0; u < NSEG; ++u) {
+            if (u > sgi) run += segG[u * DK + c];
+            if (u < sgi) pre += segK[u * DK + c];
+        }
+        float val[RPS];
+#pragma unroll
+        for (int i = RPS - 1; i >= 0; --i) {
+            run += dGat(r0 + i, c);
+            val[i] = run;
+        }
+#pragma unroll
+        for (int i = 0; i < RPS; ++i) {
+            const int r = r0 + i;
+            if (r < L) p.gg[((t0 + r) * H + h) * DK + c] = val[i] + pre;
             pre += sKK[r * DK + c];
         }
     }
