@@ -231,8 +231,12 @@ kda_status kda_decode_step(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
  * course index's module list, Module 08 "Vision, MTP, and Hybrid Serving
  * State", on why a rollback must restore the recurrent state).
  * Per (sequence, head) the state is read once, the m tokens are applied in
- * order in registers, and the results are written once; the fused step is
- * the same as kda_decode_step's.
+ * registers, and the results are written once.  With 2 <= m <= 4 and no
+ * token_states the m tokens are applied in the chunked form of the
+ * recurrence (Module 04 — KDA II, §1 "The recurrence has affine form"): one
+ * pass of reductions over the state and a rank-m update, equal to applying
+ * them one by one up to fp32 rounding; otherwise token by token with the
+ * same fused step as kda_decode_step.
  *
  *   q, k, log_alpha  DEVICE [B, m, H, d_k]  in_dtype
  *   v                DEVICE [B, m, H, d_v]  in_dtype
