@@ -70,3 +70,34 @@ def test_noalloc_refuses_a_call_beyond_its_scratch():
     assert ei.value.status == 7
     torch.cuda.synchronize()
     assert bool((o == 7.0).all())
+
+
+def test_noalloc_prefill_replays_from_a_captured_graph():
+    """The use the allocation-free entry point is for: captured once in a
+    HIP graph (torch.cuda.graph; one eager call before the capture looks up
+    the scratch address), the graph replays to the eager result every time,
+    with other library calls on the same scratch and synchronisations
+    between the replays."""
+    x = synth.workload(2)   # the T=4096, H=16 prefill workload
+    q, k, v, b, la, _, _ = dev_tensors(x)
+    B, T, H, _ = q.shape
+    o_ref = torch.empty((B, T, H, x.d_v), dtype=torch.float32, device="cuda")
+    S_ref = torch.empty((B, H, x.d_k, x.d_v), dtype=torch.float32, device="cuda")
+    kda.prefill_noalloc(q, k, v, b, la, o_ref, final_state=S_ref)
+    torch.cuda.synchronize()
+    o, S = torch.empty_like(o_ref), torch.empty_like(S_ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kda.prefill_noalloc(q, k, v, b, la, o, final_state=S)
+    y = synth.make_uniform(74, 1, 300, 2, 128, 128, "bf16", chunk=64, state_std=0.1)
+    yq, yk, yv, yb, yla, yinit, _ = dev_tensors(y)
+    yo = torch.empty((1, 300, 2, 128), dtype=torch.float32, device="cuda")
+    for rep in range(4):
+        o.fill_(float("nan"))
+        S.fill_(float("nan"))
+        kda.prefill_noalloc(yq, yk, yv, yb, yla, yo, initial_state=yinit)   # other contents in the scratch
+        kda.prefill(yq, yk, yv, yb, yla, initial_state=yinit)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(S, S_ref), f"replay {rep}"
