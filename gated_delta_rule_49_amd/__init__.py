@@ -244,7 +244,7 @@ def max_chunks(q, k, v, beta, log_alpha, cu_seqlens=None, chunk_size=64) -> int:
 def prefill(q, k, v, beta, log_alpha, initial_state=None, output_final_state=True,
             cu_seqlens=None, chunk_size=64, out_dtype=None, chunk_states=False,
             workspace=None, final_state=None, o=None, check_seqlens=True, timing_events=None,
-            prologue=0):
+            prologue=0, device_status=None):
     """Chunked prefill.
 
     q, k, log_alpha [B,T,H,d_k]; v [B,T,H,d_v]; beta [B,T,H]; all float32 or
@@ -270,8 +270,11 @@ def prefill(q, k, v, beta, log_alpha, initial_state=None, output_final_state=Tru
 
     ``timing_events`` (a ctypes pointer to three hipEvent_t) is passed
     through to the library's profiling hook.  ``prologue``: PROLOGUE_* bits
-    (which inputs are pre-activations)."""
-    dev = _check_dev(q, k, v, beta, log_alpha, initial_state, cu_seqlens, workspace, final_state, o)
+    (which inputs are pre-activations).  ``device_status`` (int32 [1] on the
+    device, optional) receives the call's device-side status (0 or a
+    kda_status code) without a synchronisation; with packed input and
+    ``check_seqlens`` it is read back and raised on as above."""
+    dev = _check_dev(q, k, v, beta, log_alpha, initial_state, cu_seqlens, workspace, final_state, o, device_status)
     if not (q.dtype == k.dtype == v.dtype == beta.dtype == log_alpha.dtype):
         raise TypeError("q, k, v, beta, log_alpha must share one dtype")
     if q.dim() != 4 or k.shape != q.shape or log_alpha.shape != q.shape:
@@ -313,7 +316,11 @@ def prefill(q, k, v, beta, log_alpha, initial_state=None, output_final_state=Tru
     if chunk_states:
         nmax = int(L.kda_prefill_max_chunks(ctypes.byref(a)))
         cs = torch.zeros((nmax, H, dk, dv), dtype=torch.float32, device=dev)
-    status = torch.zeros(1, dtype=torch.int32, device=dev) if (check_seqlens and cu_seqlens is not None) else None
+    status = device_status
+    if device_status is not None:
+        _check_buffer(device_status, "device_status", (1,), (torch.int32,))
+    elif check_seqlens and cu_seqlens is not None:
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
     a.o = _ptr(o)
     a.initial_state = _ptr(initial_state)
     a.final_state = _ptr(final_state)
@@ -325,7 +332,7 @@ def prefill(q, k, v, beta, log_alpha, initial_state=None, output_final_state=Tru
     st = L.kda_prefill_chunked(ctypes.byref(a), _stream(dev))
     if st != 0:
         raise KDAError(st, "kda_prefill_chunked")
-    if status is not None and int(status.item()) != 0:
+    if check_seqlens and cu_seqlens is not None and int(status.item()) != 0:
         raise KDAError(int(status.item()), "kda_prefill_chunked (device check)")
     if chunk_states:
         return o, final_state, cs[:_host_chunk_count(B, T, cu_seqlens, chunk_size)]

@@ -4,6 +4,9 @@
 #include "../../include/kda.h"
 #include "kda_launch.hpp"
 
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 
 using namespace kda;
@@ -66,10 +69,21 @@ bool use_f32mm(const kda_prefill_args *a) {
     return a->chunk_size > 16 || blocks <= 4.0 * (1u << 30);
 }
 
+// shapes whose matrix-core prefill may run as one overlapped launch
+bool overlap_shape(const kda_prefill_args *a) {
+    return use_mfma(a) && mfma_overlap_shape(a->num_seqs, a->H, a->d_k, a->chunk_size);
+}
+
+size_t mfma_blocks_bytes(const kda_prefill_args *a) {
+    return static_cast<size_t>(max_chunks(a)) * a->H * mfma_block_bytes(a->chunk_size, a->d_k);
+}
+
 size_t workspace_for(const kda_prefill_args *a) {
     size_t bytes = table_bytes(a->num_seqs, max_chunks(a));
-    if (use_mfma(a))
-        bytes += static_cast<size_t>(max_chunks(a)) * a->H * mfma_block_bytes(a->chunk_size, a->d_k);
+    if (use_mfma(a)) {
+        bytes += mfma_blocks_bytes(a);
+        if (overlap_shape(a)) bytes += mfma_ready_bytes(max_chunks(a), a->H);
+    }
     else if (use_f32mm(a))
         bytes += static_cast<size_t>(max_chunks(a)) * a->H * cb_block_bytes(a->d_k);
     return bytes;
@@ -91,6 +105,7 @@ const char *kda_status_string(int32_t s) {
         case KDA_ERR_HIP: return "HIP launch failed";
         case KDA_ERR_BAD_SEQLENS: return "cu_seqlens malformed";
         case KDA_ERR_SCRATCH_LIMIT: return "needs more scratch than the allocation-free entry point holds";
+        case KDA_ERR_DEVICE_WAIT: return "a hand-off between workgroups of the overlapped prefill failed";
         default: return "unknown status";
     }
 }
@@ -108,6 +123,41 @@ size_t kda_prefill_workspace_bytes(const kda_prefill_args *a) {
 }  // extern "C"
 
 namespace {
+
+constexpr int kMaxDevices = 64;
+
+// The device that owns hip_stream (the current device for the null stream).
+kda_status stream_device(void *hip_stream, int *dev) {
+    int d = -1;
+    if (hip_stream) {
+        hipDevice_t sd = -1;
+        if (hipStreamGetDevice(static_cast<hipStream_t>(hip_stream), &sd) != hipSuccess) return KDA_ERR_HIP;
+        d = static_cast<int>(sd);
+    } else if (hipGetDevice(&d) != hipSuccess) {
+        return KDA_ERR_HIP;
+    }
+    if (d < 0 || d >= kMaxDevices) return KDA_ERR_UNSUPPORTED;
+    *dev = d;
+    return KDA_OK;
+}
+
+// The overlapped launch places one workgroup on each of the 256 CUs of the
+// 8 XCDs; it is used on devices with that many CUs unless the environment
+// sets KDA_PREFILL_OVERLAP=0.  CU counts are looked up once per device.
+std::atomic<int> g_cu_count[kMaxDevices];
+
+bool overlap_enabled(void *hip_stream) {
+    const char *env = std::getenv("KDA_PREFILL_OVERLAP");
+    if (env && std::strcmp(env, "0") == 0) return false;
+    int dev = -1;
+    if (stream_device(hip_stream, &dev) != KDA_OK) return false;
+    int n = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+        g_cu_count[dev].store(n, std::memory_order_relaxed);
+    }
+    return n == 256;
+}
 
 // The prefill after host validation, with its scratch at ws (ws_bytes long).
 kda_status prefill_on(const kda_prefill_args *a, char *ws, size_t ws_bytes, void *hip_stream) {
@@ -135,6 +185,9 @@ kda_status prefill_on(const kda_prefill_args *a, char *ws, size_t ws_bytes, void
     p.N = a->num_seqs; p.C = a->chunk_size;
     p.n_chunks_bound = static_cast<int32_t>(max_chunks(a));
     p.prologue = a->prologue;
+    p.ready = nullptr;
+    if (overlap_shape(a) && overlap_enabled(hip_stream))
+        p.ready = reinterpret_cast<int32_t *>(ws + table_bytes(p.N, p.n_chunks_bound) + mfma_blocks_bytes(a));
 
     if (p.N == 0) return KDA_OK;
     hipEvent_t *ev = static_cast<hipEvent_t *>(a->timing_events);
@@ -163,7 +216,6 @@ kda_status prefill_on(const kda_prefill_args *a, char *ws, size_t ws_bytes, void
 // that scratch_address() looks up.
 static __device__ __align__(256) char scratch[KDA_NOALLOC_SCRATCH_BYTES];
 
-constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mutex;
 void *g_scratch_ptr[kMaxDevices] = {};
 
@@ -174,12 +226,8 @@ kda_status scratch_address(void *hip_stream, char **out) {
     int cur = -1;
     if (hipGetDevice(&cur) != hipSuccess) return KDA_ERR_HIP;
     int dev = cur;
-    if (hip_stream) {
-        hipDevice_t d = -1;
-        if (hipStreamGetDevice(static_cast<hipStream_t>(hip_stream), &d) != hipSuccess) return KDA_ERR_HIP;
-        dev = static_cast<int>(d);
-    }
-    if (dev < 0 || dev >= kMaxDevices) return KDA_ERR_UNSUPPORTED;
+    const kda_status st = stream_device(hip_stream, &dev);
+    if (st != KDA_OK) return st;
     std::lock_guard<std::mutex> lock(g_scratch_mutex);
     if (!g_scratch_ptr[dev]) {
         if (dev != cur && hipSetDevice(dev) != hipSuccess) return KDA_ERR_HIP;

@@ -10,7 +10,8 @@ namespace kda {
 //   [0, 256)            status word (int32) + padding
 //   [256, 256 + 4(N+1)) chunk_off table, rounded up to 256
 //   then chunk_info, 16 bytes per chunk (up to the chunk bound), rounded up
-//   then, matrix-core path only, the per-(chunk, head) intermediate blocks.
+//   then, matrix-core path only, the per-(chunk, head) intermediate blocks,
+//   then, for the shapes of the overlapped launch, one int32 flag per (chunk, head).
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline size_t chunk_off_bytes(int N) { return align_up(sizeof(int32_t) * (static_cast<size_t>(N) + 1)); }
@@ -21,6 +22,16 @@ inline size_t table_bytes(int N, int64_t n_chunks_bound) {
 // matrix-core path: bytes of intermediates per (chunk, head)
 size_t mfma_block_bytes(int C, int D);
 bool mfma_supported(int dk, int dv, int C);
+// shapes the overlapped matrix-core launch takes (one sequence, few heads);
+// after the blocks it needs 64 int32 role counters and one int32 flag per
+// (chunk, head), cleared by the chunk-table kernel
+bool mfma_overlap_shape(int N, int H, int D, int C);
+__host__ __device__ inline size_t mfma_ready_words(int64_t n_chunks_bound, int H) {
+    return 64 + static_cast<size_t>(n_chunks_bound) * H;
+}
+inline size_t mfma_ready_bytes(int64_t n_chunks_bound, int H) {
+    return align_up(sizeof(int32_t) * mfma_ready_words(n_chunks_bound, H));
+}
 
 hipError_t launch_chunk_table(const PrefillParams &p, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillParams &p, int in_dtype, int out_dtype, hipStream_t s);

@@ -18,6 +18,7 @@ struct PrefillParams {
     int32_t B, T, H, dk, dv, N, C;
     int32_t n_chunks_bound;      // grid bound on the total number of chunks
     uint32_t prologue;           // kPro* bits: which inputs are pre-activations
+    int32_t *ready;              // device, nullable: role counters and per-(head, chunk) flags of the overlapped launch (workspace)
 };
 
 // Token range of sequence n: tokens [start, start + len) of the flattened

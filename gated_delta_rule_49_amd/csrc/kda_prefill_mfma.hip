@@ -292,19 +292,114 @@ __device__ __forceinline__ int gram_pair(int grp, int u) {
     return code == 0xff ? -1 : code;
 }
 
-// Persistent: each workgroup walks work items item = blockIdx.x + i * gridDim.x
-// (item = chunk * H + head).
-template <int C, int D>
-__global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__restrict__ blocks) {
+// ------------------------------------------- overlapped launch hand-off --
+// In the overlapped launch one workgroup writes a (chunk, head) block and
+// another one of the same XCD reads it while the kernel still runs.  Within
+// an XCD the L2 is the point of coherence: a store has reached it once the
+// storing thread's vector memory counter is zero, and a load that misses the
+// L1 reads it there.  The reader never touches a block before its flag is
+// set, so the block's lines cannot be in the reader's L1 from earlier.  A
+// flag holds 1 + the XCD of its writer; a reader on another XCD (which the
+// role assignment below never makes) would take a device-wide acquire.
+//
+// The ready area of the workspace: kReadyTickets role counters (one per
+// XCD, the rest padding), then one flag per (head, chunk).
+constexpr int kReadyTickets = 64;
+
+// Status code of an expired hand-off wait (KDA_ERR_DEVICE_WAIT).
+constexpr int32_t kErrDeviceWait = 8;
+// Bound of a hand-off wait, in ticks of the 100 MHz real-time counter (1 s).
+constexpr uint64_t kReadyWaitTicks = 100000000ull;
+
+__device__ __forceinline__ int xcc_id() {
+    return __builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11));  // HW_REG_XCC_ID, bits [3:0]
+}
+
+// Waits until every vector memory access of this thread has completed.
+__device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
+// After the block's stores have completed (wait_memory by every thread and a
+// barrier): flag = 1 + xcc.
+__device__ __forceinline__ void publish_ready(int32_t *flag, int xcc) {
+    __hip_atomic_store(flag, 1 + xcc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void report_device_error(const PrefillParams &p, int32_t code) {
+    __hip_atomic_store(p.status, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (p.user_status) __hip_atomic_store(p.user_status, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A reader's view of one head's flags (flags[c] for chunk c < nch, one
+// sequence): chunks below `known` are published.  ensure(j) returns once
+// chunk j is; each poll reads the flags of the next 64 chunks at once (one
+// per lane), so a reader behind its writers polls once per 64 chunks.
+// Bounded: once the call's status word holds an error, or after
+// kReadyWaitTicks without progress, ensure returns anyway (recording
+// kErrDeviceWait), so every wave still runs to its end; the call's results
+// are then undefined and its status says so.  Uniform per wave.
+struct ReadyView {
+    const int32_t *flags;
+    int nch, known, xcc;
+    __device__ __forceinline__ void ensure(int j, const PrefillParams &p) {
+        if (j < known) return;
+        const int lane = __lane_id();
+        uint64_t t0 = 0;
+        for (int spin = 0;; ++spin) {
+            const int c = known + lane;
+            const int f = c < nch ? __hip_atomic_load(flags + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1 + xcc;
+            const uint64_t unset = __builtin_amdgcn_ballot_w64(f == 0);
+            const int m = unset ? __builtin_ctzll(unset) : 64;  // leading published chunks
+            // a block written on another XCD is only visible after a device-wide acquire
+            if (__builtin_amdgcn_ballot_w64(lane < m && f - 1 != xcc)) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            known += m;
+            if (j < known) return;
+            if (spin == 0) t0 = __builtin_amdgcn_s_memrealtime();
+            if (m > 0) t0 = __builtin_amdgcn_s_memrealtime();
+            if (__builtin_amdgcn_readfirstlane(
+                    __hip_atomic_load(p.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0) {
+                known = nch;
+                return;
+            }
+            if (__builtin_amdgcn_s_memrealtime() - t0 > kReadyWaitTicks) {
+                report_device_error(p, kErrDeviceWait);
+                known = nch;
+                return;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+};
+
+// Flag of (chunk x, head h) in the overlapped launch: one sequence, flags
+// of a head contiguous in chunk order.
+__device__ __forceinline__ int ready_index(const PrefillParams &p, int x, int h) {
+    return kReadyTickets + h * p.n_chunks_bound + x;
+}
+
+// The (chunk, head) items one workgroup of the per-chunk stage computes, in
+// order: schedule positions first, first + stride, ... below total.  In the
+// plain order (npx == 0) position k is item k = chunk * H + head; in the
+// XCD-local order of a single sequence (npx > 0) it is chunk k / npx of head
+// x + 8 (k % npx), one of the npx heads whose scan runs on XCD x.
+struct IntraSched {
+    int first, stride, total;
+    int npx, x, H;
+    __device__ __forceinline__ int item(int k) const { return npx == 0 ? k : (k / npx) * H + x + 8 * (k % npx); }
+};
+
+// The per-chunk stage over the items of schedule sc, with its LDS at smem
+// (IntraLds<C, D>::BYTES bytes).  Persistent: pass i computes one item and
+// loads the inputs of the next.  PUB (the overlapped launch): once every
+// store of an item's block has completed, its flag is set to 1 + the XCD
+// the workgroup runs on (xcc).
+template <int C, int D, bool PUB>
+__device__ __forceinline__ void intra_run(const PrefillParams &p, char *__restrict__ blocks, char *smem,
+                                          const IntraSched &sc, int32_t *ready, int xcc) {
     using Y = Lay<C, D>;
     using M = IntraLds<C, D>;
     constexpr int CP = Y::CP;
     constexpr int KH = Y::KSD / 2;  // channel k-steps per Gram half
-    if (*p.status != 0) return;
     const int H = p.H;
-    const int nitems = p.chunk_off[p.N] * H;
-
-    __shared__ __attribute__((aligned(16))) char smem[M::BYTES];
     auto SK = reinterpret_cast<bf16_t(*)[M::RK]>(smem + M::SK);
     auto SQ = reinterpret_cast<bf16_t(*)[M::RK]>(smem + M::SQ);
     auto SA = reinterpret_cast<float(*)[M::RA]>(smem + M::SA);
@@ -319,18 +414,19 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
     auto TH = reinterpret_cast<bf16_t(*)[M::RTF]>(smem + M::TH);
     auto TL = reinterpret_cast<bf16_t(*)[M::RTF]>(smem + M::TL);
 
-    if (static_cast<int>(blockIdx.x) >= nitems) return;
+    if (sc.first >= sc.total) return;
     IntraRaw<C, D> raw;
     IntraItem it{};
-    int4 nci = p.chunk_info[blockIdx.x / H];  // coordinates of the next item
+    int4 nci = p.chunk_info[sc.item(sc.first) / H];  // coordinates of the next item
     IntraPend<C, D> pend;
     pend.blk = nullptr;
+    int pub = -1;  // PUB: the item whose block is stored last, published after its W and U tiles
 
     // Pass i computes item_i and loads the raw inputs of item_{i+1}; the first
     // pass (item < 0) only loads.  A single load site keeps the prefetched
     // registers in place across the loop instead of being copied (a copy
     // would wait for the loads).
-    for (int item = static_cast<int>(blockIdx.x) - static_cast<int>(gridDim.x);; item += gridDim.x) {
+    for (int item = sc.first - sc.stride;; item += sc.stride) {  // schedule positions
         // The thread index is made opaque for each item so that the compiler
         // recomputes per-thread addresses inside the loop instead of keeping
         // dozens of them live (and spilled) across the whole kernel.
@@ -339,12 +435,12 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
         const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int g = lane >> 4, li = lane & 15;
         const int L = it.L;
-        const int next = item + static_cast<int>(gridDim.x);
+        const int next = item + sc.stride;
         const bool live = item >= 0;
         char *blk = blocks + (static_cast<size_t>(it.x) * H + it.h) * Y::BYTES;
         // (the wait for this load coincides with the staging's wait for the
         // prefetched inputs, which were issued before it)
-        const IntraItem itn = intra_item(next, H, make_int4(__builtin_amdgcn_readfirstlane(nci.x),
+        const IntraItem itn = intra_item(sc.item(next), H, make_int4(__builtin_amdgcn_readfirstlane(nci.x),
                                                             __builtin_amdgcn_readfirstlane(nci.y),
                                                             __builtin_amdgcn_readfirstlane(nci.z), 0));
         const int kh = wave & 1, grp = wave >> 1;
@@ -443,7 +539,14 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
 #pragma unroll
                 for (int j = 0; j < M::RS; ++j) SG[seg * M::RS + j][ch] = (off + gv[j]) * kLog2e;
             }
+            // PUB: the previous item's W and U tiles were stored at the
+            // staging barrier, its other parts during that item
+            if (PUB && pub >= 0) wait_memory();
             lds_barrier();
+            if (PUB && pub >= 0) {
+                if (tid == 0) publish_ready(ready + pub, xcc);
+                pub = -1;
+            }
 
             // ---- 2. Gram blocks A^T(b,a), P^T(b,a) for b <= a.  Work unit =
             //         (block pair, half of the channels): wave w = kh + 2 grp takes
@@ -649,7 +752,7 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
         }  // live
         // the next item's k and q: loads in flight during the rest of this
         // item (issued after the Gram phase, whose registers they would crowd)
-        if (next < nitems) raw.load_kq(p, itn.t0, itn.L, itn.h, tid);
+        if (next < sc.total) raw.load_kq(p, itn.t0, itn.L, itn.h, tid);
         if (live) {
             lds_barrier();
 
@@ -768,7 +871,7 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
             }
         }  // live
         // the next item's v, gate and beta
-        if (next < nitems) raw.load_va(p, itn.t0, itn.L, itn.h, tid);
+        if (next < sc.total) raw.load_va(p, itn.t0, itn.L, itn.h, tid);
         if (live) {
             lds_barrier();
 
@@ -799,6 +902,7 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
             // ---- 4. W^T = (k e^G)^T T^T (bf16) per channel tile; U = T V (T split)
             //         per value tile.  Items: NDT W tiles then NDT U tiles.
             pend.blk = blk;
+            pub = ready_index(p, it.x, it.h);
             for (int wi = wave; wi < 2 * Y::NDT; wi += 8) {
                 const bool isW = wi < Y::NDT;
                 const int ct = isW ? wi : wi - Y::NDT;
@@ -852,12 +956,28 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
             }
             lds_barrier();  // LDS is restaged by the next item
         }  // live
-        if (next >= nitems) break;
+        if (next >= sc.total) break;
         it = itn;
-        const int after = next + static_cast<int>(gridDim.x);
-        nci = after < nitems ? p.chunk_info[after / H] : make_int4(0, 0, 1, 0);
+        const int after = next + sc.stride;
+        nci = after < sc.total ? p.chunk_info[sc.item(after) / H] : make_int4(0, 0, 1, 0);
     }
     pend.flush(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6), threadIdx.x & 63);
+    if (PUB && pub >= 0) {
+        wait_memory();
+        lds_barrier();
+        if (threadIdx.x == 0) publish_ready(ready + pub, xcc);
+    }
+}
+
+// The per-chunk stage on its own: workgroup b computes items b, b + G, ...
+// (G = gridDim.x) of the chunk-major order.
+template <int C, int D>
+__global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__restrict__ blocks) {
+    __shared__ __attribute__((aligned(16))) char smem[IntraLds<C, D>::BYTES];
+    if (*p.status != 0) return;
+    const IntraSched sc{static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x), p.chunk_off[p.N] * p.H, 0, 0,
+                        p.H};
+    intra_run<C, D, false>(p, blocks, smem, sc, nullptr, 0);
 }
 
 // ------------------------------------------------------------------ K2 --
@@ -943,11 +1063,13 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const ScanOps<64, 128>::u32x4 &u) { 
 // updates the state tiles S in place.
 // The next chunk's operands are requested into `nx` in four parts between
 // the phases, so that the transfers overlap this chunk's computation.
-template <int C, int D, typename TO>
+// gate() runs before the first load of the next block (the overlapped
+// launch waits there until that block is published).
+template <int C, int D, typename TO, typename Gate>
 __device__ __forceinline__ void scan_chunk(const ScanOps<C, D> &op, ScanOps<C, D> &nx, const char *nblk,
                                            uint32_t lane16, f32x4 (&S)[2], ScanShared<C, D> &sh,
                                            const PrefillParams &p, int64_t x, int64_t t0, int L, int h, int w,
-                                           int nt, int lane) {
+                                           int nt, int lane, Gate &&gate) {
     using Y = Lay<C, D>;
     constexpr int NW = D / 32;
     constexpr int OWN = ScanOps<C, D>::OWN;
@@ -976,6 +1098,7 @@ __device__ __forceinline__ void scan_chunk(const ScanOps<C, D> &op, ScanOps<C, D
         pq = mfma16(as_bf16x8(op.ql[mt]), sh_.v, pq);
         sh.red[1][w][mt][lane] = pq;
     }
+    gate();
     nx.load(0, nblk, lane16, w, nt, g);
     lds_barrier();
     // (c) reduce the owned token tiles: Delta = U - sum_w W S
@@ -1045,18 +1168,16 @@ __device__ __forceinline__ void scan_chunk(const ScanOps<C, D> &op, ScanOps<C, D
     nx.load(3, nblk, lane16, w, nt, g);
 }
 
-template <int C, int D, typename TO>
-__global__ void __launch_bounds__(64 * (D / 32)) scan_kernel(PrefillParams p, const char *__restrict__ blocks) {
+// The scan of one (sequence, head) pair's 16-column state tile nt, with its
+// LDS at sh; wave w = threadIdx.x / 64 < D / 32.  WAIT (the overlapped
+// launch, one sequence): every block is read only after its flag is set,
+// the L2 warm-up included (a line read before it is written could stay in
+// this CU's L1).
+template <int C, int D, typename TO, bool WAIT>
+__device__ __forceinline__ void scan_run(const PrefillParams &p, const char *__restrict__ blocks,
+                                         ScanShared<C, D> &sh, int pair, int nt, const int32_t *ready, int xcc) {
     using Y = Lay<C, D>;
     constexpr int NVT = D / 16;   // 16-column state tiles per head
-    if (*p.status != 0) return;
-    // XCD-aware order: the NVT column tiles of one (sequence, head) share
-    // blockIdx % 8, hence one XCD and its L2.
-    const int bid = blockIdx.x;
-    const int xcd = bid & 7, slot = bid >> 3;
-    const int nt = slot % NVT;
-    const int pair = xcd + 8 * (slot / NVT);
-    if (pair >= p.N * p.H) return;
     const int H = p.H;
     const int n = pair / H, h = pair % H;
     const SeqRange sr = seq_range(p, n);
@@ -1065,8 +1186,6 @@ __global__ void __launch_bounds__(64 * (D / 32)) scan_kernel(PrefillParams p, co
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, li = lane & 15;
     const int col = 16 * nt + li;
-
-    __shared__ ScanShared<C, D> sh;
 
     const int64_t soff = (static_cast<int64_t>(n) * H + h) * D * D;
     f32x4 S[2];
@@ -1088,31 +1207,39 @@ __global__ void __launch_bounds__(64 * (D / 32)) scan_kernel(PrefillParams p, co
     // together touch every 128-byte line of chunk c + kWarmAhead's block (one
     // dword per line, this workgroup's eighth), so that block is in L2 before
     // its operands are requested; the loaded word is only consumed (without
-    // instructions) one chunk later, so the wait for it is free.
+    // instructions) two chunks later (two registers, by chunk parity), so the
+    // wait for it is free.
     constexpr int kWarmAhead = 2;
     constexpr int kLines = static_cast<int>(Y::BYTES / 128);
     constexpr int kSlots = NVT * (D / 32) * 64;  // lanes of all the head's workgroups
     const uint32_t warm_off = static_cast<uint32_t>(((nt * (D / 32) + w) * 64 + lane) * kLines / kSlots) * 128u;
-    uint32_t warm = 0;
-    auto warm_up = [&](int c) {
+    uint32_t warmA = 0, warmB = 0;
+    auto warm_up = [&](uint32_t &warm, int c) {
         asm volatile("" ::"v"(warm));
         warm = *reinterpret_cast<const uint32_t *>(blk_of(min(c + kWarmAhead, nch - 1)) + warm_off);
     };
+    // WAIT: a block is warmed only when its writers are at least
+    // kWarmPublished chunks further on (it may have left the L2 since it was
+    // written); closer behind them the warm-up measured slower than none.
+    constexpr int kWarmPublished = 16;
     ScanOps<C, D> A, B;
     if (nch > 0) {
         const uint32_t lane16 = 16u * lane;
+        ReadyView rv{WAIT ? ready + ready_index(p, 0, h) : nullptr, nch, WAIT ? 0 : nch, xcc};
+        if (WAIT) rv.ensure(0, p);
         A.load(blk_of(0), lane16, w, nt, g);
         for (int c = 0; c < nch; c += 2) {
-            warm_up(c);
+            if (!WAIT || min(c + kWarmAhead, nch - 1) + kWarmPublished < rv.known) warm_up(warmA, c);
             scan_chunk<C, D, TO>(A, B, blk_of(min(c + 1, nch - 1)), lane16, S, sh, p, cbase + c,
-                                 sr.start + static_cast<int64_t>(c) * C, min(C, sr.len - c * C), h, w, nt, lane);
+                                 sr.start + static_cast<int64_t>(c) * C, min(C, sr.len - c * C), h, w, nt, lane,
+                                 [&] { if (WAIT) rv.ensure(min(c + 1, nch - 1), p); });
             if (c + 1 >= nch) break;
-            warm_up(c + 1);
+            if (!WAIT || min(c + 1 + kWarmAhead, nch - 1) + kWarmPublished < rv.known) warm_up(warmB, c + 1);
             scan_chunk<C, D, TO>(B, A, blk_of(min(c + 2, nch - 1)), lane16, S, sh, p, cbase + c + 1,
-                                 sr.start + static_cast<int64_t>(c + 1) * C, min(C, sr.len - (c + 1) * C), h, w,
-                                 nt, lane);
+                                 sr.start + static_cast<int64_t>(c + 1) * C, min(C, sr.len - (c + 1) * C), h, w, nt,
+                                 lane, [&] { if (WAIT) rv.ensure(min(c + 2, nch - 1), p); });
         }
-        asm volatile("" ::"v"(warm));
+        asm volatile("" ::"v"(warmA), "v"(warmB));
     }
     if (p.final_state) {
 #pragma unroll
@@ -1123,7 +1250,78 @@ __global__ void __launch_bounds__(64 * (D / 32)) scan_kernel(PrefillParams p, co
     }
 }
 
+template <int C, int D, typename TO>
+__global__ void __launch_bounds__(64 * (D / 32)) scan_kernel(PrefillParams p, const char *__restrict__ blocks) {
+    constexpr int NVT = D / 16;   // 16-column state tiles per head
+    __shared__ ScanShared<C, D> sh;
+    if (*p.status != 0) return;
+    // XCD-aware order: the NVT column tiles of one (sequence, head) share
+    // blockIdx % 8, hence one XCD and its L2.
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, slot = bid >> 3;
+    const int nt = slot % NVT;
+    const int pair = xcd + 8 * (slot / NVT);
+    if (pair >= p.N * p.H) return;
+    scan_run<C, D, TO, false>(p, blocks, sh, pair, nt, nullptr, 0);
+}
+
+// ---------------------------------------------------- overlapped launch --
+// For one sequence whose scan would leave most CUs idle (at most
+// kOverlapScanSlots column-tile workgroups per XCD), the two stages run in
+// one launch of 8 x kOverlapSlots workgroups, one per CU.  The hardware
+// deals a launch's workgroups to the 8 XCDs round-robin, but from an XCD
+// that depends on earlier launches, so roles follow the XCD a workgroup
+// finds itself on (xcc_id()) and its arrival there: it takes the next
+// ticket of its XCD's counter.  On XCD x the first SI arrivals compute the
+// per-chunk stage of the heads h = x + 8j, chunk by chunk (the order in
+// which the scan consumes them), and publish each block; the next
+// NVT x (number of those heads) arrivals run their scans, each reading a
+// block as soon as its flag is set, so the scan no longer waits for the
+// whole per-chunk stage.  Producers never wait and take the first tickets,
+// so the consumers' waits end however many workgroups are resident.  Every
+// role is taken once when each XCD receives kOverlapSlots workgroups (the
+// round-robin deal); a workgroup that finds its XCD's roles all taken
+// records kErrDeviceWait and leaves (a role of another XCD then has no
+// workgroup, and the call's results are undefined).
+constexpr int kOverlapSlots = 32;      // workgroups per XCD (its CUs)
+constexpr int kOverlapScanSlots = 16;  // at most this many scan workgroups per XCD
+
+template <int C, int D, typename TO>
+__global__ void __launch_bounds__(512) overlap_kernel(PrefillParams p, char *__restrict__ blocks) {
+    constexpr int NVT = D / 16;
+    constexpr size_t LDS =
+        IntraLds<C, D>::BYTES > sizeof(ScanShared<C, D>) ? IntraLds<C, D>::BYTES : sizeof(ScanShared<C, D>);
+    __shared__ __attribute__((aligned(16))) char smem[LDS];
+    __shared__ int s_slot;
+    if (*p.status != 0) return;
+    const int x = xcc_id();
+    if (threadIdx.x == 0)
+        s_slot = __hip_atomic_fetch_add(p.ready + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int slot = s_slot;
+    if (slot >= kOverlapSlots) {
+        if (threadIdx.x == 0) report_device_error(p, kErrDeviceWait);
+        return;
+    }
+    const int H = p.H;  // one sequence: (sequence, head) pair = head
+    const int npx = x < H ? (H - x + 7) / 8 : 0;
+    const int si = kOverlapSlots - npx * NVT;
+    if (slot < si) {
+        const IntraSched sc{slot, si, npx * p.chunk_off[1], npx, x, H};
+        intra_run<C, D, true>(p, blocks, smem, sc, p.ready, x);
+    } else {
+        if (threadIdx.x >= 64 * (D / 32)) return;  // the scan's D/32 waves
+        const int s = slot - si;
+        scan_run<C, D, TO, true>(p, blocks, *reinterpret_cast<ScanShared<C, D> *>(smem), x + 8 * (s / NVT), s % NVT,
+                                 p.ready, x);
+    }
+}
+
 // ---------------------------------------------------------------- host --
+bool mfma_overlap_shape(int N, int H, int D, int C) {
+    return N == 1 && C == 64 && (H + 7) / 8 * (D / 16) <= kOverlapScanSlots;
+}
+
 size_t mfma_block_bytes(int C, int D) {
     if (D == 128) {
         if (C == 64) return Lay<64, 128>::BYTES;
@@ -1142,6 +1340,14 @@ bool mfma_supported(int dk, int dv, int C) {
 namespace {
 template <int C, int D, typename TO>
 hipError_t run_mfma(const PrefillParams &p, char *blocks, hipStream_t s, hipEvent_t mid) {
+    if constexpr (C == 64) {
+        if (p.ready) {
+            hipLaunchKernelGGL((overlap_kernel<C, D, TO>), dim3(8 * kOverlapSlots), dim3(512), 0, s, p, blocks);
+            hipError_t e = hipGetLastError();
+            if (e == hipSuccess && mid) e = hipEventRecord(mid, s);
+            return e;
+        }
+    }
     const int items = p.n_chunks_bound * p.H;  // upper bound; the kernel reads the exact count
     const int igrid = items < kIntraGrid ? items : kIntraGrid;
     hipLaunchKernelGGL((intra_kernel<C, D>), dim3(igrid), dim3(512), 0, s, p, blocks);

@@ -15,6 +15,9 @@ __global__ void __launch_bounds__(1024) chunk_table_kernel(PrefillParams p) {
     __shared__ int32_t s_bad;
     const int tid = threadIdx.x;
     const int N = p.N;
+    // the overlapped launch's role counters and hand-off flags start cleared
+    if (p.ready)
+        for (size_t i = tid; i < mfma_ready_words(p.n_chunks_bound, p.H); i += 1024) p.ready[i] = 0;
     if (tid == 0) s_bad = 0;
     __syncthreads();
     // each thread owns a contiguous block of sequences

@@ -72,8 +72,12 @@ typedef enum {
     KDA_ERR_WORKSPACE_TOO_SMALL = 4,
     KDA_ERR_HIP = 5,                /* a HIP launch failed                        */
     KDA_ERR_BAD_SEQLENS = 6,        /* host-visible cu_seqlens are malformed      */
-    KDA_ERR_SCRATCH_LIMIT = 7       /* needs more than the fixed scratch of
+    KDA_ERR_SCRATCH_LIMIT = 7,      /* needs more than the fixed scratch of
                                        kda_prefill_chunked_noalloc             */
+    KDA_ERR_DEVICE_WAIT = 8         /* device-side only (*device_status): a
+                                       hand-off between workgroups of the
+                                       overlapped prefill failed; the call's
+                                       results are undefined                  */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
