@@ -32,7 +32,7 @@ Prints ONE JSON line:
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload long|prefill|packed] [--no-cpu-baseline]
-       python bench.py --leg prefill_long|prefill_c2|prefill_c4|decode|backward
+       python bench.py --leg prefill_long|prefill_c2|prefill_c4|decode|decode_multi|short_conv|backward
                        [--steps K] [--warmup W]
                        only that workload's calls (one rocprofv3 trace per workload)
        python bench.py --summarize DIR    per-kernel means of a rocprofv3 CSV run
@@ -104,7 +104,7 @@ CALL_KERNELS = {
 }
 # call keys whose kernels each `--leg` runs
 LEG_CALLS = {"prefill_long": ["prefill_long"], "decode": ["decode"], "decode_multi": ["decode_multi_m4"],
-             "backward": ["backward_T4096_H16"]}
+             "backward": ["backward_T4096_H16"], "short_conv": ["short_conv_prefill", "short_conv_decode"]}
 
 
 def kernel_sources_sha(group: str) -> str:
@@ -445,17 +445,34 @@ def prefill_leg(kda, name, dev, reps, warmup, flush):
         kda.prefill(P["q"], P["k"], P["v"], P["beta"], P["log_alpha"], initial_state=P["init"],
                     cu_seqlens=P["cu"], chunk_size=P["chunk"], workspace=ws, o=o, final_state=fin,
                     check_seqlens=False)
-    for _ in range(warmup):
-        call()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a_, b_ in evs:
-        if flush is not None:
-            flush()
-        a_.record()
-        call()
-        b_.record()
-    torch.cuda.synchronize()
-    st = stats([a_.elapsed_time(b_) for a_, b_ in evs])
+
+    def timed():
+        for _ in range(warmup):
+            call()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a_, b_ in evs:
+            if flush is not None:
+                flush()
+            a_.record()
+            call()
+            b_.record()
+        torch.cuda.synchronize()
+        return stats([a_.elapsed_time(b_) for a_, b_ in evs])
+    st = timed()
+    # one sequence with few heads runs both stages in one overlapped launch
+    # (the library's own choice); the two-kernel launch is timed beside it
+    overlapped = N == 1 and P["chunk"] == 64 and (H + 7) // 8 * (d // 16) <= 16
+    two_kernel = None
+    if overlapped:
+        saved = os.environ.get("KDA_PREFILL_OVERLAP")
+        os.environ["KDA_PREFILL_OVERLAP"] = "0"
+        try:
+            two_kernel = timed()
+        finally:
+            if saved is None:
+                del os.environ["KDA_PREFILL_OVERLAP"]
+            else:
+                os.environ["KDA_PREFILL_OVERLAP"] = saved
     tokens = int(P["cu_host"][-1]) if P["cu_host"] is not None else Bp * T
     nbytes = tokens * H * PREFILL_BYTES_PER_TOKEN_HEAD + (2 * N * H * d * d * 4 if P["init"] is not None else 0)
     gbs = nbytes / (st["median"] * 1e-3) / 1e9
@@ -466,7 +483,11 @@ def prefill_leg(kda, name, dev, reps, warmup, flush):
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
                         "useful_mfma_frac": useful_tf / BF16_PEAK_TFLOPS,
-                        "kernel": "kda_prefill_chunked (chunk table + intra_kernel + scan_kernel)"}}
+                        "kernel": ("kda_prefill_chunked (chunk table + overlap_kernel: both stages in one launch)"
+                                   if overlapped else
+                                   "kda_prefill_chunked (chunk table + intra_kernel + scan_kernel)")}}
+    if two_kernel is not None:
+        out["two_kernel_launch_ms"] = two_kernel
     del P, ws, o, fin
     return out
 
@@ -594,7 +615,8 @@ def run_leg(kda, args, dev):
         name = {"prefill_long": "long", "prefill_c2": "prefill", "prefill_c4": "packed"}[args.leg]
         r = prefill_leg(kda, name, dev, reps=args.steps, warmup=args.warmup, flush=None)
         print(json.dumps({"leg": args.leg, "workload": r["workload"], "ms": r["ms"], "value": r["value"],
-                          "unit": r["unit"]}), flush=True)
+                          "unit": r["unit"], "kernel": r["roofline"]["kernel"],
+                          "two_kernel_launch_ms": r.get("two_kernel_launch_ms")}), flush=True)
         return
     if args.leg == "decode":
         gg = _gen(3, dev)
@@ -614,6 +636,28 @@ def run_leg(kda, args, dev):
         st = stats([a_.elapsed_time(b_) for a_, b_ in evs[args.warmup:]])
         print(json.dumps({"leg": "decode", "workload": "decode_B256_H32_d128", "ms": st,
                           "value": 256 / (st["median"] * 1e-3), "unit": "seq-steps/s"}), flush=True)
+        return
+    if args.leg == "short_conv":   # width 4: the long prefill's q shape, then the decode rows (state in place)
+        g = _gen(7, dev)
+        cw = torch.randn((32 * 128, 4), generator=g, device=dev) / 2
+        cx = torch.randn((1, 131072, 32 * 128), generator=g, device=dev).to(torch.bfloat16)
+        cy = torch.empty_like(cx)
+        cfin = torch.empty((1, 32 * 128, 3), dtype=torch.float32, device=dev)
+        dx = torch.randn((256, 1, 32 * 128), generator=g, device=dev).to(torch.bfloat16)
+        dy = torch.empty_like(dx)
+        dst = torch.zeros((256, 32 * 128, 3), dtype=torch.float32, device=dev)
+        evs = []
+        for i in range(args.warmup + args.steps):
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record()
+            kda.short_conv(cx, cw, final_state=cfin, y=cy)
+            b_.record()
+            kda.short_conv(dx, cw, initial_state=dst, update_state=True, y=dy)
+            evs.append((a_, b_))
+        torch.cuda.synchronize()
+        st = stats([a_.elapsed_time(b_) for a_, b_ in evs[args.warmup:]])
+        print(json.dumps({"leg": "short_conv", "workload": "[1, 131072, 4096] bf16, W=4 (+ [256, 1, 4096] rows)",
+                          "ms": st, "value": 131072 / (st["median"] * 1e-3), "unit": "tokens/s"}), flush=True)
         return
     if args.leg == "decode_multi":   # 4 tokens per sequence per launch, no per-token states
         gg = _gen(3, dev)
@@ -668,7 +712,7 @@ def main():
     ap.add_argument("--record-leg-traffic", nargs=3, metavar=("LEG", "FETCH_DIR", "WRITE_DIR"),
                     help="refresh the traffic.json entries of one --leg's calls from a FETCH_SIZE and a "
                          "WRITE_SIZE rocprofv3 --pmc run of that leg")
-    ap.add_argument("--leg", choices=["prefill_long", "prefill_c2", "prefill_c4", "decode", "decode_multi",
+    ap.add_argument("--leg", choices=["prefill_long", "prefill_c2", "prefill_c4", "decode", "decode_multi", "short_conv",
                                       "backward"],
                     help="run only this workload's calls (warmup + steps), for a per-workload profile")
     ap.add_argument("--summarize", metavar="DIR")
