@@ -151,6 +151,17 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  * 240 KB (d_k = 128) per (chunk, head) whatever the chunk size
  * (chunk_size 16 only while that stays within 4 GiB); larger chunk-16 calls
  * run in fp32 on the vector ALUs.
+ *
+ * On the bf16 matrix-core path, one sequence (num_seqs == 1) whose
+ * inter-chunk scan needs at most 16 workgroups per XCD (ceil(H / 8) *
+ * d_v / 16 <= 16) with chunk_size 64 runs, on a device with 256 CUs, as one
+ * launch in which the scan consumes each chunk's intermediate block as soon
+ * as it is written (Module 04 — KDA II, §2: the per-chunk work is parallel,
+ * only the composition across chunks is sequential).  Results are bitwise
+ * those of the two-kernel launch, which KDA_PREFILL_OVERLAP=0 in the
+ * environment forces.  Its cross-workgroup waits are bounded: a hand-off
+ * that does not complete sets *device_status to KDA_ERR_DEVICE_WAIT and the
+ * call's results are then undefined.
  */
 typedef struct kda_prefill_args {
     int32_t B, T, H, d_k, d_v;
