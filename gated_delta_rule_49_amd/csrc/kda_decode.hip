@@ -993,8 +993,14 @@ hipError_t run_decode(const DecodeParams &p, int B, hipStream_t s) {
         const int G = BH < kDecodeGrid ? BH : kDecodeGrid;
         hipLaunchKernelGGL((decode1_kernel<DK, DV, TI, TO>), dim3(G), block, 0, s, p, BH);
     } else if (p.m >= 2 && p.m <= 4 && !p.token_states) {
+        // one workgroup per CU at these register counts; 3 and 4 tokens per
+        // launch ran faster with one persistent workgroup per CU, 2 tokens
+        // with two rounds of them (B=256, H=32, d=128: m = 4 in 203 against
+        // 207 us, m = 3 in 188 against 190 us, m = 2 in 190 against 200 us;
+        // grids that are not a multiple of 256 leave a partial second round)
         const int BH = B * p.H;
-        const int G = BH < kDecodeGrid ? BH : kDecodeGrid;
+        const int GM = p.m == 2 ? kDecodeGrid : kDecodeGrid / 2;
+        const int G = BH < GM ? BH : GM;
         if (p.m == 2) hipLaunchKernelGGL((decodec_kernel<DK, DV, TI, TO, 2>), dim3(G), block, 0, s, p, BH);
         else if (p.m == 3) hipLaunchKernelGGL((decodec_kernel<DK, DV, TI, TO, 3>), dim3(G), block, 0, s, p, BH);
         else hipLaunchKernelGGL((decodec_kernel<DK, DV, TI, TO, 4>), dim3(G), block, 0, s, p, BH);
