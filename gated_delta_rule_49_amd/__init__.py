@@ -489,14 +489,18 @@ def short_conv(x, weight, initial_state=None, bias=None, cu_seqlens=None, silu=F
 
 
 def backward(q, k, v, beta, log_alpha, d_o, initial_state=None, d_final_state=None, cu_seqlens=None,
-             checkpoints=None, chunk_size=None):
+             checkpoints=None, chunk_size=None, device_status=None):
     """Gradients of the recurrence: (dq, dk, dv, dbeta, dlog_alpha,
     d_initial_state), all float32, from d_o [B,T,H,d_v] fp32 (and
     d_final_state fp32 [N,H,d_k,d_v] or None).  ``checkpoints`` are the
     states entering every chunk of ``chunk_size`` tokens (default 64 for
     bf16 inputs, 16 for fp32); when None they are produced here by a chunked
-    prefill with that chunk size."""
-    dev = _check_dev(q, k, v, beta, log_alpha, d_o, initial_state, d_final_state, cu_seqlens, checkpoints)
+    prefill with that chunk size.  ``device_status`` (int32 [1] on the
+    device, optional) receives the call's device-side status (the
+    workspace's status word, copied on the stream: no synchronisation)."""
+    dev = _check_dev(q, k, v, beta, log_alpha, d_o, initial_state, d_final_state, cu_seqlens, checkpoints,
+                     device_status)
+    _check_buffer(device_status, "device_status", (1,), (torch.int32,))
     if not (q.dtype == k.dtype == v.dtype == beta.dtype == log_alpha.dtype):
         raise TypeError("q, k, v, beta, log_alpha must share one dtype")
     B, T, H, dk = q.shape
@@ -540,4 +544,6 @@ def backward(q, k, v, beta, log_alpha, d_o, initial_state=None, d_final_state=No
     st = L.kda_backward(ctypes.byref(a), _stream(dev))
     if st != 0:
         raise KDAError(st, "kda_backward")
+    if device_status is not None:  # the workspace's first word is the call's status
+        device_status.copy_(ws[:4].view(torch.int32))
     return out["dq"], out["dk"], out["dv"], out["dbeta"], out["dlog_alpha"], out["d_initial_state"]

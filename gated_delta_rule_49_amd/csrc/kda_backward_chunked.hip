@@ -638,7 +638,8 @@ struct CbGradLds {
     static constexpr int AG = BASE;             // dgamma [DK]
     static constexpr int SB = AG + DK;          // beta [C]
     static constexpr int PD = SB + C;           // diagonal of dP [C]
-    static constexpr int FLOATS = PD + C;
+    static constexpr int DBP = PD + C;          // dbeta partial sums [C][4 key blocks]
+    static constexpr int FLOATS = DBP + 4 * C;
 };
 
 __device__ __forceinline__ f32x4 mfma4(float a0, float a1, float a2, float a3, const float4 &b, f32x4 acc) {
@@ -866,7 +867,7 @@ __global__ void __launch_bounds__(CB_GRAD_NT) cb_grad_kernel(CbParams p) {
     float *sGc = lds + Q::GC;
     uint16_t *sk16 = reinterpret_cast<uint16_t *>(sGc + C * DK), *sq16 = sk16 + C * DK;
     float *sT = lds + Q::TA, *Z = lds + Q::ZZ, *sDB = lds + Q::DB, *sM = lds + Q::MM, *sMT = lds + Q::MTT;
-    float *sdP = lds + Q::DP;
+    float *sdP = lds + Q::DP, *sDBP = lds + Q::DBP;
     // dT on and below the diagonal, dP strictly below it with its diagonal
     // apart; the rest is zero
 #pragma unroll
@@ -953,12 +954,16 @@ __global__ void __launch_bounds__(CB_GRAD_NT) cb_grad_kernel(CbParams p) {
             float gs = dA * blk[Y::GH + r * C + i];
 #pragma unroll
             for (int o = 8; o > 0; o >>= 1) gs += __shfl_xor(gs, o);  // over the 16 columns
-            if (n == 0) atomicAdd(&sDB[r], gs);
+            if (n == 0) sDBP[r * 4 + ib] = gs;  // summed below in a fixed order
             sDA[r * LA + i] = dA * sB[r];
         }
     }
     lds_barrier();
-    if (tid < L) p.gbeta[(t0 + tid) * H + h] = sDB[tid];
+    if (tid < L) {  // blocks ib <= the row's own block, in order
+        float db = sDB[tid];
+        for (int ib = 0; ib <= tid / 16; ++ib) db += sDBP[tid * 4 + ib];
+        p.gbeta[(t0 + tid) * H + h] = db;
+    }
     // pair sums over the decay factors, per (row r, channel c):
     //   rowA = sum_{i<r} dGh_ri k_i e^{G_r-G_i}    rowP = sum_{i<r} dP_ri k_i e^{G_r-G_i}
     //   colA = sum_{i>r} dGh_ir k_i e^{G_i-G_r}    colP = sum_{i>r} dP_ir q_i e^{G_i-G_r}

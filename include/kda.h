@@ -369,6 +369,8 @@ kda_status kda_short_conv(const kda_conv_args *a, void *hip_stream);
  * Supported: d_k, d_v in {16, 32, 64, 128}; in_dtype f32 or bf16; with bf16
  * inputs checkpoints and d_o must be 16-byte aligned (KDA_ERR_UNSUPPORTED
  * otherwise).
+ * The first int32 word of the workspace holds the call's device status once
+ * it has run (0, or KDA_ERR_BAD_SEQLENS for malformed cu_seqlens).
  */
 typedef struct kda_backward_args {
     int32_t B, T, H, d_k, d_v;
