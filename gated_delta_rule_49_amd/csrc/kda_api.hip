@@ -159,6 +159,19 @@ bool overlap_enabled(void *hip_stream) {
     return n == 256;
 }
 
+// Bound of the overlapped launch's cross-workgroup waits, in ticks of the
+// device's 100 MHz real-time counter: 1 s, or KDA_PREFILL_WAIT_TICKS from the
+// environment (a small bound makes the waits expire: the failure path's test).
+uint64_t overlap_wait_ticks() {
+    const char *env = std::getenv("KDA_PREFILL_WAIT_TICKS");
+    if (env && *env) {
+        char *end = nullptr;
+        const unsigned long long v = std::strtoull(env, &end, 10);
+        if (end && *end == 0) return v;
+    }
+    return 100000000ull;
+}
+
 // The prefill after host validation, with its scratch at ws (ws_bytes long).
 kda_status prefill_on(const kda_prefill_args *a, char *ws, size_t ws_bytes, void *hip_stream) {
     if (!ws) return KDA_ERR_NULL_ARG;
@@ -186,6 +199,7 @@ kda_status prefill_on(const kda_prefill_args *a, char *ws, size_t ws_bytes, void
     p.n_chunks_bound = static_cast<int32_t>(max_chunks(a));
     p.prologue = a->prologue;
     p.ready = nullptr;
+    p.wait_ticks = overlap_wait_ticks();
     if (overlap_shape(a) && overlap_enabled(hip_stream))
         p.ready = reinterpret_cast<int32_t *>(ws + table_bytes(p.N, p.n_chunks_bound) + mfma_blocks_bytes(a));
 

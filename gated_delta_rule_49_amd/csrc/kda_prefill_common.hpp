@@ -19,6 +19,7 @@ struct PrefillParams {
     int32_t n_chunks_bound;      // grid bound on the total number of chunks
     uint32_t prologue;           // kPro* bits: which inputs are pre-activations
     int32_t *ready;              // device, nullable: role counters and per-(head, chunk) flags of the overlapped launch (workspace)
+    uint64_t wait_ticks;         // bound of the overlapped launch's waits, in 100 MHz real-time ticks
 };
 
 // Token range of sequence n: tokens [start, start + len) of the flattened

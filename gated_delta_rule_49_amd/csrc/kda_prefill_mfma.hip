@@ -308,8 +308,6 @@ constexpr int kReadyTickets = 64;
 
 // Status code of an expired hand-off wait (KDA_ERR_DEVICE_WAIT).
 constexpr int32_t kErrDeviceWait = 8;
-// Bound of a hand-off wait, in ticks of the 100 MHz real-time counter (1 s).
-constexpr uint64_t kReadyWaitTicks = 100000000ull;
 
 __device__ __forceinline__ int xcc_id() {
     return __builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11));  // HW_REG_XCC_ID, bits [3:0]
@@ -334,9 +332,10 @@ __device__ __forceinline__ void report_device_error(const PrefillParams &p, int3
 // chunk j is; each poll reads the flags of the next 64 chunks at once (one
 // per lane), so a reader behind its writers polls once per 64 chunks.
 // Bounded: once the call's status word holds an error, or after
-// kReadyWaitTicks without progress, ensure returns anyway (recording
-// kErrDeviceWait), so every wave still runs to its end; the call's results
-// are then undefined and its status says so.  Uniform per wave.
+// p.wait_ticks of the 100 MHz real-time counter without progress, ensure
+// returns anyway (recording kErrDeviceWait), so every wave still runs to its
+// end; the call's results are then undefined and its status says so.
+// Uniform per wave.
 struct ReadyView {
     const int32_t *flags;
     int nch, known, xcc;
@@ -360,7 +359,7 @@ struct ReadyView {
                 known = nch;
                 return;
             }
-            if (__builtin_amdgcn_s_memrealtime() - t0 > kReadyWaitTicks) {
+            if (__builtin_amdgcn_s_memrealtime() - t0 > p.wait_ticks) {
                 report_device_error(p, kErrDeviceWait);
                 known = nch;
                 return;

@@ -159,9 +159,11 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  * as it is written (Module 04 — KDA II, §2: the per-chunk work is parallel,
  * only the composition across chunks is sequential).  Results are bitwise
  * those of the two-kernel launch, which KDA_PREFILL_OVERLAP=0 in the
- * environment forces.  Its cross-workgroup waits are bounded: a hand-off
- * that does not complete sets *device_status to KDA_ERR_DEVICE_WAIT and the
- * call's results are then undefined.
+ * environment forces.  Its cross-workgroup waits are bounded (1 s, or
+ * KDA_PREFILL_WAIT_TICKS ticks of the device's 100 MHz real-time counter
+ * from the environment, for tests of this path): a hand-off that does not
+ * complete sets *device_status to KDA_ERR_DEVICE_WAIT, every kernel still
+ * runs to its end, and the call's results are undefined.
  */
 typedef struct kda_prefill_args {
     int32_t B, T, H, d_k, d_v;

@@ -94,3 +94,24 @@ def test_overlapped_launch_under_every_xcd_rotation():
         assert got[3] == 0, (shift, got[3])
         for u, w in zip(got[:3], ref[:3]):
             assert torch.equal(u, w), shift
+
+
+def test_expired_wait_reports_and_the_next_call_recovers():
+    """The failure path of the hand-off, forced from the host: with a wait
+    bound of 0 ticks the scan workgroups give up at their first unpublished
+    block (every block takes microseconds to produce), so the call records
+    KDA_ERR_DEVICE_WAIT (8) and still completes; the next call, with the
+    normal bound, clears the status and gives the two-kernel launch's
+    bits."""
+    x = synth.make_uniform(810, 1, 1024, 16, 128, 128, "bf16", chunk=64, state_std=0.1)
+    ref = _run(False, x)
+    os.environ["KDA_PREFILL_WAIT_TICKS"] = "0"
+    try:
+        bad = _run(True, x)
+    finally:
+        del os.environ["KDA_PREFILL_WAIT_TICKS"]
+    assert bad[3] == 8, bad[3]
+    good = _run(True, x)
+    assert good[3] == 0
+    for u, w in zip(good[:3], ref[:3]):
+        assert torch.equal(u, w)
