@@ -32,7 +32,7 @@ Prints ONE JSON line:
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload long|prefill|packed] [--no-cpu-baseline]
-       python bench.py --leg prefill_long|prefill_c2|prefill_c4|decode|decode_multi|short_conv|backward
+       python bench.py --leg prefill_long|prefill_c2|prefill_c4|prefill_f32|decode|decode_multi|short_conv|backward
                        [--steps K] [--warmup W]
                        only that workload's calls (one rocprofv3 trace per workload)
        python bench.py --summarize DIR    per-kernel means of a rocprofv3 CSV run
@@ -82,10 +82,10 @@ def chunk_flops_per_token_head(C=64, d=128):
 # Kernel sources behind each measured call: a recorded counter stays valid
 # only while its group's sources (and the shared device headers) are unchanged.
 SOURCE_GROUPS = {
-    "prefill": ["kda_prefill_mfma.hip", "kda_prefill_table.hip"],
+    "prefill": ["kda_prefill_mfma.hip", "kda_prefill_table.hip", "kda_handoff.hpp"],
     "decode": ["kda_decode.hip"],
     "short_conv": ["kda_conv.hip"],
-    "backward": ["kda_backward_chunked.hip", "kda_prefill_table.hip", "kda_chunk_block.hpp"],
+    "backward": ["kda_backward_chunked.hip", "kda_prefill_table.hip", "kda_chunk_block.hpp", "kda_chunk_prep.hpp"],
 }
 SHARED_HEADERS = ["kda_common.hpp", "kda_prefill_common.hpp", "kda_launch.hpp"]
 # call key in profiles/traffic.json -> source group
@@ -611,7 +611,7 @@ def run_leg(kda, args, dev):
     per-kernel averages are per-call figures of that workload."""
     import torch
     from synth.kda_inputs import _draw_tokens, _gen, _state
-    if args.leg.startswith("prefill"):
+    if args.leg in ("prefill_long", "prefill_c2", "prefill_c4"):
         name = {"prefill_long": "long", "prefill_c2": "prefill", "prefill_c4": "packed"}[args.leg]
         r = prefill_leg(kda, name, dev, reps=args.steps, warmup=args.warmup, flush=None)
         print(json.dumps({"leg": args.leg, "workload": r["workload"], "ms": r["ms"], "value": r["value"],
@@ -680,6 +680,23 @@ def run_leg(kda, args, dev):
         return
     import synth
     BX = synth.workload(2, device=dev)
+    if args.leg == "prefill_f32":   # the T=4096, H=16 prefill shape with fp32 inputs, chunk 64
+        ft = lambda a: torch.from_numpy(a).to(dev, torch.float32)  # noqa: E731
+        fq, fk, fv, fb, fla = (ft(a) for a in (BX.q, BX.k, BX.v, BX.beta, BX.log_alpha))
+        fo = torch.empty_like(fv)
+        ffin = torch.empty((1, BX.H, 128, 128), dtype=torch.float32, device=dev)
+        evs = []
+        for i in range(args.warmup + args.steps):
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record()
+            kda.prefill(fq, fk, fv, fb, fla, chunk_size=64, o=fo, final_state=ffin)
+            b_.record()
+            evs.append((a_, b_))
+        torch.cuda.synchronize()
+        st = stats([a_.elapsed_time(b_) for a_, b_ in evs[args.warmup:]])
+        print(json.dumps({"leg": "prefill_f32", "workload": "prefill shape B=1 T=4096 H=16 d=128, fp32 inputs",
+                          "ms": st, "value": BX.T / (st["median"] * 1e-3), "unit": "tokens/s"}), flush=True)
+        return
     bt = lambda a: torch.from_numpy(a).to(dev, torch.bfloat16)  # noqa: E731
     bq, bk, bv, bb, bla = (bt(a) for a in (BX.q, BX.k, BX.v, BX.beta, BX.log_alpha))
     bdo = torch.randn(bv.shape, generator=_gen(9, dev), device=dev)
@@ -712,7 +729,8 @@ def main():
     ap.add_argument("--record-leg-traffic", nargs=3, metavar=("LEG", "FETCH_DIR", "WRITE_DIR"),
                     help="refresh the traffic.json entries of one --leg's calls from a FETCH_SIZE and a "
                          "WRITE_SIZE rocprofv3 --pmc run of that leg")
-    ap.add_argument("--leg", choices=["prefill_long", "prefill_c2", "prefill_c4", "decode", "decode_multi", "short_conv",
+    ap.add_argument("--leg", choices=["prefill_long", "prefill_c2", "prefill_c4", "prefill_f32", "decode",
+                                      "decode_multi", "short_conv",
                                       "backward"],
                     help="run only this workload's calls (warmup + steps), for a per-workload profile")
     ap.add_argument("--summarize", metavar="DIR")
@@ -981,23 +999,38 @@ def main():
     fq, fk, fv, fb, fla = (ft(a) for a in (BX.q, BX.k, BX.v, BX.beta, BX.log_alpha))
     fo = torch.empty_like(fv)
     ffin = torch.empty((1, bH, 128, 128), dtype=torch.float32, device=dev)
-    for _ in range(2):
-        kda.prefill(fq, fk, fv, fb, fla, chunk_size=64, o=fo, final_state=ffin)
-    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    f0.record()
-    for _ in range(5):
-        kda.prefill(fq, fk, fv, fb, fla, chunk_size=64, o=fo, final_state=ffin)
-    f1.record()
-    torch.cuda.synchronize()
-    f_ms = f0.elapsed_time(f1) / 5
+    def f32_avg_ms():
+        for _ in range(2):
+            kda.prefill(fq, fk, fv, fb, fla, chunk_size=64, o=fo, final_state=ffin)
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record()
+        for _ in range(5):
+            kda.prefill(fq, fk, fv, fb, fla, chunk_size=64, o=fo, final_state=ffin)
+        f1.record()
+        torch.cuda.synchronize()
+        return f0.elapsed_time(f1) / 5
+    f_ms = f32_avg_ms()
+    # one sequence, 16 heads: the library overlaps the two stages in one
+    # launch; the two-kernel launch is timed beside it
+    saved = os.environ.get("KDA_PREFILL_OVERLAP")
+    os.environ["KDA_PREFILL_OVERLAP"] = "0"
+    try:
+        f_two_ms = f32_avg_ms()
+    finally:
+        if saved is None:
+            del os.environ["KDA_PREFILL_OVERLAP"]
+        else:
+            os.environ["KDA_PREFILL_OVERLAP"] = saved
     f_tf = bT * bH * chunk_flops_per_token_head(64, 128) / (f_ms * 1e-3) / 1e12
     prefill_f32 = {"value": bT / (f_ms * 1e-3), "unit": "tokens/s", "avg_ms": f_ms,
+                   "two_kernel_launch_avg_ms": f_two_ms,
                    "workload": f"prefill shape B=1 T={bT} H={bH} d=128, fp32 inputs, chunk 64",
                    "roofline": {"bound": "mfma", "achieved": f_tf, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
                                 "frac": f_tf / FP32_PEAK_TFLOPS,
                                 "basis": "useful chunked-form flops (10 C d + 6 d^2 per token-head) against "
                                          "the fp32 matrix-core peak",
-                                "kernel": "cb_prep_kernel (forward mode) + f32mm_scan_kernel"}}
+                                "kernel": "chunk table + f32mm_overlap_kernel (chunk prep and fp32 scan in one "
+                                          "launch; two-kernel launch: cb_prep_kernel + f32mm_scan_kernel)"}}
     del fq, fk, fv, fb, fla, fo, ffin, BX
 
     rng = range(args.warmup, n_ev)

@@ -78,14 +78,26 @@ size_t mfma_blocks_bytes(const kda_prefill_args *a) {
     return static_cast<size_t>(max_chunks(a)) * a->H * mfma_block_bytes(a->chunk_size, a->d_k);
 }
 
+// fp32 inputs on the fp32 matrix cores: shapes whose prep and scan may run
+// as one overlapped launch
+bool f32_overlap_shape(const kda_prefill_args *a) {
+    return use_f32mm(a) && a->in_dtype == KDA_F32 && f32mm_overlap_shape(a->num_seqs, a->H, a->d_k, a->d_v);
+}
+
+size_t f32mm_blocks_bytes(const kda_prefill_args *a) {
+    return static_cast<size_t>(max_chunks(a)) * a->H * cb_block_bytes(a->d_k);
+}
+
 size_t workspace_for(const kda_prefill_args *a) {
     size_t bytes = table_bytes(a->num_seqs, max_chunks(a));
     if (use_mfma(a)) {
         bytes += mfma_blocks_bytes(a);
         if (overlap_shape(a)) bytes += mfma_ready_bytes(max_chunks(a), a->H);
     }
-    else if (use_f32mm(a))
-        bytes += static_cast<size_t>(max_chunks(a)) * a->H * cb_block_bytes(a->d_k);
+    else if (use_f32mm(a)) {
+        bytes += f32mm_blocks_bytes(a);
+        if (f32_overlap_shape(a)) bytes += mfma_ready_bytes(max_chunks(a), a->H);
+    }
     return bytes;
 }
 
@@ -202,6 +214,8 @@ kda_status prefill_on(const kda_prefill_args *a, char *ws, size_t ws_bytes, void
     p.wait_ticks = overlap_wait_ticks();
     if (overlap_shape(a) && overlap_enabled(hip_stream))
         p.ready = reinterpret_cast<int32_t *>(ws + table_bytes(p.N, p.n_chunks_bound) + mfma_blocks_bytes(a));
+    else if (f32_overlap_shape(a) && overlap_enabled(hip_stream))
+        p.ready = reinterpret_cast<int32_t *>(ws + table_bytes(p.N, p.n_chunks_bound) + f32mm_blocks_bytes(a));
 
     if (p.N == 0) return KDA_OK;
     hipEvent_t *ev = static_cast<hipEvent_t *>(a->timing_events);

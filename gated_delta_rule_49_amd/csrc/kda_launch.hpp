@@ -92,6 +92,10 @@ hipError_t launch_chunk_prep_fwd(const CbParams &p, int n_items, int in_dtype, h
 // fp32 matrix-core prefill: chunk prep (with the prologue, if any), then
 // the forward scan; blocks = n_chunks_bound x H prep blocks
 bool f32mm_supported(int dk, int dv, int C, uint32_t prologue);
+// shapes the overlapped fp32 prefill takes (one sequence, d_k = 128, at most
+// 16 scan workgroups per XCD; fp32 inputs); its counters and flags take
+// mfma_ready_bytes(chunks, H) after the blocks
+bool f32mm_overlap_shape(int N, int H, int dk, int dv);
 hipError_t launch_prefill_f32mm(const PrefillParams &p, float *blocks, int in_dtype, int out_dtype, hipStream_t s,
                                 hipEvent_t mid);
 

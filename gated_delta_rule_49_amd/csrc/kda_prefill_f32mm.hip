@@ -14,6 +14,8 @@
 // fused prologue) writes K~, Q~, K^, g, beta, P and M per (chunk, head); the scan below walks each sequence's
 // chunks in order, one workgroup per (sequence, head, 16-column tile of S).
 #include "kda_chunk_block.hpp"
+#include "kda_chunk_prep.hpp"
+#include "kda_handoff.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
@@ -80,24 +82,21 @@ struct F32ScanOps {
     }
 };
 
+// The scan of one (sequence, head) pair's 16-column state tile vt; 4 waves.
 // Wave w computes token block w of X, Delta and O and owns key blocks
 // w, w + 4 of the state (accumulator layout, for the whole sequence).  S, X
 // and Delta pass between the waves through LDS transposed ([column][row]),
-// so a lane's four contraction values are one 16-byte read.
-template <int DK, typename TI, typename TO>
-__global__ void __launch_bounds__(256) f32mm_scan_kernel(PrefillParams p, const float *__restrict__ blocks) {
-    if (*p.status != 0) return;
+// so a lane's four contraction values are one 16-byte read.  WAIT (the
+// overlapped launch, one sequence): a block's first load waits until its
+// flag is set.
+template <int DK, typename TI, typename TO, bool WAIT>
+__device__ __forceinline__ void f32mm_scan_run(const PrefillParams &p, const float *__restrict__ blocks, int pair,
+                                               int vt, const int32_t *ready, int xcc) {
     using Y = CbLay<DK>;
     using Ops = F32ScanOps<DK, TI>;
     constexpr int C = CB_C, NKB = Ops::NKB, KPW = Ops::KPW;
     constexpr int LC = C + 4, LK = DK + 4;  // padded strides of the [column][row] tiles
     const int H = p.H, dv = p.dv;
-    const int nvt = dv / 16;
-    // XCD-aware order: the column tiles of one (sequence, head) share
-    // blockIdx % 8, hence one XCD and its L2, where their chunk blocks are
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int vt = slot % nvt, pair = xcd + 8 * (slot / nvt);
-    if (pair >= p.N * H) return;
     const int h = pair % H, n_seq = pair / H;
     const int j0 = 16 * vt;
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -128,7 +127,9 @@ __global__ void __launch_bounds__(256) f32mm_scan_kernel(PrefillParams p, const 
     auto len_of = [&](int ch) { return min(p.C, sr.len - ch * p.C); };
     auto t0_of = [&](int ch) { return sr.start + static_cast<int64_t>(ch) * p.C; };
     Ops op;
+    ReadyView rv{WAIT ? ready + ready_index(p, 0, h) : nullptr, nch, WAIT ? 0 : nch, xcc};
     if (nch > 0) {
+        if (WAIT) rv.ensure(0, p);
         op.load1(blk_of(0), v, t0_of(0), len_of(0), H, h, dv, j0, w, g, n);
         op.load23(blk_of(0), w, g, n);
         op.load4(blk_of(0), w, g, n);
@@ -168,6 +169,7 @@ __global__ void __launch_bounds__(256) f32mm_scan_kernel(PrefillParams p, const 
 #pragma unroll
         for (int u = 0; u < 4; ++u) xv[u] = op.vv[u] - xa[u];
         if (live) *reinterpret_cast<f32x4 *>(&xT[n][r0 + 4 * g]) = xv;
+        if (WAIT) rv.ensure(nx, p);
         op.load1(blk_of(nx), v, t0_of(nx), len_of(nx), H, h, dv, j0, w, g, n);
         __syncthreads();
         // (2) token block w: Delta = M Diag(beta) X (M lower triangular)
@@ -220,6 +222,67 @@ __global__ void __launch_bounds__(256) f32mm_scan_kernel(PrefillParams p, const 
         }
 }
 
+template <int DK, typename TI, typename TO>
+__global__ void __launch_bounds__(256) f32mm_scan_kernel(PrefillParams p, const float *__restrict__ blocks) {
+    if (*p.status != 0) return;
+    // XCD-aware order: the column tiles of one (sequence, head) share
+    // blockIdx % 8, hence one XCD and its L2, where their chunk blocks are
+    const int nvt = p.dv / 16;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int vt = slot % nvt, pair = xcd + 8 * (slot / nvt);
+    if (pair >= p.N * p.H) return;
+    f32mm_scan_run<DK, TI, TO, false>(p, blocks, pair, vt, nullptr, 0);
+}
+
+// ---------------------------------------------------- overlapped launch --
+// One sequence whose scan would leave most CUs idle (at most
+// kF32OverlapScanSlots column-tile workgroups per XCD; d_k = 128): the
+// chunk prep and the scan run in one launch of 8 x kF32OverlapSlots
+// workgroups, one per CU, with the roles of the bf16 path's overlapped
+// launch (kda_prefill_mfma.hip): a workgroup takes the next ticket of the
+// XCD it runs on; the first SI tickets prepare the chunks of the heads
+// h = x + 8j in chunk order, flagging each block once its stores have
+// completed, and the next ones run those heads' scans, each block read as
+// soon as its flag is set.  Producers never wait and hold the first tickets,
+// so every wait ends; a workgroup finding its XCD's roles all taken records
+// KDA_ERR_DEVICE_WAIT.  The two bodies' static LDS (prep and scan) fit
+// one CU together.
+constexpr int kF32OverlapSlots = 32;
+constexpr int kF32OverlapScanSlots = 16;
+
+template <typename TO>
+__global__ void __launch_bounds__(256) f32mm_overlap_kernel(PrefillParams p, CbParams c,
+                                                            const float *__restrict__ blocks) {
+    constexpr int DK = 128;
+    __shared__ int s_slot;
+    if (*p.status != 0) return;
+    const int x = xcc_id();
+    if (threadIdx.x == 0)
+        s_slot = __hip_atomic_fetch_add(p.ready + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int slot = s_slot;
+    if (slot >= kF32OverlapSlots) {
+        if (threadIdx.x == 0) report_device_error(p, kErrDeviceWait);
+        return;
+    }
+    const int H = p.H, nvt = p.dv / 16;
+    const int npx = x < H ? (H - x + 7) / 8 : 0;
+    const int si = kF32OverlapSlots - npx * nvt;
+    if (slot < si) {
+        const int total = npx * p.chunk_off[1];
+        for (int k = slot; k < total; k += si) {
+            const int xc = k / npx, h = x + 8 * (k % npx);
+            cb_prep_run<DK, float, true>(c, xc, h);
+            wait_memory();
+            __syncthreads();  // every thread's stores have completed; the LDS is free
+            if (threadIdx.x == 0) publish_ready(p.ready + ready_index(p, xc, h), x);
+        }
+    } else {
+        const int s = slot - si;
+        f32mm_scan_run<DK, float, TO, true>(p, blocks, x + 8 * (s / nvt), s % nvt, p.ready, x);
+    }
+}
+
 namespace {
 
 template <int DK, typename TI>
@@ -245,6 +308,10 @@ hipError_t run_scan_dk(const PrefillParams &p, const float *blocks, int out_dtyp
 
 }  // namespace
 
+bool f32mm_overlap_shape(int N, int H, int dk, int dv) {
+    return N == 1 && dk == 128 && (H + 7) / 8 * (dv / 16) <= kF32OverlapScanSlots;
+}
+
 bool f32mm_supported(int dk, int dv, int C, uint32_t prologue) {
     const bool dim = [](int d) { return d == 16 || d == 32 || d == 64 || d == 128; }(dk);
     return dim && dv % 16 == 0 && dv >= 16 && dv <= 128 && (C == 16 || C == 32 || C == 64);
@@ -260,6 +327,17 @@ hipError_t launch_prefill_f32mm(const PrefillParams &p, float *blocks, int in_dt
     c.status = p.status;
     c.N = p.N; c.H = p.H; c.dk = p.dk; c.dv = p.dv;
     c.prologue = p.prologue;
+    if (p.ready && p.dk == 128 && in_dtype == 0) {  // the overlapped launch (fp32 inputs)
+        if (out_dtype == 0)
+            hipLaunchKernelGGL((f32mm_overlap_kernel<float>), dim3(8 * kF32OverlapSlots), dim3(256), 0, s, p, c,
+                               static_cast<const float *>(blocks));
+        else
+            hipLaunchKernelGGL((f32mm_overlap_kernel<bf16_t>), dim3(8 * kF32OverlapSlots), dim3(256), 0, s, p, c,
+                               static_cast<const float *>(blocks));
+        hipError_t e = hipGetLastError();
+        if (e == hipSuccess && mid) e = hipEventRecord(mid, s);
+        return e;
+    }
     hipError_t e = launch_chunk_prep_fwd(c, p.n_chunks_bound * p.H, in_dtype, s);
     if (e == hipSuccess && mid) e = hipEventRecord(mid, s);
     if (e != hipSuccess) return e;

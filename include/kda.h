@@ -157,9 +157,11 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  * d_v / 16 <= 16) with chunk_size 64 runs, on a device with 256 CUs, as one
  * launch in which the scan consumes each chunk's intermediate block as soon
  * as it is written (Module 04 — KDA II, §2: the per-chunk work is parallel,
- * only the composition across chunks is sequential).  Results are bitwise
- * those of the two-kernel launch, which KDA_PREFILL_OVERLAP=0 in the
- * environment forces.  Its cross-workgroup waits are bounded (1 s, or
+ * only the composition across chunks is sequential).  fp32 inputs with
+ * d_k = 128 on the fp32 matrix-core path (any chunk size) overlap the same
+ * way when one sequence's scan needs at most 16 workgroups per XCD.
+ * Results are bitwise those of the two-kernel launch, which
+ * KDA_PREFILL_OVERLAP=0 in the environment forces.  Its cross-workgroup waits are bounded (1 s, or
  * KDA_PREFILL_WAIT_TICKS ticks of the device's 100 MHz real-time counter
  * from the environment, for tests of this path): a hand-off that does not
  * complete sets *device_status to KDA_ERR_DEVICE_WAIT, every kernel still

@@ -10,7 +10,8 @@ outputs, final states and chunk-entry states must be bitwise equal to the
 two-kernel launch's (forced with KDA_PREFILL_OVERLAP=0), and the device
 status must stay 0.  The oracle comparisons of the single-sequence bf16
 tests in test_prefill_gpu.py (the T=4096, H=16 workload among them) run on
-this launch as well."""
+this launch as well.  With fp32 inputs and d_k = 128 the fp32 path
+overlaps its chunk prep and scan the same way (the last cases)."""
 import os
 
 import pytest
@@ -23,14 +24,14 @@ from kda_testutil import dev_tensors
 pytestmark = pytest.mark.gpu
 
 
-def _run(overlap, x, prologue=0, out_dtype=torch.float32):
+def _run(overlap, x, prologue=0, out_dtype=torch.float32, chunk=64):
     q, k, v, b, la, init, _ = dev_tensors(x)
     saved = os.environ.get("KDA_PREFILL_OVERLAP")
     os.environ["KDA_PREFILL_OVERLAP"] = "1" if overlap else "0"
     try:
         status = torch.full((1,), -1, dtype=torch.int32, device=q.device)
         o, S, cs = kda.prefill(q, k, v, b, la, initial_state=init, chunk_states=True, out_dtype=out_dtype,
-                               prologue=prologue, device_status=status)
+                               prologue=prologue, device_status=status, chunk_size=chunk)
         torch.cuda.synchronize()
     finally:
         if saved is None:
@@ -115,3 +116,24 @@ def test_expired_wait_reports_and_the_next_call_recovers():
     assert good[3] == 0
     for u, w in zip(good[:3], ref[:3]):
         assert torch.equal(u, w)
+
+
+# fp32 inputs (the 1e-5 contract, fp32 matrix cores): with d_k = 128 the
+# chunk prep and the fp32 scan overlap the same way, at every chunk size
+F32_CASES = [(811, 4096, 16, 64, torch.float32, 0), (812, 1000, 3, 64, torch.bfloat16, 0),
+             (813, 130, 11, 64, torch.float32, 0), (814, 1500, 16, 64, torch.float32, 7),
+             (815, 999, 5, 32, torch.float32, 0), (816, 777, 16, 16, torch.float32, 0)]
+
+
+@pytest.mark.parametrize("seed,T,H,C,odt,pro", F32_CASES)
+def test_overlapped_fp32_launch_equals_two_kernel_launch(seed, T, H, C, odt, pro):
+    if pro:
+        x = synth.make_preact(seed, 1, T, H, 128, 128, "f32", chunk=C, state_std=0.1, prologue=pro)
+    else:
+        x = synth.make_uniform(seed, 1, T, H, 128, 128, "f32", chunk=C, state_std=0.1)
+    a = _run(True, x, pro, odt, C)
+    b = _run(False, x, pro, odt, C)
+    assert a[3] == 0 and b[3] == 0, (a[3], b[3])
+    for name, u, w in zip(("o", "final state", "chunk states"), a[:3], b[:3]):
+        assert torch.equal(u, w), name
+    print(f"[overlap fp32] T={T} H={H} C={C}: bitwise equal to the two-kernel launch", flush=True)
