@@ -94,7 +94,7 @@ CALL_GROUPS = {"prefill_long": "prefill", "decode": "decode", "decode_multi_m4":
                "backward_T4096_H16": "backward"}
 # kernels of each call key, as rocprofv3 names them (without namespace, spaces and arguments)
 CALL_KERNELS = {
-    "prefill_long": ["intra_kernel<64,128>", "scan_kernel<64,128,float>", "chunk_table_kernel"],
+    "prefill_long": ["intra_kernel<64,128>", "scan_kernel<64,128,float,1>", "chunk_table_kernel"],
     "decode": ["decode1_kernel<128,128,unsignedshort,float>"],
     "decode_multi_m4": ["decodec_kernel<128,128,unsignedshort,float,4>"],
     "short_conv_prefill": ["short_conv_kernel<unsignedshort,unsignedshort,4,16>", "conv_state_kernel<unsignedshort,4>"],
@@ -197,7 +197,7 @@ def record_traffic(fetch_dir, write_dir, sq_dir, cal_fetch_dir, cal_write_dir, m
         out_calls[key] = {"fetch_kib": sum(v[0] for v in per.values()),
                           "write_kib": sum(v[1] for v in per.values()), "kernels": per}
     counters = {}
-    for k in ("intra_kernel<64,128>", "scan_kernel<64,128,float>"):
+    for k in ("intra_kernel<64,128>", "scan_kernel<64,128,float,1>"):
         counters[k] = {c: mean(acc, k, c, calls) for (kk, c) in acc
                        if kk == k and (c.startswith("SQ_") or c == "GRBM_GUI_ACTIVE")}
     rec = {"what": "HBM bytes per call = FETCH_SIZE KiB * 1024 * fetch_scale + WRITE_SIZE KiB * 1024 * "
@@ -232,7 +232,7 @@ def record_prefill_traffic(fetch_dir, write_dir, sq_dir, mfma_dir, calls):
         v = v[:calls]
         return sum(v) / len(v)
 
-    ks = ["intra_kernel<64,128>", "scan_kernel<64,128,float>", "chunk_table_kernel"]
+    ks = ["intra_kernel<64,128>", "scan_kernel<64,128,float,1>", "chunk_table_kernel"]
     per = {k: [mean(k, "FETCH_SIZE"), mean(k, "WRITE_SIZE")] for k in ks}
     rec["calls"]["prefill_long"] = {"fetch_kib": sum(v[0] for v in per.values()),
                                     "write_kib": sum(v[1] for v in per.values()), "kernels": per}
@@ -575,7 +575,7 @@ def mfma_busy(kernel_ms):
     8 XCDs / 8), and the MFMA flops issued (SQ_INSTS_VALU_MFMA_MOPS_* x 512)
     per live kernel time; null when the record does not match the sources."""
     out = {}
-    for name, key in (("intra_kernel", "intra_kernel<64,128>"), ("scan_kernel", "scan_kernel<64,128,float>")):
+    for name, key in (("intra_kernel", "intra_kernel<64,128>"), ("scan_kernel", "scan_kernel<64,128,float,1>")):
         busy = measured_counter(key, "SQ_VALU_MFMA_BUSY_CYCLES")
         active = measured_counter(key, "GRBM_GUI_ACTIVE")
         if busy is None or active is None:

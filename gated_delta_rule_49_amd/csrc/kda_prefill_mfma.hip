@@ -899,11 +899,14 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
 
 // ------------------------------------------------------------------ K2 --
 // One wave's operands for one chunk, read from the chunk's workspace block in
-// MFMA register order as 128-bit register tuples.  Wave w owns state rows
-// [32w, 32w + 32): channel k-step w of the W S and (q e^G) S products and
-// channel tiles 2w, 2w + 1 of the state update; it also finishes the output
-// token tiles w, w + D/32, ...
-template <int C, int D>
+// MFMA register order as 128-bit register tuples.  A workgroup owns NT
+// adjacent 16-column state tiles of one head (columns [16 NT g, 16 NT g +
+// 16 NT) for tile group g); wave w owns state rows [32w, 32w + 32) of each:
+// channel k-step w of the W S and (q e^G) S products and channel tiles 2w,
+// 2w + 1 of the state update; it also finishes the output token tiles w,
+// w + D/32, ...  The W, q e^G, k e^{G_L-G} and P operands are shared by the
+// NT tiles (loaded once); U is per tile.
+template <int C, int D, int NT = 1>
 struct ScanOps {
     using Y = Lay<C, D>;
     static constexpr int NW = D / 32;
@@ -912,12 +915,13 @@ struct ScanOps {
     u32x4 w[Y::NMT], qh[Y::NMT], ql[Y::NMT];   // token tile mt, channel step = wave
     u32x4 kh[2][Y::KSC], kl[2][Y::KSC];       // the wave's two channel tiles x token steps
     u32x4 ph[OWN][Y::KSC], pl[OWN][Y::KSC];   // owned token tiles x token steps
-    f32x4 u[OWN];                             // owned token tiles, this column tile
+    f32x4 u[NT][OWN];                         // the group's column tiles x owned token tiles
     f32x4 gam[2];
 
-    // blk: the chunk's block (uniform); lane16 = 16 * lane.  Four parts, so
-    // that the requests can be spread over the previous chunk's computation.
-    __device__ __forceinline__ void load(int part, const char *blk, uint32_t lane16, int wv, int nt, int g) {
+    // blk: the chunk's block (uniform); lane16 = 16 * lane; ng: tile group.
+    // Four parts, so that the requests can be spread over the previous
+    // chunk's computation.
+    __device__ __forceinline__ void load(int part, const char *blk, uint32_t lane16, int wv, int ng, int g) {
         auto at = [&](size_t off) { return reinterpret_cast<const u32x4 *>(blk + off + lane16); };
         if (part == 0) {
 #pragma unroll
@@ -929,11 +933,14 @@ struct ScanOps {
             }
         } else if (part == 1) {
 #pragma unroll
-            for (int uu = 0; uu < OWN; ++uu) {
-                const int mt = wv + uu * NW;
-                if (mt >= Y::NMT) continue;
-                u[uu] = __builtin_bit_cast(f32x4, *at(Y::U + (static_cast<size_t>(mt) * Y::NDT + nt) * Y::FRAG));
-            }
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int uu = 0; uu < OWN; ++uu) {
+                    const int mt = wv + uu * NW;
+                    if (mt >= Y::NMT) continue;
+                    u[j][uu] = __builtin_bit_cast(
+                        f32x4, *at(Y::U + (static_cast<size_t>(mt) * Y::NDT + NT * ng + j) * Y::FRAG));
+                }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
                 gam[i] = *reinterpret_cast<const f32x4 *>(blk + Y::GAM + (32 * wv + 16 * i + 4 * g) * sizeof(float));
@@ -961,140 +968,152 @@ struct ScanOps {
             }
         }
     }
-    __device__ __forceinline__ void load(const char *blk, uint32_t lane16, int wv, int nt, int g) {
+    __device__ __forceinline__ void load(const char *blk, uint32_t lane16, int wv, int ng, int g) {
 #pragma unroll
-        for (int part = 0; part < 4; ++part) load(part, blk, lane16, wv, nt, g);
+        for (int part = 0; part < 4; ++part) load(part, blk, lane16, wv, ng, g);
     }
 };
 
-template <int C, int D>
+template <int C, int D, int NT = 1>
 struct ScanShared {
     using Y = Lay<C, D>;
-    f32x4 red[2][D / 32][Y::NMT][64];
-    uint4 dls[Y::NMT][64];
+    f32x4 red[NT][2][D / 32][Y::NMT][64];
+    uint4 dls[NT][Y::NMT][64];
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const ScanOps<64, 128>::u32x4 &u) { return __builtin_bit_cast(bf16x8, u); }
 
 // One chunk of the scan for one wave: consumes the operands in `op` and
-// updates the state tiles S in place.
+// updates the state tiles S (one pair per column tile of the group) in place.
 // The next chunk's operands are requested into `nx` in four parts between
 // the phases, so that the transfers overlap this chunk's computation.
 // gate() runs before the first load of the next block (the overlapped
 // launch waits there until that block is published).
-template <int C, int D, typename TO, typename Gate>
-__device__ __forceinline__ void scan_chunk(const ScanOps<C, D> &op, ScanOps<C, D> &nx, const char *nblk,
-                                           uint32_t lane16, f32x4 (&S)[2], ScanShared<C, D> &sh,
+template <int C, int D, typename TO, int NT, typename Gate>
+__device__ __forceinline__ void scan_chunk(const ScanOps<C, D, NT> &op, ScanOps<C, D, NT> &nx, const char *nblk,
+                                           uint32_t lane16, f32x4 (&S)[NT][2], ScanShared<C, D, NT> &sh,
                                            const PrefillParams &p, int64_t x, int64_t t0, int L, int h, int w,
-                                           int nt, int lane, Gate &&gate) {
+                                           int ng, int lane, Gate &&gate) {
     using Y = Lay<C, D>;
     constexpr int NW = D / 32;
-    constexpr int OWN = ScanOps<C, D>::OWN;
+    constexpr int OWN = ScanOps<C, D, NT>::OWN;
     const int g = lane >> 4, li = lane & 15;
-    const int col = 16 * nt + li;
+    const int col0 = 16 * NT * ng + li;   // column of tile j: col0 + 16 j
     const int H = p.H;
     if (p.chunk_states) {
         float *cs = p.chunk_states + (x * H + h) * static_cast<int64_t>(D) * D;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int jt = 0; jt < NT; ++jt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) cs[static_cast<int64_t>(32 * w + 16 * i + 4 * g + j) * D + col] = S[i][j];
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    cs[static_cast<int64_t>(32 * w + 16 * i + 4 * g + j) * D + col0 + 16 * jt] = S[jt][i][j];
     }
-    // (a) this wave's state rows as a B operand, hi/lo
-    frag8 sh_, sl_;
-    acc2_to_split(S[0], S[1], sh_, sl_);
-    // (b) partial W S (W and S both rounded to bf16: the product only reaches
-    //     the outputs through Delta's first-order term) and (q e^G) S over this
-    //     wave's 32 channels
 #pragma unroll
-    for (int mt = 0; mt < Y::NMT; ++mt) {
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        sh.red[0][w][mt][lane] = mfma16(as_bf16x8(op.w[mt]), sh_.v, z);
-        f32x4 pq = mfma16(as_bf16x8(op.qh[mt]), sh_.v, z);
-        pq = mfma16(as_bf16x8(op.qh[mt]), sl_.v, pq);
-        pq = mfma16(as_bf16x8(op.ql[mt]), sh_.v, pq);
-        sh.red[1][w][mt][lane] = pq;
+    for (int jt = 0; jt < NT; ++jt) {
+        // (a) this wave's state rows as a B operand, hi/lo
+        frag8 sh_, sl_;
+        acc2_to_split(S[jt][0], S[jt][1], sh_, sl_);
+        // (b) partial W S (W and S both rounded to bf16: the product only
+        //     reaches the outputs through Delta's first-order term) and
+        //     (q e^G) S over this wave's 32 channels
+#pragma unroll
+        for (int mt = 0; mt < Y::NMT; ++mt) {
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            sh.red[jt][0][w][mt][lane] = mfma16(as_bf16x8(op.w[mt]), sh_.v, z);
+            f32x4 pq = mfma16(as_bf16x8(op.qh[mt]), sh_.v, z);
+            pq = mfma16(as_bf16x8(op.qh[mt]), sl_.v, pq);
+            pq = mfma16(as_bf16x8(op.ql[mt]), sh_.v, pq);
+            sh.red[jt][1][w][mt][lane] = pq;
+        }
     }
     gate();
-    nx.load(0, nblk, lane16, w, nt, g);
+    nx.load(0, nblk, lane16, w, ng, g);
     lds_barrier();
     // (c) reduce the owned token tiles: Delta = U - sum_w W S
-    f32x4 oq[OWN];
+    f32x4 oq[NT][OWN];
 #pragma unroll
-    for (int uu = 0; uu < OWN; ++uu) {
-        const int mt = w + uu * NW;
-        if (mt >= Y::NMT) continue;
-        f32x4 d = op.u[uu];
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int jt = 0; jt < NT; ++jt)
 #pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-            d -= sh.red[0][ww][mt][lane];
-            acc += sh.red[1][ww][mt][lane];
+        for (int uu = 0; uu < OWN; ++uu) {
+            const int mt = w + uu * NW;
+            if (mt >= Y::NMT) continue;
+            f32x4 d = op.u[jt][uu];
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+                d -= sh.red[jt][0][ww][mt][lane];
+                acc += sh.red[jt][1][ww][mt][lane];
+            }
+            oq[jt][uu] = acc;
+            bf16_t hi[4], lo[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) split_bf16(d[j], hi[j], lo[j]);
+            const uint2 ph = pack4(hi), pl = pack4(lo);
+            sh.dls[jt][mt][lane] = make_uint4(ph.x, ph.y, pl.x, pl.y);
         }
-        oq[uu] = acc;
-        bf16_t hi[4], lo[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) split_bf16(d[j], hi[j], lo[j]);
-        const uint2 ph = pack4(hi), pl = pack4(lo);
-        sh.dls[mt][lane] = make_uint4(ph.x, ph.y, pl.x, pl.y);
-    }
-    nx.load(1, nblk, lane16, w, nt, g);
+    nx.load(1, nblk, lane16, w, ng, g);
     lds_barrier();
-    // (d) Delta as B operands, one per 32-token step
-    frag8 dh[Y::KSC], dl[Y::KSC];
-#pragma unroll
-    for (int st = 0; st < Y::KSC; ++st) {
-        const uint4 a0 = sh.dls[2 * st][lane];
-        const uint4 a1 = (2 * st + 1 < Y::NMT) ? sh.dls[2 * st + 1][lane] : make_uint4(0, 0, 0, 0);
-        dh[st].u = make_uint4(a0.x, a0.y, a1.x, a1.y);
-        dl[st].u = make_uint4(a0.z, a0.w, a1.z, a1.w);
-    }
-    // (e) state: S = e^{G_L} S + (k e^{G_L - G})^T Delta  (first: it carries
-    //     the dependency into the next chunk)
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        S[i] *= op.gam[i];
-#pragma unroll
-        for (int st = 0; st < Y::KSC; ++st) {
-            S[i] = mfma16(as_bf16x8(op.kh[i][st]), dh[st].v, S[i]);
-            S[i] = mfma16(as_bf16x8(op.kh[i][st]), dl[st].v, S[i]);
-            S[i] = mfma16(as_bf16x8(op.kl[i][st]), dh[st].v, S[i]);
-        }
-    }
-    nx.load(2, nblk, lane16, w, nt, g);
-    // (f) outputs of the owned token tiles: O = (q e^G) S + P Delta
     TO *o = static_cast<TO *>(p.o);
 #pragma unroll
-    for (int uu = 0; uu < OWN; ++uu) {
-        const int mt = w + uu * NW;
-        if (mt >= Y::NMT) continue;
-        f32x4 acc = oq[uu];
+    for (int jt = 0; jt < NT; ++jt) {
+        // (d) Delta as B operands, one per 32-token step
+        frag8 dh[Y::KSC], dl[Y::KSC];
 #pragma unroll
         for (int st = 0; st < Y::KSC; ++st) {
-            if (32 * st > 16 * mt + 15) continue;
-            acc = mfma16(as_bf16x8(op.ph[uu][st]), dh[st].v, acc);
-            acc = mfma16(as_bf16x8(op.ph[uu][st]), dl[st].v, acc);
-            acc = mfma16(as_bf16x8(op.pl[uu][st]), dh[st].v, acc);
+            const uint4 a0 = sh.dls[jt][2 * st][lane];
+            const uint4 a1 = (2 * st + 1 < Y::NMT) ? sh.dls[jt][2 * st + 1][lane] : make_uint4(0, 0, 0, 0);
+            dh[st].u = make_uint4(a0.x, a0.y, a1.x, a1.y);
+            dl[st].u = make_uint4(a0.z, a0.w, a1.z, a1.w);
         }
+        // (e) state: S = e^{G_L} S + (k e^{G_L - G})^T Delta  (first: it
+        //     carries the dependency into the next chunk)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int tok = 16 * mt + 4 * g + j;
-            if (tok < L) io<TO>::st(o, ((t0 + tok) * H + h) * D + col, acc[j]);
+        for (int i = 0; i < 2; ++i) {
+            S[jt][i] *= op.gam[i];
+#pragma unroll
+            for (int st = 0; st < Y::KSC; ++st) {
+                S[jt][i] = mfma16(as_bf16x8(op.kh[i][st]), dh[st].v, S[jt][i]);
+                S[jt][i] = mfma16(as_bf16x8(op.kh[i][st]), dl[st].v, S[jt][i]);
+                S[jt][i] = mfma16(as_bf16x8(op.kl[i][st]), dh[st].v, S[jt][i]);
+            }
+        }
+        if (jt == 0) nx.load(2, nblk, lane16, w, ng, g);
+        // (f) outputs of the owned token tiles: O = (q e^G) S + P Delta
+#pragma unroll
+        for (int uu = 0; uu < OWN; ++uu) {
+            const int mt = w + uu * NW;
+            if (mt >= Y::NMT) continue;
+            f32x4 acc = oq[jt][uu];
+#pragma unroll
+            for (int st = 0; st < Y::KSC; ++st) {
+                if (32 * st > 16 * mt + 15) continue;
+                acc = mfma16(as_bf16x8(op.ph[uu][st]), dh[st].v, acc);
+                acc = mfma16(as_bf16x8(op.ph[uu][st]), dl[st].v, acc);
+                acc = mfma16(as_bf16x8(op.pl[uu][st]), dh[st].v, acc);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int tok = 16 * mt + 4 * g + j;
+                if (tok < L) io<TO>::st(o, ((t0 + tok) * H + h) * D + col0 + 16 * jt, acc[j]);
+            }
         }
     }
-    nx.load(3, nblk, lane16, w, nt, g);
+    nx.load(3, nblk, lane16, w, ng, g);
 }
 
-// The scan of one (sequence, head) pair's 16-column state tile nt, with its
-// LDS at sh; wave w = threadIdx.x / 64 < D / 32.  WAIT (the overlapped
-// launch, one sequence): every block is read only after its flag is set,
-// the L2 warm-up included (a line read before it is written could stay in
-// this CU's L1).
-template <int C, int D, typename TO, bool WAIT>
+// The scan of one (sequence, head) pair's tile group ng (NT 16-column state
+// tiles), with its LDS at sh; wave w = threadIdx.x / 64 < D / 32.  WAIT (the
+// overlapped launch, one sequence): every block is read only after its flag
+// is set, the L2 warm-up included (a line read before it is written could
+// stay in this CU's L1).
+template <int C, int D, typename TO, bool WAIT, int NT = 1>
 __device__ __forceinline__ void scan_run(const PrefillParams &p, const char *__restrict__ blocks,
-                                         ScanShared<C, D> &sh, int pair, int nt, const int32_t *ready, int xcc) {
+                                         ScanShared<C, D, NT> &sh, int pair, int ng, const int32_t *ready,
+                                         int xcc) {
     using Y = Lay<C, D>;
-    constexpr int NVT = D / 16;   // 16-column state tiles per head
+    constexpr int NG = D / 16 / NT;   // tile groups per head
     const int H = p.H;
     const int n = pair / H, h = pair % H;
     const SeqRange sr = seq_range(p, n);
@@ -1102,17 +1121,20 @@ __device__ __forceinline__ void scan_run(const PrefillParams &p, const char *__r
     const int64_t cbase = p.chunk_off[n];
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, li = lane & 15;
-    const int col = 16 * nt + li;
+    const int col0 = 16 * NT * ng + li;
 
     const int64_t soff = (static_cast<int64_t>(n) * H + h) * D * D;
-    f32x4 S[2];
+    f32x4 S[NT][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int jt = 0; jt < NT; ++jt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = 32 * w + 16 * i + 4 * g + j;
-            S[i][j] = p.initial_state ? p.initial_state[soff + static_cast<int64_t>(row) * D + col] : 0.f;
-        }
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 32 * w + 16 * i + 4 * g + j;
+                S[jt][i][j] =
+                    p.initial_state ? p.initial_state[soff + static_cast<int64_t>(row) * D + col0 + 16 * jt] : 0.f;
+            }
 
     auto blk_of = [&](int c) {
         return blocks + (static_cast<size_t>(cbase + c) * H + h) * Y::BYTES;
@@ -1120,66 +1142,80 @@ __device__ __forceinline__ void scan_run(const PrefillParams &p, const char *__r
     // Every operand of chunk c + 1 is requested while chunk c is computed
     // (two buffers, alternating); chunk indices are clamped, so every load is
     // inside the sequence's blocks.  Waves exchange data through LDS only.
-    // L2 warm-up: while chunk c is computed, the column tiles of the head
-    // together touch every 128-byte line of chunk c + kWarmAhead's block (one
-    // dword per line, this workgroup's eighth), so that block is in L2 before
-    // its operands are requested; the loaded word is only consumed (without
-    // instructions) two chunks later (two registers, by chunk parity), so the
-    // wait for it is free.
+    // L2 warm-up: while chunk c is computed, the tile groups of the head
+    // together touch every 128-byte line of chunk c + kWarmAhead's block
+    // (one dword per line; KW lines per lane when the head's lanes are fewer
+    // than its lines), so that block is in L2 before its operands are
+    // requested; the loaded words are only consumed (without instructions)
+    // two chunks later (two register sets, by chunk parity), so the wait for
+    // them is free.
     constexpr int kWarmAhead = 2;
     constexpr int kLines = static_cast<int>(Y::BYTES / 128);
-    constexpr int kSlots = NVT * (D / 32) * 64;  // lanes of all the head's workgroups
-    const uint32_t warm_off = static_cast<uint32_t>(((nt * (D / 32) + w) * 64 + lane) * kLines / kSlots) * 128u;
-    uint32_t warmA = 0, warmB = 0;
-    auto warm_up = [&](uint32_t &warm, int c) {
-        asm volatile("" ::"v"(warm));
-        warm = *reinterpret_cast<const uint32_t *>(blk_of(min(c + kWarmAhead, nch - 1)) + warm_off);
+    constexpr int kLanes = NG * (D / 32) * 64;  // lanes of all the head's workgroups
+    constexpr int KW = (kLines + kLanes - 1) / kLanes;
+    constexpr int kSlots = kLanes * KW;
+    const int slot0 = ((ng * (D / 32) + w) * 64 + lane) * KW;
+    uint32_t warmA[KW], warmB[KW];
+#pragma unroll
+    for (int k = 0; k < KW; ++k) warmA[k] = warmB[k] = 0;
+    auto warm_up = [&](uint32_t (&warm)[KW], int c) {
+        const char *wb = blk_of(min(c + kWarmAhead, nch - 1));
+#pragma unroll
+        for (int k = 0; k < KW; ++k) {
+            asm volatile("" ::"v"(warm[k]));
+            warm[k] = *reinterpret_cast<const uint32_t *>(
+                wb + static_cast<uint32_t>((slot0 + k) * kLines / kSlots) * 128u);
+        }
     };
     // WAIT: a block is warmed only when its writers are at least
     // kWarmPublished chunks further on (it may have left the L2 since it was
     // written); closer behind them the warm-up measured slower than none.
     constexpr int kWarmPublished = 16;
-    ScanOps<C, D> A, B;
+    ScanOps<C, D, NT> A, B;
     if (nch > 0) {
         const uint32_t lane16 = 16u * lane;
         ReadyView rv{WAIT ? ready + ready_index(p, 0, h) : nullptr, nch, WAIT ? 0 : nch, xcc};
         if (WAIT) rv.ensure(0, p);
-        A.load(blk_of(0), lane16, w, nt, g);
+        A.load(blk_of(0), lane16, w, ng, g);
         for (int c = 0; c < nch; c += 2) {
             if (!WAIT || min(c + kWarmAhead, nch - 1) + kWarmPublished < rv.known) warm_up(warmA, c);
-            scan_chunk<C, D, TO>(A, B, blk_of(min(c + 1, nch - 1)), lane16, S, sh, p, cbase + c,
-                                 sr.start + static_cast<int64_t>(c) * C, min(C, sr.len - c * C), h, w, nt, lane,
-                                 [&] { if (WAIT) rv.ensure(min(c + 1, nch - 1), p); });
+            scan_chunk<C, D, TO, NT>(A, B, blk_of(min(c + 1, nch - 1)), lane16, S, sh, p, cbase + c,
+                                     sr.start + static_cast<int64_t>(c) * C, min(C, sr.len - c * C), h, w, ng, lane,
+                                     [&] { if (WAIT) rv.ensure(min(c + 1, nch - 1), p); });
             if (c + 1 >= nch) break;
             if (!WAIT || min(c + 1 + kWarmAhead, nch - 1) + kWarmPublished < rv.known) warm_up(warmB, c + 1);
-            scan_chunk<C, D, TO>(B, A, blk_of(min(c + 2, nch - 1)), lane16, S, sh, p, cbase + c + 1,
-                                 sr.start + static_cast<int64_t>(c + 1) * C, min(C, sr.len - (c + 1) * C), h, w, nt,
-                                 lane, [&] { if (WAIT) rv.ensure(min(c + 2, nch - 1), p); });
+            scan_chunk<C, D, TO, NT>(B, A, blk_of(min(c + 2, nch - 1)), lane16, S, sh, p, cbase + c + 1,
+                                     sr.start + static_cast<int64_t>(c + 1) * C, min(C, sr.len - (c + 1) * C), h, w,
+                                     ng, lane, [&] { if (WAIT) rv.ensure(min(c + 2, nch - 1), p); });
         }
-        asm volatile("" ::"v"(warmA), "v"(warmB));
+#pragma unroll
+        for (int k = 0; k < KW; ++k) asm volatile("" ::"v"(warmA[k]), "v"(warmB[k]));
     }
     if (p.final_state) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int jt = 0; jt < NT; ++jt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                p.final_state[soff + static_cast<int64_t>(32 * w + 16 * i + 4 * g + j) * D + col] = S[i][j];
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    p.final_state[soff + static_cast<int64_t>(32 * w + 16 * i + 4 * g + j) * D + col0 + 16 * jt] =
+                        S[jt][i][j];
     }
 }
 
-template <int C, int D, typename TO>
+template <int C, int D, typename TO, int NT>
 __global__ void __launch_bounds__(64 * (D / 32)) scan_kernel(PrefillParams p, const char *__restrict__ blocks) {
-    constexpr int NVT = D / 16;   // 16-column state tiles per head
-    __shared__ ScanShared<C, D> sh;
+    constexpr int NG = D / 16 / NT;   // tile groups per head
+    __shared__ ScanShared<C, D, NT> sh;
     if (*p.status != 0) return;
-    // XCD-aware order: the NVT column tiles of one (sequence, head) share
+    // XCD-aware order: the NG tile groups of one (sequence, head) share
     // blockIdx % 8, hence one XCD and its L2.
     const int bid = blockIdx.x;
     const int xcd = bid & 7, slot = bid >> 3;
-    const int nt = slot % NVT;
-    const int pair = xcd + 8 * (slot / NVT);
+    const int ng = slot % NG;
+    const int pair = xcd + 8 * (slot / NG);
     if (pair >= p.N * p.H) return;
-    scan_run<C, D, TO, false>(p, blocks, sh, pair, nt, nullptr, 0);
+    scan_run<C, D, TO, false, NT>(p, blocks, sh, pair, ng, nullptr, 0);
 }
 
 // ---------------------------------------------------- overlapped launch --
@@ -1255,6 +1291,30 @@ bool mfma_supported(int dk, int dv, int C) {
 }
 
 namespace {
+// Column tiles per scan workgroup.  A workgroup's time per chunk grows with
+// its tile count (the tiles' products, reductions and exchanges run one
+// after another in each wave: 1.77, 2.70 and 4.97 us per chunk at 1, 2, 4
+// tiles on the T=131072, H=32 workload), while sharing the block's W, q e^G,
+// k e^{G_L-G} and P loads saves the CUs work.  So one tile per workgroup
+// while the grid does not fill the CUs, else the most tiles for which it
+// still gives every CU a workgroup.
+int scan_tiles_per_workgroup(int pairs, int D) {
+    const long tiles = static_cast<long>(pairs) * (D / 16);
+    if (tiles >= 4L * kIntraGrid) return 4;
+    if (tiles >= 2L * kIntraGrid) return 2;
+    return 1;
+}
+
+template <int C, int D, typename TO, int NT>
+hipError_t launch_scan(const PrefillParams &p, char *blocks, hipStream_t s) {
+    constexpr int NG = D / 16 / NT;   // tile groups per head
+    const int pairs = p.N * p.H;
+    const unsigned grid = static_cast<unsigned>((pairs + 7) / 8) * NG * 8;
+    hipLaunchKernelGGL((scan_kernel<C, D, TO, NT>), dim3(grid), dim3(64 * (D / 32)), 0, s, p,
+                       static_cast<const char *>(blocks));
+    return hipGetLastError();
+}
+
 template <int C, int D, typename TO>
 hipError_t run_mfma(const PrefillParams &p, char *blocks, hipStream_t s, hipEvent_t mid) {
     if constexpr (C == 64) {
@@ -1271,12 +1331,13 @@ hipError_t run_mfma(const PrefillParams &p, char *blocks, hipStream_t s, hipEven
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && mid) e = hipEventRecord(mid, s);
     if (e != hipSuccess) return e;
-    constexpr int NVT = D / 16;
     const int pairs = p.N * p.H;
-    const unsigned grid = static_cast<unsigned>((pairs + 7) / 8) * NVT * 8;
-    hipLaunchKernelGGL((scan_kernel<C, D, TO>), dim3(grid), dim3(64 * (D / 32)), 0, s, p,
-                       static_cast<const char *>(blocks));
-    return hipGetLastError();
+    if constexpr (C == 64 && D == 128) {   // measured there
+        const int nt = scan_tiles_per_workgroup(pairs, D);
+        if (nt == 4) return launch_scan<C, D, TO, 4>(p, blocks, s);
+        if (nt == 2) return launch_scan<C, D, TO, 2>(p, blocks, s);
+    }
+    return launch_scan<C, D, TO, 1>(p, blocks, s);
 }
 
 template <int D, typename TO>

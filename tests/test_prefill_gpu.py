@@ -293,6 +293,40 @@ def test_mfma_packed_equals_separate_and_is_deterministic():
         assert torch.equal(Sn, S[n:n + 1]), f"document {n}: packed state differs from separate"
 
 
+@pytest.mark.parametrize("seed,ndocs,H,odt", [(22, 16, 4, torch.float32), (23, 32, 4, torch.float32),
+                                               (24, 40, 4, torch.bfloat16)])
+def test_mfma_wide_scan_tiles_equal_one_tile(seed, ndocs, H, odt):
+    """With many (sequence, head) pairs the scan gives each workgroup 2
+    (64 pairs) or 4 (128 or more) column tiles of a head, loading the
+    block's shared operands once for them; each tile's arithmetic is that of
+    a one-tile workgroup, which one call per document uses (a single
+    sequence with 4 heads).  Outputs, final states and every chunk-entry
+    state must be bitwise equal."""
+    g = np.random.default_rng(seed)
+    lens = [int(n) for n in g.integers(1, 300, ndocs)]
+    lens[0], lens[1] = 0, 64
+    x = synth.make_packed(seed, lens, H, 128, 128, "bf16", chunk=64)
+    q, k, v, b, la, init, cu = dev_tensors(x)
+    o, S, cs = kda.prefill(q, k, v, b, la, initial_state=init, cu_seqlens=cu, chunk_states=True, out_dtype=odt)
+    c = x.cu_seqlens
+    ch = 0
+    for n in range(ndocs):
+        sl = slice(int(c[n]), int(c[n + 1]))
+        if lens[n] == 0:
+            assert torch.equal(S[n:n + 1], init[n:n + 1])
+            continue
+        on, Sn, csn = kda.prefill(q[:, sl].contiguous(), k[:, sl].contiguous(), v[:, sl].contiguous(),
+                                  b[:, sl].contiguous(), la[:, sl].contiguous(), initial_state=init[n:n + 1].contiguous(),
+                                  chunk_states=True, out_dtype=odt)
+        nc = csn.shape[0]
+        assert torch.equal(on, o[:, sl]), f"document {n}: output differs"
+        assert torch.equal(Sn, S[n:n + 1]), f"document {n}: final state differs"
+        assert torch.equal(csn, cs[ch:ch + nc]), f"document {n}: chunk-entry states differ"
+        ch += nc
+    assert ch == cs.shape[0]
+    print(f"[wide scan] {ndocs} documents x {H} heads: bitwise equal to one call per document", flush=True)
+
+
 def test_mfma_power_of_two_homogeneity():
     x = synth.make_uniform(21, 1, 150, 2, 128, 128, "bf16", chunk=64, state_std=0.2)
     q, k, v, b, la, init, _ = dev_tensors(x)
