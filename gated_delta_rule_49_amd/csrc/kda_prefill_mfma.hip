@@ -42,6 +42,8 @@
 // 2^(+-span/2), span = that decay in powers of two.  When the span exceeds
 // 200 in some channel of a wave's channel half, that half of the block is
 // computed exactly, pair by pair, on the vector ALUs.
+#include <type_traits>
+
 #include "kda_handoff.hpp"
 #include "kda_launch.hpp"
 
@@ -899,6 +901,282 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
 
 // ------------------------------------------------------------------ K2 --
 // One wave's operands for one chunk, read from the chunk's workspace block in
+// MFMA register order as 128-bit register tuples.  Wave w owns state rows
+// [32w, 32w + 32): channel k-step w of the W S and (q e^G) S products and
+// channel tiles 2w, 2w + 1 of the state update; it also finishes the output
+// token tiles w, w + D/32, ...
+template <int C, int D>
+struct ScanOps {
+    using Y = Lay<C, D>;
+    static constexpr int NW = D / 32;
+    static constexpr int OWN = (Y::NMT + NW - 1) / NW;
+    typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+    u32x4 w[Y::NMT], qh[Y::NMT], ql[Y::NMT];   // token tile mt, channel step = wave
+    u32x4 kh[2][Y::KSC], kl[2][Y::KSC];       // the wave's two channel tiles x token steps
+    u32x4 ph[OWN][Y::KSC], pl[OWN][Y::KSC];   // owned token tiles x token steps
+    f32x4 u[OWN];                             // owned token tiles, this column tile
+    f32x4 gam[2];
+
+    // blk: the chunk's block (uniform); lane16 = 16 * lane.  Four parts, so
+    // that the requests can be spread over the previous chunk's computation.
+    __device__ __forceinline__ void load(int part, const char *blk, uint32_t lane16, int wv, int nt, int g) {
+        auto at = [&](size_t off) { return reinterpret_cast<const u32x4 *>(blk + off + lane16); };
+        if (part == 0) {
+#pragma unroll
+            for (int mt = 0; mt < Y::NMT; ++mt) {
+                const size_t fo = (static_cast<size_t>(mt) * Y::KSD + wv) * Y::FRAG;
+                w[mt] = *at(Y::W + fo);
+                qh[mt] = *at(Y::QH + fo);
+                ql[mt] = *at(Y::QL + fo);
+            }
+        } else if (part == 1) {
+#pragma unroll
+            for (int uu = 0; uu < OWN; ++uu) {
+                const int mt = wv + uu * NW;
+                if (mt >= Y::NMT) continue;
+                u[uu] = __builtin_bit_cast(f32x4, *at(Y::U + (static_cast<size_t>(mt) * Y::NDT + nt) * Y::FRAG));
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                gam[i] = *reinterpret_cast<const f32x4 *>(blk + Y::GAM + (32 * wv + 16 * i + 4 * g) * sizeof(float));
+        } else if (part == 2) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int st = 0; st < Y::KSC; ++st) {
+                    const size_t fo = (static_cast<size_t>(2 * wv + i) * Y::KSC + st) * Y::FRAG;
+                    kh[i][st] = *at(Y::KBH + fo);
+                    kl[i][st] = *at(Y::KBL + fo);
+                }
+        } else {
+#pragma unroll
+            for (int uu = 0; uu < OWN; ++uu) {
+                const int mt = wv + uu * NW;
+                if (mt >= Y::NMT) continue;
+#pragma unroll
+                for (int st = 0; st < Y::KSC; ++st) {
+                    if (32 * st > 16 * mt + 15) continue;  // zero above the diagonal
+                    const size_t fo = (static_cast<size_t>(mt) * Y::KSC + st) * Y::FRAG;
+                    ph[uu][st] = *at(Y::PH + fo);
+                    pl[uu][st] = *at(Y::PL + fo);
+                }
+            }
+        }
+    }
+    __device__ __forceinline__ void load(const char *blk, uint32_t lane16, int wv, int nt, int g) {
+#pragma unroll
+        for (int part = 0; part < 4; ++part) load(part, blk, lane16, wv, nt, g);
+    }
+};
+
+template <int C, int D>
+struct ScanShared {
+    using Y = Lay<C, D>;
+    f32x4 red[2][D / 32][Y::NMT][64];
+    uint4 dls[Y::NMT][64];
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const ScanOps<64, 128>::u32x4 &u) { return __builtin_bit_cast(bf16x8, u); }
+
+// One chunk of the scan for one wave: consumes the operands in `op` and
+// updates the state tiles S in place.
+// The next chunk's operands are requested into `nx` in four parts between
+// the phases, so that the transfers overlap this chunk's computation.
+// gate() runs before the first load of the next block (the overlapped
+// launch waits there until that block is published).
+template <int C, int D, typename TO, typename Gate>
+__device__ __forceinline__ void scan_chunk(const ScanOps<C, D> &op, ScanOps<C, D> &nx, const char *nblk,
+                                           uint32_t lane16, f32x4 (&S)[2], ScanShared<C, D> &sh,
+                                           const PrefillParams &p, int64_t x, int64_t t0, int L, int h, int w,
+                                           int nt, int lane, Gate &&gate) {
+    using Y = Lay<C, D>;
+    constexpr int NW = D / 32;
+    constexpr int OWN = ScanOps<C, D>::OWN;
+    const int g = lane >> 4, li = lane & 15;
+    const int col = 16 * nt + li;
+    const int H = p.H;
+    if (p.chunk_states) {
+        float *cs = p.chunk_states + (x * H + h) * static_cast<int64_t>(D) * D;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cs[static_cast<int64_t>(32 * w + 16 * i + 4 * g + j) * D + col] = S[i][j];
+    }
+    // (a) this wave's state rows as a B operand, hi/lo
+    frag8 sh_, sl_;
+    acc2_to_split(S[0], S[1], sh_, sl_);
+    // (b) partial W S (W and S both rounded to bf16: the product only reaches
+    //     the outputs through Delta's first-order term) and (q e^G) S over this
+    //     wave's 32 channels
+#pragma unroll
+    for (int mt = 0; mt < Y::NMT; ++mt) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        sh.red[0][w][mt][lane] = mfma16(as_bf16x8(op.w[mt]), sh_.v, z);
+        f32x4 pq = mfma16(as_bf16x8(op.qh[mt]), sh_.v, z);
+        pq = mfma16(as_bf16x8(op.qh[mt]), sl_.v, pq);
+        pq = mfma16(as_bf16x8(op.ql[mt]), sh_.v, pq);
+        sh.red[1][w][mt][lane] = pq;
+    }
+    gate();
+    nx.load(0, nblk, lane16, w, nt, g);
+    lds_barrier();
+    // (c) reduce the owned token tiles: Delta = U - sum_w W S
+    f32x4 oq[OWN];
+#pragma unroll
+    for (int uu = 0; uu < OWN; ++uu) {
+        const int mt = w + uu * NW;
+        if (mt >= Y::NMT) continue;
+        f32x4 d = op.u[uu];
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+            d -= sh.red[0][ww][mt][lane];
+            acc += sh.red[1][ww][mt][lane];
+        }
+        oq[uu] = acc;
+        bf16_t hi[4], lo[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) split_bf16(d[j], hi[j], lo[j]);
+        const uint2 ph = pack4(hi), pl = pack4(lo);
+        sh.dls[mt][lane] = make_uint4(ph.x, ph.y, pl.x, pl.y);
+    }
+    nx.load(1, nblk, lane16, w, nt, g);
+    lds_barrier();
+    // (d) Delta as B operands, one per 32-token step
+    frag8 dh[Y::KSC], dl[Y::KSC];
+#pragma unroll
+    for (int st = 0; st < Y::KSC; ++st) {
+        const uint4 a0 = sh.dls[2 * st][lane];
+        const uint4 a1 = (2 * st + 1 < Y::NMT) ? sh.dls[2 * st + 1][lane] : make_uint4(0, 0, 0, 0);
+        dh[st].u = make_uint4(a0.x, a0.y, a1.x, a1.y);
+        dl[st].u = make_uint4(a0.z, a0.w, a1.z, a1.w);
+    }
+    // (e) state: S = e^{G_L} S + (k e^{G_L - G})^T Delta  (first: it carries
+    //     the dependency into the next chunk)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        S[i] *= op.gam[i];
+#pragma unroll
+        for (int st = 0; st < Y::KSC; ++st) {
+            S[i] = mfma16(as_bf16x8(op.kh[i][st]), dh[st].v, S[i]);
+            S[i] = mfma16(as_bf16x8(op.kh[i][st]), dl[st].v, S[i]);
+            S[i] = mfma16(as_bf16x8(op.kl[i][st]), dh[st].v, S[i]);
+        }
+    }
+    nx.load(2, nblk, lane16, w, nt, g);
+    // (f) outputs of the owned token tiles: O = (q e^G) S + P Delta
+    TO *o = static_cast<TO *>(p.o);
+#pragma unroll
+    for (int uu = 0; uu < OWN; ++uu) {
+        const int mt = w + uu * NW;
+        if (mt >= Y::NMT) continue;
+        f32x4 acc = oq[uu];
+#pragma unroll
+        for (int st = 0; st < Y::KSC; ++st) {
+            if (32 * st > 16 * mt + 15) continue;
+            acc = mfma16(as_bf16x8(op.ph[uu][st]), dh[st].v, acc);
+            acc = mfma16(as_bf16x8(op.ph[uu][st]), dl[st].v, acc);
+            acc = mfma16(as_bf16x8(op.pl[uu][st]), dh[st].v, acc);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int tok = 16 * mt + 4 * g + j;
+            if (tok < L) io<TO>::st(o, ((t0 + tok) * H + h) * D + col, acc[j]);
+        }
+    }
+    nx.load(3, nblk, lane16, w, nt, g);
+}
+
+// The scan of one (sequence, head) pair's 16-column state tile nt, with its
+// LDS at sh; wave w = threadIdx.x / 64 < D / 32.  WAIT (the overlapped
+// launch, one sequence): every block is read only after its flag is set,
+// the L2 warm-up included (a line read before it is written could stay in
+// this CU's L1).
+template <int C, int D, typename TO, bool WAIT>
+__device__ __forceinline__ void scan_run(const PrefillParams &p, const char *__restrict__ blocks,
+                                         ScanShared<C, D> &sh, int pair, int nt, const int32_t *ready, int xcc) {
+    using Y = Lay<C, D>;
+    constexpr int NVT = D / 16;   // 16-column state tiles per head
+    const int H = p.H;
+    const int n = pair / H, h = pair % H;
+    const SeqRange sr = seq_range(p, n);
+    const int nch = (sr.len + C - 1) / C;
+    const int64_t cbase = p.chunk_off[n];
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, li = lane & 15;
+    const int col = 16 * nt + li;
+
+    const int64_t soff = (static_cast<int64_t>(n) * H + h) * D * D;
+    f32x4 S[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 32 * w + 16 * i + 4 * g + j;
+            S[i][j] = p.initial_state ? p.initial_state[soff + static_cast<int64_t>(row) * D + col] : 0.f;
+        }
+
+    auto blk_of = [&](int c) {
+        return blocks + (static_cast<size_t>(cbase + c) * H + h) * Y::BYTES;
+    };
+    // Every operand of chunk c + 1 is requested while chunk c is computed
+    // (two buffers, alternating); chunk indices are clamped, so every load is
+    // inside the sequence's blocks.  Waves exchange data through LDS only.
+    // L2 warm-up: while chunk c is computed, the column tiles of the head
+    // together touch every 128-byte line of chunk c + kWarmAhead's block (one
+    // dword per line, this workgroup's eighth), so that block is in L2 before
+    // its operands are requested; the loaded word is only consumed (without
+    // instructions) two chunks later (two registers, by chunk parity), so the
+    // wait for it is free.
+    constexpr int kWarmAhead = 2;
+    constexpr int kLines = static_cast<int>(Y::BYTES / 128);
+    constexpr int kSlots = NVT * (D / 32) * 64;  // lanes of all the head's workgroups
+    const uint32_t warm_off = static_cast<uint32_t>(((nt * (D / 32) + w) * 64 + lane) * kLines / kSlots) * 128u;
+    uint32_t warmA = 0, warmB = 0;
+    auto warm_up = [&](uint32_t &warm, int c) {
+        asm volatile("" ::"v"(warm));
+        warm = *reinterpret_cast<const uint32_t *>(blk_of(min(c + kWarmAhead, nch - 1)) + warm_off);
+    };
+    // WAIT: a block is warmed only when its writers are at least
+    // kWarmPublished chunks further on (it may have left the L2 since it was
+    // written); closer behind them the warm-up measured slower than none.
+    constexpr int kWarmPublished = 16;
+    ScanOps<C, D> A, B;
+    if (nch > 0) {
+        const uint32_t lane16 = 16u * lane;
+        ReadyView rv{WAIT ? ready + ready_index(p, 0, h) : nullptr, nch, WAIT ? 0 : nch, xcc};
+        if (WAIT) rv.ensure(0, p);
+        A.load(blk_of(0), lane16, w, nt, g);
+        for (int c = 0; c < nch; c += 2) {
+            if (!WAIT || min(c + kWarmAhead, nch - 1) + kWarmPublished < rv.known) warm_up(warmA, c);
+            scan_chunk<C, D, TO>(A, B, blk_of(min(c + 1, nch - 1)), lane16, S, sh, p, cbase + c,
+                                 sr.start + static_cast<int64_t>(c) * C, min(C, sr.len - c * C), h, w, nt, lane,
+                                 [&] { if (WAIT) rv.ensure(min(c + 1, nch - 1), p); });
+            if (c + 1 >= nch) break;
+            if (!WAIT || min(c + 1 + kWarmAhead, nch - 1) + kWarmPublished < rv.known) warm_up(warmB, c + 1);
+            scan_chunk<C, D, TO>(B, A, blk_of(min(c + 2, nch - 1)), lane16, S, sh, p, cbase + c + 1,
+                                 sr.start + static_cast<int64_t>(c + 1) * C, min(C, sr.len - (c + 1) * C), h, w, nt,
+                                 lane, [&] { if (WAIT) rv.ensure(min(c + 2, nch - 1), p); });
+        }
+        asm volatile("" ::"v"(warmA), "v"(warmB));
+    }
+    if (p.final_state) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                p.final_state[soff + static_cast<int64_t>(32 * w + 16 * i + 4 * g + j) * D + col] = S[i][j];
+    }
+}
+
+// -------------------------------------------------- K2, NT tiles per WG --
+// The same scan for a workgroup that owns NT > 1 adjacent column tiles of a
+// head (the launch picks NT; see scan_tiles_per_workgroup).  Each tile's
+// arithmetic is the one-tile code's, so the results are bitwise equal.  The
+// one-tile functions above are kept as they are: written in this generic
+// form, their one-tile instance was scheduled differently by the compiler
+// and ran 4 % slower (3.64 against 3.50 ms on the T=131072, H=32 workload).
+// One wave's operands for one chunk, read from the chunk's workspace block in
 // MFMA register order as 128-bit register tuples.  A workgroup owns NT
 // adjacent 16-column state tiles of one head (columns [16 NT g, 16 NT g +
 // 16 NT) for tile group g); wave w owns state rows [32w, 32w + 32) of each:
@@ -906,8 +1184,8 @@ __global__ void __launch_bounds__(512) intra_kernel(PrefillParams p, char *__res
 // 2w + 1 of the state update; it also finishes the output token tiles w,
 // w + D/32, ...  The W, q e^G, k e^{G_L-G} and P operands are shared by the
 // NT tiles (loaded once); U is per tile.
-template <int C, int D, int NT = 1>
-struct ScanOps {
+template <int C, int D, int NT>
+struct WideScanOps {
     using Y = Lay<C, D>;
     static constexpr int NW = D / 32;
     static constexpr int OWN = (Y::NMT + NW - 1) / NW;
@@ -974,14 +1252,12 @@ struct ScanOps {
     }
 };
 
-template <int C, int D, int NT = 1>
-struct ScanShared {
+template <int C, int D, int NT>
+struct WideScanShared {
     using Y = Lay<C, D>;
     f32x4 red[NT][2][D / 32][Y::NMT][64];
     uint4 dls[NT][Y::NMT][64];
 };
-
-__device__ __forceinline__ bf16x8 as_bf16x8(const ScanOps<64, 128>::u32x4 &u) { return __builtin_bit_cast(bf16x8, u); }
 
 // One chunk of the scan for one wave: consumes the operands in `op` and
 // updates the state tiles S (one pair per column tile of the group) in place.
@@ -990,13 +1266,13 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const ScanOps<64, 128>::u32x4 &u) { 
 // gate() runs before the first load of the next block (the overlapped
 // launch waits there until that block is published).
 template <int C, int D, typename TO, int NT, typename Gate>
-__device__ __forceinline__ void scan_chunk(const ScanOps<C, D, NT> &op, ScanOps<C, D, NT> &nx, const char *nblk,
-                                           uint32_t lane16, f32x4 (&S)[NT][2], ScanShared<C, D, NT> &sh,
+__device__ __forceinline__ void wide_scan_chunk(const WideScanOps<C, D, NT> &op, WideScanOps<C, D, NT> &nx, const char *nblk,
+                                           uint32_t lane16, f32x4 (&S)[NT][2], WideScanShared<C, D, NT> &sh,
                                            const PrefillParams &p, int64_t x, int64_t t0, int L, int h, int w,
                                            int ng, int lane, Gate &&gate) {
     using Y = Lay<C, D>;
     constexpr int NW = D / 32;
-    constexpr int OWN = ScanOps<C, D, NT>::OWN;
+    constexpr int OWN = WideScanOps<C, D, NT>::OWN;
     const int g = lane >> 4, li = lane & 15;
     const int col0 = 16 * NT * ng + li;   // column of tile j: col0 + 16 j
     const int H = p.H;
@@ -1108,9 +1384,9 @@ __device__ __forceinline__ void scan_chunk(const ScanOps<C, D, NT> &op, ScanOps<
 // overlapped launch, one sequence): every block is read only after its flag
 // is set, the L2 warm-up included (a line read before it is written could
 // stay in this CU's L1).
-template <int C, int D, typename TO, bool WAIT, int NT = 1>
-__device__ __forceinline__ void scan_run(const PrefillParams &p, const char *__restrict__ blocks,
-                                         ScanShared<C, D, NT> &sh, int pair, int ng, const int32_t *ready,
+template <int C, int D, typename TO, bool WAIT, int NT>
+__device__ __forceinline__ void wide_scan_run(const PrefillParams &p, const char *__restrict__ blocks,
+                                         WideScanShared<C, D, NT> &sh, int pair, int ng, const int32_t *ready,
                                          int xcc) {
     using Y = Lay<C, D>;
     constexpr int NG = D / 16 / NT;   // tile groups per head
@@ -1171,7 +1447,7 @@ __device__ __forceinline__ void scan_run(const PrefillParams &p, const char *__r
     // kWarmPublished chunks further on (it may have left the L2 since it was
     // written); closer behind them the warm-up measured slower than none.
     constexpr int kWarmPublished = 16;
-    ScanOps<C, D, NT> A, B;
+    WideScanOps<C, D, NT> A, B;
     if (nch > 0) {
         const uint32_t lane16 = 16u * lane;
         ReadyView rv{WAIT ? ready + ready_index(p, 0, h) : nullptr, nch, WAIT ? 0 : nch, xcc};
@@ -1179,12 +1455,12 @@ __device__ __forceinline__ void scan_run(const PrefillParams &p, const char *__r
         A.load(blk_of(0), lane16, w, ng, g);
         for (int c = 0; c < nch; c += 2) {
             if (!WAIT || min(c + kWarmAhead, nch - 1) + kWarmPublished < rv.known) warm_up(warmA, c);
-            scan_chunk<C, D, TO, NT>(A, B, blk_of(min(c + 1, nch - 1)), lane16, S, sh, p, cbase + c,
+            wide_scan_chunk<C, D, TO, NT>(A, B, blk_of(min(c + 1, nch - 1)), lane16, S, sh, p, cbase + c,
                                      sr.start + static_cast<int64_t>(c) * C, min(C, sr.len - c * C), h, w, ng, lane,
                                      [&] { if (WAIT) rv.ensure(min(c + 1, nch - 1), p); });
             if (c + 1 >= nch) break;
             if (!WAIT || min(c + 1 + kWarmAhead, nch - 1) + kWarmPublished < rv.known) warm_up(warmB, c + 1);
-            scan_chunk<C, D, TO, NT>(B, A, blk_of(min(c + 2, nch - 1)), lane16, S, sh, p, cbase + c + 1,
+            wide_scan_chunk<C, D, TO, NT>(B, A, blk_of(min(c + 2, nch - 1)), lane16, S, sh, p, cbase + c + 1,
                                      sr.start + static_cast<int64_t>(c + 1) * C, min(C, sr.len - (c + 1) * C), h, w,
                                      ng, lane, [&] { if (WAIT) rv.ensure(min(c + 2, nch - 1), p); });
         }
@@ -1206,7 +1482,8 @@ __device__ __forceinline__ void scan_run(const PrefillParams &p, const char *__r
 template <int C, int D, typename TO, int NT>
 __global__ void __launch_bounds__(64 * (D / 32)) scan_kernel(PrefillParams p, const char *__restrict__ blocks) {
     constexpr int NG = D / 16 / NT;   // tile groups per head
-    __shared__ ScanShared<C, D, NT> sh;
+    using Shared = typename std::conditional<NT == 1, ScanShared<C, D>, WideScanShared<C, D, NT>>::type;
+    __shared__ Shared sh;
     if (*p.status != 0) return;
     // XCD-aware order: the NG tile groups of one (sequence, head) share
     // blockIdx % 8, hence one XCD and its L2.
@@ -1215,7 +1492,10 @@ __global__ void __launch_bounds__(64 * (D / 32)) scan_kernel(PrefillParams p, co
     const int ng = slot % NG;
     const int pair = xcd + 8 * (slot / NG);
     if (pair >= p.N * p.H) return;
-    scan_run<C, D, TO, false, NT>(p, blocks, sh, pair, ng, nullptr, 0);
+    if constexpr (NT == 1)
+        scan_run<C, D, TO, false>(p, blocks, sh, pair, ng, nullptr, 0);
+    else
+        wide_scan_run<C, D, TO, false, NT>(p, blocks, sh, pair, ng, nullptr, 0);
 }
 
 // ---------------------------------------------------- overlapped launch --
