@@ -63,7 +63,7 @@ template <int DK>
 struct CbScanOps {
     static constexpr int NKB = DK / 16;           // key blocks
     static constexpr int KPW = (NKB + 3) / 4;     // key blocks per wave
-    f32x4 pt[4];          // P^T[16w + n][16ib + 4g ..], token blocks ib >= w
+    f32x4 pt[4];          // P^T[16w + n][16ib + 4g ..] = P[16ib + 4g ..][16w + n], token blocks ib >= w
     f32x4 kb[NKB];        // K^[16w + n][16cb + 4g ..]
     f32x4 qt[KPW][4];     // Q~[16rb + 4g + s][16kb + n], s = 0..3
     f32x4 wt[KPW][4];     // W [16rb + 4g + s][16kb + n]
@@ -74,7 +74,9 @@ struct CbScanOps {
         using Y = CbLay<DK>;
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib)
-            if (ib >= w) pt[ib] = *reinterpret_cast<const f32x4 *>(blk + Y::PT + (16 * w + n) * CB_C + 16 * ib + 4 * g);
+            if (ib >= w)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) pt[ib][s] = blk[Y::P + (16 * ib + 4 * g + s) * CB_C + 16 * w + n];
 #pragma unroll
         for (int cb = 0; cb < NKB; ++cb)
             kb[cb] = *reinterpret_cast<const f32x4 *>(blk + Y::KB + (16 * w + n) * DK + 16 * cb + 4 * g);
@@ -171,7 +173,7 @@ __global__ void __launch_bounds__(256) cb_scan_kernel(CbParams p) {
     };
     // L2 warm-up (as in the forward scan): while chunk ch is computed, the
     // column tiles of the head together touch every 128-byte line of the
-    // block regions this scan reads (Q~, K^ and W, which are contiguous, P^T
+    // block regions this scan reads (Q~, K^ and W, which are contiguous, P
     // and e^{G_L}) of chunk ch - kWarmAhead, one line per thread, so the
     // next chunk's operand loads find them in L2; the loaded word is only
     // consumed (without instructions) a chunk later.  Threads without a
@@ -181,7 +183,7 @@ __global__ void __launch_bounds__(256) cb_scan_kernel(CbParams p) {
     static_assert(Y::KB == Y::QT + C * DK && Y::W == Y::KB + C * DK, "Q~, K^, W contiguous");
     const int wl = vt + nvt * tid;
     const int woff = wl < kLinesA ? static_cast<int>(Y::QT) + 32 * wl
-                   : wl < kLinesA + kLinesB ? static_cast<int>(Y::PT) + 32 * (wl - kLinesA)
+                   : wl < kLinesA + kLinesB ? static_cast<int>(Y::P) + 32 * (wl - kLinesA)
                    : wl < kLinesA + kLinesB + kLinesC ? static_cast<int>(Y::GAM) + 32 * (wl - kLinesA - kLinesB)
                    : static_cast<int>(Y::QT);
     uint32_t warm = 0;
@@ -399,16 +401,21 @@ __global__ void __launch_bounds__(CB_GRAD_NT) cb_grad_kernel(CbParams p) {
             const float4 t = ld4(ka + kb * 16 + 4 * g);
             fa[4 * kb] = sg * t.x; fa[4 * kb + 1] = sg * t.y; fa[4 * kb + 2] = sg * t.z; fa[4 * kb + 3] = sg * t.w;
         }
-        const float *mb = blk + (half ? Y::PT : Y::M) + row * C;
-        const float *mc = blk + Y::MT + row * C;
+        // P^T and M^T rows are P and M columns
+        const float *mc = blk + Y::M + row;
         const float br = blk[Y::BETA + row];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            const float4 t = ld4(mb + kb * 16 + 4 * g);
-            const float4 bc = half ? make_float4(1.f, 1.f, 1.f, 1.f) : ld4(blk + Y::BETA + kb * 16 + 4 * g);
-            fb[4 * kb] = t.x * bc.x; fb[4 * kb + 1] = t.y * bc.y; fb[4 * kb + 2] = t.z * bc.z; fb[4 * kb + 3] = t.w * bc.w;
-            const float4 u = ld4(mc + kb * 16 + 4 * g);
-            fc[4 * kb] = br * u.x; fc[4 * kb + 1] = br * u.y; fc[4 * kb + 2] = br * u.z; fc[4 * kb + 3] = br * u.w;
+            if (half) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) fb[4 * kb + s] = blk[Y::P + (kb * 16 + 4 * g + s) * C + row];
+            } else {
+                const float4 t = ld4(blk + Y::M + row * C + kb * 16 + 4 * g);
+                const float4 bc = ld4(blk + Y::BETA + kb * 16 + 4 * g);
+                fb[4 * kb] = t.x * bc.x; fb[4 * kb + 1] = t.y * bc.y; fb[4 * kb + 2] = t.z * bc.z; fb[4 * kb + 3] = t.w * bc.w;
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) fc[4 * kb + s] = br * mc[(kb * 16 + 4 * g + s) * C];
         }
     }
     for (int e = tid; e < DK; e += NT) aG[e] = 0.f;
@@ -558,8 +565,12 @@ __global__ void __launch_bounds__(CB_GRAD_NT) cb_grad_kernel(CbParams p) {
     }
     for (int e = tid; e < C * C / 4; e += NT) {
         const int r = e / (C / 4), a4 = 4 * (e % (C / 4));
-        *reinterpret_cast<float4 *>(sM + r * LM + a4) = ld4(blk + Y::M + r * C + a4);
-        *reinterpret_cast<float4 *>(sMT + r * LM + a4) = ld4(blk + Y::MT + r * C + a4);
+        const float4 t = ld4(blk + Y::M + r * C + a4);
+        *reinterpret_cast<float4 *>(sM + r * LM + a4) = t;
+        sMT[a4 * LM + r] = t.x;
+        sMT[(a4 + 1) * LM + r] = t.y;
+        sMT[(a4 + 2) * LM + r] = t.z;
+        sMT[(a4 + 3) * LM + r] = t.w;
     }
     for (int e = tid; e < C; e += NT) sB[e] = blk[Y::BETA + e];
     lds_barrier();

@@ -16,7 +16,8 @@ constexpr int CB_C = 64;  // maximum chunk length
 // its midpoint while it decays by at most this many nats in every channel
 constexpr float kCbDiagSpan = 80.f;
 
-// per-(chunk, head) block of the prep kernel, fp32, row-major
+// per-(chunk, head) block of the prep kernel, fp32, row-major; consumers
+// that need P^T or M^T read P or M with the indices swapped
 template <int DK>
 struct CbLay {
     static constexpr size_t G = 0;                       // [C][DK]  cumulative log decay
@@ -26,10 +27,8 @@ struct CbLay {
     static constexpr size_t W = KB + CB_C * DK;          // [C][DK]  T K~
     static constexpr size_t GH = W + CB_C * DK;          // [C][C]   k_r . k_i e^{..}, i < r
     static constexpr size_t P = GH + CB_C * CB_C;        // [C][C]   q_r . k_i e^{..}, i <= r
-    static constexpr size_t PT = P + CB_C * CB_C;        // [C][C]   P^T
-    static constexpr size_t M = PT + CB_C * CB_C;        // [C][C]   (I + A)^-1
-    static constexpr size_t MT = M + CB_C * CB_C;        // [C][C]   M^T
-    static constexpr size_t GAM = MT + CB_C * CB_C;      // [DK]     e^{G_L}
+    static constexpr size_t M = P + CB_C * CB_C;         // [C][C]   (I + A)^-1
+    static constexpr size_t GAM = M + CB_C * CB_C;       // [DK]     e^{G_L}
     static constexpr size_t BETA = GAM + DK;             // [C]
     static constexpr size_t FLOATS = (BETA + CB_C + 63) / 64 * 64;
 };

@@ -195,10 +195,7 @@ __device__ __forceinline__ void cb_prep_run(const CbParams &p, int x, int h) {
                 const bool in = r < L && i <= r;
                 const float ghv = (in && i < r) ? gh[u] : 0.f, pv = in ? pp[u] : 0.f;
                 blk[Y::P + r * CB_C + i] = pv;
-                if (!FWD) {
-                    blk[Y::GH + r * CB_C + i] = ghv;
-                    blk[Y::PT + i * CB_C + r] = pv;
-                }
+                if (!FWD) blk[Y::GH + r * CB_C + i] = ghv;
                 av[t][u] = ghv * sb[r];
             }
         };
@@ -278,10 +275,7 @@ __device__ __forceinline__ void cb_prep_run(const CbParams &p, int x, int h) {
         if (i / 16 > r / 16) {
             sA[r][i] = 0.f;
             blk[Y::P + e] = 0.f;
-            if (!FWD) {
-                blk[Y::GH + e] = 0.f;
-                blk[Y::PT + i * CB_C + r] = 0.f;
-            }
+            if (!FWD) blk[Y::GH + e] = 0.f;
         }
     }
     __syncthreads();
@@ -312,10 +306,7 @@ __device__ __forceinline__ void cb_prep_run(const CbParams &p, int x, int h) {
         return;
     }
     __syncthreads();
-    for (int e = tid; e < CB_C * CB_C; e += 256) {
-        blk[Y::M + e] = sA[e / CB_C][e % CB_C];
-        blk[Y::MT + e] = sA[e % CB_C][e / CB_C];
-    }
+    for (int e = tid; e < CB_C * CB_C; e += 256) blk[Y::M + e] = sA[e / CB_C][e % CB_C];
     // W = T K~ = M Diag(beta) K~ on the fp32 matrix cores: 16 x 16 output
     // blocks (token block rb, key block cb) dealt round-robin to the four
     // waves, the contraction over the token blocks ib <= rb (M is lower

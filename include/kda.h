@@ -148,7 +148,7 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  * must be 16-byte aligned there, else KDA_ERR_UNSUPPORTED); every other
  * case (fp32 inputs for the 1e-5 contract, other
  * bf16 head sizes) runs on the fp32 matrix cores, with a workspace of about
- * 240 KB (d_k = 128) per (chunk, head) whatever the chunk size
+ * 209 KB (d_k = 128) per (chunk, head) whatever the chunk size
  * (chunk_size 16 only while that stays within 4 GiB); larger chunk-16 calls
  * run in fp32 on the vector ALUs.
  *

@@ -112,10 +112,10 @@ def test_fp32_long_sequence_on_fp32_matrix_cores(chunk):
     assert max(e.values()) <= TOL["f32"]
 
 
-@pytest.mark.parametrize("T,H,d", [(32768, 16, 128), (16384, 48, 16)])
+@pytest.mark.parametrize("T,H,d", [(32768, 16, 128), (16384, 64, 16)])
 def test_fp32_chunk16_beyond_the_block_budget_uses_the_vector_path(T, H, d):
     """A chunk-16 fp32 call whose 64-row chunk blocks would exceed 4 GiB
-    (T/16 x H blocks of 240 KB at d = 128, 103 KB at d = 16) runs on the
+    (T/16 x H blocks of 209 KB at d = 128, 69 KB at d = 16) runs on the
     vector-ALU kernel: the workspace query shows no blocks, and the result
     meets the contract on every head."""
     x = synth.make_uniform(33, 1, T, H, d, d, "f32", chunk=16, state_std=0.1)
