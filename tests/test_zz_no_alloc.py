@@ -2,7 +2,7 @@
 ABI) against the workspace entry point (kda_prefill_chunked) on the same
 inputs: two calls in a row on the shared per-GPU scratch, the second smaller
 than the first (so the second finds the first call's contents there), then a
-third on the fp32 path; outputs and final states must be identical (same
+third on the fp32 path and a fourth on its overlapped launch; outputs and final states must be identical (same
 kernels, same scratch layout) and within the contract of the fp64 oracle.
 A call beyond the scratch is refused before it writes anything."""
 import pytest
@@ -51,6 +51,13 @@ def test_noalloc_matches_the_workspace_entry_point_on_consecutive_calls():
     o, S, o_ref, S_ref = _both(x3, 32)
     assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
     _oracle_check(x3, o, S, "noalloc fp32 (third call)")
+    # 4: fp32 inputs, d = 128, one sequence with 4 heads: the overlapped fp32
+    #    launch, whose flags live in the same scratch after the first three
+    #    calls' contents (cleared by the call's own chunk-table kernel)
+    x4 = synth.make_uniform(74, 1, 1000, 4, 128, 128, "f32", chunk=64, state_std=0.1)
+    o, S, o_ref, S_ref = _both(x4, 64)
+    assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
+    _oracle_check(x4, o, S, "noalloc fp32 overlapped launch (fourth call)")
 
 
 def test_noalloc_refuses_a_call_beyond_its_scratch():
