@@ -86,7 +86,9 @@ struct F32ScanOps {
 // Wave w computes token block w of X, Delta and O and owns key blocks
 // w, w + 4 of the state (accumulator layout, for the whole sequence).  S, X
 // and Delta pass between the waves through LDS transposed ([column][row]),
-// so a lane's four contraction values are one 16-byte read.  WAIT (the
+// so a lane's four contraction values are one 16-byte read.  Inside the
+// walk the waves meet at LDS-only barriers: __syncthreads() would also wait
+// for the next chunk's operand loads and drain the prefetch.  WAIT (the
 // overlapped launch, one sequence): a block's first load waits until its
 // flag is set.
 template <int DK, typename TI, typename TO, bool WAIT>
@@ -171,7 +173,7 @@ __device__ __forceinline__ void f32mm_scan_run(const PrefillParams &p, const flo
         if (live) *reinterpret_cast<f32x4 *>(&xT[n][r0 + 4 * g]) = xv;
         if (WAIT) rv.ensure(nx, p);
         op.load1(blk_of(nx), v, t0_of(nx), len_of(nx), H, h, dv, j0, w, g, n);
-        __syncthreads();
+        lds_barrier();
         // (2) token block w: Delta = M Diag(beta) X (M lower triangular)
         f32x4 da = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -180,7 +182,7 @@ __device__ __forceinline__ void f32mm_scan_run(const PrefillParams &p, const flo
             da = mmf32(op.mb[ib], *reinterpret_cast<const f32x4 *>(&xT[n][16 * ib + 4 * g]), da);
         }
         if (live) *reinterpret_cast<f32x4 *>(&dT[n][r0 + 4 * g]) = da;
-        __syncthreads();
+        lds_barrier();
         // (3) token block w: O = (q e^G) S + P Delta (P lower triangular)
 #pragma unroll
         for (int ib = 0; ib < C / 16; ++ib) {
@@ -209,7 +211,7 @@ __device__ __forceinline__ void f32mm_scan_run(const PrefillParams &p, const flo
             *reinterpret_cast<f32x4 *>(&sT[n][16 * kb + 4 * g]) = acc;
         }
         op.load4(blk_of(nx), w, g, n);
-        __syncthreads();
+        lds_barrier();
     }
     if (p.final_state)
 #pragma unroll
