@@ -33,4 +33,15 @@ struct CbLay {
     static constexpr size_t FLOATS = (BETA + CB_C + 63) / 64 * 64;
 };
 
+// Blocks of the chunk prep in forward mode (read only by the forward fp32
+// scan) hold K~, Q~ and M in the register order of the scan's
+// v_mfma_f32_16x16x4f32 A operands, so that each wave reads a 16 x 16
+// fragment as one contiguous 1 KB (16 bytes per lane); the other parts stay
+// row-major.  Element (r, c) of a row-major matrix with ncb 16-column blocks
+// sits in fragment (r / 16, c / 16), lane 16 ((c % 16) / 4) + r % 16, slot
+// c % 4.
+__host__ __device__ constexpr int frag_a(int r, int c, int ncb) {
+    return (((r >> 4) * ncb + (c >> 4)) * 64 + 16 * ((c & 15) >> 2) + (r & 15)) * 4 + (c & 3);
+}
+
 }  // namespace kda

@@ -149,7 +149,8 @@ __device__ __forceinline__ void cb_prep_run(const CbParams &p, int x, int h) {
     }
     __syncthreads();
     // elementwise factors and the decay of the whole chunk, four
-    // consecutive channels per thread (16-byte stores)
+    // consecutive channels per thread (16-byte stores; in forward mode K~
+    // and Q~ go to their fragment-order slots, frag_a)
     for (int e4 = tid; e4 < CB_C * DK / 4; e4 += 256) {
         const int e = 4 * e4, r = e / DK, c0 = e % DK;
         f32x4 gv, kt, qt, kb;
@@ -163,8 +164,8 @@ __device__ __forceinline__ void cb_prep_run(const CbParams &p, int x, int h) {
             kb[j] = ldk(r, c0 + j) * ex(sG[CB_C - 1][c0 + j] - G);
         }
         if (!FWD) *reinterpret_cast<f32x4 *>(blk + Y::G + e) = gv;
-        *reinterpret_cast<f32x4 *>(blk + Y::KT + e) = kt;
-        *reinterpret_cast<f32x4 *>(blk + Y::QT + e) = qt;
+        *reinterpret_cast<f32x4 *>(blk + Y::KT + (FWD ? frag_a(r, c0, DK / 16) : e)) = kt;
+        *reinterpret_cast<f32x4 *>(blk + Y::QT + (FWD ? frag_a(r, c0, DK / 16) : e)) = qt;
         *reinterpret_cast<f32x4 *>(blk + Y::KB + e) = kb;
     }
     for (int c = tid; c < DK; c += 256) blk[Y::GAM + c] = ex(sG[CB_C - 1][c]);
@@ -302,7 +303,15 @@ __device__ __forceinline__ void cb_prep_run(const CbParams &p, int x, int h) {
     }
     if (FWD) {
         __syncthreads();
-        for (int e = tid; e < CB_C * CB_C; e += 256) blk[Y::M + e] = sA[e / CB_C][e % CB_C];
+        // in fragment order, walking the destination (16-byte stores):
+        // slot d4 of fragment (R, B) holds row 16R + lane % 16, columns
+        // 16B + 4 (lane / 16) .. + 3
+        for (int d4 = tid; d4 < CB_C * CB_C / 4; d4 += 256) {
+            const int fr = d4 / 64, lane = d4 % 64;
+            const int r = 16 * (fr / (CB_C / 16)) + lane % 16, c = 16 * (fr % (CB_C / 16)) + 4 * (lane / 16);
+            const f32x4 mv = {sA[r][c], sA[r][c + 1], sA[r][c + 2], sA[r][c + 3]};
+            *reinterpret_cast<f32x4 *>(blk + Y::M + 4 * d4) = mv;
+        }
         return;
     }
     __syncthreads();

@@ -35,7 +35,11 @@ __device__ __forceinline__ f32x4 mmf32(const f32x4 &a, const f32x4 &b, f32x4 acc
 
 // One wave's operands of one chunk (token block w, key blocks w, w + 4),
 // loaded into registers a chunk ahead: each part is reloaded for the next
-// chunk right after the current chunk's products have used it.
+// chunk right after the current chunk's products have used it.  The forward
+// prep stores K~, Q~ and M in fragment order (frag_a), so each of those
+// loads is one contiguous 1 KB per wave (row-major, a 16-byte-per-lane load
+// touches 16 cache lines); P and K^ stay row-major (their fragment-order
+// stores cost the prep more than they saved here).
 template <int DK, typename TI>
 struct F32ScanOps {
     using Y = CbLay<DK>;
@@ -48,10 +52,11 @@ struct F32ScanOps {
 
     __device__ __forceinline__ void load1(const float *blk, const TI *v, int64_t t0, int L, int H, int h, int dv,
                                           int j0, int w, int g, int n) {
+        const int lane = 16 * g + n;
 #pragma unroll
         for (int cb = 0; cb < NKB; ++cb) {
-            kt[cb] = *reinterpret_cast<const f32x4 *>(blk + Y::KT + (16 * w + n) * DK + 16 * cb + 4 * g);
-            qt[cb] = *reinterpret_cast<const f32x4 *>(blk + Y::QT + (16 * w + n) * DK + 16 * cb + 4 * g);
+            kt[cb] = *reinterpret_cast<const f32x4 *>(blk + Y::KT + ((w * NKB + cb) * 64 + lane) * 4);
+            qt[cb] = *reinterpret_cast<const f32x4 *>(blk + Y::QT + ((w * NKB + cb) * 64 + lane) * 4);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -60,10 +65,11 @@ struct F32ScanOps {
         }
     }
     __device__ __forceinline__ void load23(const float *blk, int w, int g, int n) {
+        const int lane = 16 * g + n;
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib) {
             if (ib > w) continue;
-            const f32x4 m4 = *reinterpret_cast<const f32x4 *>(blk + Y::M + (16 * w + n) * CB_C + 16 * ib + 4 * g);
+            const f32x4 m4 = *reinterpret_cast<const f32x4 *>(blk + Y::M + ((w * 4 + ib) * 64 + lane) * 4);
             mb[ib] = m4 * *reinterpret_cast<const f32x4 *>(blk + Y::BETA + 16 * ib + 4 * g);
             pb[ib] = *reinterpret_cast<const f32x4 *>(blk + Y::P + (16 * w + n) * CB_C + 16 * ib + 4 * g);
         }
