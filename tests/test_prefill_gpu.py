@@ -294,14 +294,16 @@ def test_mfma_packed_equals_separate_and_is_deterministic():
 
 
 @pytest.mark.parametrize("seed,ndocs,H,odt", [(22, 16, 4, torch.float32), (23, 32, 4, torch.float32),
-                                               (24, 40, 4, torch.bfloat16)])
+                                               (24, 40, 4, torch.bfloat16), (25, 17, 5, torch.float32),
+                                               (26, 41, 7, torch.float32)])
 def test_mfma_wide_scan_tiles_equal_one_tile(seed, ndocs, H, odt):
     """With many (sequence, head) pairs the scan gives each workgroup 2
-    (64 pairs) or 4 (128 or more) column tiles of a head, loading the
+    (64 to 127 pairs) or 4 (128 or more) column tiles of a head, loading the
     block's shared operands once for them; each tile's arithmetic is that of
     a one-tile workgroup, which one call per document uses (a single
-    sequence with 4 heads).  Outputs, final states and every chunk-entry
-    state must be bitwise equal."""
+    sequence with a few heads).  Outputs, final states and every chunk-entry
+    state must be bitwise equal.  85 and 287 pairs (H = 5, 7) leave the
+    last group of 8 pairs partly empty."""
     g = np.random.default_rng(seed)
     lens = [int(n) for n in g.integers(1, 300, ndocs)]
     lens[0], lens[1] = 0, 64
